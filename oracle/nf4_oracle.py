@@ -1,0 +1,312 @@
+"""CPU oracle for the NF4 weight path -- TEST INFRASTRUCTURE ONLY.
+
+Plain, slow, obviously correct numpy code that states what the NF4 path
+computes.  Only the tests, the smoke check and the CPU-baseline leg of the
+benchmark may import it; the product path (the HIP library and its Python
+binding) never does, and the two share no code, tables or constants.
+
+Sources (web pages, cited by title and section):
+  [TOOL]  "bitsandbytes" (ozercemkelahmet.com/tools/bitsandbytes):
+          "How it works" Steps 1-5, "How NF4 works", "Double quantization",
+          "A worked example", "Memory arithmetic".
+  [TUT]   "bitsandbytes quantization tutorial: 4-bit and 8-bit models"
+          (mljourney.com): "4-bit Loading with NF4", "How NF4 Works",
+          "Memory Requirements at Different Precisions".
+
+Readings where the pages leave a step open are marked READING below.
+
+Pins: every function here is pinned by tests/test_oracle_pins.py against
+closed forms, exact rational arithmetic, brute force on tiny inputs, library
+routines, or the pages' worked example.  No function is parity-unpinned.
+"""
+
+from __future__ import annotations
+
+import math
+import statistics
+from fractions import Fraction
+
+import numpy as np
+
+BLOCKSIZE = 64      # [TOOL] "How it works", Step 1: "for example 64 values at a time"
+BLOCKSIZE2 = 256    # second-level block for the quantized scales (READING, see double_quant)
+
+# ------------------------------------------------------------------ code book
+#
+# [TOOL] "How NF4 works": the 16 code values are placed so that each covers an
+# equal share of the bell curve.  [TUT] "How NF4 Works": information-
+# theoretically optimal for normally distributed data.  READING: the
+# asymmetric equal-probability construction introduced with NF4 (the QLoRA
+# paper the tool page names): 8 positive and 7 negative normal quantiles at
+# evenly spaced probabilities between delta and 1/2 (1/2 itself excluded),
+# plus an exact zero, all divided by the quantile at delta so the ends are
+# exactly -1 and +1.  delta = 1 - (1/30 + 1/32)/2 is the mean of the
+# outermost bin-centre probabilities for 15 and 16 equal bins.
+
+DELTA = Fraction(1) - (Fraction(1, 30) + Fraction(1, 32)) / 2
+
+
+def _upper_tail(x: float) -> float:
+    """1 - Phi(x) for the standard normal, from the complementary error function."""
+    return 0.5 * math.erfc(x / math.sqrt(2.0))
+
+
+def inv_phi_bisect(p: Fraction) -> float:
+    """Phi^{-1}(p) for 1/2 < p < 1 by bisection on the upper tail 1 - Phi(x)."""
+    q = float(1 - p)          # tail probability, formed exactly then rounded once
+    lo, hi = 0.0, 16.0
+    for _ in range(2000):
+        mid = 0.5 * (lo + hi)
+        if mid == lo or mid == hi:
+            break
+        if _upper_tail(mid) > q:
+            lo = mid
+        else:
+            hi = mid
+    return 0.5 * (lo + hi)
+
+
+def inv_phi_stdlib(p: Fraction) -> float:
+    """Phi^{-1}(p) from Python's statistics.NormalDist (an independent routine)."""
+    return statistics.NormalDist().inv_cdf(float(p))
+
+
+def level_probabilities():
+    """(positive, negative) probability lists, exact rationals, outermost first."""
+    pos = [DELTA + (Fraction(1, 2) - DELTA) * i / 8 for i in range(8)]
+    neg = [DELTA + (Fraction(1, 2) - DELTA) * j / 7 for j in range(7)]
+    return pos, neg
+
+
+def levels_f64(inv=inv_phi_bisect) -> np.ndarray:
+    """The 16 NF4 levels in float64, ascending (index 0 = -1, 7 = 0, 15 = +1)."""
+    pos_p, neg_p = level_probabilities()
+    top = inv(DELTA)
+    pos = [inv(p) / top for p in pos_p]
+    neg = [-inv(p) / top for p in neg_p]
+    vals = sorted(neg + [0.0] + pos)
+    return np.array(vals, dtype=np.float64)
+
+
+def codebook() -> np.ndarray:
+    """The 16 NF4 levels rounded once to float32, ascending (READING: index order)."""
+    return levels_f64().astype(np.float32)
+
+
+# ------------------------------------------------------- blockwise quantization
+
+def block_absmax(x: np.ndarray, blocksize: int = BLOCKSIZE) -> np.ndarray:
+    """[TOOL] "How it works", Steps 1-2: per block, the largest absolute value.
+
+    The last block covers only the elements that exist (READING)."""
+    x = np.asarray(x, dtype=np.float32).reshape(-1)
+    nb = -(-x.size // blocksize)
+    padded = np.zeros(nb * blocksize, dtype=np.float32)
+    padded[: x.size] = np.abs(x)
+    return padded.reshape(nb, blocksize).max(axis=1)
+
+
+def nearest_code(v: np.ndarray) -> np.ndarray:
+    """[TOOL] "How it works", Step 3: index of the nearest code-book entry.
+
+    READING: an exact tie between two levels goes to the level farther from
+    zero (the only rounding rule the pages state, in "A worked example", rounds
+    away from zero).  Distances are taken in float64: the difference of two
+    float32 numbers whose exponents differ by at most 29 is exact there, and
+    when |v| is too small for that, the zero level wins by a wide margin, so
+    the minimum and any tie are decided exactly."""
+    lv = codebook().astype(np.float64)
+    out = np.empty(v.size, dtype=np.uint8)
+    flat = np.asarray(v, dtype=np.float32).reshape(-1)
+    step = 1 << 18
+    for s in range(0, flat.size, step):
+        vv = flat[s : s + step].astype(np.float64)[:, None]
+        d = np.abs(vv - lv[None, :])
+        dmin = d.min(axis=1, keepdims=True)
+        tied = d == dmin
+        score = np.where(tied, np.abs(lv)[None, :], -1.0)
+        out[s : s + step] = score.argmax(axis=1)
+    return out
+
+
+def normalize(x: np.ndarray, absmax: np.ndarray, blocksize: int = BLOCKSIZE) -> np.ndarray:
+    """[TOOL] "How it works", Step 2: every value divided by its block's absmax.
+
+    READING: one IEEE float32 division x / a (round to nearest even).  Blocks
+    with a = 0 are left at 0."""
+    x = np.asarray(x, dtype=np.float32).reshape(-1)
+    nb = absmax.size
+    padded = np.zeros(nb * blocksize, dtype=np.float32)
+    padded[: x.size] = x
+    blocks = padded.reshape(nb, blocksize)
+    a = np.where(absmax > 0, absmax, np.float32(1.0)).astype(np.float32)
+    with np.errstate(over="raise", divide="raise", invalid="raise", under="ignore"):
+        out = blocks / a[:, None]
+    out[absmax == 0] = 0
+    return out.reshape(-1)[: x.size]
+
+
+def pack(codes: np.ndarray) -> np.ndarray:
+    """[TOOL] "How it works", Step 4: two 4-bit indices share one byte.
+
+    READING: element 2j in the high nibble, element 2j+1 in the low nibble; an
+    odd count is completed with the zero level's index 7."""
+    c = np.asarray(codes, dtype=np.uint8).reshape(-1)
+    if c.size % 2:
+        c = np.concatenate([c, np.array([7], dtype=np.uint8)])
+    return ((c[0::2] << 4) | c[1::2]).astype(np.uint8)
+
+
+def unpack(packed: np.ndarray, n: int) -> np.ndarray:
+    p = np.asarray(packed, dtype=np.uint8).reshape(-1)
+    c = np.empty(2 * p.size, dtype=np.uint8)
+    c[0::2] = p >> 4
+    c[1::2] = p & 0xF
+    return c[:n]
+
+
+def quantize(x: np.ndarray, blocksize: int = BLOCKSIZE):
+    """Steps 1-4: returns (packed uint8 [ceil(n/2)], absmax float32 [ceil(n/64)]).
+
+    Inputs are float32 values (bf16 inputs are passed as their exact float32
+    widening)."""
+    x = np.asarray(x, dtype=np.float32).reshape(-1)
+    absmax = block_absmax(x, blocksize)
+    codes = nearest_code(normalize(x, absmax, blocksize))
+    return pack(codes), absmax
+
+
+# --------------------------------------------------------- double quantization
+#
+# [TOOL] "Double quantization" and [TUT] "4-bit Loading with NF4": the per-block
+# scales are quantized again.  READING: the scales are centred on their mean
+# and quantized to int8 in blocks of 256 with the linear absmax scheme of
+# [TOOL] "A worked example" (scale by 127, round half away from zero; dequantize
+# by dividing by 127 and multiplying by the block's absmax).  [TUT] "How NF4
+# Works" says float8; the int8 reading is the one used here.
+
+def int8_absmax_quantize(v: np.ndarray, blocksize: int):
+    """[TOOL] "A worked example": linear int8 absmax quantization per block.
+
+    t = fl32(fl32(v / s) * 127), q = sign(t) * floor(|t| + 1/2); s = the block's
+    largest |v|; a block with s = 0 gets q = 0.  Returns (q int8, s float32)."""
+    v = np.asarray(v, dtype=np.float32).reshape(-1)
+    nb = -(-v.size // blocksize)
+    padded = np.zeros(nb * blocksize, dtype=np.float32)
+    padded[: v.size] = v
+    blocks = padded.reshape(nb, blocksize)
+    s = np.abs(blocks).max(axis=1).astype(np.float32)
+    safe = np.where(s > 0, s, np.float32(1.0)).astype(np.float32)
+    with np.errstate(under="ignore"):
+        t = (blocks / safe[:, None]).astype(np.float32) * np.float32(127.0)
+    t = t.astype(np.float32)
+    t64 = t.astype(np.float64)                      # exact widening
+    q = np.sign(t64) * np.floor(np.abs(t64) + 0.5)  # exact: |t| <= 127
+    q = np.clip(q, -127, 127)
+    q[s == 0] = 0
+    return q.reshape(-1)[: v.size].astype(np.int8), s
+
+
+def exact_mean_f32(a: np.ndarray) -> np.float32:
+    """Mean of the scales: the exact sum rounded once to float64 (math.fsum),
+    divided by the count in float64, rounded to float32 (READING)."""
+    a = np.asarray(a, dtype=np.float32).reshape(-1)
+    total = math.fsum(a.astype(np.float64).tolist())
+    return np.float32(total / a.size)
+
+
+def double_quant(absmax: np.ndarray, blocksize2: int = BLOCKSIZE2):
+    """Returns (qabsmax int8 [nb], absmax2 float32 [ceil(nb/256)], mean float32)."""
+    a = np.asarray(absmax, dtype=np.float32).reshape(-1)
+    mean = exact_mean_f32(a)
+    centred = (a - mean).astype(np.float32)
+    q, s2 = int8_absmax_quantize(centred, blocksize2)
+    return q, s2, mean
+
+
+def dequant_scales(q: np.ndarray, absmax2: np.ndarray, mean, blocksize2: int = BLOCKSIZE2) -> np.ndarray:
+    """a_hat = fl32(fl32(fl32(q / 127) * s2) + mean): [TOOL] "A worked example"
+    (divide by 127, multiply by the scale) followed by adding the mean back."""
+    q = np.asarray(q, dtype=np.int8).reshape(-1)
+    s2 = np.asarray(absmax2, dtype=np.float32).reshape(-1)
+    g = np.arange(q.size) // blocksize2
+    t = (q.astype(np.float32) / np.float32(127.0)).astype(np.float32)
+    t = (t * s2[g]).astype(np.float32)
+    return (t + np.float32(mean)).astype(np.float32)
+
+
+# ------------------------------------------------------------- dequantization
+
+def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
+    """Round-to-nearest-even float32 -> bfloat16 bit patterns (finite inputs)."""
+    u = np.asarray(x, dtype=np.float32).view(np.uint32).astype(np.uint64)
+    bias = ((u >> 16) & 1) + 0x7FFF
+    return ((u + bias) >> 16).astype(np.uint16)
+
+
+def bf16_bits_to_f32(b: np.ndarray) -> np.ndarray:
+    return (np.asarray(b, dtype=np.uint16).astype(np.uint32) << 16).view(np.float32)
+
+
+def dequantize(packed, n: int, absmax=None, qabsmax=None, absmax2=None, mean=None,
+               blocksize: int = BLOCKSIZE, blocksize2: int = BLOCKSIZE2, out: str = "f32"):
+    """[TOOL] "How it works", Step 5: expand each code with its block's scale.
+
+    w = fl32(level[code] * a_hat); for out="bf16" the float32 value is rounded
+    once to nearest even and the bf16 bit patterns (uint16) are returned."""
+    codes = unpack(packed, n)
+    lv = codebook()
+    if absmax is not None:
+        a_hat = np.asarray(absmax, dtype=np.float32).reshape(-1)
+    else:
+        a_hat = dequant_scales(qabsmax, absmax2, mean, blocksize2)
+    blk = np.arange(n) // blocksize
+    w = (lv[codes] * a_hat[blk]).astype(np.float32)
+    if out == "f32":
+        return w
+    if out == "bf16":
+        return f32_to_bf16_bits(w)
+    raise ValueError(out)
+
+
+# -------------------------------------------------------------- matmul reference
+
+def matmul_ref(x: np.ndarray, w_deq: np.ndarray, lora_a=None, lora_b=None, lora_scale: float = 0.0):
+    """Y = X . W^T (+ s . (X . A^T) . B^T), all in float64.
+
+    x: [M, K] values, w_deq: [N, K] dequantized weights, lora_a: [r, K],
+    lora_b: [N, r].  [TOOL] "How it works", Step 5 (dequantize then multiply);
+    [TUT] "QLoRA: Fine-Tuning a 4-bit Model" (adapters on the frozen base, the
+    adapter output multiplied by a scale factor)."""
+    x64 = np.asarray(x, dtype=np.float64)
+    w64 = np.asarray(w_deq, dtype=np.float64)
+    y = x64 @ w64.T
+    if lora_a is not None:
+        t = x64 @ np.asarray(lora_a, dtype=np.float64).T
+        y = y + float(lora_scale) * (t @ np.asarray(lora_b, dtype=np.float64).T)
+    return y
+
+
+def rel_frobenius(y, y_ref) -> float:
+    y = np.asarray(y, dtype=np.float64)
+    y_ref = np.asarray(y_ref, dtype=np.float64)
+    den = np.linalg.norm(y_ref)
+    return float(np.linalg.norm(y - y_ref) / den) if den > 0 else float(np.linalg.norm(y))
+
+
+# ------------------------------------------------------------ storage footprint
+
+def storage_bytes(n: int, double_quant: bool, blocksize: int = BLOCKSIZE, blocksize2: int = BLOCKSIZE2) -> dict:
+    """Bytes of each stored array for n weights ([TOOL] "How it works", Step 4:
+    packed indices with the scales stored beside them)."""
+    nb = -(-n // blocksize)
+    out = {"packed": -(-n // 2)}
+    if double_quant:
+        out.update(qabsmax=nb, absmax2=4 * (-(-nb // blocksize2)), mean=4)
+    else:
+        out.update(absmax=4 * nb)
+    return out
+
+
+def bits_per_param(n: int, double_quant: bool) -> float:
+    return 8.0 * sum(storage_bytes(n, double_quant).values()) / n
