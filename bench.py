@@ -1,0 +1,304 @@
+"""Benchmark of the NF4 hot path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--pool P]
+
+Workload: the Llama-8B attention projection (4096 x 4096 bf16 weight ~ N(0,
+0.02) with 0.1 % of entries scaled by 20; batch-1 decode with x bf16 ~ N(0,1)).
+One step is one pass of the whole path over a pool of P such weights: for each
+weight, nf4_quantize -> nf4_double_quant -> nf4_gemv.  The pool (P = 16 by
+default, 512 MiB of bf16) is larger than the 256 MiB Infinity Cache, so every
+step streams its inputs from HBM.  `value` is the algorithmic bytes of the
+whole step (bf16 weights read, codes and scales written and read back, x read,
+y written) divided by the step time.
+
+Extra legs (not part of `value`): the GEMV alone over a pool of distinct
+quantized weights (decode from HBM), and the dequant-into-LDS GEMM of the
+QLoRA forward workload (X [4096, 4096] x NF4 W [14336, 4096] + LoRA r = 16).
+`cpu_baseline` times the CPU oracle on one weight of the same workload.
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import platform
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "NF4 dequant-GEMV GB/s (% HBM peak); NF4 GEMM bf16 TFLOP/s (% MFMA peak)"
+HBM_PEAK_GBS = 8000.0
+MFMA_BF16_PEAK_TFLOPS = 2500.0
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=100)
+    p.add_argument("--warmup", type=int, default=10)
+    p.add_argument("--pool", type=int, default=16)
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-extra", action="store_true")
+    return p.parse_args()
+
+
+def step_bytes(rows: int, cols: int, m: int = 1) -> dict:
+    """Algorithmic bytes of quantize, double quant and GEMV for one weight."""
+    n = rows * cols
+    nb = n // 64
+    ng = -(-nb // 256)
+    quant = 2 * n + n // 2 + 4 * nb
+    dq = 4 * nb + nb + 4 * ng + 4
+    gemv = n // 2 + nb + 4 * ng + 4 + 2 * m * cols + 2 * m * rows
+    return {"quantize": quant, "double_quant": dq, "gemv": gemv}
+
+
+class EventTimer:
+    """HIP events recorded on the stream the kernels run on."""
+
+    def __init__(self, torch, stream):
+        self.torch, self.stream, self.pairs = torch, stream, []
+
+    def start(self):
+        e = self.torch.cuda.Event(enable_timing=True)
+        e.record(self.stream)
+        return e
+
+    def stop(self, s):
+        e = self.torch.cuda.Event(enable_timing=True)
+        e.record(self.stream)
+        self.pairs.append((s, e))
+
+    def mean_us(self):
+        return 1e3 * sum(a.elapsed_time(b) for a, b in self.pairs) / max(1, len(self.pairs))
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; use --gpus 1"}))
+        print("bench.py: only --gpus 1 is supported (single-GPU build)", file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+
+    import dequant_matmul_nf4_amd as nf4
+    import synthetic as syn
+
+    nf4.lib()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream()
+    rows = cols = 4096
+    P = args.pool
+
+    print(f"[bench] generating {P} weights 4096x4096 bf16", file=sys.stderr, flush=True)
+    ws = [syn.c2_weight(pool_index=i).to(dev) for i in range(P)]
+    x = syn.c2_inputs()["x"].to(dev)
+    n = rows * cols
+    nb = n // 64
+    bufs = []
+    for _ in range(P):
+        bufs.append(dict(
+            packed=torch.empty(n // 2, dtype=torch.uint8, device=dev),
+            absmax=torch.empty(nb, dtype=torch.float32, device=dev),
+            q=torch.empty(nb, dtype=torch.int8, device=dev),
+            s2=torch.empty(-(-nb // 256), dtype=torch.float32, device=dev),
+            mean=torch.empty(1, dtype=torch.float32, device=dev),
+            y=torch.empty((1, rows), dtype=torch.bfloat16, device=dev),
+        ))
+    dq_ws = torch.empty(nf4.nf4_double_quant_workspace(nb), dtype=torch.uint8, device=dev)
+    tq = EventTimer(torch, stream)
+    tg = EventTimer(torch, stream)
+
+    def one_step(timed: bool):
+        for i in range(P):
+            b = bufs[i]
+            s = tq.start() if timed else None
+            nf4.nf4_quantize(ws[i], b["packed"], b["absmax"])
+            if timed:
+                tq.stop(s)
+            nf4.nf4_double_quant(b["absmax"], b["q"], b["s2"], b["mean"], dq_ws)
+            W = nf4.NF4Weight(b["packed"], rows, cols, qabsmax=b["q"], absmax2=b["s2"], mean=b["mean"])
+            s = tg.start() if timed else None
+            nf4.nf4_gemv(W, x, b["y"])
+            if timed:
+                tg.stop(s)
+
+    print("[bench] warmup", file=sys.stderr, flush=True)
+    for _ in range(args.warmup):
+        one_step(False)
+    torch.cuda.synchronize()
+    print(f"[bench] timing {args.steps} steps", file=sys.stderr, flush=True)
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        one_step(True)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    sb = step_bytes(rows, cols)
+    bytes_per_step = P * sum(sb.values())
+    value = bytes_per_step * args.steps / elapsed / 1e9
+    q_us = tq.mean_us()
+    g_us = tg.mean_us()
+    q_gbs = sb["quantize"] / (q_us * 1e-6) / 1e9
+    g_gbs_hot = sb["gemv"] / (g_us * 1e-6) / 1e9
+
+    out = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(1e3 * elapsed / args.steps, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {
+            "workload": "Llama-8B attention projection 4096x4096 bf16, N(0,0.02) + 0.1% outliers x20; "
+                        "NF4 blocksize 64 + double quant (int8, groups of 256); batch-1 decode GEMV",
+            "pool_weights": P,
+            "step": "per weight: nf4_quantize + nf4_double_quant + nf4_gemv",
+            "bytes_per_step": bytes_per_step,
+        },
+        "roofline": {
+            "kernel": "k_quantize<bf16>",
+            "bound": "hbm",
+            "achieved": round(q_gbs, 1),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(q_gbs / HBM_PEAK_GBS, 4),
+            "traffic": None,
+            "bytes_per_launch": sb["quantize"],
+            "avg_launch_us": round(q_us, 3),
+        },
+        "kernels_in_step": {
+            "quantize_us": round(q_us, 3),
+            "gemv_us": round(g_us, 3),
+            "gemv_GBps_after_quantize": round(g_gbs_hot, 1),
+        },
+    }
+
+    if not args.no_extra:
+        out.update(extra_legs(torch, nf4, syn, dev, stream, EventTimer))
+
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(np, syn)
+
+    out["host"] = {"cpu": platform.processor() or platform.machine(), "gpu": torch.cuda.get_device_name(dev),
+                   "hip": torch.version.hip}
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+def extra_legs(torch, nf4, syn, dev, stream, EventTimer):
+    """GEMV alone from HBM (decode), and the QLoRA forward GEMM."""
+    res = {}
+    rows = cols = 4096
+    print("[bench] gemv-only leg", file=sys.stderr, flush=True)
+    pool = 64
+    g = torch.Generator(device=dev)
+    Ws = []
+    for i in range(pool):
+        g.manual_seed(7_000 + i)
+        w = (torch.randn((rows, cols), generator=g, device=dev) * 0.02).to(torch.bfloat16)
+        Ws.append(nf4.quantize_weight(w, double_quant=True))
+        del w
+    x = syn.c2_inputs()["x"].to(dev)
+    y = torch.empty((1, rows), dtype=torch.bfloat16, device=dev)
+    for W in Ws[:8]:
+        nf4.nf4_gemv(W, x, y)
+    torch.cuda.synchronize()
+    t = EventTimer(torch, stream)
+    s = t.start()
+    reps = 20
+    for _ in range(reps):
+        for W in Ws:
+            nf4.nf4_gemv(W, x, y)
+    t.stop(s)
+    torch.cuda.synchronize()
+    per_call_us = t.mean_us() / (reps * pool)
+    gb = step_bytes(rows, cols)["gemv"]
+    res["gemv_decode_hbm"] = {
+        "workload": "4096x4096 NF4+DQ, M=1, pool of 64 distinct weights (557 MB)",
+        "per_call_us": round(per_call_us, 3),
+        "GBps": round(gb / (per_call_us * 1e-6) / 1e9, 1),
+        "frac_hbm_peak": round(gb / (per_call_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+    }
+    del Ws
+
+    print("[bench] gemm leg", file=sys.stderr, flush=True)
+    M, N, K, r = 4096, 14336, 4096, 16
+    g.manual_seed(4_005)
+    X = torch.randn((M, K), generator=g, device=dev).to(torch.bfloat16)
+    g.manual_seed(4_000)
+    W = nf4.quantize_weight((torch.randn((N, K), generator=g, device=dev) * 0.02).to(torch.bfloat16))
+    g.manual_seed(4_006)
+    A = (torch.randn((r, K), generator=g, device=dev) * 0.01).to(torch.bfloat16)
+    g.manual_seed(4_007)
+    B = (torch.randn((N, r), generator=g, device=dev) * 0.01).to(torch.bfloat16)
+    Y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+    wsb = torch.empty(nf4.nf4_gemm_workspace(M, N, r), dtype=torch.uint8, device=dev)
+    for _ in range(3):
+        nf4.nf4_gemm(W, X, Y, A, B, 2.0, wsb)
+    torch.cuda.synchronize()
+    t = EventTimer(torch, stream)
+    reps = 10
+    for _ in range(reps):
+        s = t.start()
+        nf4.nf4_gemm(W, X, Y, A, B, 2.0, wsb)
+        t.stop(s)
+    torch.cuda.synchronize()
+    us = t.mean_us()
+    flops = 2.0 * M * N * K + 2.0 * M * K * r + 2.0 * M * r * N
+    tf = flops / (us * 1e-6) / 1e12
+    res["gemm_qlora_forward"] = {
+        "workload": "X 4096x4096 bf16 . NF4(DQ) W 14336x4096^T + LoRA r=16 alpha=32",
+        "us": round(us, 1),
+        "TFLOPs": round(tf, 1),
+        "frac_mfma_bf16_peak": round(tf / MFMA_BF16_PEAK_TFLOPS, 4),
+    }
+    return res
+
+
+def cpu_baseline(np, syn):
+    """The CPU oracle (as it stands) on one weight of the same workload:
+    quantize, double quant, dequantize and the float64 GEMV, single-threaded."""
+    import oracle
+    try:
+        from threadpoolctl import threadpool_limits
+    except ImportError:  # pragma: no cover
+        threadpool_limits = None
+    print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
+    rows = cols = 4096
+    w = syn.bf16_to_f32(syn.c2_weight()).reshape(-1)
+    x = syn.bf16_to_f32(syn.c2_inputs()["x"])
+    import contextlib
+    ctx = threadpool_limits(1) if threadpool_limits else contextlib.nullcontext()
+    with ctx:
+        t0 = time.perf_counter()
+        p, a = oracle.quantize(w)
+        q, s2, mu = oracle.double_quant(a)
+        wdeq = oracle.bf16_bits_to_f32(oracle.dequantize(p, w.size, qabsmax=q, absmax2=s2, mean=mu, out="bf16"))
+        oracle.matmul_ref(x, wdeq.reshape(rows, cols))
+        dt = time.perf_counter() - t0
+    sb = step_bytes(rows, cols)
+    return {
+        "value": round(sum(sb.values()) / dt / 1e9, 4),
+        "unit": "GB/s",
+        "cores": 1,
+        "kind": "oracle",
+        "sample": "one 4096x4096 weight of the workload: quantize + double quant + dequant + float64 GEMV",
+        "seconds": round(dt, 2),
+    }
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,207 @@
+// C-ABI front end: argument checks, device check and dispatch to the kernels.
+// Every check runs on the host before any HIP call, so a rejected call
+// touches no device state.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <mutex>
+
+#include "nf4.h"
+#include "nf4_internal.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+int fail(int code, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof g_err, fmt, ap);
+  va_end(ap);
+  return code;
+}
+
+int ok() {
+  g_err[0] = '\0';
+  return NF4_OK;
+}
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+constexpr int64_t kMaxN = int64_t(1) << 40;
+
+// gfx950 check, cached per device id.
+std::mutex g_dev_mu;
+int g_dev_state[64];  // 0 unknown, 1 gfx950, 2 other
+
+int check_device() {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(NF4_ERR_DEVICE, "hipGetDevice failed: %s", hipGetErrorString(e));
+  if (dev < 0 || dev >= 64) return fail(NF4_ERR_DEVICE, "device id %d out of range", dev);
+  std::lock_guard<std::mutex> lk(g_dev_mu);
+  if (g_dev_state[dev] == 0) {
+    hipDeviceProp_t prop;
+    e = hipGetDeviceProperties(&prop, dev);
+    if (e != hipSuccess)
+      return fail(NF4_ERR_DEVICE, "hipGetDeviceProperties failed: %s", hipGetErrorString(e));
+    g_dev_state[dev] = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : 2;
+  }
+  if (g_dev_state[dev] != 1) return fail(NF4_ERR_DEVICE, "device %d is not a gfx950 (MI355X)", dev);
+  return NF4_OK;
+}
+
+int launched(hipError_t e, const char* what) {
+  if (e != hipSuccess) return fail(NF4_ERR_DEVICE, "%s: launch failed: %s", what, hipGetErrorString(e));
+  return ok();
+}
+
+// Validates a weight descriptor; fills `sc` and the element count.
+int check_weight(const nf4_weight* w, nf4i::Scales* sc, int64_t* n_out, const char* who) {
+  if (!w) return fail(NF4_ERR_NULL, "%s: weight descriptor is NULL", who);
+  if (!w->packed) return fail(NF4_ERR_NULL, "%s: weight packed pointer is NULL", who);
+  if (w->blocksize != NF4_BLOCKSIZE)
+    return fail(NF4_ERR_BLOCKSIZE, "%s: blocksize %d unsupported (only 64)", who, (int)w->blocksize);
+  if (w->rows < 1 || w->cols < 1 || w->rows > kMaxN || w->cols > kMaxN || w->rows > kMaxN / w->cols)
+    return fail(NF4_ERR_SIZE, "%s: bad shape %lld x %lld", who, (long long)w->rows, (long long)w->cols);
+  if (!aligned(w->packed, 16)) return fail(NF4_ERR_ALIGN, "%s: packed must be 16-byte aligned", who);
+  const int64_t n = w->rows * w->cols;
+  const int64_t nb = (n + 63) / 64;
+  if (w->absmax) {
+    if (!aligned(w->absmax, 4)) return fail(NF4_ERR_ALIGN, "%s: absmax must be 4-byte aligned", who);
+    *sc = nf4i::Scales{w->absmax, nullptr, nullptr, nullptr};
+  } else {
+    if (!w->qabsmax || !w->absmax2 || !w->mean)
+      return fail(NF4_ERR_NULL, "%s: absmax is NULL, so qabsmax, absmax2 and mean are required", who);
+    if (w->blocksize2 != NF4_BLOCKSIZE2)
+      return fail(NF4_ERR_BLOCKSIZE, "%s: blocksize2 %d unsupported (only 256)", who, (int)w->blocksize2);
+    if (nb >= (int64_t(1) << 31)) return fail(NF4_ERR_SIZE, "%s: too many blocks for double quant", who);
+    if (!aligned(w->absmax2, 4) || !aligned(w->mean, 4))
+      return fail(NF4_ERR_ALIGN, "%s: absmax2 and mean must be 4-byte aligned", who);
+    *sc = nf4i::Scales{nullptr, w->qabsmax, w->absmax2, w->mean};
+  }
+  *n_out = n;
+  return NF4_OK;
+}
+
+hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
+
+}  // namespace
+
+extern "C" {
+
+const char* nf4_last_error(void) { return g_err; }
+
+int nf4_codebook(float out[16]) {
+  if (!out) return fail(NF4_ERR_NULL, "nf4_codebook: out is NULL");
+  std::memcpy(out, nf4i::codebook().level, 16 * sizeof(float));
+  return ok();
+}
+
+int nf4_quantize(const void* x, int x_dtype, int64_t n, int32_t blocksize, uint8_t* packed,
+                 float* absmax, void* stream) {
+  if (!x || !packed || !absmax) return fail(NF4_ERR_NULL, "nf4_quantize: x, packed and absmax are required");
+  if (x_dtype != NF4_F32 && x_dtype != NF4_BF16) return fail(NF4_ERR_DTYPE, "nf4_quantize: x_dtype %d unknown", x_dtype);
+  if (n < 1 || n >= kMaxN) return fail(NF4_ERR_SIZE, "nf4_quantize: n = %lld out of range", (long long)n);
+  if (blocksize != NF4_BLOCKSIZE) return fail(NF4_ERR_BLOCKSIZE, "nf4_quantize: blocksize %d unsupported (only 64)", (int)blocksize);
+  if (!aligned(x, 16) || !aligned(packed, 16)) return fail(NF4_ERR_ALIGN, "nf4_quantize: x and packed must be 16-byte aligned");
+  if (!aligned(absmax, 4)) return fail(NF4_ERR_ALIGN, "nf4_quantize: absmax must be 4-byte aligned");
+  if (int rc = check_device()) return rc;
+  return launched(nf4i::launch_quantize(x, x_dtype == NF4_BF16, n, packed, absmax, as_stream(stream)), "nf4_quantize");
+}
+
+size_t nf4_double_quant_workspace(int64_t nblocks) {
+  (void)nblocks;
+  return nf4i::kDqWorkspaceBytes;
+}
+
+int nf4_double_quant(const float* absmax, int64_t nblocks, int32_t blocksize2, int8_t* qabsmax,
+                     float* absmax2, float* mean, void* workspace, size_t workspace_bytes,
+                     void* stream) {
+  if (!absmax || !qabsmax || !absmax2 || !mean)
+    return fail(NF4_ERR_NULL, "nf4_double_quant: absmax, qabsmax, absmax2 and mean are required");
+  if (nblocks < 1 || nblocks >= (int64_t(1) << 31))
+    return fail(NF4_ERR_SIZE, "nf4_double_quant: nblocks = %lld out of range", (long long)nblocks);
+  if (blocksize2 != NF4_BLOCKSIZE2)
+    return fail(NF4_ERR_BLOCKSIZE, "nf4_double_quant: blocksize2 %d unsupported (only 256)", (int)blocksize2);
+  if (!workspace || workspace_bytes < nf4i::kDqWorkspaceBytes)
+    return fail(NF4_ERR_WORKSPACE, "nf4_double_quant: workspace needs %zu bytes", nf4i::kDqWorkspaceBytes);
+  if (!aligned(absmax, 16) || !aligned(qabsmax, 16) || !aligned(workspace, 16))
+    return fail(NF4_ERR_ALIGN, "nf4_double_quant: absmax, qabsmax and workspace must be 16-byte aligned");
+  if (!aligned(absmax2, 4) || !aligned(mean, 4))
+    return fail(NF4_ERR_ALIGN, "nf4_double_quant: absmax2 and mean must be 4-byte aligned");
+  if (int rc = check_device()) return rc;
+  return launched(nf4i::launch_double_quant(absmax, nblocks, qabsmax, absmax2, mean,
+                                            static_cast<unsigned long long*>(workspace), as_stream(stream)),
+                  "nf4_double_quant");
+}
+
+int nf4_dequantize(const nf4_weight* w, void* out, int out_dtype, void* stream) {
+  nf4i::Scales sc{};
+  int64_t n = 0;
+  if (int rc = check_weight(w, &sc, &n, "nf4_dequantize")) return rc;
+  if (!out) return fail(NF4_ERR_NULL, "nf4_dequantize: out is NULL");
+  if (out_dtype != NF4_F32 && out_dtype != NF4_BF16) return fail(NF4_ERR_DTYPE, "nf4_dequantize: out_dtype %d unknown", out_dtype);
+  if (!aligned(out, 16)) return fail(NF4_ERR_ALIGN, "nf4_dequantize: out must be 16-byte aligned");
+  if (int rc = check_device()) return rc;
+  return launched(nf4i::launch_dequantize(w->packed, n, sc, out, out_dtype == NF4_BF16, as_stream(stream)), "nf4_dequantize");
+}
+
+int nf4_gemv(const nf4_weight* w, const void* x, int64_t m, void* y, int y_dtype, void* stream) {
+  nf4i::Scales sc{};
+  int64_t n = 0;
+  if (int rc = check_weight(w, &sc, &n, "nf4_gemv")) return rc;
+  if (!x || !y) return fail(NF4_ERR_NULL, "nf4_gemv: x and y are required");
+  if (w->cols % 64) return fail(NF4_ERR_SIZE, "nf4_gemv: cols = %lld is not a multiple of 64", (long long)w->cols);
+  if (m < 1 || m > 16) return fail(NF4_ERR_SIZE, "nf4_gemv: m = %lld out of range 1..16", (long long)m);
+  if (y_dtype != NF4_F32 && y_dtype != NF4_BF16) return fail(NF4_ERR_DTYPE, "nf4_gemv: y_dtype %d unknown", y_dtype);
+  if (!aligned(x, 16) || !aligned(y, 16)) return fail(NF4_ERR_ALIGN, "nf4_gemv: x and y must be 16-byte aligned");
+  if (int rc = check_device()) return rc;
+  return launched(nf4i::launch_gemv(w->packed, w->rows, w->cols, sc, static_cast<const uint16_t*>(x), m, y,
+                                    y_dtype == NF4_BF16, as_stream(stream)),
+                  "nf4_gemv");
+}
+
+size_t nf4_gemm_workspace(int64_t m, int64_t rows, int32_t r) {
+  (void)rows;
+  if (m < 1 || r < 1) return 0;
+  const size_t bytes = static_cast<size_t>(m) * static_cast<size_t>(r) * sizeof(float);
+  return (bytes + 255) & ~size_t(255);
+}
+
+int nf4_gemm(const nf4_weight* w, const void* x, int64_t m, void* y, const void* lora_a,
+             const void* lora_b, int32_t r, float lora_scale, void* workspace,
+             size_t workspace_bytes, void* stream) {
+  nf4i::Scales sc{};
+  int64_t n = 0;
+  if (int rc = check_weight(w, &sc, &n, "nf4_gemm")) return rc;
+  if (!x || !y) return fail(NF4_ERR_NULL, "nf4_gemm: x and y are required");
+  if (w->cols % 64) return fail(NF4_ERR_SIZE, "nf4_gemm: cols = %lld is not a multiple of 64", (long long)w->cols);
+  if (m < 1 || m > (int64_t(1) << 31)) return fail(NF4_ERR_SIZE, "nf4_gemm: m = %lld out of range", (long long)m);
+  if ((lora_a == nullptr) != (lora_b == nullptr))
+    return fail(NF4_ERR_NULL, "nf4_gemm: lora_a and lora_b must both be NULL or both be set");
+  if (lora_a) {
+    if (r < 1 || r > 64) return fail(NF4_ERR_SIZE, "nf4_gemm: LoRA rank r = %d out of range 1..64", (int)r);
+    if (!std::isfinite(lora_scale)) return fail(NF4_ERR_SIZE, "nf4_gemm: lora_scale is not finite");
+    if (!aligned(lora_a, 16) || !aligned(lora_b, 16))
+      return fail(NF4_ERR_ALIGN, "nf4_gemm: lora_a and lora_b must be 16-byte aligned");
+    const size_t need = nf4_gemm_workspace(m, w->rows, r);
+    if (!workspace || workspace_bytes < need)
+      return fail(NF4_ERR_WORKSPACE, "nf4_gemm: workspace needs %zu bytes", need);
+    if (!aligned(workspace, 16)) return fail(NF4_ERR_ALIGN, "nf4_gemm: workspace must be 16-byte aligned");
+  } else if (r != 0) {
+    return fail(NF4_ERR_SIZE, "nf4_gemm: r must be 0 without LoRA matrices");
+  }
+  if (!aligned(x, 16) || !aligned(y, 16)) return fail(NF4_ERR_ALIGN, "nf4_gemm: x and y must be 16-byte aligned");
+  if (int rc = check_device()) return rc;
+  return launched(nf4i::launch_gemm(w->packed, w->rows, w->cols, sc, static_cast<const uint16_t*>(x), m,
+                                    static_cast<uint16_t*>(y), static_cast<const uint16_t*>(lora_a),
+                                    static_cast<const uint16_t*>(lora_b), lora_a ? r : 0, lora_scale,
+                                    static_cast<float*>(workspace), as_stream(stream)),
+                  "nf4_gemm");
+}
+
+}  // extern "C"

@@ -1,0 +1,47 @@
+// Device helpers shared by the NF4 kernels (gfx950, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <cstdint>
+
+#include "nf4_internal.h"
+
+namespace nf4i {
+
+constexpr int kWave = 64;
+
+__device__ __forceinline__ float bf16_to_f32(uint32_t bits16) { return __uint_as_float(bits16 << 16); }
+
+// Round-to-nearest-even float32 -> bfloat16 bits (finite inputs).
+__device__ __forceinline__ uint32_t f32_to_bf16(float f) {
+  const uint32_t u = __float_as_uint(f);
+  return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return f32_to_bf16(lo) | (f32_to_bf16(hi) << 16);
+}
+
+// The scale of block b: either the stored fp32 absmax, or the double-quantized
+// form a_hat = fl32(fl32(fl32(q / 127) * s2) + mean), three separate roundings.
+__device__ __forceinline__ float block_scale(const Scales& sc, int64_t b, float mean) {
+  if (sc.absmax) return sc.absmax[b];
+  const float t = static_cast<float>(sc.q[b]) / 127.0f;
+  const float u = t * sc.absmax2[b >> 8];
+  return u + mean;
+}
+
+template <int kWidth>
+__device__ __forceinline__ float group_max(float v) {
+#pragma unroll
+  for (int off = 1; off < kWidth; off <<= 1) v = fmaxf(v, __shfl_xor(v, off, kWave));
+  return v;
+}
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, kWave);
+  return v;
+}
+
+}  // namespace nf4i

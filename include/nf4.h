@@ -1,0 +1,168 @@
+/*
+ * nf4.h -- C ABI of the NF4 (4-bit NormalFloat) weight library for AMD
+ * Instinct MI355X (gfx950).
+ *
+ * What the calls compute is stated on the bitsandbytes tool page
+ * (ozercemkelahmet.com/tools/bitsandbytes), section "How it works", Steps 1-5:
+ * weights are cut into blocks of 64, each block is divided by its largest
+ * absolute value, each value is replaced by the index of the nearest entry of
+ * a 16-entry code book spaced to a bell curve ("How NF4 works"), two indices
+ * are packed per byte with the scales stored beside them, and at run time a
+ * block is expanded back to 16-bit with its scale and multiplied.  The scales
+ * themselves can be quantized again ("Double quantization"; the tutorial page
+ * "bitsandbytes quantization tutorial: 4-bit and 8-bit models", section
+ * "4-bit Loading with NF4").
+ *
+ * Conventions shared by every call
+ * --------------------------------
+ *  - Array arguments are DEVICE pointers unless marked [host].
+ *  - The caller allocates, sizes and owns every buffer.  The library never
+ *    allocates or frees memory, never synchronizes, and keeps no per-call
+ *    state; the only state it keeps is a per-device record of whether the
+ *    device is a gfx950.
+ *  - Every call checks its arguments on the host first.  On failure it
+ *    returns a non-zero nf4_status, launches nothing and writes nothing; the
+ *    reason is available from nf4_last_error().  On success the work is
+ *    enqueued on `stream` (a hipStream_t passed as void*; NULL = the null
+ *    stream of the current device) and the call returns NF4_OK.  Faults inside
+ *    a kernel surface at the caller's next synchronization.
+ *  - Calls are thread-safe.  Calls on different streams may overlap; they
+ *    share nothing except caller-provided buffers.
+ *  - bf16 buffers are passed as void* and hold IEEE bfloat16 bit patterns.
+ *  - Inputs must be finite; results for NaN or infinite inputs are undefined.
+ */
+#ifndef NF4_H
+#define NF4_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum nf4_status {
+  NF4_OK = 0,
+  NF4_ERR_NULL = 1,       /* a required pointer is NULL                           */
+  NF4_ERR_SIZE = 2,       /* a size or count is out of range                      */
+  NF4_ERR_BLOCKSIZE = 3,  /* blocksize != 64 or blocksize2 != 256                 */
+  NF4_ERR_ALIGN = 4,      /* a pointer is not aligned as documented               */
+  NF4_ERR_DTYPE = 5,      /* unknown nf4_dtype, or a dtype the call does not take */
+  NF4_ERR_WORKSPACE = 6,  /* workspace missing or smaller than the *_workspace()  */
+  NF4_ERR_DEVICE = 7      /* the device is not gfx950, or a HIP call failed       */
+} nf4_status;
+
+typedef enum nf4_dtype { NF4_F32 = 0, NF4_BF16 = 1 } nf4_dtype;
+
+#define NF4_BLOCKSIZE 64
+#define NF4_BLOCKSIZE2 256
+
+/* [host] Text describing the last failure on the calling thread ("" if none). */
+const char* nf4_last_error(void);
+
+/* [host] The 16 NF4 levels as float32, ascending: out[0] = -1, out[7] = 0,
+ * out[15] = +1.  Tool page, "How NF4 works": the 16 code values each cover an
+ * equal share of the bell curve.  They are the normal quantiles at 8 (positive
+ * side) and 7 (negative side) evenly spaced probabilities between
+ * delta = 1 - (1/30 + 1/32)/2 and 1/2 (1/2 excluded), plus 0, divided by the
+ * quantile at delta.  Derived on the host in extended precision at first use.
+ * Needs no GPU.  Returns NF4_ERR_NULL if out is NULL. */
+int nf4_codebook(float out[16]);
+
+/* Blockwise NF4 quantization -- tool page "How it works", Steps 1-4.
+ *   x       : n input values, x_dtype NF4_F32 or NF4_BF16; 16-byte aligned.
+ *   n       : number of values, 1 <= n < 2^40.  Blocks run along x in order;
+ *             the last block may be partial and its absmax covers only the
+ *             values that exist.
+ *   blocksize: must be 64.
+ *   packed  : out, ceil(n/2) bytes, 16-byte aligned.  Byte j holds the code of
+ *             element 2j in bits 7..4 and of element 2j+1 in bits 3..0; when n
+ *             is odd the final low nibble is 7 (the zero level).
+ *   absmax  : out, ceil(n/64) float32, 4-byte aligned: the largest |x| of each
+ *             block (exact).
+ * Each code is the index of the level nearest to fl32(x / absmax) (an IEEE
+ * float32 division), an exact tie going to the level farther from zero; a
+ * block whose absmax is 0 gets code 7 throughout. */
+int nf4_quantize(const void* x, int x_dtype, int64_t n, int32_t blocksize,
+                 uint8_t* packed, float* absmax, void* stream);
+
+/* Bytes of device workspace nf4_double_quant needs (a small constant). */
+size_t nf4_double_quant_workspace(int64_t nblocks);
+
+/* Double quantization of the block scales -- tool page "Double quantization"
+ * with the int8 scheme of its section "A worked example".
+ *   absmax  : nblocks float32 scales from nf4_quantize, 16-byte aligned,
+ *             1 <= nblocks < 2^31.
+ *   blocksize2: must be 256.
+ *   qabsmax : out, nblocks int8, 16-byte aligned.
+ *   absmax2 : out, ceil(nblocks/256) float32, 4-byte aligned.
+ *   mean    : out, one float32 (device).
+ *   workspace: at least nf4_double_quant_workspace(nblocks) bytes, 16-byte
+ *             aligned; its contents on entry do not matter.
+ * mean = fl32(fl64(S) / nblocks) where S is the exact sum of the scales (the
+ * sum is accumulated exactly in a wide integer, so mean does not depend on
+ * summation order).  With c = fl32(absmax - mean) and, per group of 256,
+ * s2 = max |c|: t = fl32(fl32(c / s2) * 127) and q = sign(t) floor(|t| + 1/2)
+ * (half away from zero); q = 0 in a group whose s2 is 0. */
+int nf4_double_quant(const float* absmax, int64_t nblocks, int32_t blocksize2,
+                     int8_t* qabsmax, float* absmax2, float* mean,
+                     void* workspace, size_t workspace_bytes, void* stream);
+
+/* [host] A quantized weight: a struct holding device pointers.  The logical
+ * matrix W[rows][cols] is row-major, element i = r*cols + c, and blocks of 64
+ * run along that order.  Exactly one scale form is given:
+ *   absmax != NULL                      : plain fp32 scales (no double quant);
+ *   absmax == NULL, qabsmax/absmax2/mean: double-quantized scales, and each
+ *     block's scale is a_hat = fl32(fl32(fl32(q / 127) * s2) + mean). */
+typedef struct nf4_weight {
+  const uint8_t* packed;    /* ceil(rows*cols/2) bytes, 16-byte aligned          */
+  int64_t rows, cols;       /* rows >= 1, cols >= 1                              */
+  int32_t blocksize;        /* 64                                                */
+  const float* absmax;      /* ceil(rows*cols/64) float32, or NULL               */
+  const int8_t* qabsmax;    /* ceil(rows*cols/64) int8 when absmax == NULL       */
+  const float* absmax2;     /* ceil(nblocks/256) float32 when absmax == NULL     */
+  const float* mean;        /* one float32 when absmax == NULL                   */
+  int32_t blocksize2;       /* 256 when absmax == NULL                           */
+} nf4_weight;
+
+/* Dequantization -- tool page "How it works", Step 5.
+ *   out: rows*cols values of out_dtype (NF4_F32 or NF4_BF16), 16-byte aligned.
+ * out[i] = fl32(level[code_i] * a_hat_block(i)); for bf16 that float32 value
+ * is rounded once to nearest even. */
+int nf4_dequantize(const nf4_weight* w, void* out, int out_dtype, void* stream);
+
+/* Fused dequantize-and-multiply for decode: y = x . deq(W)^T.
+ *   x : bf16 [m][cols], 16-byte aligned;  1 <= m <= 16;  cols % 64 == 0.
+ *   y : [m][rows] of y_dtype (NF4_F32 or NF4_BF16), 16-byte aligned.
+ * Products are accumulated in float32; no dequantized copy of W is written
+ * to memory (tool page "How it works", Step 5: the expanded copy is
+ * temporary). */
+int nf4_gemv(const nf4_weight* w, const void* x, int64_t m, void* y, int y_dtype,
+             void* stream);
+
+/* Bytes of device workspace nf4_gemm needs for m rows of x and LoRA rank r
+ * (0 when r == 0). */
+size_t nf4_gemm_workspace(int64_t m, int64_t rows, int32_t r);
+
+/* Dequantize-into-LDS bf16 matrix-core GEMM for prefill and training, with an
+ * optional fused LoRA term (tutorial page "QLoRA: Fine-Tuning a 4-bit Model"
+ * and tool page "Fine-tuning with adapters on a 4-bit model": a frozen 4-bit
+ * base plus low-rank adapters whose output is multiplied by a scale factor):
+ *   y = x . deq(W)^T + lora_scale . (x . A^T) . B^T
+ *   x      : bf16 [m][cols], 16-byte aligned, m >= 1, cols % 64 == 0.
+ *   y      : bf16 [m][rows], 16-byte aligned.
+ *   lora_a : bf16 [r][cols] and lora_b : bf16 [rows][r], both NULL (then r
+ *            must be 0) or both set with 1 <= r <= 64; 16-byte aligned.
+ *   workspace: at least nf4_gemm_workspace(m, rows, r) bytes, 16-byte aligned
+ *            (may be NULL when that is 0).
+ * W is dequantized to bf16 exactly as nf4_dequantize does; products are
+ * accumulated in float32 and y is rounded once to bf16. */
+int nf4_gemm(const nf4_weight* w, const void* x, int64_t m, void* y,
+             const void* lora_a, const void* lora_b, int32_t r, float lora_scale,
+             void* workspace, size_t workspace_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* NF4_H */

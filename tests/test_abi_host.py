@@ -1,0 +1,130 @@
+"""Host-only checks of the C ABI (no GPU needed): the library loads, exports
+every function include/nf4.h declares, derives the same code book as the
+oracle, and rejects bad arguments before touching the device."""
+
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+import subprocess
+
+import numpy as np
+import pytest
+
+import dequant_matmul_nf4_amd as nf4
+import oracle
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "nf4.h")
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(nf4.LIB_PATH):
+        from dequant_matmul_nf4_amd import build
+        build.build()
+    return nf4.lib()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(nf4_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_header_declares_the_expected_calls():
+    assert declared_functions() == sorted(nf4.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol(L):
+    out = subprocess.run(["nm", "-D", "--defined-only", nf4.LIB_PATH], capture_output=True, text=True, check=True).stdout
+    exported = set(re.findall(r"\bT (nf4_[a-z_0-9]+)", out))
+    for name in declared_functions():
+        assert name in exported, name
+        assert getattr(L, name) is not None
+
+
+def test_codebook_bit_identical_to_oracle(L):
+    cb = np.array(nf4.nf4_codebook(), dtype=np.float32)
+    assert np.array_equal(cb.view(np.uint32), oracle.codebook().view(np.uint32))
+
+
+def test_workspace_sizes(L):
+    assert nf4.nf4_double_quant_workspace(1) >= 16 * 8
+    assert nf4.nf4_gemm_workspace(4096, 14336, 0) == 0
+    assert nf4.nf4_gemm_workspace(4096, 14336, 16) >= 4096 * 16 * 4
+    assert nf4.nf4_gemm_workspace(4096, 14336, 16) % 256 == 0
+
+
+def test_struct_layout():
+    assert ctypes.sizeof(nf4.nf4_weight) == 72
+    assert nf4.nf4_weight.blocksize2.offset == 64
+
+
+# Fake but aligned device addresses: every call below fails validation on the
+# host, before any HIP call, so nothing is dereferenced.
+A = 0x10000
+A2 = 0x20000
+
+
+def _w(**kw):
+    base = dict(packed=A, rows=16, cols=64, blocksize=64, absmax=A2, qabsmax=None, absmax2=None, mean=None, blocksize2=256)
+    base.update(kw)
+    return nf4.nf4_weight(**base)
+
+
+CASES = [
+    ("quantize null x", lambda L: L.nf4_quantize(None, 1, 64, 64, A, A2, None), nf4.NF4_ERR_NULL),
+    ("quantize null packed", lambda L: L.nf4_quantize(A, 1, 64, 64, None, A2, None), nf4.NF4_ERR_NULL),
+    ("quantize bad dtype", lambda L: L.nf4_quantize(A, 7, 64, 64, A, A2, None), nf4.NF4_ERR_DTYPE),
+    ("quantize n=0", lambda L: L.nf4_quantize(A, 1, 0, 64, A, A2, None), nf4.NF4_ERR_SIZE),
+    ("quantize n<0", lambda L: L.nf4_quantize(A, 1, -5, 64, A, A2, None), nf4.NF4_ERR_SIZE),
+    ("quantize blocksize", lambda L: L.nf4_quantize(A, 1, 64, 128, A, A2, None), nf4.NF4_ERR_BLOCKSIZE),
+    ("quantize misaligned x", lambda L: L.nf4_quantize(A + 2, 1, 64, 64, A, A2, None), nf4.NF4_ERR_ALIGN),
+    ("quantize misaligned packed", lambda L: L.nf4_quantize(A, 1, 64, 64, A + 8, A2, None), nf4.NF4_ERR_ALIGN),
+    ("quantize misaligned absmax", lambda L: L.nf4_quantize(A, 1, 64, 64, A, A2 + 2, None), nf4.NF4_ERR_ALIGN),
+    ("dq null", lambda L: L.nf4_double_quant(A, 10, 256, None, A2, A2, A, 128, None), nf4.NF4_ERR_NULL),
+    ("dq nblocks", lambda L: L.nf4_double_quant(A, 0, 256, A, A2, A2, A, 128, None), nf4.NF4_ERR_SIZE),
+    ("dq blocksize2", lambda L: L.nf4_double_quant(A, 10, 128, A, A2, A2, A, 128, None), nf4.NF4_ERR_BLOCKSIZE),
+    ("dq workspace small", lambda L: L.nf4_double_quant(A, 10, 256, A, A2, A2, A, 8, None), nf4.NF4_ERR_WORKSPACE),
+    ("dq workspace null", lambda L: L.nf4_double_quant(A, 10, 256, A, A2, A2, None, 128, None), nf4.NF4_ERR_WORKSPACE),
+    ("dq misaligned q", lambda L: L.nf4_double_quant(A, 10, 256, A + 1, A2, A2, A, 128, None), nf4.NF4_ERR_ALIGN),
+    ("dequant null weight", lambda L: L.nf4_dequantize(None, A, 1, None), nf4.NF4_ERR_NULL),
+    ("dequant null out", lambda L: L.nf4_dequantize(ctypes.byref(_w()), None, 1, None), nf4.NF4_ERR_NULL),
+    ("dequant bad dtype", lambda L: L.nf4_dequantize(ctypes.byref(_w()), A, 3, None), nf4.NF4_ERR_DTYPE),
+    ("dequant blocksize", lambda L: L.nf4_dequantize(ctypes.byref(_w(blocksize=32)), A, 1, None), nf4.NF4_ERR_BLOCKSIZE),
+    ("dequant shape", lambda L: L.nf4_dequantize(ctypes.byref(_w(rows=0)), A, 1, None), nf4.NF4_ERR_SIZE),
+    ("dequant dq missing", lambda L: L.nf4_dequantize(ctypes.byref(_w(absmax=None)), A, 1, None), nf4.NF4_ERR_NULL),
+    ("dequant blocksize2", lambda L: L.nf4_dequantize(ctypes.byref(_w(absmax=None, qabsmax=A, absmax2=A2, mean=A2, blocksize2=64)), A, 1, None), nf4.NF4_ERR_BLOCKSIZE),
+    ("dequant misaligned out", lambda L: L.nf4_dequantize(ctypes.byref(_w()), A + 4, 1, None), nf4.NF4_ERR_ALIGN),
+    ("dequant misaligned packed", lambda L: L.nf4_dequantize(ctypes.byref(_w(packed=A + 1)), A, 1, None), nf4.NF4_ERR_ALIGN),
+    ("gemv cols%64", lambda L: L.nf4_gemv(ctypes.byref(_w(cols=96)), A, 1, A, 1, None), nf4.NF4_ERR_SIZE),
+    ("gemv m=0", lambda L: L.nf4_gemv(ctypes.byref(_w()), A, 0, A, 1, None), nf4.NF4_ERR_SIZE),
+    ("gemv m=17", lambda L: L.nf4_gemv(ctypes.byref(_w()), A, 17, A, 1, None), nf4.NF4_ERR_SIZE),
+    ("gemv null y", lambda L: L.nf4_gemv(ctypes.byref(_w()), A, 1, None, 1, None), nf4.NF4_ERR_NULL),
+    ("gemv bad dtype", lambda L: L.nf4_gemv(ctypes.byref(_w()), A, 1, A, 9, None), nf4.NF4_ERR_DTYPE),
+    ("gemv misaligned x", lambda L: L.nf4_gemv(ctypes.byref(_w()), A + 2, 1, A, 1, None), nf4.NF4_ERR_ALIGN),
+    ("gemm cols%64", lambda L: L.nf4_gemm(ctypes.byref(_w(cols=100)), A, 4, A, None, None, 0, 0.0, None, 0, None), nf4.NF4_ERR_SIZE),
+    ("gemm m=0", lambda L: L.nf4_gemm(ctypes.byref(_w()), A, 0, A, None, None, 0, 0.0, None, 0, None), nf4.NF4_ERR_SIZE),
+    ("gemm half lora", lambda L: L.nf4_gemm(ctypes.byref(_w()), A, 4, A, A, None, 16, 2.0, A, 4096, None), nf4.NF4_ERR_NULL),
+    ("gemm rank 0", lambda L: L.nf4_gemm(ctypes.byref(_w()), A, 4, A, A, A, 0, 2.0, A, 4096, None), nf4.NF4_ERR_SIZE),
+    ("gemm rank 65", lambda L: L.nf4_gemm(ctypes.byref(_w()), A, 4, A, A, A, 65, 2.0, A, 1 << 20, None), nf4.NF4_ERR_SIZE),
+    ("gemm r without lora", lambda L: L.nf4_gemm(ctypes.byref(_w()), A, 4, A, None, None, 3, 0.0, None, 0, None), nf4.NF4_ERR_SIZE),
+    ("gemm workspace small", lambda L: L.nf4_gemm(ctypes.byref(_w()), A, 4, A, A, A, 16, 2.0, A, 16, None), nf4.NF4_ERR_WORKSPACE),
+    ("gemm workspace null", lambda L: L.nf4_gemm(ctypes.byref(_w()), A, 4, A, A, A, 16, 2.0, None, 4096, None), nf4.NF4_ERR_WORKSPACE),
+    ("gemm scale nan", lambda L: L.nf4_gemm(ctypes.byref(_w()), A, 4, A, A, A, 16, float("nan"), A, 4096, None), nf4.NF4_ERR_SIZE),
+    ("gemm misaligned y", lambda L: L.nf4_gemm(ctypes.byref(_w()), A, 4, A + 2, None, None, 0, 0.0, None, 0, None), nf4.NF4_ERR_ALIGN),
+]
+
+
+@pytest.mark.parametrize("name,call,code", CASES, ids=[c[0] for c in CASES])
+def test_invalid_arguments_rejected_on_host(L, name, call, code):
+    rc = call(L)
+    assert rc == code, (name, rc, nf4.nf4_last_error())
+    msg = nf4.nf4_last_error()
+    assert msg.startswith("nf4_"), msg
+
+
+def test_codebook_null(L):
+    assert L.nf4_codebook(None) == nf4.NF4_ERR_NULL

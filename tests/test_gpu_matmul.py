@@ -1,0 +1,199 @@
+"""GPU parity of nf4_gemv and nf4_gemm against the oracle's float64 product of
+its bf16-dequantized weights: relative Frobenius error <= 1e-2 (MATMUL_RTOL).
+Full-size workloads are checked on sampled rows, each computed by the oracle
+on its own (a weight row holds whole 64-blocks)."""
+
+from __future__ import annotations
+
+import numpy as np
+import pytest
+
+import dequant_matmul_nf4_amd as nf4
+import oracle
+import synthetic as syn
+from tests.gpu_common import MATMUL_RTOL, need_gpu, oracle_rows_dequant_bf16, say, to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+def _full_oracle_wdeq(w_f32: np.ndarray, dq: bool) -> np.ndarray:
+    p, a = oracle.quantize(w_f32.reshape(-1))
+    if dq:
+        q, s2, mean = oracle.double_quant(a)
+        bits = oracle.dequantize(p, w_f32.size, qabsmax=q, absmax2=s2, mean=mean, out="bf16")
+    else:
+        bits = oracle.dequantize(p, w_f32.size, absmax=a, out="bf16")
+    return oracle.bf16_bits_to_f32(bits).reshape(w_f32.shape)
+
+
+def _y_f64(y):
+    import torch
+    return y.detach().to(torch.float32).cpu().numpy().astype(np.float64)
+
+
+@pytest.mark.parametrize("rows,cols", [(1, 64), (5, 128), (33, 192), (1024, 1024), (300, 4096)])
+@pytest.mark.parametrize("m", [1, 2, 4, 5, 16])
+@pytest.mark.parametrize("dq", [False, True])
+def test_gemv_small(rows, cols, m, dq):
+    say("gemv", rows, cols, "m", m, "dq" if dq else "plain")
+    torch = need_gpu()
+    w = syn.normal_f32((rows, cols), 0.02, rows + 7 * cols)
+    xb = syn.to_bf16(syn.normal_f32((m, cols), 1.0, 99 + m))
+    W = nf4.quantize_weight(to_dev(w), double_quant=dq)
+    y32 = nf4.nf4_gemv(W, xb.to("cuda"), y_dtype=torch.float32)
+    yb = nf4.nf4_gemv(W, xb.to("cuda"), y_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    ref = oracle.matmul_ref(syn.bf16_to_f32(xb), _full_oracle_wdeq(w, dq))
+    e32 = oracle.rel_frobenius(_y_f64(y32), ref)
+    eb = oracle.rel_frobenius(_y_f64(yb), ref)
+    say(f"  rel err f32 {e32:.2e} bf16 {eb:.2e}")
+    assert e32 <= MATMUL_RTOL and eb <= MATMUL_RTOL
+
+
+def test_gemv_c1_full():
+    say("gemv C1")
+    torch = need_gpu()
+    inp = syn.c1_inputs()
+    W = nf4.quantize_weight(to_dev(inp["w_f32"]), double_quant=False)
+    y = nf4.nf4_gemv(W, inp["x"].to("cuda"), y_dtype=torch.float32)
+    torch.cuda.synchronize()
+    ref = oracle.matmul_ref(syn.bf16_to_f32(inp["x"]), _full_oracle_wdeq(inp["w_f32"], False))
+    e = oracle.rel_frobenius(_y_f64(y), ref)
+    say(f"  rel err {e:.2e}")
+    assert e <= MATMUL_RTOL
+
+
+def test_gemv_c2_full():
+    say("gemv C2 4096x4096 dq")
+    torch = need_gpu()
+    inp = syn.c2_inputs()
+    W = nf4.quantize_weight(inp["w"].to("cuda"), double_quant=True)
+    y = nf4.nf4_gemv(W, inp["x"].to("cuda"))
+    torch.cuda.synchronize()
+    ref = oracle.matmul_ref(syn.bf16_to_f32(inp["x"]), _full_oracle_wdeq(syn.bf16_to_f32(inp["w"]), True))
+    e = oracle.rel_frobenius(_y_f64(y), ref)
+    say(f"  rel err {e:.2e}")
+    assert e <= MATMUL_RTOL
+
+
+@pytest.mark.parametrize("name", ["gate", "down"])
+@pytest.mark.parametrize("m", [1, 4, 16])
+def test_gemv_c3_sampled_rows(name, m):
+    say("gemv C3", name, "m", m)
+    torch = need_gpu()
+    wt = syn.c3_weight(name)
+    rows, cols = wt.shape
+    x = syn.c3_x(m, cols)
+    W = nf4.quantize_weight(wt.to("cuda"), double_quant=True)
+    y = nf4.nf4_gemv(W, x.to("cuda"))
+    torch.cuda.synchronize()
+    w_f32 = syn.bf16_to_f32(wt)
+    rng = np.random.default_rng(3)
+    sel = np.unique(np.concatenate([[0, rows - 1], rng.choice(rows, 192, replace=False)]))
+    absmax_all = oracle.block_absmax(w_f32.reshape(-1))
+    wdeq = oracle_rows_dequant_bf16(w_f32[sel], sel, cols, absmax_all, True)
+    ref = oracle.matmul_ref(syn.bf16_to_f32(x), wdeq)
+    e = oracle.rel_frobenius(_y_f64(y)[:, sel], ref)
+    say(f"  rel err {e:.2e}")
+    assert e <= MATMUL_RTOL
+
+
+def test_gemv_one_hot_and_determinism():
+    """x = e_k returns column k of the dequantized weight (to float32
+    accumulation of exact products); two runs give identical bits."""
+    say("gemv one-hot")
+    torch = need_gpu()
+    rows, cols = 256, 512
+    w = syn.normal_f32((rows, cols), 0.02, 4)
+    W = nf4.quantize_weight(to_dev(w), double_quant=True)
+    wdeq_f32 = nf4.nf4_dequantize(W, out_dtype=torch.float32)
+    for k in (0, 77, 511):
+        x = torch.zeros((1, cols), dtype=torch.bfloat16, device="cuda")
+        x[0, k] = 1.0
+        y = nf4.nf4_gemv(W, x, y_dtype=torch.float32)
+        torch.cuda.synchronize()
+        assert torch.equal(y[0], wdeq_f32[:, k])
+    x = syn.to_bf16(syn.normal_f32((4, cols), 1.0, 8)).to("cuda")
+    y1 = nf4.nf4_gemv(W, x)
+    y2 = nf4.nf4_gemv(W, x)
+    torch.cuda.synchronize()
+    assert torch.equal(y1, y2)
+
+
+@pytest.mark.parametrize("m,rows,cols", [(1, 64, 64), (37, 200, 128), (130, 129, 192), (256, 256, 512), (300, 520, 1024)])
+@pytest.mark.parametrize("lora", [0, 1, 16])
+@pytest.mark.parametrize("dq", [False, True])
+def test_gemm_small(m, rows, cols, lora, dq):
+    say("gemm", m, rows, cols, "lora", lora, "dq" if dq else "plain")
+    torch = need_gpu()
+    w = syn.normal_f32((rows, cols), 0.02, m + rows + cols)
+    xb = syn.to_bf16(syn.normal_f32((m, cols), 1.0, 17 + m))
+    W = nf4.quantize_weight(to_dev(w), double_quant=dq)
+    a = b = None
+    s = 0.0
+    if lora:
+        a = syn.to_bf16(syn.normal_f32((lora, cols), 0.01, 6))
+        b = syn.to_bf16(syn.normal_f32((rows, lora), 0.01, 7))
+        s = 32.0 / lora
+    y = nf4.nf4_gemm(W, xb.to("cuda"), lora_a=None if a is None else a.to("cuda"),
+                     lora_b=None if b is None else b.to("cuda"), lora_scale=s)
+    torch.cuda.synchronize()
+    ref = oracle.matmul_ref(syn.bf16_to_f32(xb), _full_oracle_wdeq(w, dq),
+                            None if a is None else syn.bf16_to_f32(a),
+                            None if b is None else syn.bf16_to_f32(b), s)
+    e = oracle.rel_frobenius(_y_f64(y), ref)
+    say(f"  rel err {e:.2e}")
+    assert e <= MATMUL_RTOL
+
+
+def test_gemm_lora_only_term_and_zero_b():
+    """With B = 0 the LoRA path adds nothing; with a one-hot x the product
+    returns a dequantized column exactly rounded to bf16."""
+    say("gemm closed forms")
+    torch = need_gpu()
+    rows, cols, m = 192, 256, 64
+    w = syn.normal_f32((rows, cols), 0.02, 12)
+    W = nf4.quantize_weight(to_dev(w), double_quant=True)
+    xb = syn.to_bf16(syn.normal_f32((m, cols), 1.0, 13)).to("cuda")
+    a = syn.to_bf16(syn.normal_f32((16, cols), 0.01, 14)).to("cuda")
+    zb = torch.zeros((rows, 16), dtype=torch.bfloat16, device="cuda")
+    y0 = nf4.nf4_gemm(W, xb)
+    y1 = nf4.nf4_gemm(W, xb, lora_a=a, lora_b=zb, lora_scale=2.0)
+    e = torch.zeros((m, cols), dtype=torch.bfloat16, device="cuda")
+    for i in range(m):
+        e[i, (i * 5) % cols] = 1.0
+    ye = nf4.nf4_gemm(W, e)
+    wdeq = nf4.nf4_dequantize(W, out_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    assert torch.equal(y0, y1)
+    for i in range(m):
+        assert torch.equal(ye[i], wdeq[:, (i * 5) % cols])
+
+
+def test_gemm_c4_sampled():
+    """C4 at full size: X [4096, 4096], W [14336, 4096] with double quant,
+    LoRA r = 16, alpha = 32; checked on 96 x 96 sampled outputs."""
+    say("gemm C4 full size")
+    torch = need_gpu()
+    inp = syn.c4_inputs()
+    x, wt, a, b = inp["x"], inp["w"], inp["a"], inp["b"]
+    s = inp["alpha"] / inp["r"]
+    W = nf4.quantize_weight(wt.to("cuda"), double_quant=True)
+    y = nf4.nf4_gemm(W, x.to("cuda"), lora_a=a.to("cuda"), lora_b=b.to("cuda"), lora_scale=s)
+    torch.cuda.synchronize()
+    rows, cols = wt.shape
+    rng = np.random.default_rng(4)
+    sel_n = np.unique(np.concatenate([[0, rows - 1], rng.choice(rows, 94, replace=False)]))
+    sel_m = np.unique(np.concatenate([[0, x.shape[0] - 1], rng.choice(x.shape[0], 94, replace=False)]))
+    w_f32 = syn.bf16_to_f32(wt)
+    wdeq = oracle_rows_dequant_bf16(w_f32[sel_n], sel_n, cols, oracle.block_absmax(w_f32.reshape(-1)), True)
+    x_f = syn.bf16_to_f32(x)[sel_m]
+    ref = oracle.matmul_ref(x_f, wdeq, syn.bf16_to_f32(a), syn.bf16_to_f32(b)[sel_n], s)
+    import torch as _t
+    got = _y_f64(y[_t.as_tensor(sel_m, device="cuda")][:, _t.as_tensor(sel_n, device="cuda")])
+    e = oracle.rel_frobenius(got, ref)
+    say(f"  rel err {e:.2e}")
+    assert e <= MATMUL_RTOL
+    y2 = nf4.nf4_gemm(W, x.to("cuda"), lora_a=a.to("cuda"), lora_b=b.to("cuda"), lora_scale=s)
+    torch.cuda.synchronize()
+    assert torch.equal(y, y2)
