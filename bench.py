@@ -234,6 +234,40 @@ def extra_legs(torch, nf4, syn, dev, stream, EventTimer):
     }
     del Ws
 
+    # larger decode GEMVs: the Llama-8B MLP (C3 shapes) and one 70B-shaped layer
+    def gemv_pool(shapes, reps, label):
+        Wl = []
+        for i, (r_, c_) in enumerate(shapes):
+            g.manual_seed(9_000 + i)
+            w = (torch.randn((r_, c_), generator=g, device=dev) * 0.02).to(torch.bfloat16)
+            Wl.append(nf4.quantize_weight(w, double_quant=True))
+            del w
+        xs = {c_: (torch.randn((1, c_), generator=g, device=dev)).to(torch.bfloat16) for _, c_ in shapes}
+        ys = [torch.empty((1, r_), dtype=torch.bfloat16, device=dev) for r_, _ in shapes]
+        for W, yy in zip(Wl, ys):
+            nf4.nf4_gemv(W, xs[W.cols], yy)
+        torch.cuda.synchronize()
+        t = EventTimer(torch, stream)
+        s = t.start()
+        for _ in range(reps):
+            for W, yy in zip(Wl, ys):
+                nf4.nf4_gemv(W, xs[W.cols], yy)
+        t.stop(s)
+        torch.cuda.synchronize()
+        total_us = t.mean_us() / reps
+        nbytes = sum(step_bytes(r_, c_)["gemv"] for r_, c_ in shapes)
+        del Wl
+        return {"workload": label, "us_per_pass": round(total_us, 2),
+                "GBps": round(nbytes / (total_us * 1e-6) / 1e9, 1),
+                "frac_hbm_peak": round(nbytes / (total_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}
+
+    print("[bench] gemv MLP / 70B-layer legs", file=sys.stderr, flush=True)
+    mlp = [(14336, 4096), (14336, 4096), (4096, 14336)] * 6
+    res["gemv_mlp_8b"] = gemv_pool(mlp, 10, "Llama-8B MLP gate/up 14336x4096 + down 4096x14336, NF4+DQ, M=1, "
+                                            "6 distinct triples (545 MB) per pass")
+    layer = [(8192, 8192), (1024, 8192), (1024, 8192), (8192, 8192), (28672, 8192), (28672, 8192), (8192, 28672)]
+    res["gemv_layer_70b"] = gemv_pool(layer, 10, "70B-shaped layer q,k,v,o,gate,up,down NF4+DQ, M=1 (442 MB)")
+
     print("[bench] gemm leg", file=sys.stderr, flush=True)
     M, N, K, r = 4096, 14336, 4096, 16
     g.manual_seed(4_005)

@@ -36,6 +36,8 @@ constexpr int64_t kMaxN = int64_t(1) << 40;
 // gfx950 check, cached per device id.
 std::mutex g_dev_mu;
 int g_dev_state[64];  // 0 unknown, 1 gfx950, 2 other
+int g_dev_cus[64];
+thread_local int t_cus = 256;
 
 int check_device() {
   int dev = 0;
@@ -49,8 +51,10 @@ int check_device() {
     if (e != hipSuccess)
       return fail(NF4_ERR_DEVICE, "hipGetDeviceProperties failed: %s", hipGetErrorString(e));
     g_dev_state[dev] = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : 2;
+    g_dev_cus[dev] = prop.multiProcessorCount > 0 ? prop.multiProcessorCount : 256;
   }
   if (g_dev_state[dev] != 1) return fail(NF4_ERR_DEVICE, "device %d is not a gfx950 (MI355X)", dev);
+  t_cus = g_dev_cus[dev];
   return NF4_OK;
 }
 
@@ -90,6 +94,8 @@ int check_weight(const nf4_weight* w, nf4i::Scales* sc, int64_t* n_out, const ch
 hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
 
 }  // namespace
+
+int nf4i::device_cus() { return t_cus; }
 
 extern "C" {
 

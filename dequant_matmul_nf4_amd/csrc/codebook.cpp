@@ -12,8 +12,12 @@
 //
 // Quantiles are found by bisection on the upper tail 0.5*erfc(x/sqrt 2) in
 // x87 extended precision and rounded once to float32.
+#include <algorithm>
 #include <cfloat>
 #include <cmath>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
 
 #include "nf4_internal.h"
 
@@ -62,11 +66,57 @@ Codebook build() {
   return cb;
 }
 
+uint32_t count_code(float v, const Codebook& cb) {
+  uint32_t c = 0;
+  for (int i = 0; i < 15; ++i) c += (v >= cb.thresh[i]) ? 1u : 0u;
+  return c;
+}
+
+float from_bits(uint32_t u) {
+  float f;
+  std::memcpy(&f, &u, sizeof f);
+  return f;
+}
+
+// Builds the bucket table and checks, for every one of the 2048 buckets, that
+// the bucket rule reproduces the threshold count at both ends of the bucket
+// (the count is monotone, so that covers every value inside).
+QuantLut build_lut(const Codebook& cb) {
+  QuantLut lut{};
+  for (int b = 0; b < kLutBuckets; ++b) {
+    const uint32_t sign = static_cast<uint32_t>(b) >> 10;
+    const uint32_t lo_mag = static_cast<uint32_t>(b & 1023) << 21, hi_mag = lo_mag | 0x1FFFFFu;
+    if ((lo_mag >> 23) > 127 || (lo_mag >> 23) == 127 && lo_mag != 0x3F800000u) continue;  // |v| > 1 never occurs
+    const uint32_t hi_bits = std::min(hi_mag, 0x3F800000u);
+    const float lo_v = from_bits((sign << 31) | (sign ? hi_bits : lo_mag));  // smallest value in bucket
+    const float hi_v = from_bits((sign << 31) | (sign ? lo_mag : hi_bits));  // largest value in bucket
+    const uint32_t c_lo = count_code(lo_v, cb), c_hi = count_code(hi_v, cb);
+    const int e = static_cast<int>(lo_mag >> 23);
+    if (c_hi > c_lo + 1) { std::fprintf(stderr, "nf4: bucket %d holds two thresholds\n", b); std::abort(); }
+    if (e < kLutFirstExp) {
+      if (c_lo != 7 || c_hi != 7) { std::fprintf(stderr, "nf4: bucket %d below 2^-5 is not code 7\n", b); std::abort(); }
+      continue;
+    }
+    int t = -1;
+    for (int k = 0; k < kLutSpecial; ++k)
+      if (lut_special_index(k) == b) t = k;
+    if (t < 0) { std::fprintf(stderr, "nf4: bucket %d missing from the table\n", b); std::abort(); }
+    lut.base[t] = c_lo;
+    lut.thr[t] = (c_hi == c_lo) ? INFINITY : cb.thresh[c_lo];
+  }
+  return lut;
+}
+
 }  // namespace
 
 const Codebook& codebook() {
   static const Codebook cb = build();
   return cb;
+}
+
+const QuantLut& quant_lut() {
+  static const QuantLut lut = build_lut(codebook());
+  return lut;
 }
 
 }  // namespace nf4i

@@ -5,20 +5,18 @@
 // The mean must not depend on summation order, so the scales are summed
 // exactly: each float32 is an integer m * 2^p times 2^-149 (m < 2^24,
 // 0 <= p <= 253), added into 32-bit digits of a wide fixed-point integer held
-// in 64-bit accumulators (no carries until the end).  The last block to finish
-// propagates the carries, rounds the integer once to float64, divides by the
-// count in float64 and rounds to float32.
+// in 64-bit accumulators (no carries until the end).  Each summing workgroup
+// writes its digit sums to its own workspace row (no atomics: device-wide
+// atomics on one address serialize in memory); a one-workgroup kernel adds the
+// rows, propagates the carries, rounds the integer once to float64, divides
+// by the count in float64 and rounds to float32.
 //
-// Kernels: k_dq_clear (fill kernel for the workspace), k_dq_sum (exact sum and
-// mean), k_dq_quant (one wave per group of 256 scales).
+// Kernels: k_dq_partial (digit sums per workgroup), k_dq_mean (one
+// workgroup), k_dq_quant (one wave per group of 256 scales).
 #include "nf4_device.h"
 
 namespace nf4i {
 namespace {
-
-__global__ void k_dq_clear(unsigned long long* ws) {
-  if (threadIdx.x < 16) ws[threadIdx.x] = 0ull;
-}
 
 __device__ __forceinline__ void scale_to_digits(float a, int* d, uint32_t* lo, uint32_t* hi) {
   const uint32_t u = __float_as_uint(a) & 0x7FFFFFFFu;
@@ -31,63 +29,122 @@ __device__ __forceinline__ void scale_to_digits(float a, int* d, uint32_t* lo, u
   *hi = static_cast<uint32_t>(v >> 32);
 }
 
-// Rounds the non-negative integer sum_k digit[k] 2^(32k) to the nearest
-// float64 (ties to even) and scales it by 2^-149.
-__device__ double digits_to_double(const uint32_t* dig, int ndig) {
+// Rounds the non-negative integer I = sum_k dig[k] 2^(32k) (12 digits, all
+// indexing static so everything stays in registers) to the nearest float64,
+// ties to even, and returns I * 2^-149.  The top three digits give a 96-bit
+// window holding the 53 result bits plus the round bit; everything below
+// only feeds the sticky bit.
+__device__ double digits_to_double(const uint32_t (&dig)[kDqDigits]) {
   int top = -1;
-  for (int k = ndig - 1; k >= 0 && top < 0; --k)
-    if (dig[k]) top = 32 * k + (31 - __clz(dig[k]));
+#pragma unroll
+  for (int k = 0; k < kDqDigits; ++k)
+    if (dig[k]) top = k;
   if (top < 0) return 0.0;
-  auto bit = [&](int i) -> uint32_t { return (i < 0) ? 0u : (dig[i >> 5] >> (i & 31)) & 1u; };
-  unsigned long long mant = 0;
-  const int low = top - 52;  // lowest kept bit (may be negative: then exact)
-  for (int i = top; i >= low && i >= 0; --i) mant = (mant << 1) | bit(i);
-  int scale = 0;
-  if (low > 0) {
-    const uint32_t round = bit(low - 1);
-    uint32_t sticky = 0;
-    for (int i = low - 2; i >= 0 && !sticky; --i) sticky |= bit(i);
-    if (round && (sticky || (mant & 1ull))) ++mant;
-    scale = low;
+  uint32_t d2 = 0, d1 = 0, d0 = 0, below = 0;
+#pragma unroll
+  for (int k = 0; k < kDqDigits; ++k) {
+    d2 = (k == top) ? dig[k] : d2;
+    d1 = (k == top - 1) ? dig[k] : d1;
+    d0 = (k == top - 2) ? dig[k] : d0;
+    below |= (k < top - 2) ? dig[k] : 0u;
   }
-  return ldexp(static_cast<double>(mant), scale - 149);
+  // window N = (H:L) with H = d2:d1, L = d0:0, so I = N * 2^(32 (top - 2) - 32)
+  const unsigned long long H = (static_cast<unsigned long long>(d2) << 32) | d1;
+  const unsigned long long L = static_cast<unsigned long long>(d0) << 32;
+  const int lz = __clzll(H);  // 0..31 because d2 != 0
+  const unsigned long long nh = lz ? (H << lz) | (L >> (64 - lz)) : H;
+  const unsigned long long nl = L << lz;
+  unsigned long long mant = nh >> 11;  // top 53 bits of the 128-bit window
+  const unsigned long long round = (nh >> 10) & 1ull;
+  const bool sticky = (nh & 0x3FFull) || nl || below;
+  if (round && (sticky || (mant & 1ull))) ++mant;
+  const int exp2 = 75 + 32 * (top - 2) - 32 - lz - 149;
+  return ldexp(static_cast<double>(mant), exp2);
 }
 
-__global__ __launch_bounds__(256) void k_dq_sum(const float* __restrict__ absmax, int64_t nb,
-                                                unsigned long long* __restrict__ ws,
-                                                float* __restrict__ mean_out) {
-  __shared__ unsigned long long acc[kDqDigits];
-  __shared__ int is_last;
-  if (threadIdx.x < kDqDigits) acc[threadIdx.x] = 0ull;
-  __syncthreads();
+__device__ __forceinline__ unsigned long long wave_sum_u64(unsigned long long v) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) {
+    const uint32_t lo = __shfl_xor(static_cast<uint32_t>(v), off, kWave);
+    const uint32_t hi = __shfl_xor(static_cast<uint32_t>(v >> 32), off, kWave);
+    v += (static_cast<unsigned long long>(hi) << 32) | lo;
+  }
+  return v;
+}
+
+__global__ __launch_bounds__(256) void k_dq_partial(const float* __restrict__ absmax, int64_t nb,
+                                                    unsigned long long* __restrict__ ws) {
+  __shared__ unsigned long long acc_lds[4][kDqDigits];
+  // Each thread keeps the digits in registers: a contribution lands in digit
+  // d (low 32 bits) and d + 1 (high bits); selects keep the indexing static.
+  unsigned long long acc[kDqDigits];
+#pragma unroll
+  for (int k = 0; k < kDqDigits; ++k) acc[k] = 0ull;
+  // 8 loads in flight per thread before any of them is used
+  constexpr int kUnroll = 8;
   const int64_t stride = static_cast<int64_t>(gridDim.x) * blockDim.x;
-  for (int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < nb; i += stride) {
-    int d;
-    uint32_t lo, hi;
-    scale_to_digits(absmax[i], &d, &lo, &hi);
-    if (lo) atomicAdd(&acc[d], static_cast<unsigned long long>(lo));
-    if (hi) atomicAdd(&acc[d + 1], static_cast<unsigned long long>(hi));
+  for (int64_t i0 = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; i0 < nb; i0 += kUnroll * stride) {
+    float v[kUnroll];
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      const int64_t i = i0 + u * stride;
+      v[u] = (i < nb) ? absmax[i] : 0.0f;
+    }
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      int d;
+      uint32_t lo, hi;
+      scale_to_digits(v[u], &d, &lo, &hi);
+#pragma unroll
+      for (int k = 0; k < kDqDigits; ++k)
+        acc[k] += static_cast<unsigned long long>((k == d ? lo : 0u)) + static_cast<unsigned long long>((k == d + 1 ? hi : 0u));
+    }
+  }
+  const int wave = threadIdx.x >> 6;
+#pragma unroll
+  for (int k = 0; k < kDqDigits; ++k) {
+    const unsigned long long v = wave_sum_u64(acc[k]);
+    if ((threadIdx.x & 63) == 0) acc_lds[wave][k] = v;
   }
   __syncthreads();
-  if (threadIdx.x < kDqDigits && acc[threadIdx.x]) atomicAdd(&ws[threadIdx.x], acc[threadIdx.x]);
-  __threadfence();
+  if (threadIdx.x < kDqDigits) {
+    const int k = threadIdx.x;
+    ws[blockIdx.x * kDqDigits + k] = acc_lds[0][k] + acc_lds[1][k] + acc_lds[2][k] + acc_lds[3][k];
+  }
+}
+
+// One workgroup of 256 threads: the partial rows (at most 256 x 12 values)
+// are loaded in parallel and added per digit in LDS; thread 0 propagates the
+// carries and rounds.
+__global__ __launch_bounds__(256) void k_dq_mean(const unsigned long long* __restrict__ ws, int nparts, int64_t nb,
+                                                 float* __restrict__ mean_out) {
+  __shared__ unsigned long long tot[kDqDigits];
+  if (threadIdx.x < kDqDigits) tot[threadIdx.x] = 0ull;
   __syncthreads();
-  if (threadIdx.x == 0) {
-    const unsigned long long prev = atomicAdd(&ws[kDqDoneSlot], 1ull);
-    is_last = (prev == gridDim.x - 1);
+  constexpr int kPer = (kDqMaxGroups * kDqDigits + 255) / 256;
+  unsigned long long v[kPer];
+  const int nvals = nparts * kDqDigits;
+#pragma unroll
+  for (int u = 0; u < kPer; ++u) {
+    const int i = threadIdx.x + 256 * u;
+    v[u] = i < nvals ? ws[i] : 0ull;
+  }
+#pragma unroll
+  for (int u = 0; u < kPer; ++u) {
+    const int i = threadIdx.x + 256 * u;
+    if (i < nvals && v[u]) atomicAdd(&tot[i % kDqDigits], v[u]);
   }
   __syncthreads();
-  if (!is_last || threadIdx.x != 0) return;
-  __threadfence();
+  if (threadIdx.x != 0) return;
   uint32_t dig[kDqDigits];
   unsigned long long carry = 0;
+#pragma unroll
   for (int k = 0; k < kDqDigits; ++k) {
-    const unsigned long long t =
-        __hip_atomic_load(&ws[k], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + carry;
+    const unsigned long long t = tot[k] + carry;
     dig[k] = static_cast<uint32_t>(t);
     carry = t >> 32;
   }
-  const double total = digits_to_double(dig, kDqDigits);
+  const double total = digits_to_double(dig);
   *mean_out = static_cast<float>(total / static_cast<double>(nb));
 }
 
@@ -138,10 +195,10 @@ __global__ __launch_bounds__(256) void k_dq_quant(const float* __restrict__ absm
 
 hipError_t launch_double_quant(const float* absmax, int64_t nb, int8_t* q, float* absmax2,
                                float* mean, unsigned long long* ws, hipStream_t s) {
-  hipLaunchKernelGGL(k_dq_clear, dim3(1), dim3(64), 0, s, ws);
-  int64_t want = (nb + 255) / 256;
-  int grid = static_cast<int>(want < 1024 ? want : 1024);
-  hipLaunchKernelGGL(k_dq_sum, dim3(grid), dim3(256), 0, s, absmax, nb, ws, mean);
+  int64_t want = (nb + 2047) / 2048;  // 8 scales per thread
+  int grid = static_cast<int>(want < kDqMaxGroups ? want : kDqMaxGroups);
+  hipLaunchKernelGGL(k_dq_partial, dim3(grid), dim3(256), 0, s, absmax, nb, ws);
+  hipLaunchKernelGGL(k_dq_mean, dim3(1), dim3(256), 0, s, ws, grid, nb, mean);
   const int64_t groups = (nb + 255) >> 8;
   want = (groups + 3) / 4;  // 4 waves per workgroup
   grid = static_cast<int>(want < 8192 ? want : 8192);

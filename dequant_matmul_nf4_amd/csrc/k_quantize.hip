@@ -1,87 +1,147 @@
 // Blockwise NF4 quantization (bitsandbytes tool page, "How it works",
 // Steps 1-4): per block of 64 values, the largest |x| is the scale; each value
-// is divided by it (IEEE float32 division) and replaced by the index of the
-// nearest NF4 level; two indices are packed per byte, the first in the high
-// nibble.
+// is divided by it and replaced by the index of the nearest NF4 level; two
+// indices are packed per byte, the first in the high nibble.
 //
-// Layout: each lane owns 8 consecutive values (one 16-byte bf16 load or two
-// 16-byte fp32 loads) and writes one 32-bit word of packed codes; 8 adjacent
-// lanes form one 64-block and reduce its absmax with lane shuffles.
+// Layout: each lane owns 16 consecutive values (two 16-byte bf16 loads or
+// four 16-byte fp32 loads) and writes 8 bytes of packed codes; 4 adjacent
+// lanes form one 64-block and reduce its absmax with DPP quad permutes.
+//
+// Division: the normalized value must be the IEEE float32 quotient
+// fl32(x / a).  With y = fl32(1 / a) correctly rounded (one IEEE division per
+// lane and block), q0 = fl32(x * y), r = fma(-q0, a, x) and q = fma(r, y, q0)
+// give exactly fl32(x / a) (Markstein's theorem: y within half an ulp of 1/a,
+// q0 within one ulp of x/a, r exact) whenever no intermediate underflows.
+// That holds for 2^-98 <= a < 2^126 and |x / a| >= 2^-5; below 2^-5 every
+// value maps to the zero level whatever its last bits.  Blocks whose absmax
+// lies outside that range take the IEEE division per value.
+//
+// Nearest level: a 2048-entry bucket table in LDS indexed by the top 11 bits
+// of the normalized value (sign, exponent, two significand bits); each bucket
+// holds at most one decision threshold, so code = base + (q >= thr).
 #include "nf4_device.h"
 
 namespace nf4i {
 namespace {
 
+constexpr int kPerLane = 16;
+
+__device__ __forceinline__ float quad_max(float v) {
+  v = fmaxf(v, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0xB1, 0xF, 0xF, false)));  // lane ^ 1
+  v = fmaxf(v, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x4E, 0xF, 0xF, false)));  // lane ^ 2
+  return v;
+}
+
 template <bool kBf16>
-__device__ __forceinline__ void load8(const void* xv, int64_t e0, int64_t n, float v[8]) {
-  if (e0 + 8 <= n) {
+__device__ __forceinline__ void load16(const void* xv, int64_t e0, int64_t, float v[kPerLane]) {
+  {
     if constexpr (kBf16) {
-      const uint4 w = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(xv) + e0);
-      const uint32_t q[4] = {w.x, w.y, w.z, w.w};
+      const uint4* p = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(xv) + e0);
+      const uint4 a = p[0], b = p[1];
+      const uint32_t q[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
+      for (int i = 0; i < 8; ++i) {
         v[2 * i] = __uint_as_float(q[i] << 16);
         v[2 * i + 1] = __uint_as_float(q[i] & 0xFFFF0000u);
       }
     } else {
       const float4* p = reinterpret_cast<const float4*>(static_cast<const float*>(xv) + e0);
-      const float4 a = p[0], b = p[1];
-      v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
-      v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
-    }
-  } else {
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      if (e0 + i < n) {
-        if constexpr (kBf16) v[i] = bf16_to_f32(static_cast<const uint16_t*>(xv)[e0 + i]);
-        else v[i] = static_cast<const float*>(xv)[e0 + i];
-      } else {
-        v[i] = 0.0f;  // padding: does not change the absmax, never stored
+      for (int i = 0; i < 4; ++i) {
+        const float4 t = p[i];
+        v[4 * i] = t.x; v[4 * i + 1] = t.y; v[4 * i + 2] = t.z; v[4 * i + 3] = t.w;
       }
     }
   }
 }
 
-__device__ __forceinline__ uint32_t nearest_code(float v, const Codebook& cb) {
-  uint32_t c = 0;
-#pragma unroll
-  for (int i = 0; i < 15; ++i) c += (v >= cb.thresh[i]) ? 1u : 0u;
-  return c;
+__device__ __forceinline__ uint32_t code_of(float q, const uint2* lut) {
+  const uint2 e = lut[__float_as_uint(q) >> 21];
+  return e.y + ((q >= __uint_as_float(e.x)) ? 1u : 0u);
 }
 
+// Quantizes one 16-value segment held by a lane (its quad holds the block)
+// and stores its 8 packed bytes and, from the quad's first lane, the absmax.
+__device__ __forceinline__ void quantize_segment(const float v[kPerLane], int64_t sg, uint8_t* __restrict__ packed,
+                                                 float* __restrict__ absmax, const uint2* lut, int64_t nbytes,
+                                                 bool full) {
+  float a = 0.0f;
+#pragma unroll
+  for (int i = 0; i < kPerLane; ++i) a = fmaxf(a, fabsf(v[i]));
+  a = quad_max(a);
+  uint32_t w0 = 0x77777777u, w1 = 0x77777777u;  // all-zero block: zero level everywhere
+  if (a > 0.0f) {
+    uint32_t c[kPerLane];
+    if (a >= 0x1p-98f && a < 0x1p126f) {
+      const float y = 1.0f / a;
+#pragma unroll
+      for (int i = 0; i < kPerLane; ++i) {
+        const float q0 = v[i] * y;
+        const float r = fmaf(-q0, a, v[i]);
+        c[i] = code_of(fmaf(r, y, q0), lut);
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < kPerLane; ++i) c[i] = code_of(v[i] / a, lut);
+    }
+    w0 = 0;
+    w1 = 0;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      // element 2j -> high nibble of byte j, element 2j+1 -> low nibble
+      const int sh = 8 * (i >> 1) + ((i & 1) ? 0 : 4);
+      w0 |= c[i] << sh;
+      w1 |= c[i + 8] << sh;
+    }
+  }
+  const int64_t byte0 = sg * (kPerLane / 2);
+  if (full) {
+    *reinterpret_cast<uint2*>(packed + byte0) = make_uint2(w0, w1);
+  } else {
+    for (int j = 0; j < 8; ++j)
+      if (byte0 + j < nbytes) packed[byte0 + j] = static_cast<uint8_t>((j < 4 ? w0 : w1) >> (8 * (j & 3)));
+  }
+  if ((threadIdx.x & 3) == 0) absmax[sg >> 2] = a;
+}
+
+// Main loop over the blocks that hold 64 values: each lane takes two
+// segments per iteration and issues both loads before using either; there
+// is no branch around any load.  A partial last block is done afterwards by
+// the first quad of workgroup 0 with guarded loads and stores.
 template <bool kBf16>
 __global__ __launch_bounds__(256) void k_quantize(const void* __restrict__ x, int64_t n,
                                                   uint8_t* __restrict__ packed,
-                                                  float* __restrict__ absmax, Codebook cb) {
-  const int64_t nblocks = (n + 63) >> 6;
-  const int64_t noct = nblocks * 8;  // whole blocks, so 8-lane groups stay together
+                                                  float* __restrict__ absmax, QuantLut tab) {
+  __shared__ uint2 lut[kLutBuckets];
+  for (int i = threadIdx.x; i < kLutBuckets; i += blockDim.x) lut[i] = make_uint2(0x7F800000u, 7u);
+  __syncthreads();
+  if (threadIdx.x < kLutSpecial)
+    lut[lut_special_index(threadIdx.x)] = make_uint2(__float_as_uint(tab.thr[threadIdx.x]), tab.base[threadIdx.x]);
+  __syncthreads();
+
+  const int64_t nfull = n >> 6;
+  const int64_t nseg = nfull * 4;
   const int64_t nbytes = (n + 1) >> 1;
   const int64_t stride = static_cast<int64_t>(gridDim.x) * blockDim.x;
-  for (int64_t o = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; o < noct; o += stride) {
-    float v[8];
-    load8<kBf16>(x, o * 8, n, v);
-    float m = 0.0f;
+  for (int64_t sg0 = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; sg0 < nseg; sg0 += 2 * stride) {
+    const int64_t sg1 = sg0 + stride;
+    const int64_t sg1c = sg1 < nseg ? sg1 : sg0;  // clamped: the load is always issued
+    float v0[kPerLane], v1[kPerLane];
+    load16<kBf16>(x, sg0 * kPerLane, n, v0);
+    load16<kBf16>(x, sg1c * kPerLane, n, v1);
+    quantize_segment(v0, sg0, packed, absmax, lut, nbytes, true);
+    if (sg1 < nseg) quantize_segment(v1, sg1, packed, absmax, lut, nbytes, true);
+  }
+  if ((n & 63) && blockIdx.x == 0 && threadIdx.x < 4) {
+    const int64_t sg = nseg + threadIdx.x;
+    float v[kPerLane];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) m = fmaxf(m, fabsf(v[i]));
-    m = group_max<8>(m);
-    uint32_t word = 0x77777777u;  // all codes 7 when the block is all zero
-    if (m > 0.0f) {
-      word = 0;
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const uint32_t c = nearest_code(v[i] / m, cb);
-        // element 2j -> high nibble of byte j, element 2j+1 -> low nibble
-        word |= c << (8 * (i >> 1) + ((i & 1) ? 0 : 4));
-      }
+    for (int i = 0; i < kPerLane; ++i) {
+      const int64_t e = sg * kPerLane + i;
+      if constexpr (kBf16) v[i] = e < n ? bf16_to_f32(static_cast<const uint16_t*>(x)[e]) : 0.0f;
+      else v[i] = e < n ? static_cast<const float*>(x)[e] : 0.0f;
     }
-    const int64_t byte0 = o * 4;
-    if (byte0 + 4 <= nbytes) {
-      *reinterpret_cast<uint32_t*>(packed + byte0) = word;
-    } else {
-      for (int j = 0; j < 4; ++j)
-        if (byte0 + j < nbytes) packed[byte0 + j] = static_cast<uint8_t>(word >> (8 * j));
-    }
-    if ((threadIdx.x & 7) == 0) absmax[o >> 3] = m;
+    quantize_segment(v, sg, packed, absmax, lut, nbytes, false);
   }
 }
 
@@ -89,14 +149,17 @@ __global__ __launch_bounds__(256) void k_quantize(const void* __restrict__ x, in
 
 hipError_t launch_quantize(const void* x, int x_bf16, int64_t n, uint8_t* packed, float* absmax,
                            hipStream_t s) {
-  const int64_t noct = ((n + 63) >> 6) * 8;
-  const int64_t want = (noct + 255) / 256;
-  const int grid = static_cast<int>(want < 16384 ? want : 16384);
-  const Codebook& cb = codebook();
+  // two segments per lane and one pass per lane: a loop would make the next
+  // loads wait for the previous stores (their registers are reused)
+  const int64_t nseg = (n >> 6) * 4;
+  const int64_t want = (nseg + 511) / 512;
+  if (want > 0x7FFFFFFF) return hipErrorInvalidValue;
+  const int grid = static_cast<int>(want < 1 ? 1 : want);
+  const QuantLut& tab = quant_lut();
   if (x_bf16)
-    hipLaunchKernelGGL(k_quantize<true>, dim3(grid), dim3(256), 0, s, x, n, packed, absmax, cb);
+    hipLaunchKernelGGL(k_quantize<true>, dim3(grid), dim3(256), 0, s, x, n, packed, absmax, tab);
   else
-    hipLaunchKernelGGL(k_quantize<false>, dim3(grid), dim3(256), 0, s, x, n, packed, absmax, cb);
+    hipLaunchKernelGGL(k_quantize<false>, dim3(grid), dim3(256), 0, s, x, n, packed, absmax, tab);
   return hipGetLastError();
 }
 

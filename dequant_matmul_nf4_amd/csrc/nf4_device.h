@@ -22,13 +22,32 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   return f32_to_bf16(lo) | (f32_to_bf16(hi) << 16);
 }
 
+// fl32(q / 127) for an int8 q: from y = fl32(1/127), q0 = fl32(q y) and the
+// exact residual r = q - q0 * 127, fl32(q0 + r y) is the correctly rounded
+// quotient (Markstein's theorem; also checked for all 256 values of q).
+__device__ __forceinline__ float div127(int q) {
+  const float f = static_cast<float>(q);
+  const float y = 1.0f / 127.0f;
+  const float q0 = f * y;
+  const float r = fmaf(-q0, 127.0f, f);
+  return fmaf(r, y, q0);
+}
+
 // The scale of block b: either the stored fp32 absmax, or the double-quantized
 // form a_hat = fl32(fl32(fl32(q / 127) * s2) + mean), three separate roundings.
 __device__ __forceinline__ float block_scale(const Scales& sc, int64_t b, float mean) {
   if (sc.absmax) return sc.absmax[b];
-  const float t = static_cast<float>(sc.q[b]) / 127.0f;
+  const float t = div127(sc.q[b]);
   const float u = t * sc.absmax2[b >> 8];
   return u + mean;
+}
+
+// Hides a value from the optimizer so that byte-field extracts of a masked
+// word stay single v_bfe_u32 instructions instead of being re-derived from
+// the unmasked word with shift-and-mask pairs.
+__device__ __forceinline__ uint32_t opaque(uint32_t v) {
+  asm volatile("" : "+v"(v));
+  return v;
 }
 
 template <int kWidth>

@@ -18,6 +18,30 @@ struct Codebook {
 // Host derivation, computed once (thread-safe) at first use.
 const Codebook& codebook();
 
+// Bucket table of the quantizer's nearest-level search.  A normalized value
+// v in [-1, 1] falls in bucket (bits(v) >> 21): its sign, exponent and two
+// leading significand bits.  Each bucket holds at most one decision
+// threshold, so code(v) = base[bucket] + (v >= thr[bucket]).  Buckets with
+// |v| < 2^-5 all give code 7; only the 48 buckets with exponent 2^-5 .. 2^0
+// differ, and those are listed here (order: sign, exponent, bits).
+constexpr int kLutBuckets = 2048;
+constexpr int kLutSpecial = 48;
+constexpr int kLutFirstExp = 122;  // 2^-5
+struct QuantLut {
+  float thr[kLutSpecial];
+  uint32_t base[kLutSpecial];
+};
+const QuantLut& quant_lut();
+
+__host__ __device__ inline int lut_special_index(int t) {
+  const int sign = t / 24, e = kLutFirstExp + (t % 24) / 4, m2 = t % 4;
+  return (sign << 10) | (e << 2) | m2;
+}
+
+// Compute units of the current device (set by the front end's device check
+// before any launch; used to size persistent grids).
+int device_cus();
+
 // Scale description shared by the consumers of a quantized weight.
 struct Scales {
   const float* absmax;   // non-null: plain scales
@@ -26,10 +50,11 @@ struct Scales {
   const float* mean;
 };
 
-// Workspace layout of the double-quant kernels (device, 16 x u64).
+// Workspace of the double-quant kernels: one row of partial digit sums per
+// summing workgroup (at most kDqMaxGroups rows of kDqDigits u64).
 constexpr int kDqDigits = 12;      // 32-bit digits of the exact scale sum
-constexpr int kDqDoneSlot = 12;    // arrival counter of the summing blocks
-constexpr size_t kDqWorkspaceBytes = 16 * sizeof(unsigned long long);
+constexpr int kDqMaxGroups = 256;
+constexpr size_t kDqWorkspaceBytes = kDqMaxGroups * kDqDigits * sizeof(unsigned long long);
 
 hipError_t launch_quantize(const void* x, int x_bf16, int64_t n, uint8_t* packed,
                            float* absmax, hipStream_t s);

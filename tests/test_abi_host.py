@@ -52,6 +52,7 @@ def test_codebook_bit_identical_to_oracle(L):
 
 def test_workspace_sizes(L):
     assert nf4.nf4_double_quant_workspace(1) >= 16 * 8
+    assert nf4.nf4_double_quant_workspace(1 << 30) <= WS
     assert nf4.nf4_gemm_workspace(4096, 14336, 0) == 0
     assert nf4.nf4_gemm_workspace(4096, 14336, 16) >= 4096 * 16 * 4
     assert nf4.nf4_gemm_workspace(4096, 14336, 16) % 256 == 0
@@ -66,6 +67,7 @@ def test_struct_layout():
 # host, before any HIP call, so nothing is dereferenced.
 A = 0x10000
 A2 = 0x20000
+WS = 1 << 20   # a workspace size larger than any call needs
 
 
 def _w(**kw):
@@ -84,12 +86,12 @@ CASES = [
     ("quantize misaligned x", lambda L: L.nf4_quantize(A + 2, 1, 64, 64, A, A2, None), nf4.NF4_ERR_ALIGN),
     ("quantize misaligned packed", lambda L: L.nf4_quantize(A, 1, 64, 64, A + 8, A2, None), nf4.NF4_ERR_ALIGN),
     ("quantize misaligned absmax", lambda L: L.nf4_quantize(A, 1, 64, 64, A, A2 + 2, None), nf4.NF4_ERR_ALIGN),
-    ("dq null", lambda L: L.nf4_double_quant(A, 10, 256, None, A2, A2, A, 128, None), nf4.NF4_ERR_NULL),
-    ("dq nblocks", lambda L: L.nf4_double_quant(A, 0, 256, A, A2, A2, A, 128, None), nf4.NF4_ERR_SIZE),
-    ("dq blocksize2", lambda L: L.nf4_double_quant(A, 10, 128, A, A2, A2, A, 128, None), nf4.NF4_ERR_BLOCKSIZE),
+    ("dq null", lambda L: L.nf4_double_quant(A, 10, 256, None, A2, A2, A, WS, None), nf4.NF4_ERR_NULL),
+    ("dq nblocks", lambda L: L.nf4_double_quant(A, 0, 256, A, A2, A2, A, WS, None), nf4.NF4_ERR_SIZE),
+    ("dq blocksize2", lambda L: L.nf4_double_quant(A, 10, 128, A, A2, A2, A, WS, None), nf4.NF4_ERR_BLOCKSIZE),
     ("dq workspace small", lambda L: L.nf4_double_quant(A, 10, 256, A, A2, A2, A, 8, None), nf4.NF4_ERR_WORKSPACE),
-    ("dq workspace null", lambda L: L.nf4_double_quant(A, 10, 256, A, A2, A2, None, 128, None), nf4.NF4_ERR_WORKSPACE),
-    ("dq misaligned q", lambda L: L.nf4_double_quant(A, 10, 256, A + 1, A2, A2, A, 128, None), nf4.NF4_ERR_ALIGN),
+    ("dq workspace null", lambda L: L.nf4_double_quant(A, 10, 256, A, A2, A2, None, WS, None), nf4.NF4_ERR_WORKSPACE),
+    ("dq misaligned q", lambda L: L.nf4_double_quant(A, 10, 256, A + 1, A2, A2, A, WS, None), nf4.NF4_ERR_ALIGN),
     ("dequant null weight", lambda L: L.nf4_dequantize(None, A, 1, None), nf4.NF4_ERR_NULL),
     ("dequant null out", lambda L: L.nf4_dequantize(ctypes.byref(_w()), None, 1, None), nf4.NF4_ERR_NULL),
     ("dequant bad dtype", lambda L: L.nf4_dequantize(ctypes.byref(_w()), A, 3, None), nf4.NF4_ERR_DTYPE),

@@ -99,8 +99,10 @@ def test_gemv_c3_sampled_rows(name, m):
 
 
 def test_gemv_one_hot_and_determinism():
-    """x = e_k returns column k of the dequantized weight (to float32
-    accumulation of exact products); two runs give identical bits."""
+    """x = e_k returns column k of the dequantized weight.  The decode GEMV
+    multiplies with each level split into two bf16 parts, which together lie
+    within 2^-17 of the float32 level, so the column is matched to 2^-16
+    relative; two runs give identical bits."""
     say("gemv one-hot")
     torch = need_gpu()
     rows, cols = 256, 512
@@ -112,7 +114,8 @@ def test_gemv_one_hot_and_determinism():
         x[0, k] = 1.0
         y = nf4.nf4_gemv(W, x, y_dtype=torch.float32)
         torch.cuda.synchronize()
-        assert torch.equal(y[0], wdeq_f32[:, k])
+        ref = wdeq_f32[:, k]
+        assert bool(((y[0] - ref).abs() <= ref.abs() * 2.0 ** -16).all())
     x = syn.to_bf16(syn.normal_f32((4, cols), 1.0, 8)).to("cuda")
     y1 = nf4.nf4_gemv(W, x)
     y2 = nf4.nf4_gemv(W, x)
