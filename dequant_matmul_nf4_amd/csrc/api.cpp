@@ -173,8 +173,8 @@ int nf4_gemv(const nf4_weight* w, const void* x, int64_t m, void* y, int y_dtype
 
 size_t nf4_gemm_workspace(int64_t m, int64_t rows, int32_t r) {
   (void)rows;
-  if (m < 1 || r < 1) return 0;
-  const size_t bytes = static_cast<size_t>(m) * static_cast<size_t>(r) * sizeof(float);
+  if (m < 1 || r < 1 || r > 64) return 0;
+  const size_t bytes = static_cast<size_t>(m) * nf4i::gemm_lora_cols(r) * sizeof(uint16_t);
   return (bytes + 255) & ~size_t(255);
 }
 
@@ -206,7 +206,7 @@ int nf4_gemm(const nf4_weight* w, const void* x, int64_t m, void* y, const void*
   return launched(nf4i::launch_gemm(w->packed, w->rows, w->cols, sc, static_cast<const uint16_t*>(x), m,
                                     static_cast<uint16_t*>(y), static_cast<const uint16_t*>(lora_a),
                                     static_cast<const uint16_t*>(lora_b), lora_a ? r : 0, lora_scale,
-                                    static_cast<float*>(workspace), as_stream(stream)),
+                                    static_cast<uint16_t*>(workspace), as_stream(stream)),
                   "nf4_gemm");
 }
 

@@ -64,9 +64,12 @@ hipError_t launch_dequantize(const uint8_t* packed, int64_t n, Scales sc, void* 
                              int out_bf16, hipStream_t s);
 hipError_t launch_gemv(const uint8_t* packed, int64_t rows, int64_t cols, Scales sc,
                        const uint16_t* x, int64_t m, void* y, int y_bf16, hipStream_t s);
+// Extra K columns the GEMM uses for a LoRA term of rank r (0 without one);
+// the workspace holds m rows of that many bf16 values.
+size_t gemm_lora_cols(int r);
 hipError_t launch_gemm(const uint8_t* packed, int64_t rows, int64_t cols, Scales sc,
                        const uint16_t* x, int64_t m, uint16_t* y, const uint16_t* lora_a,
-                       const uint16_t* lora_b, int r, float lora_scale, float* t_ws,
+                       const uint16_t* lora_b, int r, float lora_scale, uint16_t* u_ws,
                        hipStream_t s);
 
 }  // namespace nf4i

@@ -141,7 +141,7 @@ int nf4_gemv(const nf4_weight* w, const void* x, int64_t m, void* y, int y_dtype
              void* stream);
 
 /* Bytes of device workspace nf4_gemm needs for m rows of x and LoRA rank r
- * (0 when r == 0). */
+ * (0 when r == 0): m rows of 2 r (rounded up to 64) bf16 values. */
 size_t nf4_gemm_workspace(int64_t m, int64_t rows, int32_t r);
 
 /* Dequantize-into-LDS bf16 matrix-core GEMM for prefill and training, with an

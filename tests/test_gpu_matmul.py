@@ -149,6 +149,26 @@ def test_gemm_small(m, rows, cols, lora, dq):
     assert e <= MATMUL_RTOL
 
 
+@pytest.mark.parametrize("m,rows,cols,r", [(513, 300, 320, 64), (100, 260, 64, 33), (33, 257, 128, 17)])
+def test_gemm_lora_ranks(m, rows, cols, r):
+    """Largest rank, ranks that are not a multiple of 16, ragged M and N."""
+    say("gemm lora rank", r, "shape", m, rows, cols)
+    torch = need_gpu()
+    w = syn.normal_f32((rows, cols), 0.02, 40 + r)
+    xb = syn.to_bf16(syn.normal_f32((m, cols), 1.0, 41 + r))
+    a = syn.to_bf16(syn.normal_f32((r, cols), 0.02, 42 + r))
+    b = syn.to_bf16(syn.normal_f32((rows, r), 0.02, 43 + r))
+    s = 16.0 / r
+    W = nf4.quantize_weight(to_dev(w), double_quant=True)
+    y = nf4.nf4_gemm(W, xb.to("cuda"), lora_a=a.to("cuda"), lora_b=b.to("cuda"), lora_scale=s)
+    torch.cuda.synchronize()
+    ref = oracle.matmul_ref(syn.bf16_to_f32(xb), _full_oracle_wdeq(w, True), syn.bf16_to_f32(a),
+                            syn.bf16_to_f32(b), s)
+    e = oracle.rel_frobenius(_y_f64(y), ref)
+    say(f"  rel err {e:.2e}")
+    assert e <= MATMUL_RTOL
+
+
 def test_gemm_lora_only_term_and_zero_b():
     """With B = 0 the LoRA path adds nothing; with a one-hot x the product
     returns a dequantized column exactly rounded to bf16."""
