@@ -43,7 +43,49 @@ def parse():
     p.add_argument("--pool", type=int, default=16)
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-extra", action="store_true")
+    p.add_argument("--calibrate-copy", action="store_true",
+                   help="only run a plain 64 MiB device copy kernel (for scaling HBM byte counters)")
     return p.parse_args()
+
+
+# HBM bytes of the dominant kernel as read by the FETCH_SIZE / WRITE_SIZE
+# counters (profiles/), kept only while the kernel's sources are unchanged.
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "k_quantize_bf16_4096x4096_traffic.json")
+QUANT_SOURCES = ["k_quantize.hip", "nf4_device.h", "nf4_internal.h"]
+
+
+def sources_digest(names) -> str:
+    import hashlib
+    h = hashlib.sha256()
+    for n in names:
+        with open(os.path.join(ROOT, "dequant_matmul_nf4_amd", "csrc", n), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def measured_traffic():
+    try:
+        with open(TRAFFIC_FILE) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if rec.get("sources_sha256") != sources_digest(QUANT_SOURCES):
+        return None
+    return rec.get("traffic_bytes_per_launch")
+
+
+def calibrate_copy():
+    """A plain elementwise copy (y = -x) of 64 MiB of float32: the kernel reads
+    and writes exactly 64 MiB, which fixes the scale of the byte counters."""
+    import torch
+    n = 16 << 20
+    src = torch.ones(n, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(5):
+        torch.neg(src, out=dst)
+    torch.cuda.synchronize()
+    print(json.dumps({"calibration": "neg_copy", "bytes_read": 4 * n, "bytes_written": 4 * n, "launches": 5}))
+    return 0
 
 
 def step_bytes(rows: int, cols: int, m: int = 1) -> dict:
@@ -55,6 +97,14 @@ def step_bytes(rows: int, cols: int, m: int = 1) -> dict:
     dq = 4 * nb + nb + 4 * ng + 4
     gemv = n // 2 + nb + 4 * ng + 4 + 2 * m * cols + 2 * m * rows
     return {"quantize": quant, "double_quant": dq, "gemv": gemv}
+
+
+def capture_graph(torch, fn):
+    """Captures the launches fn() makes on the current stream into a HIP graph."""
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, capture_error_mode="relaxed"):
+        fn()
+    return g
 
 
 class EventTimer:
@@ -83,6 +133,9 @@ def main():
         print(json.dumps({"error": "this build runs on one GPU only; use --gpus 1"}))
         print("bench.py: only --gpus 1 is supported (single-GPU build)", file=sys.stderr)
         return 2
+
+    if args.calibrate_copy:
+        return calibrate_copy()
 
     import numpy as np
     import torch
@@ -113,38 +166,56 @@ def main():
             y=torch.empty((1, rows), dtype=torch.bfloat16, device=dev),
         ))
     dq_ws = torch.empty(nf4.nf4_double_quant_workspace(nb), dtype=torch.uint8, device=dev)
-    tq = EventTimer(torch, stream)
-    tg = EventTimer(torch, stream)
+    Wq = [nf4.NF4Weight(b["packed"], rows, cols, qabsmax=b["q"], absmax2=b["s2"], mean=b["mean"]) for b in bufs]
 
-    def one_step(timed: bool):
+    def run_quantize():
         for i in range(P):
-            b = bufs[i]
-            s = tq.start() if timed else None
-            nf4.nf4_quantize(ws[i], b["packed"], b["absmax"])
-            if timed:
-                tq.stop(s)
+            nf4.nf4_quantize(ws[i], bufs[i]["packed"], bufs[i]["absmax"])
+
+    def run_double_quant():
+        for b in bufs:
             nf4.nf4_double_quant(b["absmax"], b["q"], b["s2"], b["mean"], dq_ws)
-            W = nf4.NF4Weight(b["packed"], rows, cols, qabsmax=b["q"], absmax2=b["s2"], mean=b["mean"])
-            s = tg.start() if timed else None
-            nf4.nf4_gemv(W, x, b["y"])
-            if timed:
-                tg.stop(s)
+
+    def run_gemv():
+        for i in range(P):
+            nf4.nf4_gemv(Wq[i], x, bufs[i]["y"])
+
+    # One step = quantize every weight of the pool, double-quantize every
+    # absmax, then the decode GEMV on every weight: three HIP graphs replayed
+    # back to back on the current stream, with events between them (so the
+    # per-kernel averages come from the timed region itself).
+    print("[bench] eager warmup and graph capture", file=sys.stderr, flush=True)
+    for f in (run_quantize, run_double_quant, run_gemv):
+        f()
+    torch.cuda.synchronize()
+    graphs = [capture_graph(torch, f) for f in (run_quantize, run_double_quant, run_gemv)]
+    torch.cuda.synchronize()
+
+    def one_step(ev=None):
+        for j, g in enumerate(graphs):
+            if ev is not None:
+                ev[j].record(stream)
+            g.replay()
+        if ev is not None:
+            ev[3].record(stream)
 
     print("[bench] warmup", file=sys.stderr, flush=True)
     for _ in range(args.warmup):
-        one_step(False)
+        one_step()
     torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
     print(f"[bench] timing {args.steps} steps", file=sys.stderr, flush=True)
+    torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for _ in range(args.steps):
-        one_step(True)
+    for k in range(args.steps):
+        one_step(evs[k])
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
     sb = step_bytes(rows, cols)
     bytes_per_step = P * sum(sb.values())
     value = bytes_per_step * args.steps / elapsed / 1e9
-    q_us = tq.mean_us()
-    g_us = tg.mean_us()
+    phase_us = [1e3 * sum(e[j].elapsed_time(e[j + 1]) for e in evs) / (args.steps * P) for j in range(3)]
+    q_us, d_us, g_us = phase_us
     q_gbs = sb["quantize"] / (q_us * 1e-6) / 1e9
     g_gbs_hot = sb["gemv"] / (g_us * 1e-6) / 1e9
 
@@ -165,7 +236,8 @@ def main():
             "workload": "Llama-8B attention projection 4096x4096 bf16, N(0,0.02) + 0.1% outliers x20; "
                         "NF4 blocksize 64 + double quant (int8, groups of 256); batch-1 decode GEMV",
             "pool_weights": P,
-            "step": "per weight: nf4_quantize + nf4_double_quant + nf4_gemv",
+            "step": "nf4_quantize of every pool weight, nf4_double_quant of every absmax, nf4_gemv on every "
+                    "weight (three HIP graphs)",
             "bytes_per_step": bytes_per_step,
         },
         "roofline": {
@@ -175,14 +247,15 @@ def main():
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(q_gbs / HBM_PEAK_GBS, 4),
-            "traffic": None,
+            "traffic": measured_traffic(),
             "bytes_per_launch": sb["quantize"],
             "avg_launch_us": round(q_us, 3),
         },
         "kernels_in_step": {
             "quantize_us": round(q_us, 3),
+            "double_quant_us": round(d_us, 3),
             "gemv_us": round(g_us, 3),
-            "gemv_GBps_after_quantize": round(g_gbs_hot, 1),
+            "gemv_GBps_packed_just_written": round(g_gbs_hot, 1),
         },
     }
 
@@ -213,15 +286,21 @@ def extra_legs(torch, nf4, syn, dev, stream, EventTimer):
         del w
     x = syn.c2_inputs()["x"].to(dev)
     y = torch.empty((1, rows), dtype=torch.bfloat16, device=dev)
-    for W in Ws[:8]:
-        nf4.nf4_gemv(W, x, y)
+
+    def run():
+        for W in Ws:
+            nf4.nf4_gemv(W, x, y)
+
+    run()
+    torch.cuda.synchronize()
+    graph = capture_graph(torch, run)
+    graph.replay()
     torch.cuda.synchronize()
     t = EventTimer(torch, stream)
     s = t.start()
     reps = 20
     for _ in range(reps):
-        for W in Ws:
-            nf4.nf4_gemv(W, x, y)
+        graph.replay()
     t.stop(s)
     torch.cuda.synchronize()
     per_call_us = t.mean_us() / (reps * pool)
@@ -244,14 +323,19 @@ def extra_legs(torch, nf4, syn, dev, stream, EventTimer):
             del w
         xs = {c_: (torch.randn((1, c_), generator=g, device=dev)).to(torch.bfloat16) for _, c_ in shapes}
         ys = [torch.empty((1, r_), dtype=torch.bfloat16, device=dev) for r_, _ in shapes]
-        for W, yy in zip(Wl, ys):
-            nf4.nf4_gemv(W, xs[W.cols], yy)
+        def run():
+            for W, yy in zip(Wl, ys):
+                nf4.nf4_gemv(W, xs[W.cols], yy)
+
+        run()
+        torch.cuda.synchronize()
+        graph = capture_graph(torch, run)
+        graph.replay()
         torch.cuda.synchronize()
         t = EventTimer(torch, stream)
         s = t.start()
         for _ in range(reps):
-            for W, yy in zip(Wl, ys):
-                nf4.nf4_gemv(W, xs[W.cols], yy)
+            graph.replay()
         t.stop(s)
         torch.cuda.synchronize()
         total_us = t.mean_us() / reps
@@ -273,7 +357,8 @@ def extra_legs(torch, nf4, syn, dev, stream, EventTimer):
     g.manual_seed(4_005)
     X = torch.randn((M, K), generator=g, device=dev).to(torch.bfloat16)
     g.manual_seed(4_000)
-    W = nf4.quantize_weight((torch.randn((N, K), generator=g, device=dev) * 0.02).to(torch.bfloat16))
+    W = nf4.quantize_weight((torch.randn((N, K), generator=g, device=dev) * 0.02).to(torch.bfloat16),
+                            double_quant=True)
     g.manual_seed(4_006)
     A = (torch.randn((r, K), generator=g, device=dev) * 0.01).to(torch.bfloat16)
     g.manual_seed(4_007)
@@ -302,9 +387,10 @@ def extra_legs(torch, nf4, syn, dev, stream, EventTimer):
     return res
 
 
-def cpu_baseline(np, syn):
+def cpu_baseline(np, syn, min_seconds: float = 10.0):
     """The CPU oracle (as it stands) on one weight of the same workload:
-    quantize, double quant, dequantize and the float64 GEMV, single-threaded."""
+    quantize, double quant, dequantize and the float64 GEMV, single-threaded,
+    repeated until at least `min_seconds` have passed."""
     import oracle
     try:
         from threadpoolctl import threadpool_limits
@@ -316,20 +402,26 @@ def cpu_baseline(np, syn):
     x = syn.bf16_to_f32(syn.c2_inputs()["x"])
     import contextlib
     ctx = threadpool_limits(1) if threadpool_limits else contextlib.nullcontext()
+    reps = 0
     with ctx:
         t0 = time.perf_counter()
-        p, a = oracle.quantize(w)
-        q, s2, mu = oracle.double_quant(a)
-        wdeq = oracle.bf16_bits_to_f32(oracle.dequantize(p, w.size, qabsmax=q, absmax2=s2, mean=mu, out="bf16"))
-        oracle.matmul_ref(x, wdeq.reshape(rows, cols))
-        dt = time.perf_counter() - t0
+        while True:
+            p, a = oracle.quantize(w)
+            q, s2, mu = oracle.double_quant(a)
+            wdeq = oracle.bf16_bits_to_f32(oracle.dequantize(p, w.size, qabsmax=q, absmax2=s2, mean=mu, out="bf16"))
+            oracle.matmul_ref(x, wdeq.reshape(rows, cols))
+            reps += 1
+            dt = time.perf_counter() - t0
+            if dt >= min_seconds:
+                break
     sb = step_bytes(rows, cols)
     return {
-        "value": round(sum(sb.values()) / dt / 1e9, 4),
+        "value": round(reps * sum(sb.values()) / dt / 1e9, 4),
         "unit": "GB/s",
         "cores": 1,
         "kind": "oracle",
-        "sample": "one 4096x4096 weight of the workload: quantize + double quant + dequant + float64 GEMV",
+        "sample": f"{reps} passes over one 4096x4096 weight of the workload: quantize + double quant + "
+                  "dequant + float64 GEMV",
         "seconds": round(dt, 2),
     }
 
