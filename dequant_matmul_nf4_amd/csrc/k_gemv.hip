@@ -288,123 +288,247 @@ __global__ __launch_bounds__(1024) void k_gemv_m1(const uint8_t* __restrict__ pa
   }
 }
 
-// Variant with x staged in LDS (cols <= kXLdsMaxCols): the workgroup copies
-// x once into LDS, block c's 64 values at byte c * 144 (16 bytes of padding
-// per block keep the lanes' 16-byte reads in distinct banks), next to the
-// pair table.  The global loads of a step are then only the R rows' codes and
-// scales, and each wave prefetches the next step into a second register set
-// while it computes the current one.
-constexpr int64_t kXLdsMaxCols = 32768;
-constexpr int kXStride = 144;
+// ---------------------------------------------------------------- rows
+//
+// Decode GEMV with the load schedule of a streaming copy.  A workgroup owns a
+// contiguous range of rows; its waves split the columns into segments of up
+// to 64 blocks (one 64-block per lane) and the rows into equal parts, so each
+// wave walks a run of rows over one fixed column segment:
+//  - the lane's 64 values of x stay in registers for the whole run, as fp16
+//    pairs scaled by a power of two chosen from their largest magnitude (so
+//    the scaling is exact and nothing overflows; it is undone on the partial
+//    sum);
+//  - a byte of packed codes (two elements) indexes a 256-entry table of fp16
+//    level pairs in LDS, one copy per lane (address = byte * 256 + lane * 4,
+//    a single byte permute, every lane in its own bank), and one
+//    v_dot2c_f32_f16 takes both products; fp16 keeps 11 significant bits of
+//    each level;
+//  - a ring of U rows of loads (32 bytes of codes and the block's scale
+//    inputs per lane and row) stays in flight: slot u is consumed and at once
+//    refilled with the row U places ahead, indices clamped so that no branch
+//    separates the loads from their use;
+//  - each row's per-lane partial sum is reduced across the wave with DPP
+//    (total in lane 63) and parked in LDS per (row, segment); at the end the
+//    segments of each row are added in a fixed order, so the result does not
+//    depend on timing.
 
-__device__ __forceinline__ void lds_x_block(uint32_t xr[32], const char* xs, int64_t b) {
-  const char* p = xs + b * kXStride;
+constexpr int kRowsMaxWg = 512;   // rows per workgroup (LDS for the partial sums)
+constexpr int kSegMax = 16;       // column segments per workgroup (cols <= 65536)
+
+typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ float dot2h(uint32_t a, uint32_t b, float c) {
+  return __builtin_amdgcn_fdot2(__builtin_bit_cast(half2_t, a), __builtin_bit_cast(half2_t, b), c, false);
+}
+
+// Sum over the wave; the total is exact in lane 63 only.
+__device__ __forceinline__ float wave_sum_to_last(float v) {
+  v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0xB1, 0xF, 0xF, false));   // quad [1,0,3,2]
+  v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x4E, 0xF, 0xF, false));   // quad [2,3,0,1]
+  v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x124, 0xF, 0xF, false));  // row_ror:4
+  v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x128, 0xF, 0xF, false));  // row_ror:8
+  // rows 1 and 3 add the total of the row below, then rows 2 and 3 that of rows 0-1
+  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x142, 0xA, 0xF, false));  // row_bcast:15
+  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x143, 0xC, 0xF, false));  // row_bcast:31
+  return v;
+}
+
+// 256 fp16 level pairs (element 2j = high nibble in the low half), one copy
+// per lane slot; built in two phases so that each wave writes consecutive
+// addresses.  Ends with a barrier.
+__device__ __forceinline__ void fill_half_table(uint32_t* tab, uint32_t* base, const Codebook& cb) {
+  if (threadIdx.x < 256) {
+    const int e = threadIdx.x;
+    float l0 = cb.level[0], l1 = cb.level[0];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const uint4 t = *reinterpret_cast<const uint4*>(p + 16 * i);
-    xr[4 * i] = t.x; xr[4 * i + 1] = t.y; xr[4 * i + 2] = t.z; xr[4 * i + 3] = t.w;
+    for (int i = 1; i < 16; ++i) {
+      l0 = ((e >> 4) == i) ? cb.level[i] : l0;
+      l1 = ((e & 15) == i) ? cb.level[i] : l1;
+    }
+    const half2_t h = {static_cast<_Float16>(l0), static_cast<_Float16>(l1)};  // round to nearest even
+    base[e] = __builtin_bit_cast(uint32_t, h);
+  }
+  __syncthreads();
+  for (int i = threadIdx.x; i < 256 * 64; i += blockDim.x) tab[i] = base[i >> 6];
+  __syncthreads();
+}
+
+struct RowItem {
+  uint4 w[2];  // 32 bytes of packed codes: the lane's 64-block of one row
+  float am;    // absmax (plain scales)
+  int q;       // int8 scale code (double quant)
+  float s2;    // second-level scale (double quant)
+};
+
+// Loads of one row.  row_blk0 = row * nblk (wave-uniform); the lane adds its
+// block bc, so the code and scale addresses are a uniform base plus a fixed
+// per-lane offset.
+template <bool kDQ>
+__device__ __forceinline__ void row_load(RowItem& it, const uint8_t* __restrict__ packed, int64_t row_blk0, int bc,
+                                         Scales sc) {
+  const uint4* p = reinterpret_cast<const uint4*>(packed + row_blk0 * 32) + 2 * bc;
+  it.w[0] = p[0];
+  it.w[1] = p[1];
+  if constexpr (kDQ) {
+    it.q = sc.q[row_blk0 + bc];
+    // group of the block: uniform part plus a small per-lane carry
+    it.s2 = sc.absmax2[(row_blk0 >> 8) + (static_cast<int>(row_blk0 & 255) + bc >> 8)];
+  } else {
+    it.am = sc.absmax[row_blk0 + bc];
   }
 }
 
-template <int R, bool kDQ, bool kBf16Out>
-__global__ __launch_bounds__(1024) void k_gemv_m1_xl(const uint8_t* __restrict__ packed, int64_t rows,
-                                                     int64_t cols, Scales sc, const uint16_t* __restrict__ x,
-                                                     void* __restrict__ y, Codebook cb) {
-  __shared__ uint2 tab[256 * kTabSlots];
-  __shared__ uint2 tab_base[256];
-  __shared__ __align__(16) char xs[(kXLdsMaxCols / 64) * kXStride + 16];  // + a dummy slot
+template <bool kDQ>
+__device__ __forceinline__ float row_dot(const RowItem& it, const uint32_t* xh, const char* tab, uint32_t slot,
+                                         float mean, float xinv) {
+  const uint32_t q[8] = {it.w[0].x, it.w[0].y, it.w[0].z, it.w[0].w, it.w[1].x, it.w[1].y, it.w[1].z, it.w[1].w};
+  float s0 = 0.0f, s1 = 0.0f;
+#pragma unroll
+  for (int j = 0; j < 8; j += 2) {
+    uint32_t e[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const uint32_t addr = __builtin_amdgcn_perm(q[j + (u >> 2)], slot, 0x0C0C0000u | ((4u + (u & 3)) << 8));
+      e[u] = *reinterpret_cast<const uint32_t*>(tab + addr);
+    }
+#pragma unroll
+    for (int u = 0; u < 8; u += 2) {
+      s0 = dot2h(e[u], xh[4 * j + u], s0);
+      s1 = dot2h(e[u + 1], xh[4 * j + u + 1], s1);
+    }
+  }
+  float a;
+  if constexpr (kDQ) a = (div127(it.q) * it.s2) + mean;  // a_hat
+  else a = it.am;
+  return (s0 + s1) * (a * xinv);
+}
+
+struct RowsPlan {
+  int grid;          // number of workgroups
+  int nseg;          // column segments
+  int seg_blocks;    // blocks per segment (<= 64)
+  int wpr;           // waves per segment (row parts)
+};
+
+template <int U, int kWaves, bool kDQ, bool kBf16Out>
+__global__ __launch_bounds__(kWaves * 64) void k_gemv_rows(const uint8_t* __restrict__ packed, int64_t rows,
+                                                           int64_t cols, Scales sc, const uint16_t* __restrict__ x,
+                                                           void* __restrict__ y, Codebook cb, RowsPlan pl) {
+  __shared__ uint32_t tab[256 * 64];
+  __shared__ uint32_t tab_base[256];
+  __shared__ float part[kRowsMaxWg * kSegMax];
   const char* smem = reinterpret_cast<const char*>(tab);
   const int lane = threadIdx.x & 63;
-  const uint32_t slot = static_cast<uint32_t>(lane & 31) << 3;
-  const int64_t wave = static_cast<int64_t>(blockIdx.x) * (blockDim.x >> 6) + (threadIdx.x >> 6);
-  const int64_t nwaves = static_cast<int64_t>(gridDim.x) * (blockDim.x >> 6);
-  const int64_t per = (rows + nwaves - 1) / nwaves;
-  const int64_t r_begin = wave * per;
-  const int64_t r_end = (r_begin + per < rows) ? r_begin + per : rows;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const uint32_t slot = static_cast<uint32_t>(lane) << 2;
   const int64_t nblk = cols / 64;
-  const int64_t nseg = (nblk + 63) / 64;
-  const int64_t nbatch = r_end > r_begin ? (r_end - r_begin + R - 1) / R : 0;
-  const int64_t n_items = nbatch * nseg;
-  const int64_t last = n_items > 0 ? n_items - 1 : 0;
-  auto row0_of = [&](int64_t t) { const int64_t r0 = r_begin + (t / nseg) * R; return r0 < rows ? r0 : rows - 1; };
-  auto blk_of = [&](int64_t t) { return (t % nseg) * 64 + lane; };
+  // Row parts are interleaved over the whole grid: part p takes rows p,
+  // p + NP, p + 2 NP, ... so that at any time the grid reads one contiguous
+  // window of rows, as a streaming copy does.
+  const int64_t np = static_cast<int64_t>(gridDim.x) * pl.wpr;
+  const int64_t kmax = (rows + np - 1) / np;  // rows per part, at most
+  const int seg = wave % pl.nseg;
+  const int prt = wave / pl.nseg;
+  const int64_t gp = static_cast<int64_t>(blockIdx.x) * pl.wpr + prt;
+  const int64_t n = (prt < pl.wpr && gp < rows) ? (rows - gp + np - 1) / np : 0;
+  const int b = seg * pl.seg_blocks + lane;
+  const bool lane_on = lane < pl.seg_blocks && b < nblk;
+  const int bc = lane_on ? b : static_cast<int>(nblk - 1);
+  const int64_t row0 = gp < rows ? gp : rows - 1;
+  const int64_t last = n > 0 ? row0 + (n - 1) * np : row0;  // loads are clamped to it
 
-  GemvItem<R> A, B;
-  // Prologue: x loads (at most 4 pieces of 16 bytes per thread with 1024
-  // threads) and the first step's loads are issued, then x and the pair
-  // table go to LDS.
-  constexpr int kXPieces = static_cast<int>(kXLdsMaxCols / 8 / 1024);
-  const int64_t npieces = nblk * 8;
-  uint4 xv[kXPieces];
+  // x of the lane's block, then the first U rows, then the table
+  uint4 xv[8];
+  {
+    const uint4* xp = reinterpret_cast<const uint4*>(x) + 8 * static_cast<int64_t>(bc);
 #pragma unroll
-  for (int u = 0; u < kXPieces; ++u) {
-    const int64_t p = threadIdx.x + static_cast<int64_t>(u) * blockDim.x;
-    xv[u] = reinterpret_cast<const uint4*>(x)[p < npieces ? p : npieces - 1];
+    for (int i = 0; i < 8; ++i) xv[i] = xp[i];
   }
-  gemv_load<R, kDQ, false>(A, packed, rows, nblk, row0_of(0), blk_of(0), sc, x);
+  RowItem it[U];
 #pragma unroll
-  for (int u = 0; u < kXPieces; ++u) {
-    // unconditional store (pieces past the end go to the dummy slot)
-    const int64_t p = threadIdx.x + static_cast<int64_t>(u) * blockDim.x;
-    const int64_t off = p < npieces ? (p >> 3) * kXStride + (p & 7) * 16 : (kXLdsMaxCols / 64) * kXStride;
-    *reinterpret_cast<uint4*>(xs + off) = xv[u];
+  for (int u = 0; u < U; ++u) {
+    const int64_t r = row0 + u * np;
+    row_load<kDQ>(it[u], packed, (r < last ? r : last) * nblk, bc, sc);
   }
-  fill_pair_table(tab, tab_base, cb);  // ends with a barrier
-  if (n_items == 0) return;
+  fill_half_table(tab, tab_base, cb);  // ends with a barrier
+
+  // x to fp16 pairs scaled by 2^k, k chosen so that the largest |x| of the
+  // block lies in [2^14, 2^15)
+  uint32_t xh[32];
+  float xinv;
+  {
+    uint32_t xw[32];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) { xw[4 * i] = xv[i].x; xw[4 * i + 1] = xv[i].y; xw[4 * i + 2] = xv[i].z; xw[4 * i + 3] = xv[i].w; }
+    uint32_t mx = 0;
+#pragma unroll
+    for (int i = 0; i < 32; ++i) mx = max(mx, max(xw[i] & 0x7FFF0000u, (xw[i] << 16) & 0x7FFF0000u));
+    int k = 14 - (static_cast<int>(mx >> 23) - 127);
+    k = k < -126 ? -126 : (k > 126 ? 126 : k);
+    const float sc2 = __uint_as_float(static_cast<uint32_t>(127 + k) << 23);
+    xinv = __uint_as_float(static_cast<uint32_t>(127 - k) << 23);
+#pragma unroll
+    for (int i = 0; i < 32; ++i) {
+      const float lo = __uint_as_float(xw[i] << 16) * sc2;         // exact: a power of two
+      const float hi = __uint_as_float(xw[i] & 0xFFFF0000u) * sc2;
+      xh[i] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(lo, hi));
+    }
+  }
   const float mean = kDQ ? *sc.mean : 0.0f;
 
-  float acc[R];
+  for (int64_t i0 = 0; i0 < n; i0 += U) {
 #pragma unroll
-  for (int r = 0; r < R; ++r) acc[r] = 0.0f;
-  float res = 0.0f;  // lane k <-> row r_begin + k
-  int nres = 0;
-  uint32_t xr[32];
-  auto step = [&](const GemvItem<R>& it, int64_t t) {
-    const int64_t b = blk_of(t);
-    const bool active = b < nblk;
-    lds_x_block(xr, xs, active ? b : 0);
-    gemv_compute<R, kDQ>(it, xr, active, smem, slot, mean, acc);
-    if ((t % nseg) == nseg - 1) {
-#pragma unroll
-      for (int r = 0; r < R; ++r) {
-        const float sum = wave_sum(acc[r]);
-        res = (lane == nres + r) ? sum : res;
-        acc[r] = 0.0f;
+    for (int u = 0; u < U; ++u) {
+      const int64_t i = i0 + u;
+      if (i < n) {  // wave-uniform
+        float v = row_dot<kDQ>(it[u], xh, smem, slot, mean, xinv);
+        v = wave_sum_to_last(lane_on ? v : 0.0f);
+        if (lane == 63) part[(prt * kmax + i) * kSegMax + seg] = v;
       }
-      nres += R;
+      const int64_t r = row0 + (i + U) * np;
+      row_load<kDQ>(it[u], packed, (r < last ? r : last) * nblk, bc, sc);
     }
-  };
-  for (int64_t t = 0; t < n_items; t += 2) {
-    const int64_t t1 = (t + 1 < last) ? t + 1 : last;
-    gemv_load<R, kDQ, false>(B, packed, rows, nblk, row0_of(t1), blk_of(t1), sc, x);
-    step(A, t);
-    if (t + 1 >= n_items) break;
-    const int64_t t2 = (t + 2 < last) ? t + 2 : last;
-    gemv_load<R, kDQ, false>(A, packed, rows, nblk, row0_of(t2), blk_of(t2), sc, x);
-    step(B, t + 1);
   }
-  const int64_t row = r_begin + lane;
-  if (lane < nres && row < r_end) {
-    if constexpr (kBf16Out) static_cast<uint16_t*>(y)[row] = static_cast<uint16_t>(f32_to_bf16(res));
-    else static_cast<float*>(y)[row] = res;
+  __syncthreads();
+  for (int64_t t = threadIdx.x; t < pl.wpr * kmax; t += blockDim.x) {
+    const int64_t row = static_cast<int64_t>(blockIdx.x) * pl.wpr + t / kmax + (t % kmax) * np;
+    if (row >= rows) continue;
+    float s = part[t * kSegMax];
+    for (int k = 1; k < pl.nseg; ++k) s += part[t * kSegMax + k];
+    if constexpr (kBf16Out) static_cast<uint16_t*>(y)[row] = static_cast<uint16_t>(f32_to_bf16(s));
+    else static_cast<float*>(y)[row] = s;
   }
 }
 
-template <int R, bool kDQ>
-void launch_m1_xl(const uint8_t* packed, int64_t rows, int64_t cols, Scales sc, const uint16_t* x, void* y,
-                  int y_bf16, hipStream_t s) {
+// Plan for k_gemv_rows: rows split evenly over at least one workgroup per CU
+// (at most kRowsMaxWg rows each), columns into the fewest segments of at most
+// 64 blocks, balanced, and the waves spread over the segments.
+RowsPlan rows_plan(int64_t rows, int64_t cols, int waves) {
   const int64_t cus = device_cus();
-  const int64_t wpg = 16;  // 1024 threads: the x copy assumes it
-  const int64_t need = (rows + wpg * 64 - 1) / (wpg * 64);
-  const int64_t want = (rows + wpg * R - 1) / (wpg * R);
-  int64_t g = want < cus ? want : cus;
-  if (g < need) g = need;
-  if (g < 1) g = 1;
-  if (g > 0x7FFFFFFF) return;
+  const int64_t nblk = cols / 64;
+  RowsPlan pl{};
+  pl.nseg = static_cast<int>((nblk + 63) / 64);
+  pl.seg_blocks = static_cast<int>((nblk + pl.nseg - 1) / pl.nseg);
+  pl.wpr = waves / pl.nseg;
+  // grid: one workgroup per CU, more if a workgroup would own more than
+  // kRowsMaxWg rows (wpr parts of ceil(rows / (grid * wpr)) rows each)
+  int64_t g = cus;
+  while (pl.wpr > 0 && pl.wpr * ((rows + g * pl.wpr - 1) / (g * pl.wpr)) > kRowsMaxWg) ++g;
+  pl.grid = static_cast<int>(g);
+  return pl;
+}
+
+template <int U, int kWaves, bool kDQ>
+hipError_t launch_rows(const uint8_t* packed, int64_t rows, int64_t cols, Scales sc, const uint16_t* x, void* y,
+                       int y_bf16, hipStream_t s) {
+  const RowsPlan pl = rows_plan(rows, cols, kWaves);
+  if (pl.nseg > kSegMax || pl.wpr < 1) return hipErrorInvalidValue;
+  const int64_t g = pl.grid;
   const Codebook& cb = codebook();
-  const dim3 gd(static_cast<unsigned>(g)), b(static_cast<unsigned>(64 * wpg));
-  if (y_bf16) hipLaunchKernelGGL((k_gemv_m1_xl<R, kDQ, true>), gd, b, 0, s, packed, rows, cols, sc, x, y, cb);
-  else hipLaunchKernelGGL((k_gemv_m1_xl<R, kDQ, false>), gd, b, 0, s, packed, rows, cols, sc, x, y, cb);
+  const dim3 gd(static_cast<unsigned>(g)), bd(64 * kWaves);
+  if (y_bf16) hipLaunchKernelGGL((k_gemv_rows<U, kWaves, kDQ, true>), gd, bd, 0, s, packed, rows, cols, sc, x, y, cb, pl);
+  else hipLaunchKernelGGL((k_gemv_rows<U, kWaves, kDQ, false>), gd, bd, 0, s, packed, rows, cols, sc, x, y, cb, pl);
+  return hipGetLastError();
 }
 
 template <int R, bool kDQ>
@@ -436,28 +560,26 @@ hipError_t launch_gemv(const uint8_t* packed, int64_t rows, int64_t cols, Scales
   const Codebook& cb = codebook();
   const int mm = static_cast<int>(m);
   if (m == 1) {
-    // rows per batch and waves per workgroup from the shape, so that every CU
-    // gets work: up to 16 waves per CU, then 2 and 4 rows per batch
+    const int64_t nseg = (cols / 64 + 63) / 64;
+    if (nseg == 1) {
+      // one column segment: two rows in flight per wave, 8 waves
+      return sc.absmax ? launch_rows<2, 8, false>(packed, rows, cols, sc, x, y, y_bf16, s)
+                       : launch_rows<2, 8, true>(packed, rows, cols, sc, x, y, y_bf16, s);
+    }
+    if (nseg <= kSegMax) {
+      return sc.absmax ? launch_rows<1, 16, false>(packed, rows, cols, sc, x, y, y_bf16, s)
+                       : launch_rows<1, 16, true>(packed, rows, cols, sc, x, y, y_bf16, s);
+    }
+    // wider than 16 segments (cols > 65536): one row group per wave
     const int64_t cus = device_cus();
     const int64_t per_cu = (rows + cus - 1) / cus;
-    if (cols <= kXLdsMaxCols && per_cu > 16) {
-      if (per_cu <= 32) {
-        if (sc.absmax) launch_m1_xl<1, false>(packed, rows, cols, sc, x, y, y_bf16, s);
-        else launch_m1_xl<1, true>(packed, rows, cols, sc, x, y, y_bf16, s);
-      } else {
-        if (sc.absmax) launch_m1_xl<2, false>(packed, rows, cols, sc, x, y, y_bf16, s);
-        else launch_m1_xl<2, true>(packed, rows, cols, sc, x, y, y_bf16, s);
-      }
-    } else if (per_cu <= 16) {
+    if (per_cu <= 16) {
       const int wpg = static_cast<int>(((per_cu + 3) / 4) * 4);  // multiple of 4 waves (256 threads)
       if (sc.absmax) launch_m1<1, false>(packed, rows, cols, sc, x, y, y_bf16, wpg, s);
       else launch_m1<1, true>(packed, rows, cols, sc, x, y, y_bf16, wpg, s);
-    } else if (per_cu <= 32) {
+    } else {
       if (sc.absmax) launch_m1<2, false>(packed, rows, cols, sc, x, y, y_bf16, 16, s);
       else launch_m1<2, true>(packed, rows, cols, sc, x, y, y_bf16, 16, s);
-    } else {
-      if (sc.absmax) launch_m1<4, false>(packed, rows, cols, sc, x, y, y_bf16, 16, s);
-      else launch_m1<4, true>(packed, rows, cols, sc, x, y, y_bf16, 16, s);
     }
   } else {
     if (y_bf16) hipLaunchKernelGGL((k_gemv<4, true>), grid, dim3(256), 0, s, packed, rows, cols, sc, x, mm, y, cb);

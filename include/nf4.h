@@ -136,7 +136,10 @@ int nf4_dequantize(const nf4_weight* w, void* out, int out_dtype, void* stream);
  *   y : [m][rows] of y_dtype (NF4_F32 or NF4_BF16), 16-byte aligned.
  * Products are accumulated in float32; no dequantized copy of W is written
  * to memory (tool page "How it works", Step 5: the expanded copy is
- * temporary). */
+ * temporary).  For m == 1 and cols <= 65536 the levels enter the products
+ * rounded to fp16 (11 significant bits, relative error <= 2^-11) and x
+ * exactly (scaled by a power of two per 64-block), and the block scale is
+ * applied once per block in float32; otherwise the float32 levels are used. */
 int nf4_gemv(const nf4_weight* w, const void* x, int64_t m, void* y, int y_dtype,
              void* stream);
 

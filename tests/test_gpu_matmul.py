@@ -99,28 +99,96 @@ def test_gemv_c3_sampled_rows(name, m):
 
 
 def test_gemv_one_hot_and_determinism():
-    """x = e_k returns column k of the dequantized weight.  The decode GEMV
-    multiplies with each level split into two bf16 parts, which together lie
-    within 2^-17 of the float32 level, so the column is matched to 2^-16
-    relative; two runs give identical bits."""
+    """x = e_k returns column k of the dequantized weight in closed form.  For
+    m = 1 the decode GEMV takes each level rounded to fp16 and x exactly
+    (scaled by a power of two that it undoes), so y[n] is exactly
+    fl32(fp16(level[code]) * a_hat): the level and a_hat come from the oracle
+    and the fp16 rounding (nearest even) from numpy.  That is within 2^-11 of
+    the float32 dequantized value.  Two runs give identical bits."""
     say("gemv one-hot")
     torch = need_gpu()
     rows, cols = 256, 512
     w = syn.normal_f32((rows, cols), 0.02, 4)
     W = nf4.quantize_weight(to_dev(w), double_quant=True)
+    p, a = oracle.quantize(w.reshape(-1))
+    q, s2, mean = oracle.double_quant(a)
+    a_hat = oracle.dequant_scales(q, s2, mean)
+    codes = oracle.unpack(p, w.size).reshape(rows, cols)
+    lv16 = oracle.codebook().astype(np.float16).astype(np.float32)
     wdeq_f32 = nf4.nf4_dequantize(W, out_dtype=torch.float32)
     for k in (0, 77, 511):
         x = torch.zeros((1, cols), dtype=torch.bfloat16, device="cuda")
         x[0, k] = 1.0
         y = nf4.nf4_gemv(W, x, y_dtype=torch.float32)
         torch.cuda.synchronize()
+        blk = (np.arange(rows) * cols + k) // 64
+        expect = (lv16[codes[:, k]] * a_hat[blk]).astype(np.float32)
+        got = y[0].cpu().numpy()
+        assert np.array_equal(got.view(np.uint32), expect.view(np.uint32)), k
         ref = wdeq_f32[:, k]
-        assert bool(((y[0] - ref).abs() <= ref.abs() * 2.0 ** -16).all())
+        assert bool(((y[0] - ref).abs() <= ref.abs() * (2.0 ** -11 + 2.0 ** -22)).all())
     x = syn.to_bf16(syn.normal_f32((4, cols), 1.0, 8)).to("cuda")
-    y1 = nf4.nf4_gemv(W, x)
-    y2 = nf4.nf4_gemv(W, x)
+    for m in (1, 4):
+        y1 = nf4.nf4_gemv(W, x[:m])
+        y2 = nf4.nf4_gemv(W, x[:m])
+        torch.cuda.synchronize()
+        assert torch.equal(y1, y2)
+
+
+def test_gemv_x_dynamic_range():
+    """x spanning 2^-60 .. 2^60 within and across blocks, and an all-zero
+    block: the per-block power-of-two scaling of x keeps the decode GEMV
+    within tolerance and finite."""
+    say("gemv x dynamic range")
+    torch = need_gpu()
+    rows, cols = 512, 1024
+    w = syn.normal_f32((rows, cols), 0.02, 64)
+    rng = np.random.default_rng(65)
+    xf = (rng.standard_normal((1, cols)) * np.exp2(rng.integers(-60, 61, (1, cols)))).astype(np.float32)
+    xf[0, 128:192] = 0.0
+    xf[0, 256:320] *= np.float32(2.0 ** -60)
+    xb = syn.to_bf16(xf)
+    W = nf4.quantize_weight(to_dev(w), double_quant=True)
+    y = nf4.nf4_gemv(W, xb.to("cuda"), y_dtype=torch.float32)
     torch.cuda.synchronize()
-    assert torch.equal(y1, y2)
+    assert bool(torch.isfinite(y).all())
+    ref = oracle.matmul_ref(syn.bf16_to_f32(xb), _full_oracle_wdeq(w, True))
+    e = oracle.rel_frobenius(_y_f64(y), ref)
+    say(f"  rel err {e:.2e}")
+    assert e <= MATMUL_RTOL
+
+
+@pytest.mark.parametrize("rows,cols", [(7, 65600), (40, 131072)])
+def test_gemv_wider_than_16_segments(rows, cols):
+    """Rows longer than 16 x 64 blocks take the per-row-group kernel."""
+    say("gemv wide", rows, cols)
+    torch = need_gpu()
+    w = syn.normal_f32((rows, cols), 0.02, 61)
+    xb = syn.to_bf16(syn.normal_f32((1, cols), 1.0, 62))
+    W = nf4.quantize_weight(to_dev(w), double_quant=True)
+    y = nf4.nf4_gemv(W, xb.to("cuda"), y_dtype=torch.float32)
+    torch.cuda.synchronize()
+    ref = oracle.matmul_ref(syn.bf16_to_f32(xb), _full_oracle_wdeq(w, True))
+    e = oracle.rel_frobenius(_y_f64(y), ref)
+    say(f"  rel err {e:.2e}")
+    assert e <= MATMUL_RTOL
+
+
+@pytest.mark.parametrize("rows,cols", [(3000, 4096), (2047, 8192), (600, 28672), (257, 1024), (4100, 128)])
+def test_gemv_m1_row_interleave_shapes(rows, cols):
+    """Row counts that do not divide evenly over the grid's row parts, with
+    one, two, four and seven column segments."""
+    say("gemv m1 shapes", rows, cols)
+    torch = need_gpu()
+    w = syn.normal_f32((rows, cols), 0.02, rows + cols)
+    xb = syn.to_bf16(syn.normal_f32((1, cols), 2.0, 63))
+    W = nf4.quantize_weight(to_dev(w), double_quant=True)
+    y = nf4.nf4_gemv(W, xb.to("cuda"), y_dtype=torch.float32)
+    torch.cuda.synchronize()
+    ref = oracle.matmul_ref(syn.bf16_to_f32(xb), _full_oracle_wdeq(w, True))
+    e = oracle.rel_frobenius(_y_f64(y), ref)
+    say(f"  rel err {e:.2e}")
+    assert e <= MATMUL_RTOL
 
 
 @pytest.mark.parametrize("m,rows,cols", [(1, 64, 64), (37, 200, 128), (130, 129, 192), (256, 256, 512), (300, 520, 1024)])
