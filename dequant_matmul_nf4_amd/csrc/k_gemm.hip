@@ -1,28 +1,42 @@
-// Dequantize-into-LDS bf16 matrix-core GEMM with an optional fused LoRA term:
+// Dequantize-and-multiply bf16 matrix-core GEMM with an optional fused LoRA
+// term:
 //   y = x . deq(W)^T + s . (x . A^T) . B^T
 // (bitsandbytes tool page, "How it works", Step 5: matrix hardware works best
 // on 16-bit numbers, so each block is expanded to 16-bit and multiplied; the
 // tutorial page, "QLoRA: Fine-Tuning a 4-bit Model": low-rank adapters on the
 // frozen 4-bit base, their output multiplied by a scale factor.)
 //
-// Tiling: a workgroup of 4 waves computes a 256 x 256 tile of y; wave (wm, wn)
-// owns the 128 x 128 quarter and runs 4 x 4 v_mfma_f32_32x32x16_bf16 per
-// 16-wide k step (256 fp32 accumulators per lane).  A K step covers 64
-// columns, i.e. exactly one NF4 block of every weight row, so thread t
-// expands row t of the W tile: 64 codes -> level (16-entry LDS table) times
-// the block scale, rounded to bf16 (the same value nf4_dequantize writes) ->
-// LDS.  The x tile is copied to LDS as is.  LDS holds two stages (x and W,
-// 256 rows of 64 bf16 each, rows padded to 144 bytes so the 16-byte fragment
-// reads of 16 consecutive rows hit distinct banks); the global loads of step
-// k+1 are issued before the MFMAs of step k and written to the other stage
-// after them.
+// Tiling: a workgroup of 4 waves (one per SIMD) computes a 256 x 256 tile of
+// y.  Wave w owns the 64 output columns [64 w, 64 w + 64) for all 256 rows:
+// 8 x 2 tiles of v_mfma_f32_32x32x16_bf16 per 16-wide k step, 256 fp32
+// accumulators per lane.  A K step covers 64 columns, exactly one NF4 block
+// of every weight row.  Within a step the LDS reads of 16-wide k step s + 1
+// (x fragments and level lookups) are issued before the MFMAs of k step s,
+// so their latency is spent while the matrix cores run.
+//
+// Operands:
+//  - x: the 256 x 64 tile is staged in LDS (two stages, rows padded to 144
+//    bytes so that 16-byte fragment reads of consecutive rows hit distinct
+//    banks); the next step's tile is loaded into registers during the current
+//    step and written to the other stage at its end.
+//  - W: never staged.  Each lane loads the 16 bytes of codes it needs
+//    (32 consecutive k of one row) and expands them straight into its MFMA
+//    B fragments: a byte (two codes) indexes a 256-entry table of float32
+//    level pairs in LDS (32 copies, lane slot (lane % 32) * 8, so the lanes
+//    served together hit distinct banks; address = one byte permute), each
+//    level is multiplied by the block scale and the pair rounded once to bf16
+//    -- the same value nf4_dequantize writes.  The next step's codes are
+//    loaded one step ahead.
+//  - The k index of a lane's fragment is a permutation of the step's 64
+//    columns (lane half h takes columns 32 h .. 32 h + 31, eight per 16-wide
+//    k step); A and B fragments use the same one, so the sum is unchanged.
 //
 // LoRA: the low-rank term is folded in as extra K columns,
 //   [x | s T_hi | s T_lo] . [deq(W) | B | B]^T  with T = x . A^T,
 // where s T is split into two bf16 parts (hi = bf16(sT), lo = bf16(sT - hi))
 // by k_lora_prep, so the adapter product keeps about 16 significant bits.
 // Those columns (2 r rounded up to a multiple of 64) run as one or two more
-// K steps with bf16 operands read directly.
+// K steps with both operands staged in LDS.
 #include "nf4_device.h"
 
 namespace nf4i {
@@ -36,8 +50,9 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));  // native vector: s
 constexpr int kBM = 256, kBN = 256, kBK = 64;
 constexpr int kRowBytes = 144;                  // 64 bf16 + 16 bytes of padding
 constexpr int kTileBytes = 256 * kRowBytes;     // one operand tile in LDS
-constexpr int kStageBytes = 2 * kTileBytes;     // x tile + W tile
-constexpr int kLdsBytes = 2 * kStageBytes + 64; // two stages + the level table
+constexpr int kPairSlots = 32;                  // copies of the level-pair table
+constexpr int kThreads = 256;                   // 4 waves
+constexpr int kXPieces = kBM * kBK * 2 / 16 / kThreads;  // 16-byte x pieces per thread and step
 
 __device__ __forceinline__ bf16x8 lds_frag(const char* p) { return *reinterpret_cast<const bf16x8*>(p); }
 
@@ -59,92 +74,181 @@ struct GemmArgs {
   Codebook cb;
 };
 
-// Global loads of one K step into registers: 8 x 16 bytes of the x tile (rows
-// t/8 + 32 i, 16-byte piece t%8) and the 32 bytes of codes of W row t.
-// Rows past the end of x or W are clamped to the last one: they only feed
-// outputs that are never written.
-struct StepRegs {
-  u32x4 xv[8];
-  u32x4 wv[2];
-  float am;      // absmax (plain scales)
-  int q;         // int8 scale code (double quant)
-  float s2;
-};
-
-struct StepPtrs {
-  const uint8_t* x0;      // x piece 0 of step 0 (bytes)
-  int64_t x_stride32;     // bytes between pieces i and i+1 (32 rows)
-  int i_max;              // last piece whose row exists; later pieces re-read it
-  const uint8_t* w0;      // codes of W row t, step 0
-  int64_t blk0;           // block index of W row t, step 0
-};
-
-template <bool kDQ>
-__device__ __forceinline__ void load_step(StepRegs& st, const StepPtrs& p, const GemmArgs& a, int64_t ks) {
-  const uint8_t* xp = p.x0 + ks * (kBK * 2);
+// The 256 level pairs (element 2j = high nibble first), kPairSlots copies;
+// entry e of slot c at byte e * 256 + c * 8.  Two phases so that each wave
+// writes consecutive addresses.  Ends with a barrier.
+__device__ __forceinline__ void fill_level_pairs(float2* tab, float2* base, const Codebook& cb) {
+  if (threadIdx.x < 256) {
+    const int e = threadIdx.x;
+    float l0 = cb.level[0], l1 = cb.level[0];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int ii = i < p.i_max ? i : p.i_max;
-    st.xv[i] = *reinterpret_cast<const u32x4*>(xp + ii * p.x_stride32);
+    for (int i = 1; i < 16; ++i) {
+      l0 = ((e >> 4) == i) ? cb.level[i] : l0;
+      l1 = ((e & 15) == i) ? cb.level[i] : l1;
+    }
+    base[e] = make_float2(l0, l1);
   }
-  const u32x4* wp = reinterpret_cast<const u32x4*>(p.w0 + ks * (kBK / 2));
-  st.wv[0] = wp[0];
-  st.wv[1] = wp[1];
-  const int64_t blk = p.blk0 + ks;
-  if constexpr (kDQ) {
-    st.q = a.sc.q[blk];
-    st.s2 = a.sc.absmax2[blk >> 8];
-  } else {
-    st.am = a.sc.absmax[blk];
+  __syncthreads();
+  for (int i = threadIdx.x; i < 256 * kPairSlots; i += blockDim.x) tab[i] = base[i / kPairSlots];
+  __syncthreads();
+}
+
+// x tile loads of one K step: thread t takes rows t/8 + 32 i (i < 8), 16-byte
+// piece t % 8.  Rows past the end of x re-read the last valid one (they only
+// feed outputs that are never stored).
+struct XPtrs {
+  const uint8_t* p0;      // piece 0 of step 0 (bytes)
+  int64_t stride;         // bytes between pieces i and i + 1 (32 rows)
+  int i_max;              // last piece whose row exists
+};
+
+__device__ __forceinline__ void load_x(u32x4 (&xv)[kXPieces], const XPtrs& p, int64_t ks) {
+  const uint8_t* b = p.p0 + ks * (kBK * 2);
+#pragma unroll
+  for (int i = 0; i < kXPieces; ++i) {
+    const int ii = i < p.i_max ? i : p.i_max;
+    xv[i] = *reinterpret_cast<const u32x4*>(b + ii * p.stride);
   }
 }
 
-// Writes a step's operands to an LDS stage, expanding the thread's W row.
-template <bool kDQ>
-__device__ __forceinline__ void store_step(const StepRegs& st, char* stage, const float* lv, float mean) {
+__device__ __forceinline__ void store_x(const u32x4 (&xv)[kXPieces], char* xs) {
   const int t = threadIdx.x;
-  char* xs = stage;
-  char* wrow = stage + kTileBytes + t * kRowBytes;
 #pragma unroll
-  for (int i = 0; i < 8; ++i)
-    *reinterpret_cast<u32x4*>(xs + ((t >> 3) + 32 * i) * kRowBytes + (t & 7) * 16) = st.xv[i];
-  float sa;
-  if constexpr (kDQ) sa = (div127(st.q) * st.s2) + mean;  // a_hat, three roundings
-  else sa = st.am;
-  const uint32_t q[8] = {st.wv[0][0], st.wv[0][1], st.wv[0][2], st.wv[0][3],
-                         st.wv[1][0], st.wv[1][1], st.wv[1][2], st.wv[1][3]};
+  for (int i = 0; i < kXPieces; ++i)
+    *reinterpret_cast<u32x4*>(xs + ((t >> 3) + 32 * i) * kRowBytes + (t & 7) * 16) = xv[i];
+}
+
+// The codes a lane expands in one K step: for its two W rows (j = 0, 1) the
+// 16 bytes of columns 32 h .. 32 h + 31, and the rows' block scale inputs.
+struct WRegs {
+  u32x4 w[2];
+  float am[2];   // absmax (plain scales)
+  int q[2];      // int8 scale code (double quant)
+  float s2[2];
+};
+
+struct WPtrs {
+  const uint8_t* c[2];    // codes of row j at step 0, lane half's 16 bytes
+  int64_t blk[2];         // block index of row j at step 0
+};
+
+template <bool kDQ>
+__device__ __forceinline__ void load_w(WRegs& r, const WPtrs& p, const GemmArgs& a, int64_t ks) {
 #pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    // byte b of word j holds elements 8j + 2b (high nibble) and 8j + 2b + 1
-    const uint32_t hi4 = opaque((q[j] >> 2) & 0x3C3C3C3Cu);
-    const uint32_t lo4 = opaque((q[j] << 2) & 0x3C3C3C3Cu);
-    uint32_t o[4];
+  for (int j = 0; j < 2; ++j) {
+    r.w[j] = *reinterpret_cast<const u32x4*>(p.c[j] + ks * (kBK / 2));
+    const int64_t blk = p.blk[j] + ks;
+    if constexpr (kDQ) {
+      r.q[j] = a.sc.q[blk];
+      r.s2[j] = a.sc.absmax2[blk >> 8];
+    } else {
+      r.am[j] = a.sc.absmax[blk];
+    }
+  }
+}
+
+// Level pairs of code bytes 4 s .. 4 s + 3 of a lane's 16 bytes (one k step
+// of one W row): four LDS reads, addresses from one byte permute each.
+struct Lookups {
+  float2 l[2][4];
+};
+
+__device__ __forceinline__ void lookup_step(Lookups& lk, const u32x4 (&w)[2], int s, const char* tab,
+                                            uint32_t slot) {
+#pragma unroll
+  for (int j = 0; j < 2; ++j)
 #pragma unroll
     for (int b = 0; b < 4; ++b) {
-      const float e0 = *reinterpret_cast<const float*>(reinterpret_cast<const char*>(lv) + __builtin_amdgcn_ubfe(hi4, 8 * b, 8));
-      const float e1 = *reinterpret_cast<const float*>(reinterpret_cast<const char*>(lv) + __builtin_amdgcn_ubfe(lo4, 8 * b, 8));
-      o[b] = bf16_pair(e0 * sa, e1 * sa);
+      const uint32_t addr = __builtin_amdgcn_perm(w[j][s], slot, 0x0C0C0000u | ((4u + b) << 8));
+      lk.l[j][b] = *reinterpret_cast<const float2*>(tab + addr);
     }
-    const u32x4 ov = {o[0], o[1], o[2], o[3]};
-    *reinterpret_cast<u32x4*>(wrow + 16 * j) = ov;
+}
+
+// Each level times the block scale, each pair rounded once to bf16.
+__device__ __forceinline__ bf16x8 expand_frag(const float2 (&l)[4], float sa) {
+  const u32x4 v = {bf16_pair(l[0].x * sa, l[0].y * sa), bf16_pair(l[1].x * sa, l[1].y * sa),
+                   bf16_pair(l[2].x * sa, l[2].y * sa), bf16_pair(l[3].x * sa, l[3].y * sa)};
+  return __builtin_bit_cast(bf16x8, v);
+}
+
+// MFMAs of one K step: A fragments from the x tile in LDS, B fragments from
+// the expanded codes.  Software pipeline over the four 16-wide k steps: while
+// the 16 MFMAs of k step s run, the wave expands the B fragments of s + 1
+// (their level lookups were issued one k step earlier) and issues the LDS
+// reads of s + 2; sched_group_barrier spreads that work between the MFMAs.
+__device__ __forceinline__ void mfma_interleave() {
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+    __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);  // VALU
+    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // LDS read
   }
 }
 
-// One LoRA step (64 extra K columns): x columns from u, W columns [B | B]
-// (zero past the rank), loaded and stored directly.
-__device__ __forceinline__ void lora_step_to_lds(char* stage, const GemmArgs& a, int64_t m0, int64_t n0, int64_t k0) {
+template <bool kDQ>
+__device__ __forceinline__ void mfma_step(const char* xs, const WRegs& wr, float mean, const char* tab,
+                                          uint32_t slot, floatx16 (&acc)[8][2], int lane) {
+  float sa[2];
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    if constexpr (kDQ) sa[j] = (div127(wr.q[j]) * wr.s2[j]) + mean;  // a_hat, three roundings
+    else sa[j] = wr.am[j];
+  }
+  const char* xa = xs + (lane & 31) * kRowBytes + (lane >> 5) * 64;  // row lane % 32, columns 32 h ..
+  Lookups lk[3];
+  bf16x8 af[3][8];
+  bf16x8 bf[2][2];
+  auto read_a = [&](int s, bf16x8 (&f)[8]) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) f[i] = lds_frag(xa + i * 32 * kRowBytes + s * 16);
+  };
+  // k steps 0 and 1: reads out, k step 0 expanded
+  lookup_step(lk[0], wr.w, 0, tab, slot);
+  read_a(0, af[0]);
+  lookup_step(lk[1], wr.w, 1, tab, slot);
+  read_a(1, af[1]);
+  bf[0][0] = expand_frag(lk[0].l[0], sa[0]);
+  bf[0][1] = expand_frag(lk[0].l[1], sa[1]);
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int s = 0; s < 4; ++s) {
+    const int c = s & 1;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      acc[i][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[s % 3][i], bf[c][0], acc[i][0], 0, 0, 0);
+      acc[i][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[s % 3][i], bf[c][1], acc[i][1], 0, 0, 0);
+    }
+    if (s + 2 < 4) {
+      lookup_step(lk[(s + 2) % 3], wr.w, s + 2, tab, slot);
+      read_a(s + 2, af[(s + 2) % 3]);
+    }
+    if (s + 1 < 4) {
+      bf[c ^ 1][0] = expand_frag(lk[(s + 1) % 3].l[0], sa[0]);
+      bf[c ^ 1][1] = expand_frag(lk[(s + 1) % 3].l[1], sa[1]);
+    }
+    mfma_interleave();
+    __builtin_amdgcn_sched_barrier(0);
+  }
+}
+
+// One LoRA step (64 extra K columns): the x side from u into xs, the W side
+// [B | B] (zero past the rank) into ws as rows of output columns; both then
+// feed the MFMAs as fragments.
+__device__ __forceinline__ void lora_step_to_lds(char* xs, char* ws, const GemmArgs& a, int64_t m0, int64_t n0,
+                                                 int64_t k0) {
   const int t = threadIdx.x;
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
+  for (int i = 0; i < kXPieces; ++i) {
     const int64_t row = m0 + (t >> 3) + 32 * i;
     const int64_t rc = row < a.m ? row : a.m - 1;
     const u32x4 v = *reinterpret_cast<const u32x4*>(a.u + rc * a.kl + k0 + (t & 7) * 8);
-    *reinterpret_cast<u32x4*>(stage + ((t >> 3) + 32 * i) * kRowBytes + (t & 7) * 16) = v;
+    *reinterpret_cast<u32x4*>(xs + ((t >> 3) + 32 * i) * kRowBytes + (t & 7) * 16) = v;
   }
+  // W side: thread t fills output row t
   const int64_t n = n0 + t;
   const int64_t nc = n < a.rows ? n : a.rows - 1;
   const uint16_t* bp = a.lb + nc * a.r;
-  char* wrow = stage + kTileBytes + t * kRowBytes;
+  char* wrow = ws + t * kRowBytes;
   for (int c = 0; c < kBK; ++c) {
     const int64_t col = k0 + c;
     const int64_t j = col < a.r_pad ? col : col - a.r_pad;
@@ -153,36 +257,34 @@ __device__ __forceinline__ void lora_step_to_lds(char* stage, const GemmArgs& a,
   }
 }
 
-__device__ __forceinline__ void mfma_stage(const char* stage, floatx16 (&acc)[4][4], int wm, int wn, int lane) {
-  const char* xs = stage;
-  const char* ws = stage + kTileBytes;
-  const int frag_row = lane & 31;
-  const int frag_k = 8 * (lane >> 5);  // bf16 offset of the lane's 8 k values
+__device__ __forceinline__ void mfma_lora(const char* xs, const char* ws, floatx16 (&acc)[8][2], int wave,
+                                          int lane) {
+  const char* xa = xs + (lane & 31) * kRowBytes + (lane >> 5) * 64;
+  const char* wb = ws + (wave * 64 + (lane & 31)) * kRowBytes + (lane >> 5) * 64;
 #pragma unroll
-  for (int kk = 0; kk < kBK; kk += 16) {
-    bf16x8 af[4], bfr[4];
+  for (int s = 0; s < 4; ++s) {
+    bf16x8 bfr[2], af[8];
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-      af[i] = lds_frag(xs + (wm * 128 + i * 32 + frag_row) * kRowBytes + (kk + frag_k) * 2);
+    for (int j = 0; j < 2; ++j) bfr[j] = lds_frag(wb + j * 32 * kRowBytes + s * 16);
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
-      bfr[j] = lds_frag(ws + (wn * 128 + j * 32 + frag_row) * kRowBytes + (kk + frag_k) * 2);
+    for (int i = 0; i < 8; ++i) af[i] = lds_frag(xa + i * 32 * kRowBytes + s * 16);
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < 8; ++i)
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
+      for (int j = 0; j < 2; ++j)
         acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
   }
 }
 
 template <bool kDQ>
-__global__ __launch_bounds__(256) void k_gemm(GemmArgs a) {
-  extern __shared__ __align__(16) char smem[];
-  float* lv = reinterpret_cast<float*>(smem + 2 * kStageBytes);
+__global__ __launch_bounds__(kThreads) void k_gemm(GemmArgs a) {
+  __shared__ __align__(16) char xs0[kTileBytes], xs1[kTileBytes];
+  __shared__ float2 tab[256 * kPairSlots];
+  __shared__ float2 tab_base[256];
+  const char* tabc = reinterpret_cast<const char*>(tab);
   const int t = threadIdx.x;
   const int lane = t & 63, wave = t >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
-  if (t < 16) lv[t] = a.cb.level[t];
+  const uint32_t slot = static_cast<uint32_t>(lane & 31) << 3;
 
   // tile order: consecutive workgroups of one XCD (dispatch is round-robin
   // over the 8 XCDs) take neighbouring tiles along N, so they share x rows
@@ -192,64 +294,73 @@ __global__ __launch_bounds__(256) void k_gemm(GemmArgs a) {
   if (tiles % 8 == 0) tid = (tid % 8) * (tiles / 8) + tid / 8;
   const int64_t m0 = (tid / tiles_n) * kBM;
   const int64_t n0 = (tid % tiles_n) * kBN;
-
-  const float mean = kDQ ? *a.sc.mean : 0.0f;
   const int64_t nk = a.cols / kBK;
 
-  StepPtrs ptr;
+  XPtrs xp;
   {
     const int64_t xr = m0 + (t >> 3);
     const int64_t xrc = xr < a.m ? xr : a.m - 1;
-    ptr.x0 = reinterpret_cast<const uint8_t*>(a.x + xrc * a.cols + (t & 7) * 8);
-    ptr.x_stride32 = 32 * a.cols * 2;
-    // ragged M: pieces whose row is past the end re-read the last valid one
-    // (they only feed outputs that are never stored)
+    xp.p0 = reinterpret_cast<const uint8_t*>(a.x + xrc * a.cols + (t & 7) * 8);
+    xp.stride = 32 * a.cols * 2;
     const int64_t last = xr < a.m ? (a.m - 1 - xr) / 32 : 0;
-    ptr.i_max = static_cast<int>(last < 7 ? last : 7);
-    const int64_t n = n0 + t;
-    const int64_t nc = n < a.rows ? n : a.rows - 1;
-    ptr.w0 = a.packed + nc * (a.cols / 2);
-    ptr.blk0 = nc * (a.cols / 64);
+    xp.i_max = static_cast<int>(last < kXPieces - 1 ? last : kXPieces - 1);
+  }
+  WPtrs wp;
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int64_t n = n0 + wave * 64 + j * 32 + (lane & 31);
+    const int64_t nc = n < a.rows ? n : a.rows - 1;  // rows past the end: never stored
+    wp.c[j] = a.packed + nc * (a.cols / 2) + (lane >> 5) * 16;
+    wp.blk[j] = nc * (a.cols / 64);
   }
 
-  floatx16 acc[4][4];
+  floatx16 acc[8][2];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < 8; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int j = 0; j < 2; ++j)
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
 
-  StepRegs st;
-  load_step<kDQ>(st, ptr, a, 0);
-  __syncthreads();  // level table
-  store_step<kDQ>(st, smem, lv, mean);
+  // Step k: MFMAs from x stage k % 2 and the codes of step k (wc); during it
+  // the x tile and codes of step k + 1 are loaded (clamped on the last step)
+  // and the x tile is written to the other stage at its end.
+  u32x4 xv[kXPieces];
+  WRegs wc, wnx;
+  load_x(xv, xp, 0);
+  load_w<kDQ>(wc, wp, a, 0);
+  fill_level_pairs(tab, tab_base, a.cb);  // ends with a barrier
+  const float mean = kDQ ? *a.sc.mean : 0.0f;
+  store_x(xv, xs0);
   __syncthreads();
   for (int64_t ks = 0; ks < nk; ++ks) {
-    // the next step's loads are always issued (clamped on the last step) so
-    // that no branch separates them from the MFMAs
     const int64_t kn = ks + 1 < nk ? ks + 1 : ks;
-    load_step<kDQ>(st, ptr, a, kn);
-    mfma_stage(smem + (ks & 1) * kStageBytes, acc, wm, wn, lane);
-    store_step<kDQ>(st, smem + ((ks + 1) & 1) * kStageBytes, lv, mean);
+    load_x(xv, xp, kn);
+    load_w<kDQ>(wnx, wp, a, kn);
+    // keep the loads here, a whole step ahead of their use (left alone, the
+    // scheduler sinks them next to the stores and exposes their latency)
+    __builtin_amdgcn_sched_barrier(0);
+    mfma_step<kDQ>((ks & 1) ? xs1 : xs0, wc, mean, tabc, slot, acc, lane);
+    store_x(xv, (ks & 1) ? xs0 : xs1);
     __syncthreads();
+    wc = wnx;
   }
   for (int64_t k0 = 0; k0 < a.kl; k0 += kBK) {
-    lora_step_to_lds(smem, a, m0, n0, k0);
+    lora_step_to_lds(xs0, xs1, a, m0, n0, k0);
     __syncthreads();
-    mfma_stage(smem, acc, wm, wn, lane);
+    mfma_lora(xs0, xs1, acc, wave, lane);
     __syncthreads();
   }
 
   // epilogue: lane holds D[(e % 4) + 4 (lane / 32) + 8 (e / 4)][lane % 32] of each 32 x 32 tile
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
+  for (int i = 0; i < 8; ++i) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int64_t col = n0 + wn * 128 + j * 32 + (lane & 31);
+    for (int j = 0; j < 2; ++j) {
+      const int64_t col = n0 + wave * 64 + j * 32 + (lane & 31);
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
-        const int64_t row = m0 + wm * 128 + i * 32 + (e & 3) + 4 * (lane >> 5) + 8 * (e >> 2);
+        const int64_t row = m0 + i * 32 + (e & 3) + 4 * (lane >> 5) + 8 * (e >> 2);
         if (row < a.m && col < a.rows)
           a.y[row * a.rows + col] = __builtin_bit_cast(uint16_t, static_cast<__bf16>(acc[i][j][e]));
       }
@@ -305,12 +416,6 @@ size_t gemm_lora_cols(int r) {
 hipError_t launch_gemm(const uint8_t* packed, int64_t rows, int64_t cols, Scales sc, const uint16_t* x,
                        int64_t m, uint16_t* y, const uint16_t* lora_a, const uint16_t* lora_b, int r,
                        float lora_scale, uint16_t* u_ws, hipStream_t s) {
-  // the two stages take 144 KiB of the 160 KiB LDS; the attribute is per
-  // function and idempotent, so setting it on every call is safe across threads
-  for (const void* f : {reinterpret_cast<const void*>(k_gemm<true>), reinterpret_cast<const void*>(k_gemm<false>)}) {
-    const hipError_t e = hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, kLdsBytes);
-    if (e != hipSuccess) return e;
-  }
   GemmArgs a{};
   a.packed = packed; a.rows = rows; a.cols = cols; a.sc = sc; a.x = x; a.m = m; a.y = y;
   a.cb = codebook();
@@ -326,8 +431,8 @@ hipError_t launch_gemm(const uint8_t* packed, int64_t rows, int64_t cols, Scales
   }
   const int64_t tiles = ((rows + kBN - 1) / kBN) * ((m + kBM - 1) / kBM);
   if (tiles > 0x7FFFFFFF) return hipErrorInvalidValue;
-  if (sc.absmax) hipLaunchKernelGGL(k_gemm<false>, dim3(static_cast<unsigned>(tiles)), dim3(256), kLdsBytes, s, a);
-  else hipLaunchKernelGGL(k_gemm<true>, dim3(static_cast<unsigned>(tiles)), dim3(256), kLdsBytes, s, a);
+  if (sc.absmax) hipLaunchKernelGGL(k_gemm<false>, dim3(static_cast<unsigned>(tiles)), dim3(kThreads), 0, s, a);
+  else hipLaunchKernelGGL(k_gemm<true>, dim3(static_cast<unsigned>(tiles)), dim3(kThreads), 0, s, a);
   return hipGetLastError();
 }
 
