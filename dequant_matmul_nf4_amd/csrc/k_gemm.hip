@@ -15,10 +15,11 @@
 // so their latency is spent while the matrix cores run.
 //
 // Operands:
-//  - x: the 256 x 64 tile is staged in LDS (two stages, rows padded to 144
-//    bytes so that 16-byte fragment reads of consecutive rows hit distinct
-//    banks); the next step's tile is loaded into registers during the current
-//    step and written to the other stage at its end.
+//  - x: the 256 x 64 tile is staged in LDS (two stages of 128-byte rows) by
+//    direct global-to-LDS loads (global_load_lds_dwordx4: each wave
+//    instruction fills 1 KB, lane l at byte 16 l), issued at the top of the
+//    previous step.  16-byte piece p of row r sits at slot p ^ ((r / 2) % 8),
+//    so the fragment reads of 16 consecutive rows hit distinct banks.
 //  - W: never staged.  Each lane loads the 16 bytes of codes it needs
 //    (32 consecutive k of one row) and expands them straight into its MFMA
 //    B fragments: a byte (two codes) indexes a 256-entry table of float32
@@ -52,7 +53,7 @@ constexpr int kRowBytes = 144;                  // 64 bf16 + 16 bytes of padding
 constexpr int kTileBytes = 256 * kRowBytes;     // one operand tile in LDS
 constexpr int kPairSlots = 32;                  // copies of the level-pair table
 constexpr int kThreads = 256;                   // 4 waves
-constexpr int kXPieces = kBM * kBK * 2 / 16 / kThreads;  // 16-byte x pieces per thread and step
+constexpr int kXPieces = kBM * kBK * 2 / 16 / kThreads;  // 16-byte x pieces per thread and step (8)
 
 __device__ __forceinline__ bf16x8 lds_frag(const char* p) { return *reinterpret_cast<const bf16x8*>(p); }
 
@@ -93,30 +94,34 @@ __device__ __forceinline__ void fill_level_pairs(float2* tab, float2* base, cons
   __syncthreads();
 }
 
-// x tile loads of one K step: thread t takes rows t/8 + 32 i (i < 8), 16-byte
-// piece t % 8.  Rows past the end of x re-read the last valid one (they only
-// feed outputs that are never stored).
+// x tile of one K step by direct global-to-LDS loads: wave w's instruction i
+// fills tile rows 64 w + 8 i .. + 7 (1 KB); its lane l takes row
+// 64 w + 8 i + l / 8, LDS slot l % 8, i.e. the row's 16-byte piece
+// (l % 8) ^ ((row / 2) % 8).  Rows past the end of x re-read the last valid
+// one (they only feed outputs that are never stored).
 struct XPtrs {
-  const uint8_t* p0;      // piece 0 of step 0 (bytes)
-  int64_t stride;         // bytes between pieces i and i + 1 (32 rows)
-  int i_max;              // last piece whose row exists
+  const uint8_t* row0;    // the lane's row for i = 0, at column 0 (bytes)
+  int64_t stride;         // bytes between the rows of i and i + 1 (8 rows)
+  int i_max;              // last i whose row exists
+  uint32_t piece[kXPieces];  // byte offset of the lane's piece for each i
 };
 
-__device__ __forceinline__ void load_x(u32x4 (&xv)[kXPieces], const XPtrs& p, int64_t ks) {
-  const uint8_t* b = p.p0 + ks * (kBK * 2);
+constexpr int kXRowBytes = kBK * 2;  // 128: swizzled x tile rows
+
+__device__ __forceinline__ void dma_x(const XPtrs& p, int64_t ks, char* stage, int wave) {
+  const uint8_t* b = p.row0 + ks * (kBK * 2);
 #pragma unroll
   for (int i = 0; i < kXPieces; ++i) {
     const int ii = i < p.i_max ? i : p.i_max;
-    xv[i] = *reinterpret_cast<const u32x4*>(b + ii * p.stride);
+    __builtin_amdgcn_global_load_lds(b + ii * p.stride + p.piece[i],
+                                     (__attribute__((address_space(3))) void*)(stage + (wave * 8 + i) * 1024), 16,
+                                     0, 0);
   }
 }
 
-__device__ __forceinline__ void store_x(const u32x4 (&xv)[kXPieces], char* xs) {
-  const int t = threadIdx.x;
-#pragma unroll
-  for (int i = 0; i < kXPieces; ++i)
-    *reinterpret_cast<u32x4*>(xs + ((t >> 3) + 32 * i) * kRowBytes + (t & 7) * 16) = xv[i];
-}
+// Waits for this wave's direct-to-LDS loads (and all other vector memory
+// loads); the barrier after it then covers every wave's.
+__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
 // The codes a lane expands in one K step: for its two W rows (j = 0, 1) the
 // 16 bytes of columns 32 h .. 32 h + 31, and the rows' block scale inputs.
@@ -171,63 +176,43 @@ __device__ __forceinline__ bf16x8 expand_frag(const float2 (&l)[4], float sa) {
   return __builtin_bit_cast(bf16x8, v);
 }
 
-// MFMAs of one K step: A fragments from the x tile in LDS, B fragments from
-// the expanded codes.  Software pipeline over the four 16-wide k steps: while
-// the 16 MFMAs of k step s run, the wave expands the B fragments of s + 1
-// (their level lookups were issued one k step earlier) and issues the LDS
-// reads of s + 2; sched_group_barrier spreads that work between the MFMAs.
+// Spreads the work issued next to 16 MFMAs between them: per MFMA three
+// VALU operations and one LDS access.
 __device__ __forceinline__ void mfma_interleave() {
 #pragma unroll
   for (int i = 0; i < 16; ++i) {
     __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
     __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);  // VALU
-    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // LDS read
+    __builtin_amdgcn_sched_group_barrier(0x080, 1, 0);  // LDS read or write
   }
 }
 
 template <bool kDQ>
-__device__ __forceinline__ void mfma_step(const char* xs, const WRegs& wr, float mean, const char* tab,
-                                          uint32_t slot, floatx16 (&acc)[8][2], int lane) {
-  float sa[2];
+__device__ __forceinline__ void block_scales(const WRegs& wr, float mean, float (&sa)[2]) {
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
     if constexpr (kDQ) sa[j] = (div127(wr.q[j]) * wr.s2[j]) + mean;  // a_hat, three roundings
     else sa[j] = wr.am[j];
   }
-  const char* xa = xs + (lane & 31) * kRowBytes + (lane >> 5) * 64;  // row lane % 32, columns 32 h ..
-  Lookups lk[3];
-  bf16x8 af[3][8];
-  bf16x8 bf[2][2];
-  auto read_a = [&](int s, bf16x8 (&f)[8]) {
+}
+
+// A fragments of 16-wide k step s: rows 32 i + lane % 32 of the swizzled x
+// tile, logical piece 4 h + s (h = lane / 32) at slot (4 h + s) ^ sw, where
+// sw = ((lane % 32) / 2) % 8 is the same for every i.
+__device__ __forceinline__ void read_a(const char* xa, int s, uint32_t sw, uint32_t h4, bf16x8 (&f)[8]) {
+  const char* p = xa + (((h4 + s) ^ sw) << 4);
 #pragma unroll
-    for (int i = 0; i < 8; ++i) f[i] = lds_frag(xa + i * 32 * kRowBytes + s * 16);
-  };
-  // k steps 0 and 1: reads out, k step 0 expanded
-  lookup_step(lk[0], wr.w, 0, tab, slot);
-  read_a(0, af[0]);
-  lookup_step(lk[1], wr.w, 1, tab, slot);
-  read_a(1, af[1]);
-  bf[0][0] = expand_frag(lk[0].l[0], sa[0]);
-  bf[0][1] = expand_frag(lk[0].l[1], sa[1]);
-  __builtin_amdgcn_sched_barrier(0);
+  for (int i = 0; i < 8; ++i) f[i] = lds_frag(p + i * 32 * kXRowBytes);
+}
+
+// The MFMAs compute y^T tiles (W fragment as the A operand, x fragment as
+// B), so that each lane ends up holding 4 consecutive output columns of one
+// output row (the A and B fragment layouts are the same).
+__device__ __forceinline__ void mfma16(const bf16x8 (&af)[8], const bf16x8 (&bf)[2], floatx16 (&acc)[8][2]) {
 #pragma unroll
-  for (int s = 0; s < 4; ++s) {
-    const int c = s & 1;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      acc[i][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[s % 3][i], bf[c][0], acc[i][0], 0, 0, 0);
-      acc[i][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[s % 3][i], bf[c][1], acc[i][1], 0, 0, 0);
-    }
-    if (s + 2 < 4) {
-      lookup_step(lk[(s + 2) % 3], wr.w, s + 2, tab, slot);
-      read_a(s + 2, af[(s + 2) % 3]);
-    }
-    if (s + 1 < 4) {
-      bf[c ^ 1][0] = expand_frag(lk[(s + 1) % 3].l[0], sa[0]);
-      bf[c ^ 1][1] = expand_frag(lk[(s + 1) % 3].l[1], sa[1]);
-    }
-    mfma_interleave();
-    __builtin_amdgcn_sched_barrier(0);
+  for (int i = 0; i < 8; ++i) {
+    acc[i][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bf[0], af[i], acc[i][0], 0, 0, 0);
+    acc[i][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bf[1], af[i], acc[i][1], 0, 0, 0);
   }
 }
 
@@ -272,7 +257,7 @@ __device__ __forceinline__ void mfma_lora(const char* xs, const char* ws, floatx
     for (int i = 0; i < 8; ++i)
 #pragma unroll
       for (int j = 0; j < 2; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[j], af[i], acc[i][j], 0, 0, 0);
   }
 }
 
@@ -286,83 +271,154 @@ __global__ __launch_bounds__(kThreads) void k_gemm(GemmArgs a) {
   const int lane = t & 63, wave = t >> 6;
   const uint32_t slot = static_cast<uint32_t>(lane & 31) << 3;
 
-  // tile order: consecutive workgroups of one XCD (dispatch is round-robin
-  // over the 8 XCDs) take neighbouring tiles along N, so they share x rows
+  fill_level_pairs(tab, tab_base, a.cb);  // once per workgroup; ends with a barrier
+  const float mean = kDQ ? *a.sc.mean : 0.0f;
   const int64_t tiles_n = (a.rows + kBN - 1) / kBN;
   const int64_t tiles = tiles_n * ((a.m + kBM - 1) / kBM);
-  int64_t tid = blockIdx.x;
-  if (tiles % 8 == 0) tid = (tid % 8) * (tiles / 8) + tid / 8;
-  const int64_t m0 = (tid / tiles_n) * kBM;
-  const int64_t n0 = (tid % tiles_n) * kBN;
   const int64_t nk = a.cols / kBK;
 
-  XPtrs xp;
-  {
-    const int64_t xr = m0 + (t >> 3);
-    const int64_t xrc = xr < a.m ? xr : a.m - 1;
-    xp.p0 = reinterpret_cast<const uint8_t*>(a.x + xrc * a.cols + (t & 7) * 8);
-    xp.stride = 32 * a.cols * 2;
-    const int64_t last = xr < a.m ? (a.m - 1 - xr) / 32 : 0;
-    xp.i_max = static_cast<int>(last < kXPieces - 1 ? last : kXPieces - 1);
-  }
-  WPtrs wp;
-#pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    const int64_t n = n0 + wave * 64 + j * 32 + (lane & 31);
-    const int64_t nc = n < a.rows ? n : a.rows - 1;  // rows past the end: never stored
-    wp.c[j] = a.packed + nc * (a.cols / 2) + (lane >> 5) * 16;
-    wp.blk[j] = nc * (a.cols / 64);
-  }
+  // Persistent: the grid holds one workgroup per CU and each takes tiles
+  // blockIdx.x, blockIdx.x + gridDim.x, ...  Tile order: dispatch deals
+  // workgroups round-robin over the 8 XCDs, so the workgroups of one XCD
+  // that run at the same time get neighbouring tiles along N and share x rows.
+  for (int64_t tile = blockIdx.x; tile < tiles; tile += gridDim.x) {
+    int64_t tid = tile;
+    if (tiles % 8 == 0) tid = (tile % 8) * (tiles / 8) + tile / 8;
+    const int64_t m0 = (tid / tiles_n) * kBM;
+    const int64_t n0 = (tid % tiles_n) * kBN;
 
-  floatx16 acc[8][2];
+    XPtrs xp;
+    {
+      const int64_t xr = m0 + wave * 64 + (lane >> 3);
+      const int64_t xrc = xr < a.m ? xr : a.m - 1;
+      xp.row0 = reinterpret_cast<const uint8_t*>(a.x + xrc * a.cols);
+      xp.stride = 8 * a.cols * 2;
+      const int64_t last = xr < a.m ? (a.m - 1 - xr) / 8 : 0;
+      xp.i_max = static_cast<int>(last < kXPieces - 1 ? last : kXPieces - 1);
 #pragma unroll
-  for (int i = 0; i < 8; ++i)
-#pragma unroll
-    for (int j = 0; j < 2; ++j)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
-
-  // Step k: MFMAs from x stage k % 2 and the codes of step k (wc); during it
-  // the x tile and codes of step k + 1 are loaded (clamped on the last step)
-  // and the x tile is written to the other stage at its end.
-  u32x4 xv[kXPieces];
-  WRegs wc, wnx;
-  load_x(xv, xp, 0);
-  load_w<kDQ>(wc, wp, a, 0);
-  fill_level_pairs(tab, tab_base, a.cb);  // ends with a barrier
-  const float mean = kDQ ? *a.sc.mean : 0.0f;
-  store_x(xv, xs0);
-  __syncthreads();
-  for (int64_t ks = 0; ks < nk; ++ks) {
-    const int64_t kn = ks + 1 < nk ? ks + 1 : ks;
-    load_x(xv, xp, kn);
-    load_w<kDQ>(wnx, wp, a, kn);
-    // keep the loads here, a whole step ahead of their use (left alone, the
-    // scheduler sinks them next to the stores and exposes their latency)
-    __builtin_amdgcn_sched_barrier(0);
-    mfma_step<kDQ>((ks & 1) ? xs1 : xs0, wc, mean, tabc, slot, acc, lane);
-    store_x(xv, (ks & 1) ? xs0 : xs1);
-    __syncthreads();
-    wc = wnx;
-  }
-  for (int64_t k0 = 0; k0 < a.kl; k0 += kBK) {
-    lora_step_to_lds(xs0, xs1, a, m0, n0, k0);
-    __syncthreads();
-    mfma_lora(xs0, xs1, acc, wave, lane);
-    __syncthreads();
-  }
-
-  // epilogue: lane holds D[(e % 4) + 4 (lane / 32) + 8 (e / 4)][lane % 32] of each 32 x 32 tile
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
+      for (int i = 0; i < kXPieces; ++i) {
+        const uint32_t r = static_cast<uint32_t>(8 * i + (lane >> 3));  // tile row - 64 wave
+        xp.piece[i] = (((lane & 7) ^ ((r >> 1) & 7)) << 4);
+      }
+    }
+    WPtrs wp;
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
-      const int64_t col = n0 + wave * 64 + j * 32 + (lane & 31);
+      const int64_t n = n0 + wave * 64 + j * 32 + (lane & 31);
+      const int64_t nc = n < a.rows ? n : a.rows - 1;  // rows past the end: never stored
+      wp.c[j] = a.packed + nc * (a.cols / 2) + (lane >> 5) * 16;
+      wp.blk[j] = nc * (a.cols / 64);
+    }
+
+    floatx16 acc[8][2];
 #pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const int64_t row = m0 + i * 32 + (e & 3) + 4 * (lane >> 5) + 8 * (e >> 2);
-        if (row < a.m && col < a.rows)
-          a.y[row * a.rows + col] = __builtin_bit_cast(uint16_t, static_cast<__bf16>(acc[i][j][e]));
+    for (int i = 0; i < 8; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
+
+    // K step k: MFMAs from x stage k % 2 and the codes of step k (wc), in
+    // four 16-wide k steps s.  Software pipeline: while the MFMAs of s run,
+    // the wave expands the B fragments of s + 1 (looked up one k step
+    // earlier) and issues the LDS reads of s + 2; during s = 3 it writes the
+    // next step's x tile to the other stage and expands the next step's
+    // s = 0, so that after the barrier the MFMAs can start at once.  The
+    // global loads of step k + 1 (clamped on the last step) go out at the top
+    // of step k.
+    WRegs wc, wnx;
+    dma_x(xp, 0, xs0, wave);
+    load_w<kDQ>(wc, wp, a, 0);
+    float sa[2];
+    bf16x8 bf[2][2];
+    Lookups lk[3];
+    bf16x8 af[3][8];
+    const uint32_t sw = ((lane & 31) >> 1) & 7, h4 = (lane >> 5) * 4;
+    block_scales<kDQ>(wc, mean, sa);
+    lookup_step(lk[0], wc.w, 0, tabc, slot);
+    bf[0][0] = expand_frag(lk[0].l[0], sa[0]);
+    bf[0][1] = expand_frag(lk[0].l[1], sa[1]);
+    wait_vmem();
+    __syncthreads();
+    for (int64_t ks = 0; ks < nk; ++ks) {
+      const int64_t kn = ks + 1 < nk ? ks + 1 : ks;
+      // the next step's x tile goes straight to the other stage (last read
+      // before the previous barrier) and its codes to registers
+      dma_x(xp, kn, (ks & 1) ? xs0 : xs1, wave);
+      load_w<kDQ>(wnx, wp, a, kn);
+      __builtin_amdgcn_sched_barrier(0);
+      const char* xa = ((ks & 1) ? xs1 : xs0) + (lane & 31) * kXRowBytes;
+      read_a(xa, 0, sw, h4, af[0]);
+      read_a(xa, 1, sw, h4, af[1]);
+      lookup_step(lk[1], wc.w, 1, tabc, slot);
+      __builtin_amdgcn_sched_barrier(0);
+      // s = 0
+      mfma16(af[0], bf[0], acc);
+      bf[1][0] = expand_frag(lk[1].l[0], sa[0]);
+      bf[1][1] = expand_frag(lk[1].l[1], sa[1]);
+      read_a(xa, 2, sw, h4, af[2]);
+      lookup_step(lk[2], wc.w, 2, tabc, slot);
+      mfma_interleave();
+      __builtin_amdgcn_sched_barrier(0);
+      // s = 1
+      mfma16(af[1], bf[1], acc);
+      bf[0][0] = expand_frag(lk[2].l[0], sa[0]);
+      bf[0][1] = expand_frag(lk[2].l[1], sa[1]);
+      read_a(xa, 3, sw, h4, af[0]);
+      lookup_step(lk[0], wc.w, 3, tabc, slot);
+      mfma_interleave();
+      __builtin_amdgcn_sched_barrier(0);
+      // s = 2
+      mfma16(af[2], bf[0], acc);
+      bf[1][0] = expand_frag(lk[0].l[0], sa[0]);
+      bf[1][1] = expand_frag(lk[0].l[1], sa[1]);
+      mfma_interleave();
+      __builtin_amdgcn_sched_barrier(0);
+      // s = 3, with the next step's s = 0 expansion
+      mfma16(af[0], bf[1], acc);
+      block_scales<kDQ>(wnx, mean, sa);
+      lookup_step(lk[1], wnx.w, 0, tabc, slot);
+      bf[0][0] = expand_frag(lk[1].l[0], sa[0]);
+      bf[0][1] = expand_frag(lk[1].l[1], sa[1]);
+      mfma_interleave();
+      __builtin_amdgcn_sched_barrier(0);
+      wait_vmem();
+      __syncthreads();
+      wc = wnx;
+    }
+    for (int64_t k0 = 0; k0 < a.kl; k0 += kBK) {
+      lora_step_to_lds(xs0, xs1, a, m0, n0, k0);
+      __syncthreads();
+      mfma_lora(xs0, xs1, acc, wave, lane);
+      __syncthreads();
+    }
+
+    // epilogue: of each 32 x 32 tile of y^T the lane holds element e at
+    // output column (e % 4) + 4 (lane / 32) + 8 (e / 4) and output row
+    // lane % 32: four consecutive columns per group of four e, written as one
+    // 8-byte store when the row holds them all and is 8-byte aligned
+    const bool vec = (a.rows & 3) == 0;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int64_t row = m0 + i * 32 + (lane & 31);
+      if (row >= a.m) continue;
+      uint16_t* yr = a.y + row * a.rows;
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int64_t col = n0 + wave * 64 + j * 32 + 4 * (lane >> 5) + 8 * g;
+          const uint32_t p0 = bf16_pair(acc[i][j][4 * g], acc[i][j][4 * g + 1]);
+          const uint32_t p1 = bf16_pair(acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]);
+          if (vec && col + 3 < a.rows) {
+            *reinterpret_cast<uint2*>(yr + col) = make_uint2(p0, p1);
+          } else {
+            const uint16_t v[4] = {static_cast<uint16_t>(p0), static_cast<uint16_t>(p0 >> 16),
+                                   static_cast<uint16_t>(p1), static_cast<uint16_t>(p1 >> 16)};
+            for (int u = 0; u < 4; ++u)
+              if (col + u < a.rows) yr[col + u] = v[u];
+          }
+        }
       }
     }
   }
@@ -430,9 +486,10 @@ hipError_t launch_gemm(const uint8_t* packed, int64_t rows, int64_t cols, Scales
                        a.kl, lora_scale, u_ws);
   }
   const int64_t tiles = ((rows + kBN - 1) / kBN) * ((m + kBM - 1) / kBM);
-  if (tiles > 0x7FFFFFFF) return hipErrorInvalidValue;
-  if (sc.absmax) hipLaunchKernelGGL(k_gemm<false>, dim3(static_cast<unsigned>(tiles)), dim3(kThreads), 0, s, a);
-  else hipLaunchKernelGGL(k_gemm<true>, dim3(static_cast<unsigned>(tiles)), dim3(kThreads), 0, s, a);
+  const int64_t cus = device_cus();
+  const unsigned grid = static_cast<unsigned>(tiles < cus ? tiles : cus);  // persistent: one per CU
+  if (sc.absmax) hipLaunchKernelGGL(k_gemm<false>, dim3(grid), dim3(kThreads), 0, s, a);
+  else hipLaunchKernelGGL(k_gemm<true>, dim3(grid), dim3(kThreads), 0, s, a);
   return hipGetLastError();
 }
 
