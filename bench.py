@@ -314,15 +314,16 @@ def extra_legs(torch, nf4, syn, dev, stream, EventTimer):
     del Ws
 
     # larger decode GEMVs: the Llama-8B MLP (C3 shapes) and one 70B-shaped layer
-    def gemv_pool(shapes, reps, label):
+    def gemv_pool(shapes, reps, label, m=1):
         Wl = []
         for i, (r_, c_) in enumerate(shapes):
             g.manual_seed(9_000 + i)
             w = (torch.randn((r_, c_), generator=g, device=dev) * 0.02).to(torch.bfloat16)
             Wl.append(nf4.quantize_weight(w, double_quant=True))
             del w
-        xs = {c_: (torch.randn((1, c_), generator=g, device=dev)).to(torch.bfloat16) for _, c_ in shapes}
-        ys = [torch.empty((1, r_), dtype=torch.bfloat16, device=dev) for r_, _ in shapes]
+        xs = {c_: (torch.randn((m, c_), generator=g, device=dev)).to(torch.bfloat16) for _, c_ in shapes}
+        ys = [torch.empty((m, r_), dtype=torch.bfloat16, device=dev) for r_, _ in shapes]
+
         def run():
             for W, yy in zip(Wl, ys):
                 nf4.nf4_gemv(W, xs[W.cols], yy)
@@ -339,16 +340,18 @@ def extra_legs(torch, nf4, syn, dev, stream, EventTimer):
         t.stop(s)
         torch.cuda.synchronize()
         total_us = t.mean_us() / reps
-        nbytes = sum(step_bytes(r_, c_)["gemv"] for r_, c_ in shapes)
+        nbytes = sum(step_bytes(r_, c_, m)["gemv"] for r_, c_ in shapes)
         del Wl
-        return {"workload": label, "us_per_pass": round(total_us, 2),
+        return {"workload": label, "m": m, "us_per_pass": round(total_us, 2),
                 "GBps": round(nbytes / (total_us * 1e-6) / 1e9, 1),
                 "frac_hbm_peak": round(nbytes / (total_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}
 
     print("[bench] gemv MLP / 70B-layer legs", file=sys.stderr, flush=True)
     mlp = [(14336, 4096), (14336, 4096), (4096, 14336)] * 6
-    res["gemv_mlp_8b"] = gemv_pool(mlp, 10, "Llama-8B MLP gate/up 14336x4096 + down 4096x14336, NF4+DQ, M=1, "
-                                            "6 distinct triples (545 MB) per pass")
+    label = ("Llama-8B MLP gate/up 14336x4096 + down 4096x14336, NF4+DQ, 6 distinct triples (545 MB) per pass")
+    res["gemv_mlp_8b"] = gemv_pool(mlp, 10, label + ", M=1")
+    res["gemv_mlp_8b_m4"] = gemv_pool(mlp, 10, label + ", M=4", m=4)
+    res["gemv_mlp_8b_m16"] = gemv_pool(mlp, 10, label + ", M=16", m=16)
     layer = [(8192, 8192), (1024, 8192), (1024, 8192), (8192, 8192), (28672, 8192), (28672, 8192), (8192, 28672)]
     res["gemv_layer_70b"] = gemv_pool(layer, 10, "70B-shaped layer q,k,v,o,gate,up,down NF4+DQ, M=1 (442 MB)")
 
@@ -384,6 +387,25 @@ def extra_legs(torch, nf4, syn, dev, stream, EventTimer):
         "TFLOPs": round(tf, 1),
         "frac_mfma_bf16_peak": round(tf / MFMA_BF16_PEAK_TFLOPS, 4),
     }
+    # Calibration only (not part of the path): the vendor library's plain bf16
+    # GEMM of the same shape on an already dequantized weight, no LoRA.
+    Wd = nf4.nf4_dequantize(W, out_dtype=torch.bfloat16)
+    for _ in range(3):
+        torch.nn.functional.linear(X, Wd)
+    torch.cuda.synchronize()
+    t = EventTimer(torch, stream)
+    for _ in range(reps):
+        s = t.start()
+        torch.nn.functional.linear(X, Wd)
+        t.stop(s)
+    torch.cuda.synchronize()
+    us_lib = t.mean_us()
+    res["gemm_qlora_forward"]["calibration_torch_linear_bf16"] = {
+        "what": "torch.nn.functional.linear (hipBLASLt) on the dequantized bf16 weight, same M, N, K, no LoRA",
+        "us": round(us_lib, 1),
+        "TFLOPs": round(2.0 * M * N * K / (us_lib * 1e-6) / 1e12, 1),
+    }
+    del Wd
     return res
 
 

@@ -372,17 +372,21 @@ __device__ __forceinline__ void row_load(RowItem& it, const uint8_t* __restrict_
   if constexpr (kDQ) {
     it.q = sc.q[row_blk0 + bc];
     // group of the block: uniform part plus a small per-lane carry
-    it.s2 = sc.absmax2[(row_blk0 >> 8) + (static_cast<int>(row_blk0 & 255) + bc >> 8)];
+    it.s2 = sc.absmax2[(row_blk0 >> 8) + ((static_cast<int>(row_blk0 & 255) + bc) >> 8)];
   } else {
     it.am = sc.absmax[row_blk0 + bc];
   }
 }
 
-template <bool kDQ>
-__device__ __forceinline__ float row_dot(const RowItem& it, const uint32_t* xh, const char* tab, uint32_t slot,
-                                         float mean, float xinv) {
+// Products of one row item with MC rows of x (the lookups are shared):
+// out[c] = a_hat * xinv[c] * sum_k level[code_k] * xh[c][k].
+template <int MC, bool kDQ>
+__device__ __forceinline__ void row_dot(const RowItem& it, const uint32_t (&xh)[MC][32], const char* tab,
+                                        uint32_t slot, float mean, const float (&xinv)[MC], float (&out)[MC]) {
   const uint32_t q[8] = {it.w[0].x, it.w[0].y, it.w[0].z, it.w[0].w, it.w[1].x, it.w[1].y, it.w[1].z, it.w[1].w};
-  float s0 = 0.0f, s1 = 0.0f;
+  float s0[MC], s1[MC];
+#pragma unroll
+  for (int c = 0; c < MC; ++c) s0[c] = s1[c] = 0.0f;
 #pragma unroll
   for (int j = 0; j < 8; j += 2) {
     uint32_t e[8];
@@ -392,15 +396,39 @@ __device__ __forceinline__ float row_dot(const RowItem& it, const uint32_t* xh, 
       e[u] = *reinterpret_cast<const uint32_t*>(tab + addr);
     }
 #pragma unroll
-    for (int u = 0; u < 8; u += 2) {
-      s0 = dot2h(e[u], xh[4 * j + u], s0);
-      s1 = dot2h(e[u + 1], xh[4 * j + u + 1], s1);
-    }
+    for (int u = 0; u < 8; u += 2)
+#pragma unroll
+      for (int c = 0; c < MC; ++c) {
+        s0[c] = dot2h(e[u], xh[c][4 * j + u], s0[c]);
+        s1[c] = dot2h(e[u + 1], xh[c][4 * j + u + 1], s1[c]);
+      }
   }
   float a;
   if constexpr (kDQ) a = (div127(it.q) * it.s2) + mean;  // a_hat
   else a = it.am;
-  return (s0 + s1) * (a * xinv);
+#pragma unroll
+  for (int c = 0; c < MC; ++c) out[c] = (s0[c] + s1[c]) * (a * xinv[c]);
+}
+
+// One row of x, the lane's 64-block: fp16 pairs scaled by 2^k, k chosen so
+// that the largest |x| of the block lies in [2^14, 2^15); xinv = 2^-k.
+__device__ __forceinline__ void x_block_to_half(const uint4 (&xv)[8], uint32_t (&xh)[32], float& xinv) {
+  uint32_t xw[32];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) { xw[4 * i] = xv[i].x; xw[4 * i + 1] = xv[i].y; xw[4 * i + 2] = xv[i].z; xw[4 * i + 3] = xv[i].w; }
+  uint32_t mx = 0;
+#pragma unroll
+  for (int i = 0; i < 32; ++i) mx = max(mx, max(xw[i] & 0x7FFF0000u, (xw[i] << 16) & 0x7FFF0000u));
+  int k = 14 - (static_cast<int>(mx >> 23) - 127);
+  k = k < -126 ? -126 : (k > 126 ? 126 : k);
+  const float sc2 = __uint_as_float(static_cast<uint32_t>(127 + k) << 23);
+  xinv = __uint_as_float(static_cast<uint32_t>(127 - k) << 23);
+#pragma unroll
+  for (int i = 0; i < 32; ++i) {
+    const float lo = __uint_as_float(xw[i] << 16) * sc2;         // exact: a power of two
+    const float hi = __uint_as_float(xw[i] & 0xFFFF0000u) * sc2;
+    xh[i] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(lo, hi));
+  }
 }
 
 struct RowsPlan {
@@ -410,13 +438,16 @@ struct RowsPlan {
   int wpr;           // waves per segment (row parts)
 };
 
-template <int U, int kWaves, bool kDQ, bool kBf16Out>
+// MC rows of x per launch (x and y point at the first of them; the x rows
+// are cols apart, the y rows `rows` apart).
+template <int U, int kWaves, int MC, bool kDQ, bool kBf16Out>
 __global__ __launch_bounds__(kWaves * 64) void k_gemv_rows(const uint8_t* __restrict__ packed, int64_t rows,
                                                            int64_t cols, Scales sc, const uint16_t* __restrict__ x,
                                                            void* __restrict__ y, Codebook cb, RowsPlan pl) {
+  constexpr int kRowsWg = kRowsMaxWg / MC;
   __shared__ uint32_t tab[256 * 64];
   __shared__ uint32_t tab_base[256];
-  __shared__ float part[kRowsMaxWg * kSegMax];
+  __shared__ float part[kRowsWg * kSegMax * MC];
   const char* smem = reinterpret_cast<const char*>(tab);
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -437,12 +468,13 @@ __global__ __launch_bounds__(kWaves * 64) void k_gemv_rows(const uint8_t* __rest
   const int64_t row0 = gp < rows ? gp : rows - 1;
   const int64_t last = n > 0 ? row0 + (n - 1) * np : row0;  // loads are clamped to it
 
-  // x of the lane's block, then the first U rows, then the table
-  uint4 xv[8];
-  {
-    const uint4* xp = reinterpret_cast<const uint4*>(x) + 8 * static_cast<int64_t>(bc);
+  // x of the lane's block (MC rows), then the first U rows, then the table
+  uint4 xv[MC][8];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) xv[i] = xp[i];
+  for (int c = 0; c < MC; ++c) {
+    const uint4* xp = reinterpret_cast<const uint4*>(x + c * cols) + 8 * static_cast<int64_t>(bc);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) xv[c][i] = xp[i];
   }
   RowItem it[U];
 #pragma unroll
@@ -452,28 +484,10 @@ __global__ __launch_bounds__(kWaves * 64) void k_gemv_rows(const uint8_t* __rest
   }
   fill_half_table(tab, tab_base, cb);  // ends with a barrier
 
-  // x to fp16 pairs scaled by 2^k, k chosen so that the largest |x| of the
-  // block lies in [2^14, 2^15)
-  uint32_t xh[32];
-  float xinv;
-  {
-    uint32_t xw[32];
+  uint32_t xh[MC][32];
+  float xinv[MC];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) { xw[4 * i] = xv[i].x; xw[4 * i + 1] = xv[i].y; xw[4 * i + 2] = xv[i].z; xw[4 * i + 3] = xv[i].w; }
-    uint32_t mx = 0;
-#pragma unroll
-    for (int i = 0; i < 32; ++i) mx = max(mx, max(xw[i] & 0x7FFF0000u, (xw[i] << 16) & 0x7FFF0000u));
-    int k = 14 - (static_cast<int>(mx >> 23) - 127);
-    k = k < -126 ? -126 : (k > 126 ? 126 : k);
-    const float sc2 = __uint_as_float(static_cast<uint32_t>(127 + k) << 23);
-    xinv = __uint_as_float(static_cast<uint32_t>(127 - k) << 23);
-#pragma unroll
-    for (int i = 0; i < 32; ++i) {
-      const float lo = __uint_as_float(xw[i] << 16) * sc2;         // exact: a power of two
-      const float hi = __uint_as_float(xw[i] & 0xFFFF0000u) * sc2;
-      xh[i] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(lo, hi));
-    }
-  }
+  for (int c = 0; c < MC; ++c) x_block_to_half(xv[c], xh[c], xinv[c]);
   const float mean = kDQ ? *sc.mean : 0.0f;
 
   for (int64_t i0 = 0; i0 < n; i0 += U) {
@@ -481,29 +495,35 @@ __global__ __launch_bounds__(kWaves * 64) void k_gemv_rows(const uint8_t* __rest
     for (int u = 0; u < U; ++u) {
       const int64_t i = i0 + u;
       if (i < n) {  // wave-uniform
-        float v = row_dot<kDQ>(it[u], xh, smem, slot, mean, xinv);
-        v = wave_sum_to_last(lane_on ? v : 0.0f);
-        if (lane == 63) part[(prt * kmax + i) * kSegMax + seg] = v;
+        float v[MC];
+        row_dot<MC, kDQ>(it[u], xh, smem, slot, mean, xinv, v);
+#pragma unroll
+        for (int c = 0; c < MC; ++c) {
+          const float t = wave_sum_to_last(lane_on ? v[c] : 0.0f);
+          if (lane == 63) part[((prt * kmax + i) * kSegMax + seg) * MC + c] = t;
+        }
       }
       const int64_t r = row0 + (i + U) * np;
       row_load<kDQ>(it[u], packed, (r < last ? r : last) * nblk, bc, sc);
     }
   }
   __syncthreads();
-  for (int64_t t = threadIdx.x; t < pl.wpr * kmax; t += blockDim.x) {
-    const int64_t row = static_cast<int64_t>(blockIdx.x) * pl.wpr + t / kmax + (t % kmax) * np;
+  for (int64_t t = threadIdx.x; t < pl.wpr * kmax * MC; t += blockDim.x) {
+    const int64_t rt = t / MC;
+    const int c = static_cast<int>(t % MC);
+    const int64_t row = static_cast<int64_t>(blockIdx.x) * pl.wpr + rt / kmax + (rt % kmax) * np;
     if (row >= rows) continue;
-    float s = part[t * kSegMax];
-    for (int k = 1; k < pl.nseg; ++k) s += part[t * kSegMax + k];
-    if constexpr (kBf16Out) static_cast<uint16_t*>(y)[row] = static_cast<uint16_t>(f32_to_bf16(s));
-    else static_cast<float*>(y)[row] = s;
+    float s = part[(rt * kSegMax) * MC + c];
+    for (int k = 1; k < pl.nseg; ++k) s += part[(rt * kSegMax + k) * MC + c];
+    if constexpr (kBf16Out) static_cast<uint16_t*>(y)[c * rows + row] = static_cast<uint16_t>(f32_to_bf16(s));
+    else static_cast<float*>(y)[c * rows + row] = s;
   }
 }
 
 // Plan for k_gemv_rows: rows split evenly over at least one workgroup per CU
-// (at most kRowsMaxWg rows each), columns into the fewest segments of at most
-// 64 blocks, balanced, and the waves spread over the segments.
-RowsPlan rows_plan(int64_t rows, int64_t cols, int waves) {
+// (at most rows_wg rows each), columns into the fewest segments of at most 64
+// blocks, balanced, and the waves spread over the segments.
+RowsPlan rows_plan(int64_t rows, int64_t cols, int waves, int rows_wg) {
   const int64_t cus = device_cus();
   const int64_t nblk = cols / 64;
   RowsPlan pl{};
@@ -511,24 +531,45 @@ RowsPlan rows_plan(int64_t rows, int64_t cols, int waves) {
   pl.seg_blocks = static_cast<int>((nblk + pl.nseg - 1) / pl.nseg);
   pl.wpr = waves / pl.nseg;
   // grid: one workgroup per CU, more if a workgroup would own more than
-  // kRowsMaxWg rows (wpr parts of ceil(rows / (grid * wpr)) rows each)
+  // rows_wg rows (wpr parts of ceil(rows / (grid * wpr)) rows each)
   int64_t g = cus;
-  while (pl.wpr > 0 && pl.wpr * ((rows + g * pl.wpr - 1) / (g * pl.wpr)) > kRowsMaxWg) ++g;
+  while (pl.wpr > 0 && pl.wpr * ((rows + g * pl.wpr - 1) / (g * pl.wpr)) > rows_wg) ++g;
   pl.grid = static_cast<int>(g);
   return pl;
 }
 
-template <int U, int kWaves, bool kDQ>
+template <int U, int kWaves, int MC, bool kDQ>
 hipError_t launch_rows(const uint8_t* packed, int64_t rows, int64_t cols, Scales sc, const uint16_t* x, void* y,
                        int y_bf16, hipStream_t s) {
-  const RowsPlan pl = rows_plan(rows, cols, kWaves);
+  const RowsPlan pl = rows_plan(rows, cols, kWaves, kRowsMaxWg / MC);
   if (pl.nseg > kSegMax || pl.wpr < 1) return hipErrorInvalidValue;
   const int64_t g = pl.grid;
   const Codebook& cb = codebook();
   const dim3 gd(static_cast<unsigned>(g)), bd(64 * kWaves);
-  if (y_bf16) hipLaunchKernelGGL((k_gemv_rows<U, kWaves, kDQ, true>), gd, bd, 0, s, packed, rows, cols, sc, x, y, cb, pl);
-  else hipLaunchKernelGGL((k_gemv_rows<U, kWaves, kDQ, false>), gd, bd, 0, s, packed, rows, cols, sc, x, y, cb, pl);
+  if (y_bf16)
+    hipLaunchKernelGGL((k_gemv_rows<U, kWaves, MC, kDQ, true>), gd, bd, 0, s, packed, rows, cols, sc, x, y, cb, pl);
+  else
+    hipLaunchKernelGGL((k_gemv_rows<U, kWaves, MC, kDQ, false>), gd, bd, 0, s, packed, rows, cols, sc, x, y, cb, pl);
   return hipGetLastError();
+}
+
+// Skinny products (m > 1): passes of up to 4 rows of x over W, 8 waves.
+template <bool kDQ>
+hipError_t launch_rows_multi(const uint8_t* packed, int64_t rows, int64_t cols, Scales sc, const uint16_t* x,
+                             int64_t m, void* y, int y_bf16, hipStream_t s) {
+  const size_t ysz = y_bf16 ? 2 : 4;
+  for (int64_t c0 = 0; c0 < m; c0 += 4) {
+    const int64_t mc = m - c0 < 4 ? m - c0 : 4;
+    const uint16_t* xc = x + c0 * cols;
+    void* yc = static_cast<char*>(y) + c0 * rows * ysz;
+    hipError_t e;
+    if (mc == 4) e = launch_rows<1, 8, 4, kDQ>(packed, rows, cols, sc, xc, yc, y_bf16, s);
+    else if (mc == 3) e = launch_rows<1, 8, 3, kDQ>(packed, rows, cols, sc, xc, yc, y_bf16, s);
+    else if (mc == 2) e = launch_rows<1, 8, 2, kDQ>(packed, rows, cols, sc, xc, yc, y_bf16, s);
+    else e = launch_rows<1, 8, 1, kDQ>(packed, rows, cols, sc, xc, yc, y_bf16, s);
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
 }
 
 template <int R, bool kDQ>
@@ -563,12 +604,12 @@ hipError_t launch_gemv(const uint8_t* packed, int64_t rows, int64_t cols, Scales
     const int64_t nseg = (cols / 64 + 63) / 64;
     if (nseg == 1) {
       // one column segment: two rows in flight per wave, 8 waves
-      return sc.absmax ? launch_rows<2, 8, false>(packed, rows, cols, sc, x, y, y_bf16, s)
-                       : launch_rows<2, 8, true>(packed, rows, cols, sc, x, y, y_bf16, s);
+      return sc.absmax ? launch_rows<2, 8, 1, false>(packed, rows, cols, sc, x, y, y_bf16, s)
+                       : launch_rows<2, 8, 1, true>(packed, rows, cols, sc, x, y, y_bf16, s);
     }
     if (nseg <= kSegMax) {
-      return sc.absmax ? launch_rows<1, 16, false>(packed, rows, cols, sc, x, y, y_bf16, s)
-                       : launch_rows<1, 16, true>(packed, rows, cols, sc, x, y, y_bf16, s);
+      return sc.absmax ? launch_rows<1, 16, 1, false>(packed, rows, cols, sc, x, y, y_bf16, s)
+                       : launch_rows<1, 16, 1, true>(packed, rows, cols, sc, x, y, y_bf16, s);
     }
     // wider than 16 segments (cols > 65536): one row group per wave
     const int64_t cus = device_cus();
@@ -582,6 +623,11 @@ hipError_t launch_gemv(const uint8_t* packed, int64_t rows, int64_t cols, Scales
       else launch_m1<2, true>(packed, rows, cols, sc, x, y, y_bf16, 16, s);
     }
   } else {
+    // skinny products: passes of up to 4 rows of x (8 waves, so nseg <= 8)
+    if ((cols / 64 + 63) / 64 <= 8) {
+      return sc.absmax ? launch_rows_multi<false>(packed, rows, cols, sc, x, m, y, y_bf16, s)
+                       : launch_rows_multi<true>(packed, rows, cols, sc, x, m, y, y_bf16, s);
+    }
     if (y_bf16) hipLaunchKernelGGL((k_gemv<4, true>), grid, dim3(256), 0, s, packed, rows, cols, sc, x, mm, y, cb);
     else hipLaunchKernelGGL((k_gemv<4, false>), grid, dim3(256), 0, s, packed, rows, cols, sc, x, mm, y, cb);
   }

@@ -158,13 +158,14 @@ def test_gemv_x_dynamic_range():
     assert e <= MATMUL_RTOL
 
 
-@pytest.mark.parametrize("rows,cols", [(7, 65600), (40, 131072)])
-def test_gemv_wider_than_16_segments(rows, cols):
-    """Rows longer than 16 x 64 blocks take the per-row-group kernel."""
-    say("gemv wide", rows, cols)
+@pytest.mark.parametrize("rows,cols,m", [(7, 65600, 1), (40, 131072, 1), (9, 32832, 3), (20, 40960, 16)])
+def test_gemv_wider_than_16_segments(rows, cols, m):
+    """Rows longer than 16 x 64 blocks (m = 1) or 8 x 64 blocks (m > 1) take
+    the per-row-group kernels."""
+    say("gemv wide", rows, cols, "m", m)
     torch = need_gpu()
     w = syn.normal_f32((rows, cols), 0.02, 61)
-    xb = syn.to_bf16(syn.normal_f32((1, cols), 1.0, 62))
+    xb = syn.to_bf16(syn.normal_f32((m, cols), 1.0, 62))
     W = nf4.quantize_weight(to_dev(w), double_quant=True)
     y = nf4.nf4_gemv(W, xb.to("cuda"), y_dtype=torch.float32)
     torch.cuda.synchronize()
@@ -174,14 +175,16 @@ def test_gemv_wider_than_16_segments(rows, cols):
     assert e <= MATMUL_RTOL
 
 
+@pytest.mark.parametrize("m", [1, 3, 4, 6])
 @pytest.mark.parametrize("rows,cols", [(3000, 4096), (2047, 8192), (600, 28672), (257, 1024), (4100, 128)])
-def test_gemv_m1_row_interleave_shapes(rows, cols):
+def test_gemv_row_interleave_shapes(rows, cols, m):
     """Row counts that do not divide evenly over the grid's row parts, with
-    one, two, four and seven column segments."""
-    say("gemv m1 shapes", rows, cols)
+    one, two, four and seven column segments, and x in passes of up to four
+    rows."""
+    say("gemv shapes", rows, cols, "m", m)
     torch = need_gpu()
     w = syn.normal_f32((rows, cols), 0.02, rows + cols)
-    xb = syn.to_bf16(syn.normal_f32((1, cols), 2.0, 63))
+    xb = syn.to_bf16(syn.normal_f32((m, cols), 2.0, 63 + m))
     W = nf4.quantize_weight(to_dev(w), double_quant=True)
     y = nf4.nf4_gemv(W, xb.to("cuda"), y_dtype=torch.float32)
     torch.cuda.synchronize()
