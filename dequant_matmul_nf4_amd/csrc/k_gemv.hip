@@ -553,6 +553,240 @@ hipError_t launch_rows(const uint8_t* packed, int64_t rows, int64_t cols, Scales
   return hipGetLastError();
 }
 
+// ---------------------------------------------------------------- m = 2..16
+//
+// Skinny products on the matrix cores: v_mfma_f32_16x16x32_f16 with x (its
+// m <= 16 rows, padded with zeros) as the A operand and the NF4 levels of 16
+// weight rows as the B operand, D[x row][weight row].
+//  - B needs no arithmetic: a byte of codes indexes the fp16 level-pair table
+//    (one permute, one LDS read) and the pair is already an operand word.
+//    The two MFMAs of a 64-block start from zero; the block's scale (one per
+//    weight row, i.e. per lane column of D) is then applied with 4 FMAs.
+//  - k order inside a block: lane group g = lane / 16 takes codes
+//    16 g .. 16 g + 15 (bytes 8 g .. 8 g + 7), the first 8 for the first MFMA
+//    and the rest for the second, for both operands.
+//  - x: a wave owns a column segment of at most 8 blocks and keeps it in
+//    registers as fp16, each x row scaled by a power of two chosen from its
+//    largest |x| in the segment (undone on the segment's partial sums).
+//  - Weight rows go in groups of 16, interleaved over the grid (group p of a
+//    workgroup is p-th of its share); waves walk the workgroup's groups for
+//    each of their segments and park each (group, segment) partial tile in
+//    LDS; the segments are added in a fixed order at the end.
+constexpr int kPartTiles = 64;   // 16 x 16 float partial tiles per workgroup (64 KiB)
+constexpr int kMfmaSeg = 4;      // blocks per column segment (x kept in registers)
+constexpr int kMfmaWaves = 16;
+
+typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+
+struct MfmaPlan {
+  int grid;          // workgroups
+  int nseg;          // column segments
+  int seg_blocks;    // blocks per segment (<= kMfmaSeg)
+  int kmax;          // row groups per workgroup, at most
+};
+
+template <bool kDQ>
+struct GroupItem {
+  uint2 c;     // 8 bytes of codes: weight row n = lane % 16, bytes 8 g .. 8 g + 7 of the block
+  float am;
+  int q;
+  float s2;
+};
+
+template <bool kDQ>
+__device__ __forceinline__ void group_load(GroupItem<kDQ>& it, const uint8_t* __restrict__ packed, int64_t nblk,
+                                           int64_t row, int64_t blk, int g, Scales sc) {
+  const int64_t b = row * nblk + blk;
+  it.c = *reinterpret_cast<const uint2*>(packed + b * 32 + 8 * g);
+  if constexpr (kDQ) {
+    it.q = sc.q[b];
+    it.s2 = sc.absmax2[b >> 8];
+  } else {
+    it.am = sc.absmax[b];
+  }
+}
+
+template <int kWaves, bool kDQ, bool kBf16Out>
+__global__ __launch_bounds__(kWaves * 64) void k_gemv_mfma(const uint8_t* __restrict__ packed, int64_t rows,
+                                                           int64_t cols, Scales sc, const uint16_t* __restrict__ x,
+                                                           int m, void* __restrict__ y, Codebook cb, MfmaPlan pl) {
+  __shared__ uint32_t tab[256 * 64];
+  __shared__ uint32_t tab_base[256];
+  __shared__ float part[kPartTiles * 256];
+  const char* smem = reinterpret_cast<const char*>(tab);
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int g = lane >> 4;       // lane group
+  const int ln = lane & 15;      // x row (A) / weight row in the group (B, D column)
+  const uint32_t slot = static_cast<uint32_t>(lane) << 2;
+  const int64_t nblk = cols / 64;
+  const int64_t ngroups = (rows + 15) / 16;
+  const int64_t G = gridDim.x;
+  const int64_t kmine = (static_cast<int64_t>(blockIdx.x) < ngroups) ? (ngroups - blockIdx.x + G - 1) / G : 0;
+  const float mean = kDQ ? *sc.mean : 0.0f;
+  fill_half_table(tab, tab_base, cb);  // ends with a barrier
+
+  for (int seg = wave; seg < pl.nseg; seg += kWaves) {
+    const int64_t b0 = static_cast<int64_t>(seg) * pl.seg_blocks;
+    const int nb = static_cast<int>(nblk - b0 < pl.seg_blocks ? nblk - b0 : pl.seg_blocks);
+    // x of the segment: lane (row ln, group g) takes columns 16 g .. 16 g + 15
+    // of each block, as fp16 pairs scaled by 2^k(ln)
+    uint32_t xh[kMfmaSeg][8];
+    float xinv_d[4];
+    {
+      uint4 xv[kMfmaSeg][2];
+      const bool live = ln < m;
+      const uint16_t* xr = x + static_cast<int64_t>(live ? ln : 0) * cols;
+#pragma unroll
+      for (int j = 0; j < kMfmaSeg; ++j) {
+        const int64_t blk = b0 + (j < nb ? j : nb - 1);
+        const uint4* p = reinterpret_cast<const uint4*>(xr + blk * 64 + 16 * g);
+        xv[j][0] = live ? p[0] : make_uint4(0, 0, 0, 0);
+        xv[j][1] = live ? p[1] : make_uint4(0, 0, 0, 0);
+      }
+      uint32_t mx = 0;
+#pragma unroll
+      for (int j = 0; j < kMfmaSeg; ++j) {
+        const uint32_t w[8] = {xv[j][0].x, xv[j][0].y, xv[j][0].z, xv[j][0].w,
+                               xv[j][1].x, xv[j][1].y, xv[j][1].z, xv[j][1].w};
+        uint32_t mj = 0;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) mj = max(mj, max(w[i] & 0x7FFF0000u, (w[i] << 16) & 0x7FFF0000u));
+        mx = j < nb ? max(mx, mj) : mx;  // clamped blocks repeat the last one
+      }
+      // largest |x| of row ln over the four lane groups
+      mx = max(mx, static_cast<uint32_t>(__shfl_xor(static_cast<int>(mx), 16, kWave)));
+      mx = max(mx, static_cast<uint32_t>(__shfl_xor(static_cast<int>(mx), 32, kWave)));
+      int k = 14 - (static_cast<int>(mx >> 23) - 127);
+      k = k < -126 ? -126 : (k > 126 ? 126 : k);
+      const float sc2 = __uint_as_float(static_cast<uint32_t>(127 + k) << 23);
+      const float xinv = __uint_as_float(static_cast<uint32_t>(127 - k) << 23);
+#pragma unroll
+      for (int j = 0; j < kMfmaSeg; ++j) {
+        const uint32_t w[8] = {xv[j][0].x, xv[j][0].y, xv[j][0].z, xv[j][0].w,
+                               xv[j][1].x, xv[j][1].y, xv[j][1].z, xv[j][1].w};
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const float lo = __uint_as_float(w[i] << 16) * sc2;  // exact: a power of two
+          const float hi = __uint_as_float(w[i] & 0xFFFF0000u) * sc2;
+          xh[j][i] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(lo, hi));
+        }
+      }
+      // D rows held by this lane are x rows 4 g + i
+#pragma unroll
+      for (int i = 0; i < 4; ++i) xinv_d[i] = __shfl(xinv, 4 * g + i, kWave);
+    }
+
+    // groups in order, the loads of group gi + 1 issued before group gi is
+    // multiplied (clamped to the last group, whose loads are then repeated)
+    auto load_group = [&](GroupItem<kDQ> (&it)[kMfmaSeg], int64_t gi) {
+      const int64_t gl = gi < kmine ? gi : (kmine > 0 ? kmine - 1 : 0);
+      const int64_t grp = blockIdx.x + gl * G;
+      const int64_t rowc = grp * 16 + ln < rows ? grp * 16 + ln : rows - 1;  // past the end: never stored
+#pragma unroll
+      for (int j = 0; j < kMfmaSeg; ++j) group_load<kDQ>(it[j], packed, nblk, rowc, b0 + (j < nb ? j : nb - 1), g, sc);
+    };
+    auto mult_group = [&](const GroupItem<kDQ> (&it)[kMfmaSeg], int64_t gi) {
+      floatx4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+      // two halves of four blocks: all lookups, then all MFMAs, then the
+      // scaling, so that the LDS and MFMA latencies overlap; blocks past the
+      // segment's end (clamped loads) get scale 0
+#pragma unroll
+      for (int h = 0; h < kMfmaSeg; h += 4) {
+        uint32_t bw[4][8];
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+          for (int u = 0; u < 8; ++u) {
+            // codes 16 g .. 16 g + 7 (bytes 8 g .. 8 g + 3) then 16 g + 8 .. + 15
+            const uint32_t word = u < 4 ? it[h + j].c.x : it[h + j].c.y;
+            const uint32_t addr = __builtin_amdgcn_perm(word, slot, 0x0C0C0000u | ((4u + (u & 3)) << 8));
+            bw[j][u] = *reinterpret_cast<const uint32_t*>(smem + addr);
+          }
+        floatx4 d[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const uint4 b0w = make_uint4(bw[j][0], bw[j][1], bw[j][2], bw[j][3]);
+          const uint4 b1w = make_uint4(bw[j][4], bw[j][5], bw[j][6], bw[j][7]);
+          const uint4 a0w = make_uint4(xh[h + j][0], xh[h + j][1], xh[h + j][2], xh[h + j][3]);
+          const uint4 a1w = make_uint4(xh[h + j][4], xh[h + j][5], xh[h + j][6], xh[h + j][7]);
+          const floatx4 zero = {0.0f, 0.0f, 0.0f, 0.0f};
+          d[j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8_t, a0w),
+                                                       __builtin_bit_cast(half8_t, b0w), zero, 0, 0, 0);
+          d[j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8_t, a1w),
+                                                       __builtin_bit_cast(half8_t, b1w), d[j], 0, 0, 0);
+        }
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          float a;
+          if constexpr (kDQ) a = (div127(it[h + j].q) * it[h + j].s2) + mean;  // a_hat of weight row ln
+          else a = it[h + j].am;
+          a = (h + j < nb) ? a : 0.0f;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) acc[i] = fmaf(d[j][i], a, acc[i]);
+        }
+      }
+      // partial tile of (group gi, segment): element (x row 4 g + i, weight row ln)
+      float* pt = part + (gi * pl.nseg + seg) * 256;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) pt[(4 * g + i) * 16 + ln] = acc[i] * xinv_d[i];
+    };
+    GroupItem<kDQ> ia[kMfmaSeg], ib[kMfmaSeg];
+    load_group(ia, 0);
+    for (int64_t gi = 0; gi < kmine; gi += 2) {
+      load_group(ib, gi + 1);
+      mult_group(ia, gi);
+      if (gi + 1 >= kmine) break;
+      load_group(ia, gi + 2);
+      mult_group(ib, gi + 1);
+    }
+  }
+  __syncthreads();
+  for (int64_t t = threadIdx.x; t < kmine * 256; t += blockDim.x) {
+    const int64_t gi = t >> 8;
+    const int xm = static_cast<int>((t >> 4) & 15);
+    const int wn = static_cast<int>(t & 15);
+    const int64_t row = (blockIdx.x + gi * G) * 16 + wn;
+    if (xm >= m || row >= rows) continue;
+    float s = 0.0f;
+    for (int sg = 0; sg < pl.nseg; ++sg) s += part[(gi * pl.nseg + sg) * 256 + xm * 16 + wn];
+    if constexpr (kBf16Out) static_cast<uint16_t*>(y)[xm * rows + row] = static_cast<uint16_t>(f32_to_bf16(s));
+    else static_cast<float*>(y)[xm * rows + row] = s;
+  }
+}
+
+// Plan: segments of at most kMfmaSeg blocks (balanced); grid of at least one
+// workgroup per CU, grown until each workgroup's (group, segment) tiles fit.
+MfmaPlan mfma_plan(int64_t rows, int64_t cols) {
+  const int64_t cus = device_cus();
+  const int64_t nblk = cols / 64;
+  MfmaPlan pl{};
+  pl.nseg = static_cast<int>((nblk + kMfmaSeg - 1) / kMfmaSeg);
+  pl.seg_blocks = static_cast<int>((nblk + pl.nseg - 1) / pl.nseg);
+  const int64_t ngroups = (rows + 15) / 16;
+  int64_t g = cus < ngroups ? cus : ngroups;
+  while (((ngroups + g - 1) / g) * pl.nseg > kPartTiles) ++g;
+  pl.grid = static_cast<int>(g);
+  pl.kmax = static_cast<int>((ngroups + g - 1) / g);
+  return pl;
+}
+
+template <bool kDQ>
+hipError_t launch_mfma(const uint8_t* packed, int64_t rows, int64_t cols, Scales sc, const uint16_t* x, int64_t m,
+                       void* y, int y_bf16, hipStream_t s) {
+  const MfmaPlan pl = mfma_plan(rows, cols);
+  if (pl.nseg > kPartTiles) return hipErrorInvalidValue;
+  const Codebook& cb = codebook();
+  const dim3 gd(static_cast<unsigned>(pl.grid)), bd(64 * kMfmaWaves);
+  const int mi = static_cast<int>(m);
+  if (y_bf16)
+    hipLaunchKernelGGL((k_gemv_mfma<kMfmaWaves, kDQ, true>), gd, bd, 0, s, packed, rows, cols, sc, x, mi, y, cb, pl);
+  else
+    hipLaunchKernelGGL((k_gemv_mfma<kMfmaWaves, kDQ, false>), gd, bd, 0, s, packed, rows, cols, sc, x, mi, y, cb, pl);
+  return hipGetLastError();
+}
+
 // Skinny products (m > 1): passes of up to 4 rows of x over W, 8 waves.
 template <bool kDQ>
 hipError_t launch_rows_multi(const uint8_t* packed, int64_t rows, int64_t cols, Scales sc, const uint16_t* x,
@@ -623,7 +857,12 @@ hipError_t launch_gemv(const uint8_t* packed, int64_t rows, int64_t cols, Scales
       else launch_m1<2, true>(packed, rows, cols, sc, x, y, y_bf16, 16, s);
     }
   } else {
-    // skinny products: passes of up to 4 rows of x (8 waves, so nseg <= 8)
+    // skinny products on the matrix cores; wider rows in passes of up to 4
+    // rows of x on the vector ALUs (8 waves, so nseg <= 8)
+    if (mfma_plan(rows, cols).nseg <= kPartTiles) {
+      return sc.absmax ? launch_mfma<false>(packed, rows, cols, sc, x, m, y, y_bf16, s)
+                       : launch_mfma<true>(packed, rows, cols, sc, x, m, y, y_bf16, s);
+    }
     if ((cols / 64 + 63) / 64 <= 8) {
       return sc.absmax ? launch_rows_multi<false>(packed, rows, cols, sc, x, m, y, y_bf16, s)
                        : launch_rows_multi<true>(packed, rows, cols, sc, x, m, y, y_bf16, s);
