@@ -7,12 +7,13 @@
 // 0 <= p <= 253), added into 32-bit digits of a wide fixed-point integer held
 // in 64-bit accumulators (no carries until the end).  Each summing workgroup
 // writes its digit sums to its own workspace row (no atomics: device-wide
-// atomics on one address serialize in memory); a one-workgroup kernel adds the
-// rows, propagates the carries, rounds the integer once to float64, divides
-// by the count in float64 and rounds to float32.
+// atomics on one address serialize in memory).  Every workgroup of the
+// quantizing kernel then adds the rows itself, propagates the carries, rounds
+// the integer once to float64, divides by the count in float64 and rounds to
+// float32 -- the same value in every workgroup, so no third launch is needed.
 //
-// Kernels: k_dq_partial (digit sums per workgroup), k_dq_mean (one
-// workgroup), k_dq_quant (one wave per group of 256 scales).
+// Kernels: k_dq_partial (digit sums per workgroup), k_dq_quant (the mean,
+// then one wave per group of 256 scales).
 #include "nf4_device.h"
 
 namespace nf4i {
@@ -62,110 +63,145 @@ __device__ double digits_to_double(const uint32_t (&dig)[kDqDigits]) {
   return ldexp(static_cast<double>(mant), exp2);
 }
 
-__device__ __forceinline__ unsigned long long wave_sum_u64(unsigned long long v) {
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) {
-    const uint32_t lo = __shfl_xor(static_cast<uint32_t>(v), off, kWave);
-    const uint32_t hi = __shfl_xor(static_cast<uint32_t>(v >> 32), off, kWave);
-    v += (static_cast<unsigned long long>(hi) << 32) | lo;
+// Adds the 256 threads' digit vectors held in vec (thread t sums digit
+// t % 12 over rows t / 12, t / 12 + 21, ..., then 12 threads finish) and
+// returns the total of digit t in threads t < 12.  Contains two barriers.
+__device__ __forceinline__ unsigned long long block_digit_sum(unsigned long long (*vec)[kDqDigits + 1],
+                                                              unsigned long long (*tot)[kDqDigits]) {
+  constexpr int kChunks = 256 / kDqDigits;  // 21
+  const int t = threadIdx.x;
+  if (t < kChunks * kDqDigits) {
+    const int k = t % kDqDigits, c = t / kDqDigits;
+    unsigned long long sum = 0ull;
+    for (int r = c; r < 256; r += kChunks) sum += vec[r][k];
+    tot[c][k] = sum;
   }
-  return v;
+  __syncthreads();
+  unsigned long long sum = 0ull;
+  if (t < kDqDigits)
+    for (int c = 0; c < kChunks; ++c) sum += tot[c][t];
+  __syncthreads();
+  return sum;
 }
+
+// Digit sums of the workgroup's scales: each thread adds kPerThread scales
+// (all loads issued first) into registers, then the 256 threads' digit
+// vectors are added through LDS into the workgroup's row.
+constexpr int kPerThread = 4;
 
 __global__ __launch_bounds__(256) void k_dq_partial(const float* __restrict__ absmax, int64_t nb,
                                                     unsigned long long* __restrict__ ws) {
-  __shared__ unsigned long long acc_lds[4][kDqDigits];
-  // Each thread keeps the digits in registers: a contribution lands in digit
-  // d (low 32 bits) and d + 1 (high bits); selects keep the indexing static.
+  constexpr int kChunks = 256 / kDqDigits;  // 21
+  __shared__ unsigned long long vec[256][kDqDigits + 1];  // +1: spreads the banks
+  __shared__ unsigned long long tot[kChunks][kDqDigits];
+  const int t = threadIdx.x;
   unsigned long long acc[kDqDigits];
 #pragma unroll
   for (int k = 0; k < kDqDigits; ++k) acc[k] = 0ull;
-  // 8 loads in flight per thread before any of them is used
-  constexpr int kUnroll = 8;
   const int64_t stride = static_cast<int64_t>(gridDim.x) * blockDim.x;
-  for (int64_t i0 = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; i0 < nb; i0 += kUnroll * stride) {
-    float v[kUnroll];
+  for (int64_t i0 = static_cast<int64_t>(blockIdx.x) * blockDim.x + t; i0 < nb; i0 += kPerThread * stride) {
+    float v[kPerThread];
 #pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
+    for (int u = 0; u < kPerThread; ++u) {
       const int64_t i = i0 + u * stride;
       v[u] = (i < nb) ? absmax[i] : 0.0f;
     }
 #pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
+    for (int u = 0; u < kPerThread; ++u) {
       int d;
       uint32_t lo, hi;
       scale_to_digits(v[u], &d, &lo, &hi);
+      // a contribution lands in digit d (low 32 bits) and d + 1 (high bits);
+      // selects keep the indexing static
 #pragma unroll
       for (int k = 0; k < kDqDigits; ++k)
         acc[k] += static_cast<unsigned long long>((k == d ? lo : 0u)) + static_cast<unsigned long long>((k == d + 1 ? hi : 0u));
     }
   }
-  const int wave = threadIdx.x >> 6;
 #pragma unroll
-  for (int k = 0; k < kDqDigits; ++k) {
-    const unsigned long long v = wave_sum_u64(acc[k]);
-    if ((threadIdx.x & 63) == 0) acc_lds[wave][k] = v;
-  }
+  for (int k = 0; k < kDqDigits; ++k) vec[t][k] = acc[k];
   __syncthreads();
-  if (threadIdx.x < kDqDigits) {
-    const int k = threadIdx.x;
-    ws[blockIdx.x * kDqDigits + k] = acc_lds[0][k] + acc_lds[1][k] + acc_lds[2][k] + acc_lds[3][k];
-  }
+  const unsigned long long sum = block_digit_sum(vec, tot);
+  if (t < kDqDigits) ws[blockIdx.x * kDqDigits + t] = sum;
 }
 
-// One workgroup of 256 threads: the partial rows (at most 256 x 12 values)
-// are loaded in parallel and added per digit in LDS; thread 0 propagates the
-// carries and rounds.
-__global__ __launch_bounds__(256) void k_dq_mean(const unsigned long long* __restrict__ ws, int nparts, int64_t nb,
-                                                 float* __restrict__ mean_out) {
-  __shared__ unsigned long long tot[kDqDigits];
-  if (threadIdx.x < kDqDigits) tot[threadIdx.x] = 0ull;
+// The mean from the partial rows (at most 256), in a workgroup of 256
+// threads: thread t loads row t, the rows are added per digit, and thread 0
+// propagates the carries, rounds and divides.  Returns the mean in every
+// thread.
+__device__ float dq_mean(const unsigned long long* __restrict__ ws, int nparts, int64_t nb) {
+  constexpr int kChunks = 256 / kDqDigits;
+  __shared__ unsigned long long vec[256][kDqDigits + 1];
+  __shared__ unsigned long long tot[kChunks][kDqDigits];
+  __shared__ unsigned long long dsum[kDqDigits];
+  __shared__ float mean_s;
+  const int t = threadIdx.x;
+  {
+    unsigned long long row[kDqDigits];
+    if (t < nparts) {
+      const ulonglong2* p = reinterpret_cast<const ulonglong2*>(ws + t * kDqDigits);
+#pragma unroll
+      for (int k = 0; k < kDqDigits / 2; ++k) {
+        const ulonglong2 v = p[k];
+        row[2 * k] = v.x;
+        row[2 * k + 1] = v.y;
+      }
+    } else {
+#pragma unroll
+      for (int k = 0; k < kDqDigits; ++k) row[k] = 0ull;
+    }
+#pragma unroll
+    for (int k = 0; k < kDqDigits; ++k) vec[t][k] = row[k];
+  }
   __syncthreads();
-  constexpr int kPer = (kDqMaxGroups * kDqDigits + 255) / 256;
-  unsigned long long v[kPer];
-  const int nvals = nparts * kDqDigits;
+  const unsigned long long s = block_digit_sum(vec, tot);
+  if (t < kDqDigits) dsum[t] = s;
+  __syncthreads();
+  if (t == 0) {
+    uint32_t dig[kDqDigits];
+    unsigned long long carry = 0;
 #pragma unroll
-  for (int u = 0; u < kPer; ++u) {
-    const int i = threadIdx.x + 256 * u;
-    v[u] = i < nvals ? ws[i] : 0ull;
-  }
-#pragma unroll
-  for (int u = 0; u < kPer; ++u) {
-    const int i = threadIdx.x + 256 * u;
-    if (i < nvals && v[u]) atomicAdd(&tot[i % kDqDigits], v[u]);
+    for (int k = 0; k < kDqDigits; ++k) {
+      const unsigned long long v = dsum[k] + carry;
+      dig[k] = static_cast<uint32_t>(v);
+      carry = v >> 32;
+    }
+    const double total = digits_to_double(dig);
+    mean_s = static_cast<float>(total / static_cast<double>(nb));
   }
   __syncthreads();
-  if (threadIdx.x != 0) return;
-  uint32_t dig[kDqDigits];
-  unsigned long long carry = 0;
-#pragma unroll
-  for (int k = 0; k < kDqDigits; ++k) {
-    const unsigned long long t = tot[k] + carry;
-    dig[k] = static_cast<uint32_t>(t);
-    carry = t >> 32;
-  }
-  const double total = digits_to_double(dig);
-  *mean_out = static_cast<float>(total / static_cast<double>(nb));
+  return mean_s;
 }
 
 __global__ __launch_bounds__(256) void k_dq_quant(const float* __restrict__ absmax, int64_t nb,
-                                                  const float* __restrict__ mean_p,
-                                                  int8_t* __restrict__ q, float* __restrict__ absmax2) {
+                                                  const unsigned long long* __restrict__ ws, int nparts,
+                                                  float* __restrict__ mean_out, int8_t* __restrict__ q,
+                                                  float* __restrict__ absmax2) {
   const int lane = threadIdx.x & 63;
   const int64_t ngroups = (nb + 255) >> 8;
   const int64_t wave = (static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x) >> 6;
   const int64_t nwaves = (static_cast<int64_t>(gridDim.x) * blockDim.x) >> 6;
-  const float mu = *mean_p;
-  for (int64_t g = wave; g < ngroups; g += nwaves) {
+  // the scales of the wave's first group are loaded before the mean is known
+  auto load4 = [&](int64_t g, float (&a)[4]) {
     const int64_t i0 = g * 256 + lane * 4;
-    float c[4];
     if (i0 + 4 <= nb) {
-      const float4 a = *reinterpret_cast<const float4*>(absmax + i0);
-      c[0] = a.x - mu; c[1] = a.y - mu; c[2] = a.z - mu; c[3] = a.w - mu;
+      const float4 v = *reinterpret_cast<const float4*>(absmax + i0);
+      a[0] = v.x; a[1] = v.y; a[2] = v.z; a[3] = v.w;
     } else {
 #pragma unroll
-      for (int j = 0; j < 4; ++j) c[j] = (i0 + j < nb) ? absmax[i0 + j] - mu : 0.0f;
+      for (int j = 0; j < 4; ++j) a[j] = (i0 + j < nb) ? absmax[i0 + j] : 0.0f;
     }
+  };
+  float a[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+  if (wave < ngroups) load4(wave, a);
+  const float mu = dq_mean(ws, nparts, nb);
+  if (blockIdx.x == 0 && threadIdx.x == 0) *mean_out = mu;
+  for (int64_t g = wave; g < ngroups; g += nwaves) {
+    if (g != wave) load4(g, a);
+    const int64_t i0 = g * 256 + lane * 4;
+    float c[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) c[j] = (i0 + j < nb) ? a[j] - mu : 0.0f;
     float s = fmaxf(fmaxf(fabsf(c[0]), fabsf(c[1])), fmaxf(fabsf(c[2]), fabsf(c[3])));
     s = group_max<64>(s);
     uint32_t word = 0;
@@ -195,14 +231,13 @@ __global__ __launch_bounds__(256) void k_dq_quant(const float* __restrict__ absm
 
 hipError_t launch_double_quant(const float* absmax, int64_t nb, int8_t* q, float* absmax2,
                                float* mean, unsigned long long* ws, hipStream_t s) {
-  int64_t want = (nb + 2047) / 2048;  // 8 scales per thread
+  int64_t want = (nb + 256 * kPerThread - 1) / (256 * kPerThread);
   int grid = static_cast<int>(want < kDqMaxGroups ? want : kDqMaxGroups);
   hipLaunchKernelGGL(k_dq_partial, dim3(grid), dim3(256), 0, s, absmax, nb, ws);
-  hipLaunchKernelGGL(k_dq_mean, dim3(1), dim3(256), 0, s, ws, grid, nb, mean);
   const int64_t groups = (nb + 255) >> 8;
   want = (groups + 3) / 4;  // 4 waves per workgroup
-  grid = static_cast<int>(want < 8192 ? want : 8192);
-  hipLaunchKernelGGL(k_dq_quant, dim3(grid), dim3(256), 0, s, absmax, nb, mean, q, absmax2);
+  const int qgrid = static_cast<int>(want < 1024 ? want : 1024);
+  hipLaunchKernelGGL(k_dq_quant, dim3(qgrid), dim3(256), 0, s, absmax, nb, ws, grid, mean, q, absmax2);
   return hipGetLastError();
 }
 
