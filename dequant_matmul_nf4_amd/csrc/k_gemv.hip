@@ -292,21 +292,25 @@ __global__ __launch_bounds__(1024) void k_gemv_m1(const uint8_t* __restrict__ pa
 //
 // Decode GEMV with the load schedule of a streaming copy.  A workgroup owns a
 // contiguous range of rows; its waves split the columns into segments of up
-// to 64 blocks (one 64-block per lane) and the rows into equal parts, so each
+// to 64 blocks (2 KiB of codes per row) and the rows into equal parts, so each
 // wave walks a run of rows over one fixed column segment:
-//  - the lane's 64 values of x stay in registers for the whole run, as fp16
-//    pairs scaled by a power of two chosen from their largest magnitude (so
-//    the scaling is exact and nothing overflows; it is undone on the partial
-//    sum);
+//  - a row's segment is read with two fully coalesced 1 KiB loads: lane l
+//    takes the 16 bytes at offsets 16 l and 1024 + 16 l, i.e. half l & 1 of
+//    blocks l / 2 and 32 + l / 2 (two pieces of 32 codes, each with its own
+//    block scale);
+//  - the lane's 2 x 32 values of x stay in registers for the whole run, as
+//    fp16 pairs, each piece scaled by a power of two chosen from its largest
+//    magnitude (so the scaling is exact and nothing overflows; it is undone on
+//    the piece's partial sum);
 //  - a byte of packed codes (two elements) indexes a 256-entry table of fp16
 //    level pairs in LDS, one copy per lane (address = byte * 256 + lane * 4,
 //    a single byte permute, every lane in its own bank), and one
 //    v_dot2c_f32_f16 takes both products; fp16 keeps 11 significant bits of
 //    each level;
-//  - a ring of U rows of loads (32 bytes of codes and the block's scale
-//    inputs per lane and row) stays in flight: slot u is consumed and at once
+//  - a ring of U rows of loads stays in flight: slot u is consumed and at once
 //    refilled with the row U places ahead, indices clamped so that no branch
-//    separates the loads from their use;
+//    separates the loads from their use; the first U rows are requested before
+//    the table is built;
 //  - each row's per-lane partial sum is reduced across the wave with DPP
 //    (total in lane 63) and parked in LDS per (row, segment); at the end the
 //    segments of each row are added in a fixed order, so the result does not
@@ -334,97 +338,107 @@ __device__ __forceinline__ float wave_sum_to_last(float v) {
 }
 
 // 256 fp16 level pairs (element 2j = high nibble in the low half), one copy
-// per lane slot; built in two phases so that each wave writes consecutive
-// addresses.  Ends with a barrier.
-__device__ __forceinline__ void fill_half_table(uint32_t* tab, uint32_t* base, const Codebook& cb) {
-  if (threadIdx.x < 256) {
-    const int e = threadIdx.x;
-    float l0 = cb.level[0], l1 = cb.level[0];
+// per lane slot: entry e occupies 64 consecutive words.  Each thread builds the
+// pair of entry threadIdx % 256 in registers and writes its share of the 64
+// copies with 16-byte stores, starting at a chunk rotated by the entry so that
+// 16 consecutive lanes cover every bank.  Ends with a barrier.
+template <int kThreads>
+__device__ __forceinline__ void fill_half_table(uint32_t* tab, const Codebook& cb) {
+  static_assert(kThreads % 256 == 0 && kThreads <= 1024, "whole entries per pass");
+  constexpr int kParts = kThreads / 256;
+  const int e = threadIdx.x & 255;
+  const int p = threadIdx.x >> 8;
+  float l0 = cb.level[0], l1 = cb.level[0];
 #pragma unroll
-    for (int i = 1; i < 16; ++i) {
-      l0 = ((e >> 4) == i) ? cb.level[i] : l0;
-      l1 = ((e & 15) == i) ? cb.level[i] : l1;
-    }
-    const half2_t h = {static_cast<_Float16>(l0), static_cast<_Float16>(l1)};  // round to nearest even
-    base[e] = __builtin_bit_cast(uint32_t, h);
+  for (int i = 1; i < 16; ++i) {
+    l0 = ((e >> 4) == i) ? cb.level[i] : l0;
+    l1 = ((e & 15) == i) ? cb.level[i] : l1;
   }
-  __syncthreads();
-  for (int i = threadIdx.x; i < 256 * 64; i += blockDim.x) tab[i] = base[i >> 6];
+  const half2_t h = {static_cast<_Float16>(l0), static_cast<_Float16>(l1)};  // round to nearest even
+  const uint32_t v = __builtin_bit_cast(uint32_t, h);
+  const uint4 v4 = {v, v, v, v};
+#pragma unroll
+  for (int j = 0; j < 16 / kParts; ++j) {
+    const int c = (j * kParts + p + e) & 15;
+    *reinterpret_cast<uint4*>(tab + e * 64 + 4 * c) = v4;
+  }
   __syncthreads();
 }
 
 struct RowItem {
-  uint4 w[2];  // 32 bytes of packed codes: the lane's 64-block of one row
-  float am;    // absmax (plain scales)
-  int q;       // int8 scale code (double quant)
-  float s2;    // second-level scale (double quant)
+  uint4 w[2];    // piece j: 16 bytes of codes at segment offset 1024 j + 16 lane
+  float am[2];   // absmax of each piece's block (plain scales)
+  int q[2];      // int8 scale codes (double quant)
+  float s2[2];   // second-level scales
 };
 
-// Loads of one row.  row_blk0 = row * nblk (wave-uniform); the lane adds its
-// block bc, so the code and scale addresses are a uniform base plus a fixed
-// per-lane offset.
+// Loads of one row.  row_blk0 = row * nblk (wave-uniform); blk[j] is the
+// lane's block of piece j (already clamped into the matrix), half = lane & 1.
 template <bool kDQ>
-__device__ __forceinline__ void row_load(RowItem& it, const uint8_t* __restrict__ packed, int64_t row_blk0, int bc,
-                                         Scales sc) {
-  const uint4* p = reinterpret_cast<const uint4*>(packed + row_blk0 * 32) + 2 * bc;
-  it.w[0] = p[0];
-  it.w[1] = p[1];
-  if constexpr (kDQ) {
-    it.q = sc.q[row_blk0 + bc];
-    // group of the block: uniform part plus a small per-lane carry
-    it.s2 = sc.absmax2[(row_blk0 >> 8) + ((static_cast<int>(row_blk0 & 255) + bc) >> 8)];
-  } else {
-    it.am = sc.absmax[row_blk0 + bc];
+__device__ __forceinline__ void row_load(RowItem& it, const uint8_t* packed, int64_t row_blk0, const int (&blk)[2],
+                                         int half, Scales sc) {
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int64_t b = row_blk0 + blk[j];
+    it.w[j] = *reinterpret_cast<const uint4*>(packed + b * 32 + 16 * half);
+    if constexpr (kDQ) {
+      it.q[j] = sc.q[b];
+      it.s2[j] = sc.absmax2[b >> 8];
+    } else {
+      it.am[j] = sc.absmax[b];
+    }
   }
 }
 
 // Products of one row item with MC rows of x (the lookups are shared):
-// out[c] = a_hat * xinv[c] * sum_k level[code_k] * xh[c][k].
+// out[c] = sum_j on[j] ? a_hat_j * xinv[c][j] * sum_k level[code_k] * xh[c][j][k] : 0.
 template <int MC, bool kDQ>
-__device__ __forceinline__ void row_dot(const RowItem& it, const uint32_t (&xh)[MC][32], const char* tab,
-                                        uint32_t slot, float mean, const float (&xinv)[MC], float (&out)[MC]) {
-  const uint32_t q[8] = {it.w[0].x, it.w[0].y, it.w[0].z, it.w[0].w, it.w[1].x, it.w[1].y, it.w[1].z, it.w[1].w};
-  float s0[MC], s1[MC];
+__device__ __forceinline__ void row_dot(const RowItem& it, const uint32_t (&xh)[MC][2][16], const char* tab,
+                                        uint32_t slot, float mean, const float (&xinv)[MC][2], const bool (&on)[2],
+                                        float (&out)[MC]) {
 #pragma unroll
-  for (int c = 0; c < MC; ++c) s0[c] = s1[c] = 0.0f;
+  for (int c = 0; c < MC; ++c) out[c] = 0.0f;
 #pragma unroll
-  for (int j = 0; j < 8; j += 2) {
-    uint32_t e[8];
+  for (int j = 0; j < 2; ++j) {
+    const uint32_t q[4] = {it.w[j].x, it.w[j].y, it.w[j].z, it.w[j].w};
+    uint32_t e[16];
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      const uint32_t addr = __builtin_amdgcn_perm(q[j + (u >> 2)], slot, 0x0C0C0000u | ((4u + (u & 3)) << 8));
+    for (int u = 0; u < 16; ++u) {
+      const uint32_t addr = __builtin_amdgcn_perm(q[u >> 2], slot, 0x0C0C0000u | ((4u + (u & 3)) << 8));
       e[u] = *reinterpret_cast<const uint32_t*>(tab + addr);
     }
+    float a;
+    if constexpr (kDQ) a = (div127(it.q[j]) * it.s2[j]) + mean;  // a_hat
+    else a = it.am[j];
 #pragma unroll
-    for (int u = 0; u < 8; u += 2)
+    for (int c = 0; c < MC; ++c) {
+      float s0 = 0.0f, s1 = 0.0f;
 #pragma unroll
-      for (int c = 0; c < MC; ++c) {
-        s0[c] = dot2h(e[u], xh[c][4 * j + u], s0[c]);
-        s1[c] = dot2h(e[u + 1], xh[c][4 * j + u + 1], s1[c]);
+      for (int u = 0; u < 16; u += 2) {
+        s0 = dot2h(e[u], xh[c][j][u], s0);
+        s1 = dot2h(e[u + 1], xh[c][j][u + 1], s1);
       }
+      const float v = (s0 + s1) * (a * xinv[c][j]);
+      out[c] += on[j] ? v : 0.0f;
+    }
   }
-  float a;
-  if constexpr (kDQ) a = (div127(it.q) * it.s2) + mean;  // a_hat
-  else a = it.am;
-#pragma unroll
-  for (int c = 0; c < MC; ++c) out[c] = (s0[c] + s1[c]) * (a * xinv[c]);
 }
 
-// One row of x, the lane's 64-block: fp16 pairs scaled by 2^k, k chosen so
-// that the largest |x| of the block lies in [2^14, 2^15); xinv = 2^-k.
-__device__ __forceinline__ void x_block_to_half(const uint4 (&xv)[8], uint32_t (&xh)[32], float& xinv) {
-  uint32_t xw[32];
+// 32 values of x (16 bf16 pairs) to fp16 pairs scaled by 2^k, k chosen so
+// that the largest |x| lies in [2^14, 2^15); xinv = 2^-k.
+__device__ __forceinline__ void x_piece_to_half(const uint4 (&xv)[4], uint32_t (&xh)[16], float& xinv) {
+  uint32_t xw[16];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) { xw[4 * i] = xv[i].x; xw[4 * i + 1] = xv[i].y; xw[4 * i + 2] = xv[i].z; xw[4 * i + 3] = xv[i].w; }
+  for (int i = 0; i < 4; ++i) { xw[4 * i] = xv[i].x; xw[4 * i + 1] = xv[i].y; xw[4 * i + 2] = xv[i].z; xw[4 * i + 3] = xv[i].w; }
   uint32_t mx = 0;
 #pragma unroll
-  for (int i = 0; i < 32; ++i) mx = max(mx, max(xw[i] & 0x7FFF0000u, (xw[i] << 16) & 0x7FFF0000u));
+  for (int i = 0; i < 16; ++i) mx = max(mx, max(xw[i] & 0x7FFF0000u, (xw[i] << 16) & 0x7FFF0000u));
   int k = 14 - (static_cast<int>(mx >> 23) - 127);
   k = k < -126 ? -126 : (k > 126 ? 126 : k);
   const float sc2 = __uint_as_float(static_cast<uint32_t>(127 + k) << 23);
   xinv = __uint_as_float(static_cast<uint32_t>(127 - k) << 23);
 #pragma unroll
-  for (int i = 0; i < 32; ++i) {
+  for (int i = 0; i < 16; ++i) {
     const float lo = __uint_as_float(xw[i] << 16) * sc2;         // exact: a power of two
     const float hi = __uint_as_float(xw[i] & 0xFFFF0000u) * sc2;
     xh[i] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(lo, hi));
@@ -441,12 +455,11 @@ struct RowsPlan {
 // MC rows of x per launch (x and y point at the first of them; the x rows
 // are cols apart, the y rows `rows` apart).
 template <int U, int kWaves, int MC, bool kDQ, bool kBf16Out>
-__global__ __launch_bounds__(kWaves * 64) void k_gemv_rows(const uint8_t* __restrict__ packed, int64_t rows,
-                                                           int64_t cols, Scales sc, const uint16_t* __restrict__ x,
+__global__ __launch_bounds__(kWaves * 64) void k_gemv_rows(const uint8_t* packed, int64_t rows,
+                                                           int64_t cols, Scales sc, const uint16_t* x,
                                                            void* __restrict__ y, Codebook cb, RowsPlan pl) {
   constexpr int kRowsWg = kRowsMaxWg / MC;
   __shared__ uint32_t tab[256 * 64];
-  __shared__ uint32_t tab_base[256];
   __shared__ float part[kRowsWg * kSegMax * MC];
   const char* smem = reinterpret_cast<const char*>(tab);
   const int lane = threadIdx.x & 63;
@@ -462,32 +475,45 @@ __global__ __launch_bounds__(kWaves * 64) void k_gemv_rows(const uint8_t* __rest
   const int prt = wave / pl.nseg;
   const int64_t gp = static_cast<int64_t>(blockIdx.x) * pl.wpr + prt;
   const int64_t n = (prt < pl.wpr && gp < rows) ? (rows - gp + np - 1) / np : 0;
-  const int b = seg * pl.seg_blocks + lane;
-  const bool lane_on = lane < pl.seg_blocks && b < nblk;
-  const int bc = lane_on ? b : static_cast<int>(nblk - 1);
+  // piece j of the lane: half `half` of block 32 j + lane / 2 of the segment
+  const int half = lane & 1;
+  const int seg_end = static_cast<int>(nblk - seg * pl.seg_blocks < pl.seg_blocks ? nblk - seg * pl.seg_blocks
+                                                                                   : pl.seg_blocks);
+  bool on[2];
+  int blk[2];
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int bj = 32 * j + (lane >> 1);
+    on[j] = bj < seg_end;
+    blk[j] = seg * pl.seg_blocks + (on[j] ? bj : seg_end - 1);
+  }
   const int64_t row0 = gp < rows ? gp : rows - 1;
   const int64_t last = n > 0 ? row0 + (n - 1) * np : row0;  // loads are clamped to it
 
-  // x of the lane's block (MC rows), then the first U rows, then the table
-  uint4 xv[MC][8];
-#pragma unroll
-  for (int c = 0; c < MC; ++c) {
-    const uint4* xp = reinterpret_cast<const uint4*>(x + c * cols) + 8 * static_cast<int64_t>(bc);
-#pragma unroll
-    for (int i = 0; i < 8; ++i) xv[c][i] = xp[i];
-  }
+  // the first U rows, x of the lane's pieces (MC rows), then the table
   RowItem it[U];
 #pragma unroll
   for (int u = 0; u < U; ++u) {
     const int64_t r = row0 + u * np;
-    row_load<kDQ>(it[u], packed, (r < last ? r : last) * nblk, bc, sc);
+    row_load<kDQ>(it[u], packed, (r < last ? r : last) * nblk, blk, half, sc);
   }
-  fill_half_table(tab, tab_base, cb);  // ends with a barrier
-
-  uint32_t xh[MC][32];
-  float xinv[MC];
+  uint4 xv[MC][2][4];
 #pragma unroll
-  for (int c = 0; c < MC; ++c) x_block_to_half(xv[c], xh[c], xinv[c]);
+  for (int c = 0; c < MC; ++c)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const uint4* xp = reinterpret_cast<const uint4*>(x + c * cols + static_cast<int64_t>(blk[j]) * 64 + 32 * half);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) xv[c][j][i] = xp[i];
+    }
+  fill_half_table<kWaves * 64>(tab, cb);  // ends with a barrier
+
+  uint32_t xh[MC][2][16];
+  float xinv[MC][2];
+#pragma unroll
+  for (int c = 0; c < MC; ++c)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) x_piece_to_half(xv[c][j], xh[c][j], xinv[c][j]);
   const float mean = kDQ ? *sc.mean : 0.0f;
 
   for (int64_t i0 = 0; i0 < n; i0 += U) {
@@ -496,15 +522,15 @@ __global__ __launch_bounds__(kWaves * 64) void k_gemv_rows(const uint8_t* __rest
       const int64_t i = i0 + u;
       if (i < n) {  // wave-uniform
         float v[MC];
-        row_dot<MC, kDQ>(it[u], xh, smem, slot, mean, xinv, v);
+        row_dot<MC, kDQ>(it[u], xh, smem, slot, mean, xinv, on, v);
 #pragma unroll
         for (int c = 0; c < MC; ++c) {
-          const float t = wave_sum_to_last(lane_on ? v[c] : 0.0f);
+          const float t = wave_sum_to_last(v[c]);
           if (lane == 63) part[((prt * kmax + i) * kSegMax + seg) * MC + c] = t;
         }
       }
       const int64_t r = row0 + (i + U) * np;
-      row_load<kDQ>(it[u], packed, (r < last ? r : last) * nblk, bc, sc);
+      row_load<kDQ>(it[u], packed, (r < last ? r : last) * nblk, blk, half, sc);
     }
   }
   __syncthreads();
@@ -612,7 +638,6 @@ __global__ __launch_bounds__(kWaves * 64) void k_gemv_mfma(const uint8_t* __rest
                                                            int64_t cols, Scales sc, const uint16_t* __restrict__ x,
                                                            int m, void* __restrict__ y, Codebook cb, MfmaPlan pl) {
   __shared__ uint32_t tab[256 * 64];
-  __shared__ uint32_t tab_base[256];
   __shared__ float part[kPartTiles * 256];
   const char* smem = reinterpret_cast<const char*>(tab);
   const int lane = threadIdx.x & 63;
@@ -625,7 +650,7 @@ __global__ __launch_bounds__(kWaves * 64) void k_gemv_mfma(const uint8_t* __rest
   const int64_t G = gridDim.x;
   const int64_t kmine = (static_cast<int64_t>(blockIdx.x) < ngroups) ? (ngroups - blockIdx.x + G - 1) / G : 0;
   const float mean = kDQ ? *sc.mean : 0.0f;
-  fill_half_table(tab, tab_base, cb);  // ends with a barrier
+  fill_half_table<kWaves * 64>(tab, cb);  // ends with a barrier
 
   for (int seg = wave; seg < pl.nseg; seg += kWaves) {
     const int64_t b0 = static_cast<int64_t>(seg) * pl.seg_blocks;
