@@ -612,28 +612,57 @@ struct MfmaPlan {
   int kmax;          // row groups per workgroup, at most
 };
 
+// The loads of one (row group, segment): for weight row n = lane % 16, the 8
+// code bytes 8 g .. 8 g + 7 of each of the segment's blocks and the blocks'
+// scale inputs.  kQ4: the segment is 4 blocks starting at a multiple of 4 in
+// the flattened block order, so the 4 int8 codes (or 4 absmax) are one
+// aligned load and the group scales are the two that can occur.
 template <bool kDQ>
-struct GroupItem {
-  uint2 c;     // 8 bytes of codes: weight row n = lane % 16, bytes 8 g .. 8 g + 7 of the block
-  float am;
-  int q;
-  float s2;
+struct SegItem {
+  uint2 c[kMfmaSeg];
+  float am[kMfmaSeg];
+  int q[kMfmaSeg];
+  float s2lo, s2hi;
+  int cross;   // blocks j >= cross of the segment use s2hi
 };
 
-template <bool kDQ>
-__device__ __forceinline__ void group_load(GroupItem<kDQ>& it, const uint8_t* __restrict__ packed, int64_t nblk,
-                                           int64_t row, int64_t blk, int g, Scales sc) {
-  const int64_t b = row * nblk + blk;
-  it.c = *reinterpret_cast<const uint2*>(packed + b * 32 + 8 * g);
-  if constexpr (kDQ) {
-    it.q = sc.q[b];
-    it.s2 = sc.absmax2[b >> 8];
+template <bool kDQ, bool kQ4>
+__device__ __forceinline__ void seg_load(SegItem<kDQ>& it, const uint8_t* __restrict__ packed, int64_t nblk,
+                                         int64_t row, int64_t b0, int nb, int g, Scales sc, int64_t ngroups2) {
+  const int64_t rb = row * nblk + b0;
+#pragma unroll
+  for (int j = 0; j < kMfmaSeg; ++j) {
+    const int64_t b = rb + (j < nb ? j : nb - 1);
+    it.c[j] = *reinterpret_cast<const uint2*>(packed + b * 32 + 8 * g);
+  }
+  if constexpr (kQ4) {
+    if constexpr (kDQ) {
+      const uint32_t q4 = *reinterpret_cast<const uint32_t*>(sc.q + rb);
+#pragma unroll
+      for (int j = 0; j < kMfmaSeg; ++j) it.q[j] = static_cast<int>(static_cast<int8_t>(q4 >> (8 * j)));
+      const int64_t g0 = rb >> 8;
+      it.s2lo = sc.absmax2[g0];
+      it.s2hi = sc.absmax2[g0 + 1 < ngroups2 ? g0 + 1 : g0];
+      it.cross = 256 - static_cast<int>(rb & 255);
+    } else {
+      const float4 a4 = *reinterpret_cast<const float4*>(sc.absmax + rb);
+      it.am[0] = a4.x; it.am[1] = a4.y; it.am[2] = a4.z; it.am[3] = a4.w;
+    }
   } else {
-    it.am = sc.absmax[b];
+#pragma unroll
+    for (int j = 0; j < kMfmaSeg; ++j) {
+      const int64_t b = rb + (j < nb ? j : nb - 1);
+      if constexpr (kDQ) {
+        it.q[j] = sc.q[b];
+        it.am[j] = sc.absmax2[b >> 8];  // the block's group scale
+      } else {
+        it.am[j] = sc.absmax[b];
+      }
+    }
   }
 }
 
-template <int kWaves, bool kDQ, bool kBf16Out>
+template <int kWaves, bool kDQ, bool kQ4, bool kBf16Out>
 __global__ __launch_bounds__(kWaves * 64) void k_gemv_mfma(const uint8_t* __restrict__ packed, int64_t rows,
                                                            int64_t cols, Scales sc, const uint16_t* __restrict__ x,
                                                            int m, void* __restrict__ y, Codebook cb, MfmaPlan pl) {
@@ -649,6 +678,7 @@ __global__ __launch_bounds__(kWaves * 64) void k_gemv_mfma(const uint8_t* __rest
   const int64_t ngroups = (rows + 15) / 16;
   const int64_t G = gridDim.x;
   const int64_t kmine = (static_cast<int64_t>(blockIdx.x) < ngroups) ? (ngroups - blockIdx.x + G - 1) / G : 0;
+  const int64_t ngroups2 = (rows * nblk + 255) / 256;  // second-level scales
   const float mean = kDQ ? *sc.mean : 0.0f;
   fill_half_table<kWaves * 64>(tab, cb);  // ends with a barrier
 
@@ -705,14 +735,13 @@ __global__ __launch_bounds__(kWaves * 64) void k_gemv_mfma(const uint8_t* __rest
 
     // groups in order, the loads of group gi + 1 issued before group gi is
     // multiplied (clamped to the last group, whose loads are then repeated)
-    auto load_group = [&](GroupItem<kDQ> (&it)[kMfmaSeg], int64_t gi) {
+    auto load_group = [&](SegItem<kDQ>& it, int64_t gi) {
       const int64_t gl = gi < kmine ? gi : (kmine > 0 ? kmine - 1 : 0);
       const int64_t grp = blockIdx.x + gl * G;
       const int64_t rowc = grp * 16 + ln < rows ? grp * 16 + ln : rows - 1;  // past the end: never stored
-#pragma unroll
-      for (int j = 0; j < kMfmaSeg; ++j) group_load<kDQ>(it[j], packed, nblk, rowc, b0 + (j < nb ? j : nb - 1), g, sc);
+      seg_load<kDQ, kQ4>(it, packed, nblk, rowc, b0, nb, g, sc, ngroups2);
     };
-    auto mult_group = [&](const GroupItem<kDQ> (&it)[kMfmaSeg], int64_t gi) {
+    auto mult_group = [&](const SegItem<kDQ>& it, int64_t gi) {
       floatx4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
       // two halves of four blocks: all lookups, then all MFMAs, then the
       // scaling, so that the LDS and MFMA latencies overlap; blocks past the
@@ -725,7 +754,7 @@ __global__ __launch_bounds__(kWaves * 64) void k_gemv_mfma(const uint8_t* __rest
 #pragma unroll
           for (int u = 0; u < 8; ++u) {
             // codes 16 g .. 16 g + 7 (bytes 8 g .. 8 g + 3) then 16 g + 8 .. + 15
-            const uint32_t word = u < 4 ? it[h + j].c.x : it[h + j].c.y;
+            const uint32_t word = u < 4 ? it.c[h + j].x : it.c[h + j].y;
             const uint32_t addr = __builtin_amdgcn_perm(word, slot, 0x0C0C0000u | ((4u + (u & 3)) << 8));
             bw[j][u] = *reinterpret_cast<const uint32_t*>(smem + addr);
           }
@@ -745,8 +774,14 @@ __global__ __launch_bounds__(kWaves * 64) void k_gemv_mfma(const uint8_t* __rest
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           float a;
-          if constexpr (kDQ) a = (div127(it[h + j].q) * it[h + j].s2) + mean;  // a_hat of weight row ln
-          else a = it[h + j].am;
+          if constexpr (kDQ) {
+            float s2;
+            if constexpr (kQ4) s2 = (h + j) >= it.cross ? it.s2hi : it.s2lo;
+            else s2 = it.am[h + j];
+            a = (div127(it.q[h + j]) * s2) + mean;  // a_hat of weight row ln
+          } else {
+            a = it.am[h + j];
+          }
           a = (h + j < nb) ? a : 0.0f;
 #pragma unroll
           for (int i = 0; i < 4; ++i) acc[i] = fmaf(d[j][i], a, acc[i]);
@@ -757,7 +792,7 @@ __global__ __launch_bounds__(kWaves * 64) void k_gemv_mfma(const uint8_t* __rest
 #pragma unroll
       for (int i = 0; i < 4; ++i) pt[(4 * g + i) * 16 + ln] = acc[i] * xinv_d[i];
     };
-    GroupItem<kDQ> ia[kMfmaSeg], ib[kMfmaSeg];
+    SegItem<kDQ> ia, ib;
     load_group(ia, 0);
     for (int64_t gi = 0; gi < kmine; gi += 2) {
       load_group(ib, gi + 1);
@@ -805,10 +840,21 @@ hipError_t launch_mfma(const uint8_t* packed, int64_t rows, int64_t cols, Scales
   const Codebook& cb = codebook();
   const dim3 gd(static_cast<unsigned>(pl.grid)), bd(64 * kMfmaWaves);
   const int mi = static_cast<int>(m);
-  if (y_bf16)
-    hipLaunchKernelGGL((k_gemv_mfma<kMfmaWaves, kDQ, true>), gd, bd, 0, s, packed, rows, cols, sc, x, mi, y, cb, pl);
-  else
-    hipLaunchKernelGGL((k_gemv_mfma<kMfmaWaves, kDQ, false>), gd, bd, 0, s, packed, rows, cols, sc, x, mi, y, cb, pl);
+  // whole 4-block segments at multiples of 4 blocks in every row, and scale
+  // arrays aligned for one 4-byte (int8 codes) or 16-byte (absmax) load
+  const uintptr_t sa = kDQ ? reinterpret_cast<uintptr_t>(sc.q) : reinterpret_cast<uintptr_t>(sc.absmax);
+  const bool q4 = pl.seg_blocks == kMfmaSeg && (cols / 64) % kMfmaSeg == 0 && (sa & (kDQ ? 3u : 15u)) == 0;
+  if (q4) {
+    if (y_bf16)
+      hipLaunchKernelGGL((k_gemv_mfma<kMfmaWaves, kDQ, true, true>), gd, bd, 0, s, packed, rows, cols, sc, x, mi, y, cb, pl);
+    else
+      hipLaunchKernelGGL((k_gemv_mfma<kMfmaWaves, kDQ, true, false>), gd, bd, 0, s, packed, rows, cols, sc, x, mi, y, cb, pl);
+  } else {
+    if (y_bf16)
+      hipLaunchKernelGGL((k_gemv_mfma<kMfmaWaves, kDQ, false, true>), gd, bd, 0, s, packed, rows, cols, sc, x, mi, y, cb, pl);
+    else
+      hipLaunchKernelGGL((k_gemv_mfma<kMfmaWaves, kDQ, false, false>), gd, bd, 0, s, packed, rows, cols, sc, x, mi, y, cb, pl);
+  }
   return hipGetLastError();
 }
 
