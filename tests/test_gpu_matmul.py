@@ -135,6 +135,39 @@ def test_gemv_one_hot_and_determinism():
         assert torch.equal(y1, y2)
 
 
+@pytest.mark.parametrize("m", [4, 16])
+@pytest.mark.parametrize("dq", [True, False])
+def test_gemv_skinny_scale_load_forms(m, dq):
+    """The skinny (2 <= m <= 16) kernel reads a segment's four scale inputs
+    with one aligned load when the scale array allows it, and block by block
+    otherwise; both forms compute the same a_hat, so the outputs must be
+    bit-identical.  Scale arrays placed at an unaligned offset force the
+    block-by-block form.  Both are also checked against the oracle."""
+    torch = need_gpu()
+    rows, cols = 300, 4096
+    say("gemv skinny scale load forms", rows, cols, m, dq)
+    w = syn.normal_f32((rows, cols), 0.02, 21)
+    W = nf4.quantize_weight(to_dev(w), double_quant=dq)
+    x = syn.to_bf16(syn.normal_f32((m, cols), 1.0, 22)).to("cuda")
+    if dq:
+        buf = torch.zeros(W.qabsmax.numel() + 1, dtype=torch.int8, device="cuda")
+        buf[1:].copy_(W.qabsmax)
+        Wu = nf4.NF4Weight(W.packed, rows, cols, qabsmax=buf[1:], absmax2=W.absmax2, mean=W.mean)
+        assert Wu.qabsmax.data_ptr() % 4 == 1
+    else:
+        buf = torch.zeros(W.absmax.numel() + 1, dtype=torch.float32, device="cuda")
+        buf[1:].copy_(W.absmax)
+        Wu = nf4.NF4Weight(W.packed, rows, cols, absmax=buf[1:])
+        assert Wu.absmax.data_ptr() % 16 == 4
+    ya = nf4.nf4_gemv(W, x, y_dtype=torch.float32)
+    yu = nf4.nf4_gemv(Wu, x, y_dtype=torch.float32)
+    torch.cuda.synchronize()
+    assert torch.equal(ya, yu)
+    ref = oracle.matmul_ref(syn.bf16_to_f32(x), _full_oracle_wdeq(w, dq))
+    err = oracle.rel_frobenius(_y_f64(ya), ref)
+    assert err <= MATMUL_RTOL, err
+
+
 def test_gemv_x_dynamic_range():
     """x spanning 2^-60 .. 2^60 within and across blocks, and an all-zero
     block: the per-block power-of-two scaling of x keeps the decode GEMV
