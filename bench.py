@@ -43,6 +43,8 @@ def parse():
     p.add_argument("--pool", type=int, default=16)
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-extra", action="store_true")
+    p.add_argument("--only", choices=LEGS, default=None,
+                   help="run only this extra leg (no step, no CPU baseline): for profiling one kernel family")
     p.add_argument("--calibrate-copy", action="store_true",
                    help="only run a plain 64 MiB device copy kernel (for scaling HBM byte counters)")
     return p.parse_args()
@@ -127,6 +129,20 @@ class EventTimer:
         return 1e3 * sum(a.elapsed_time(b) for a, b in self.pairs) / max(1, len(self.pairs))
 
 
+def only_leg(name: str) -> int:
+    import torch
+
+    import dequant_matmul_nf4_amd as nf4
+    import synthetic as syn
+
+    nf4.lib()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    res = extra_legs(torch, nf4, syn, dev, torch.cuda.current_stream(), EventTimer, only=name)
+    print(json.dumps({"leg": name, **res}), flush=True)
+    return 0
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -136,6 +152,8 @@ def main():
 
     if args.calibrate_copy:
         return calibrate_copy()
+    if args.only:
+        return only_leg(args.only)
 
     import numpy as np
     import torch
@@ -271,13 +289,28 @@ def main():
     return 0
 
 
-def extra_legs(torch, nf4, syn, dev, stream, EventTimer):
-    """GEMV alone from HBM (decode), and the QLoRA forward GEMM."""
+LEGS = ("gemv-decode", "gemv-mlp", "gemv-70b", "gemm")
+
+
+def extra_legs(torch, nf4, syn, dev, stream, EventTimer, only=None):
+    """GEMV alone from HBM (decode), the Llama-8B MLP and 70B-layer GEMVs, and
+    the QLoRA forward GEMM; `only` runs a single one of LEGS."""
+    res = {}
+    g = torch.Generator(device=dev)
+    if only in (None, "gemv-decode"):
+        res.update(leg_gemv_decode(torch, nf4, syn, dev, stream, EventTimer, g))
+    if only in (None, "gemv-mlp", "gemv-70b"):
+        res.update(legs_gemv_pools(torch, nf4, dev, stream, EventTimer, g, only))
+    if only in (None, "gemm"):
+        res.update(leg_gemm(torch, nf4, dev, stream, EventTimer, g))
+    return res
+
+
+def leg_gemv_decode(torch, nf4, syn, dev, stream, EventTimer, g):
     res = {}
     rows = cols = 4096
     print("[bench] gemv-only leg", file=sys.stderr, flush=True)
     pool = 64
-    g = torch.Generator(device=dev)
     Ws = []
     for i in range(pool):
         g.manual_seed(7_000 + i)
@@ -312,8 +345,13 @@ def extra_legs(torch, nf4, syn, dev, stream, EventTimer):
         "frac_hbm_peak": round(gb / (per_call_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
     }
     del Ws
+    return res
 
-    # larger decode GEMVs: the Llama-8B MLP (C3 shapes) and one 70B-shaped layer
+
+def legs_gemv_pools(torch, nf4, dev, stream, EventTimer, g, only=None):
+    """Larger decode GEMVs: the Llama-8B MLP (M = 1, 4, 16) and one 70B-shaped layer."""
+    res = {}
+
     def gemv_pool(shapes, reps, label, m=1):
         Wl = []
         for i, (r_, c_) in enumerate(shapes):
@@ -347,14 +385,21 @@ def extra_legs(torch, nf4, syn, dev, stream, EventTimer):
                 "frac_hbm_peak": round(nbytes / (total_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}
 
     print("[bench] gemv MLP / 70B-layer legs", file=sys.stderr, flush=True)
-    mlp = [(14336, 4096), (14336, 4096), (4096, 14336)] * 6
-    label = ("Llama-8B MLP gate/up 14336x4096 + down 4096x14336, NF4+DQ, 6 distinct triples (545 MB) per pass")
-    res["gemv_mlp_8b"] = gemv_pool(mlp, 10, label + ", M=1")
-    res["gemv_mlp_8b_m4"] = gemv_pool(mlp, 10, label + ", M=4", m=4)
-    res["gemv_mlp_8b_m16"] = gemv_pool(mlp, 10, label + ", M=16", m=16)
-    layer = [(8192, 8192), (1024, 8192), (1024, 8192), (8192, 8192), (28672, 8192), (28672, 8192), (8192, 28672)]
-    res["gemv_layer_70b"] = gemv_pool(layer, 10, "70B-shaped layer q,k,v,o,gate,up,down NF4+DQ, M=1 (442 MB)")
+    if only in (None, "gemv-mlp"):
+        mlp = [(14336, 4096), (14336, 4096), (4096, 14336)] * 6
+        label = ("Llama-8B MLP gate/up 14336x4096 + down 4096x14336, NF4+DQ, 6 distinct triples (545 MB) per pass")
+        res["gemv_mlp_8b"] = gemv_pool(mlp, 10, label + ", M=1")
+        res["gemv_mlp_8b_m4"] = gemv_pool(mlp, 10, label + ", M=4", m=4)
+        res["gemv_mlp_8b_m16"] = gemv_pool(mlp, 10, label + ", M=16", m=16)
+    if only in (None, "gemv-70b"):
+        layer = [(8192, 8192), (1024, 8192), (1024, 8192), (8192, 8192), (28672, 8192), (28672, 8192),
+                 (8192, 28672)]
+        res["gemv_layer_70b"] = gemv_pool(layer, 10, "70B-shaped layer q,k,v,o,gate,up,down NF4+DQ, M=1 (442 MB)")
+    return res
 
+
+def leg_gemm(torch, nf4, dev, stream, EventTimer, g):
+    res = {}
     print("[bench] gemm leg", file=sys.stderr, flush=True)
     M, N, K, r = 4096, 14336, 4096, 16
     g.manual_seed(4_005)
