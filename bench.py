@@ -289,7 +289,7 @@ def main():
     return 0
 
 
-LEGS = ("gemv-decode", "gemv-mlp", "gemv-70b", "gemm")
+LEGS = ("gemv-decode", "gemv-mlp", "gemv-70b", "stack-70b", "gemm")
 
 
 def extra_legs(torch, nf4, syn, dev, stream, EventTimer, only=None):
@@ -301,9 +301,95 @@ def extra_legs(torch, nf4, syn, dev, stream, EventTimer, only=None):
         res.update(leg_gemv_decode(torch, nf4, syn, dev, stream, EventTimer, g))
     if only in (None, "gemv-mlp", "gemv-70b"):
         res.update(legs_gemv_pools(torch, nf4, dev, stream, EventTimer, g, only))
+    if only in (None, "stack-70b"):
+        res.update(leg_stack_70b(torch, nf4, syn, dev, stream, EventTimer))
     if only in (None, "gemm"):
         res.update(leg_gemm(torch, nf4, dev, stream, EventTimer, g))
     return res
+
+
+def leg_stack_70b(torch, nf4, syn, dev, stream, EventTimer, layers=80, gemv_passes=20):
+    """The 80-layer 70B-shaped stack.  Layer by layer, the seven bf16 weights
+    (q, k, v, o, gate, up, down) are drawn on the device (untimed) and then
+    quantized and double-quantized into a persistent NF4 store (timed: one HIP
+    graph of the 7 x 3 launches per layer).  Afterwards the decode GEMV runs
+    over one layer's seven matrices, a different stored layer on every pass,
+    so that no pass finds its 441 MB in the last-level cache."""
+    print(f"[bench] 70B stack leg: {layers} layers", file=sys.stderr, flush=True)
+    LAYER_70B = [syn.C5_SHAPES[name] for name in syn.C5_ORDER]
+    g = torch.Generator(device=dev)
+    src = [torch.empty(sh, dtype=torch.bfloat16, device=dev) for sh in LAYER_70B]
+    nbs = [r * c // 64 for r, c in LAYER_70B]
+    absmax = [torch.empty(nb, dtype=torch.float32, device=dev) for nb in nbs]
+    dq_ws = torch.empty(nf4.nf4_double_quant_workspace(max(nbs)), dtype=torch.uint8, device=dev)
+    store, t = [], EventTimer(torch, stream)
+    for layer in range(layers):
+        Ws = []
+        for (r, c), nb in zip(LAYER_70B, nbs):
+            Ws.append(nf4.NF4Weight(torch.empty(r * c // 2, dtype=torch.uint8, device=dev), r, c,
+                                    qabsmax=torch.empty(nb, dtype=torch.int8, device=dev),
+                                    absmax2=torch.empty(-(-nb // 256), dtype=torch.float32, device=dev),
+                                    mean=torch.empty(1, dtype=torch.float32, device=dev)))
+
+        def run():
+            for w, W, am in zip(src, Ws, absmax):
+                nf4.nf4_quantize(w, W.packed, am)
+                nf4.nf4_double_quant(am, W.qabsmax, W.absmax2, W.mean, dq_ws)
+
+        graph = capture_graph(torch, run)
+        graph.replay()  # first launch of the graph (upload), on the previous layer's data; untimed
+        for j, name in enumerate(syn.C5_ORDER):
+            src[j].copy_(syn.c5_weight_device(layer, name, device=dev))
+        s = t.start()
+        graph.replay()
+        t.stop(s)
+        torch.cuda.synchronize()
+        del graph
+        store.append(Ws)
+    q_us = [1e3 * a.elapsed_time(b) for a, b in t.pairs]
+    n_layer = sum(r * c for r, c in LAYER_70B)
+    alg_layer = sum(step_bytes(r, c)["quantize"] + step_bytes(r, c)["double_quant"] for r, c in LAYER_70B)
+    total_s = sum(q_us) * 1e-6
+    del src, absmax
+
+    g.manual_seed(5_000_009)
+    xs = {c: (torch.randn((1, c), generator=g, device=dev)).to(torch.bfloat16) for _, c in LAYER_70B}
+    ys = [torch.empty((1, r), dtype=torch.bfloat16, device=dev) for r, _ in LAYER_70B]
+    step = max(1, layers // gemv_passes)
+    pass_layers = [(i * step) % layers for i in range(gemv_passes)]
+    graphs = []
+    for layer in pass_layers:
+        def run_gemv(Ws=store[layer]):
+            for W, yy in zip(Ws, ys):
+                nf4.nf4_gemv(W, xs[W.cols], yy)
+        run_gemv()
+        graphs.append(capture_graph(torch, run_gemv))
+    torch.cuda.synchronize()
+    tg = EventTimer(torch, stream)
+    for gr in graphs:
+        s = tg.start()
+        gr.replay()
+        tg.stop(s)
+    torch.cuda.synchronize()
+    g_us = sorted(1e3 * a.elapsed_time(b) for a, b in tg.pairs)
+    g_med = g_us[len(g_us) // 2]
+    g_bytes = sum(step_bytes(r, c)["gemv"] for r, c in LAYER_70B)
+    del graphs, store
+    return {"stack_70b": {
+        "workload": f"{layers} layers of q,o 8192x8192, k,v 1024x8192, gate,up 28672x8192, down 8192x28672, bf16 "
+                    "N(0,0.02) drawn per layer on the device; NF4 + double quant into a persistent store",
+        "layers": layers,
+        "quantize_dq_us_per_layer": round(sum(q_us) / layers, 1),
+        "quantize_dq_input_GBps": round(2 * n_layer * layers / total_s / 1e9, 1),
+        "quantize_dq_algorithmic_GBps": round(alg_layer * layers / total_s / 1e9, 1),
+        "quantize_dq_frac_hbm_peak": round(alg_layer * layers / total_s / 1e9 / HBM_PEAK_GBS, 4),
+        "nf4_store_GB": round(layers * g_bytes / 1e9, 2),
+        "gemv_layer_rotating": {
+            "passes": gemv_passes, "median_us": round(g_med, 2),
+            "GBps": round(g_bytes / (g_med * 1e-6) / 1e9, 1),
+            "frac_hbm_peak": round(g_bytes / (g_med * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+        },
+    }}
 
 
 def leg_gemv_decode(torch, nf4, syn, dev, stream, EventTimer, g):
