@@ -128,6 +128,10 @@ class EventTimer:
     def mean_us(self):
         return 1e3 * sum(a.elapsed_time(b) for a, b in self.pairs) / max(1, len(self.pairs))
 
+    def median_us(self):
+        v = sorted(1e3 * a.elapsed_time(b) for a, b in self.pairs)
+        return v[len(v) // 2] if v else 0.0
+
 
 def only_leg(name: str) -> int:
     import torch
@@ -289,7 +293,7 @@ def main():
     return 0
 
 
-LEGS = ("gemv-decode", "gemv-mlp", "gemv-70b", "stack-70b", "gemm")
+LEGS = ("hbm", "gemv-decode", "gemv-mlp", "gemv-70b", "stack-70b", "gemm")
 
 
 def extra_legs(torch, nf4, syn, dev, stream, EventTimer, only=None):
@@ -297,6 +301,8 @@ def extra_legs(torch, nf4, syn, dev, stream, EventTimer, only=None):
     the QLoRA forward GEMM; `only` runs a single one of LEGS."""
     res = {}
     g = torch.Generator(device=dev)
+    if only in (None, "hbm"):
+        res.update(leg_hbm_calibration(torch, dev, stream, EventTimer))
     if only in (None, "gemv-decode"):
         res.update(leg_gemv_decode(torch, nf4, syn, dev, stream, EventTimer, g))
     if only in (None, "gemv-mlp", "gemv-70b"):
@@ -390,6 +396,32 @@ def leg_stack_70b(torch, nf4, syn, dev, stream, EventTimer, layers=80, gemv_pass
             "frac_hbm_peak": round(g_bytes / (g_med * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
         },
     }}
+
+
+def leg_hbm_calibration(torch, dev, stream, EventTimer):
+    """What the memory system gives vendor kernels on this GPU, as the
+    measured-achievable context for the HBM-bound kernels: torch's device copy
+    (read + write) and a full reduction (read only) over 2 GiB."""
+    print("[bench] HBM calibration", file=sys.stderr, flush=True)
+    n = 1 << 30  # bf16 elements: 2 GiB
+    a = torch.empty(n, dtype=torch.bfloat16, device=dev).fill_(1.0)
+    b = torch.empty_like(a)
+    out = {}
+    for what, fn, nbytes in (("copy", lambda: b.copy_(a), 4 * n), ("sum", lambda: a.sum(dtype=torch.float32), 2 * n)):
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        t = EventTimer(torch, stream)
+        for _ in range(10):
+            s = t.start()
+            fn()
+            t.stop(s)
+        torch.cuda.synchronize()
+        us = t.median_us()
+        out[what] = {"GBps": round(nbytes / (us * 1e-6) / 1e9, 1), "us": round(us, 1)}
+    del a, b
+    return {"hbm_calibration": {"what": "torch copy_ (2 GiB read + 2 GiB write) and sum (2 GiB read), median of 10",
+                                **out}}
 
 
 def leg_gemv_decode(torch, nf4, syn, dev, stream, EventTimer, g):
@@ -499,29 +531,32 @@ def leg_gemm(torch, nf4, dev, stream, EventTimer, g):
     B = (torch.randn((N, r), generator=g, device=dev) * 0.01).to(torch.bfloat16)
     Y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
     wsb = torch.empty(nf4.nf4_gemm_workspace(M, N, r), dtype=torch.uint8, device=dev)
-    for _ in range(3):
+    # median of 50 event-timed calls after 10 warm-ups
+    for _ in range(10):
         nf4.nf4_gemm(W, X, Y, A, B, 2.0, wsb)
     torch.cuda.synchronize()
     t = EventTimer(torch, stream)
-    reps = 10
+    reps = 50
     for _ in range(reps):
         s = t.start()
         nf4.nf4_gemm(W, X, Y, A, B, 2.0, wsb)
         t.stop(s)
     torch.cuda.synchronize()
-    us = t.mean_us()
+    us = t.median_us()
     flops = 2.0 * M * N * K + 2.0 * M * K * r + 2.0 * M * r * N
     tf = flops / (us * 1e-6) / 1e12
     res["gemm_qlora_forward"] = {
         "workload": "X 4096x4096 bf16 . NF4(DQ) W 14336x4096^T + LoRA r=16 alpha=32",
         "us": round(us, 1),
+        "us_mean": round(t.mean_us(), 1),
         "TFLOPs": round(tf, 1),
         "frac_mfma_bf16_peak": round(tf / MFMA_BF16_PEAK_TFLOPS, 4),
+        "timing": f"median of {reps} calls (LoRA prep + GEMM) after 10 warm-ups",
     }
     # Calibration only (not part of the path): the vendor library's plain bf16
     # GEMM of the same shape on an already dequantized weight, no LoRA.
     Wd = nf4.nf4_dequantize(W, out_dtype=torch.bfloat16)
-    for _ in range(3):
+    for _ in range(10):
         torch.nn.functional.linear(X, Wd)
     torch.cuda.synchronize()
     t = EventTimer(torch, stream)
@@ -530,7 +565,7 @@ def leg_gemm(torch, nf4, dev, stream, EventTimer, g):
         torch.nn.functional.linear(X, Wd)
         t.stop(s)
     torch.cuda.synchronize()
-    us_lib = t.mean_us()
+    us_lib = t.median_us()
     res["gemm_qlora_forward"]["calibration_torch_linear_bf16"] = {
         "what": "torch.nn.functional.linear (hipBLASLt) on the dequantized bf16 weight, same M, N, K, no LoRA",
         "us": round(us_lib, 1),
