@@ -8,10 +8,12 @@ binding) never does, and the two share no code, tables or constants.
 Sources (web pages, cited by title and section):
   [TOOL]  "bitsandbytes" (ozercemkelahmet.com/tools/bitsandbytes):
           "How it works" Steps 1-5, "How NF4 works", "Double quantization",
-          "A worked example", "Memory arithmetic".
+          "A worked example", "Memory arithmetic", "Practical guidance and
+          best practices".
   [TUT]   "bitsandbytes quantization tutorial: 4-bit and 8-bit models"
           (mljourney.com): "4-bit Loading with NF4", "How NF4 Works",
-          "Memory Requirements at Different Precisions".
+          "Memory Requirements at Different Precisions", "Merging LoRA
+          Adapters After Fine-Tuning".
 
 Readings where the pages leave a step open are marked READING below.
 
@@ -292,6 +294,62 @@ def rel_frobenius(y, y_ref) -> float:
     y_ref = np.asarray(y_ref, dtype=np.float64)
     den = np.linalg.norm(y_ref)
     return float(np.linalg.norm(y - y_ref) / den) if den > 0 else float(np.linalg.norm(y))
+
+
+# ------------------------------------------------------------------ LoRA merge
+
+def f64_to_bf16_bits(v: np.ndarray) -> np.ndarray:
+    """float64 -> bfloat16 bit patterns, one rounding to nearest even (finite
+    inputs).  Method: round to odd into float32 (24 significant bits, at least
+    two more than bfloat16's 8 and the same exponent range), then round to
+    nearest even into bfloat16; rounding to odd first makes the two steps
+    equal one correct rounding."""
+    v = np.asarray(v, dtype=np.float64)
+    f = v.astype(np.float32)
+    back = f.astype(np.float64)
+    u = f.view(np.uint32).copy()
+    inexact = back != v
+    away = inexact & (np.abs(back) > np.abs(v))  # rounded away from zero: step back one ulp
+    u[away] -= np.uint32(1)
+    u[inexact] |= np.uint32(1)
+    return f32_to_bf16_bits(u.view(np.float32))
+
+
+def f64_to_f16_bits(v: np.ndarray) -> np.ndarray:
+    """float64 -> IEEE binary16 bit patterns, one rounding to nearest even,
+    subnormals included (numpy's double-to-half conversion rounds once)."""
+    return np.asarray(v, dtype=np.float64).astype(np.float16).view(np.uint16)
+
+
+def lora_merge(w_deq_f32: np.ndarray, lora_a: np.ndarray, lora_b: np.ndarray, lora_scale: float,
+               out: str = "bf16") -> np.ndarray:
+    """[TUT] "Merging LoRA Adapters After Fine-Tuning": after training, the
+    adapters are folded into one dense 16-bit copy of the base, which first
+    needs the base dequantized ([TOOL] "Practical guidance and best
+    practices": merging adds another rounding step).
+
+        W'[n][k] = round( deq[n][k] + s * sum_j B[n][j] * A[j][k] )
+
+    w_deq_f32: [N, K] float32 dequantized base (as dequantize(..., "f32"));
+    lora_a: [r, K], lora_b: [N, r] (bf16 values as float32); s = lora_scale
+    as float32.  READING: the sum is formed in float64 with j ascending (each
+    bf16 x bf16 product is exact in float64, and so is the sum unless its
+    terms span more than about 37 binary orders), multiplied by s, added to
+    deq in float64, then rounded once to nearest even into out ("bf16" or
+    "f16"; the tutorial's merged checkpoint is float16).  Returns uint16 bit
+    patterns."""
+    deq = np.asarray(w_deq_f32, dtype=np.float32).astype(np.float64)
+    a = np.asarray(lora_a, dtype=np.float32).astype(np.float64)
+    b = np.asarray(lora_b, dtype=np.float32).astype(np.float64)
+    acc = np.zeros(deq.shape, dtype=np.float64)
+    for j in range(a.shape[0]):
+        acc = acc + b[:, j:j + 1] * a[j:j + 1, :]
+    v = deq + np.float64(np.float32(lora_scale)) * acc
+    if out == "bf16":
+        return f64_to_bf16_bits(v)
+    if out == "f16":
+        return f64_to_f16_bits(v)
+    raise ValueError(out)
 
 
 # ------------------------------------------------------------ storage footprint

@@ -385,3 +385,104 @@ def test_dequantize_matches_per_element_exact_product():
 def test_rel_frobenius():
     assert oracle.rel_frobenius([3.0, 4.0], [3.0, 4.0]) == 0.0
     assert abs(oracle.rel_frobenius([3.0, 4.5], [3.0, 4.0]) - 0.1) < 1e-15
+
+
+# ------------------------------------------------------------- NEXT-2 LoRA merge
+
+def _round_exact(x: Fraction, man_bits: int, emin: int) -> Fraction:
+    """Round-to-nearest-even of a rational into a binary format with
+    man_bits significant bits and smallest normal exponent emin (subnormals
+    below it), by integer arithmetic on the exact value."""
+    if x == 0:
+        return Fraction(0)
+    sign = -1 if x < 0 else 1
+    ax = abs(x)
+    e = ax.numerator.bit_length() - ax.denominator.bit_length()
+    if Fraction(2) ** e > ax:
+        e -= 1
+    e = max(e, emin)
+    quantum = Fraction(2) ** (e - man_bits + 1)
+    q = ax / quantum
+    lo = q.numerator // q.denominator
+    rem = q - lo
+    if rem > Fraction(1, 2) or (rem == Fraction(1, 2) and lo % 2 == 1):
+        lo += 1
+    return sign * lo * quantum
+
+
+def _bf16_bits_of(v: Fraction, negative: bool = False) -> int:
+    if v == 0:
+        return 0x8000 if negative else 0
+    f = np.float32(float(v))  # exact: v is on the bf16 grid
+    assert Fraction(float(f)) == v
+    return int(f.view(np.uint32)) >> 16
+
+
+def _f16_bits_of(v: Fraction, negative: bool = False) -> int:
+    if v == 0:
+        return 0x8000 if negative else 0
+    h = np.float16(float(v))
+    assert Fraction(float(h)) == v
+    return int(h.view(np.uint16))
+
+
+def _f64_cases():
+    rng = np.random.default_rng(5)
+    mags = np.exp2(rng.uniform(-30, 12, 4000))
+    v = (mags * rng.choice([-1.0, 1.0], 4000)).astype(np.float64)
+    # exact ties and their float64 neighbours, for bf16 (8 bits) and fp16 (11 bits)
+    extra = []
+    for bits in (8, 11):
+        base = rng.integers(1 << (bits - 1), 1 << bits, 200).astype(np.float64)
+        for t in (base + 0.5) * np.exp2(rng.integers(-20, 4, 200) - bits):
+            extra += [t, np.nextafter(t, 0.0), np.nextafter(t, np.inf), -t]
+    # fp16 subnormal range
+    extra += list(rng.uniform(-6.2e-5, 6.2e-5, 500)) + [2.0 ** -24 * 0.5, 2.0 ** -24 * 1.5, 2.0 ** -25 + 2.0 ** -60]
+    return np.concatenate([v, np.array(extra, dtype=np.float64)])
+
+
+def test_f64_to_bf16_and_f16_round_once_to_nearest_even():
+    """Both conversions equal the correctly rounded exact value (rational
+    arithmetic), ties to even included, fp16 subnormals included."""
+    v = _f64_cases()
+    bf = oracle.f64_to_bf16_bits(v)
+    hf = oracle.f64_to_f16_bits(v)
+    for i, x in enumerate(v):
+        fx = Fraction(float(x))
+        assert int(bf[i]) == _bf16_bits_of(_round_exact(fx, 8, -126), x < 0), x
+        assert int(hf[i]) == _f16_bits_of(_round_exact(fx, 11, -14), x < 0), x
+
+
+def test_lora_merge_closed_forms():
+    """B = 0 gives the dequantized base rounded once (the bf16 dequantize
+    output); rank 1 with power-of-two adapters gives deq + s*b*a exactly."""
+    rng = np.random.default_rng(11)
+    deq = (rng.standard_normal((6, 64)) * 0.02).astype(np.float32)
+    a = (rng.standard_normal((3, 64)) * 0.01).astype(np.float32)
+    a = oracle.bf16_bits_to_f32(oracle.f32_to_bf16_bits(a))
+    zero_b = np.zeros((6, 3), dtype=np.float32)
+    assert np.array_equal(oracle.lora_merge(deq, a, zero_b, 2.0, "bf16"), oracle.f32_to_bf16_bits(deq))
+    assert np.array_equal(oracle.lora_merge(deq, a, zero_b, 2.0, "f16"), deq.astype(np.float16).view(np.uint16))
+    a1 = np.full((1, 64), 2.0 ** -7, dtype=np.float32)
+    b1 = np.full((6, 1), 2.0 ** -5, dtype=np.float32)
+    expect = deq.astype(np.float64) + 2.0 * 2.0 ** -12
+    assert np.array_equal(oracle.lora_merge(deq, a1, b1, 2.0, "bf16"), oracle.f64_to_bf16_bits(expect))
+
+
+def test_lora_merge_is_the_rounded_exact_value():
+    """For bf16 adapters the float64 evaluation is exact, so the merge equals
+    the exact rational value rounded once -- checked element by element."""
+    rng = np.random.default_rng(12)
+    rows, cols, r = 5, 64, 16
+    deq = (rng.standard_normal((rows, cols)) * 0.02).astype(np.float32)
+    a = oracle.bf16_bits_to_f32(oracle.f32_to_bf16_bits((rng.standard_normal((r, cols)) * 0.01).astype(np.float32)))
+    b = oracle.bf16_bits_to_f32(oracle.f32_to_bf16_bits((rng.standard_normal((rows, r)) * 0.01).astype(np.float32)))
+    s = 2.0
+    got_b = oracle.lora_merge(deq, a, b, s, "bf16")
+    got_h = oracle.lora_merge(deq, a, b, s, "f16")
+    for n in range(rows):
+        for k in range(cols):
+            x = Fraction(float(deq[n, k])) + Fraction(s) * sum(
+                Fraction(float(b[n, j])) * Fraction(float(a[j, k])) for j in range(r))
+            assert int(got_b[n, k]) == _bf16_bits_of(_round_exact(x, 8, -126), x < 0)
+            assert int(got_h[n, k]) == _f16_bits_of(_round_exact(x, 11, -14), x < 0)
