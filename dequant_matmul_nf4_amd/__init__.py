@@ -18,12 +18,12 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libnf4.so")
 
 NF4_OK, NF4_ERR_NULL, NF4_ERR_SIZE, NF4_ERR_BLOCKSIZE, NF4_ERR_ALIGN, NF4_ERR_DTYPE, NF4_ERR_WORKSPACE, NF4_ERR_DEVICE = range(8)
-NF4_F32, NF4_BF16 = 0, 1
+NF4_F32, NF4_BF16, NF4_F16 = 0, 1, 2
 BLOCKSIZE, BLOCKSIZE2 = 64, 256
 
 EXPORTS = (
     "nf4_last_error", "nf4_codebook", "nf4_quantize", "nf4_double_quant_workspace",
-    "nf4_double_quant", "nf4_dequantize", "nf4_gemv", "nf4_gemm_workspace", "nf4_gemm",
+    "nf4_double_quant", "nf4_dequantize", "nf4_gemv", "nf4_gemm_workspace", "nf4_gemm", "nf4_lora_merge",
 )
 
 
@@ -65,6 +65,7 @@ def lib() -> ctypes.CDLL:
         "nf4_gemv": (ctypes.c_int, [wp, vp, i64, vp, ctypes.c_int, vp]),
         "nf4_gemm_workspace": (sz, [i64, i64, i32]),
         "nf4_gemm": (ctypes.c_int, [wp, vp, i64, vp, vp, vp, i32, ctypes.c_float, vp, sz, vp]),
+        "nf4_lora_merge": (ctypes.c_int, [wp, vp, vp, i32, ctypes.c_float, vp, ctypes.c_int, vp]),
     }
     for name, (res, args) in sig.items():
         f = getattr(L, name)
@@ -120,6 +121,8 @@ def _dtype_code(t) -> int:
         return NF4_F32
     if t.dtype == torch.bfloat16:
         return NF4_BF16
+    if t.dtype == torch.float16:
+        return NF4_F16
     raise TypeError(f"unsupported dtype {t.dtype}")
 
 
@@ -256,3 +259,23 @@ def nf4_gemm(w: NF4Weight, x, y=None, lora_a=None, lora_b=None, lora_scale: floa
     _check(lib().nf4_gemm(ctypes.byref(cs), _ptr(x2), m, _ptr(y), _ptr(lora_a), _ptr(lora_b), r,
                           float(lora_scale), _ptr(workspace), wsn, _stream(stream)))
     return y
+
+
+def nf4_lora_merge(w: NF4Weight, lora_a, lora_b, lora_scale: float, out=None, out_dtype=None, stream=None):
+    """W' = round(deq(W) + lora_scale . B . A) as a dense [rows, cols] bf16 or fp16 tensor."""
+    torch = _torch()
+    _need_cuda(lora_a, lora_b)
+    r = lora_a.shape[0]
+    if lora_a.dtype != torch.bfloat16 or lora_b.dtype != torch.bfloat16:
+        raise TypeError("lora_a and lora_b must be bf16")
+    if tuple(lora_a.shape) != (r, w.cols) or tuple(lora_b.shape) != (w.rows, r):
+        raise ValueError("LoRA shapes must be A [r, cols] and B [rows, r]")
+    if out is None:
+        out = torch.empty((w.rows, w.cols), dtype=out_dtype or torch.bfloat16, device=lora_a.device)
+    _need_cuda(out)
+    if out.numel() != w.rows * w.cols:
+        raise ValueError("out has the wrong size")
+    cs = w.c_struct()
+    _check(lib().nf4_lora_merge(ctypes.byref(cs), _ptr(lora_a), _ptr(lora_b), r, float(lora_scale), _ptr(out),
+                                _dtype_code(out), _stream(stream)))
+    return out

@@ -210,4 +210,27 @@ int nf4_gemm(const nf4_weight* w, const void* x, int64_t m, void* y, const void*
                   "nf4_gemm");
 }
 
+int nf4_lora_merge(const nf4_weight* w, const void* lora_a, const void* lora_b, int32_t r, float lora_scale,
+                   void* out, int out_dtype, void* stream) {
+  nf4i::Scales sc{};
+  int64_t n = 0;
+  if (int rc = check_weight(w, &sc, &n, "nf4_lora_merge")) return rc;
+  if (!lora_a || !lora_b || !out) return fail(NF4_ERR_NULL, "nf4_lora_merge: lora_a, lora_b and out are required");
+  if (w->cols % 8) return fail(NF4_ERR_SIZE, "nf4_lora_merge: cols = %lld is not a multiple of 8", (long long)w->cols);
+  if (w->rows > (int64_t(1) << 24)) return fail(NF4_ERR_SIZE, "nf4_lora_merge: rows = %lld out of range", (long long)w->rows);
+  if (w->cols > int64_t(65535) * 2048)
+    return fail(NF4_ERR_SIZE, "nf4_lora_merge: cols = %lld out of range", (long long)w->cols);
+  if (r < 1 || r > 64) return fail(NF4_ERR_SIZE, "nf4_lora_merge: LoRA rank r = %d out of range 1..64", (int)r);
+  if (!std::isfinite(lora_scale)) return fail(NF4_ERR_SIZE, "nf4_lora_merge: lora_scale is not finite");
+  if (out_dtype != NF4_BF16 && out_dtype != NF4_F16)
+    return fail(NF4_ERR_DTYPE, "nf4_lora_merge: out_dtype %d is not NF4_BF16 or NF4_F16", out_dtype);
+  if (!aligned(lora_a, 16) || !aligned(lora_b, 16) || !aligned(out, 16))
+    return fail(NF4_ERR_ALIGN, "nf4_lora_merge: lora_a, lora_b and out must be 16-byte aligned");
+  if (int rc = check_device()) return rc;
+  return launched(nf4i::launch_lora_merge(w->packed, w->rows, w->cols, sc, static_cast<const uint16_t*>(lora_a),
+                                          static_cast<const uint16_t*>(lora_b), r, lora_scale,
+                                          static_cast<uint16_t*>(out), out_dtype == NF4_F16, as_stream(stream)),
+                  "nf4_lora_merge");
+}
+
 }  // extern "C"

@@ -71,5 +71,8 @@ hipError_t launch_gemm(const uint8_t* packed, int64_t rows, int64_t cols, Scales
                        const uint16_t* x, int64_t m, uint16_t* y, const uint16_t* lora_a,
                        const uint16_t* lora_b, int r, float lora_scale, uint16_t* u_ws,
                        hipStream_t s);
+hipError_t launch_lora_merge(const uint8_t* packed, int64_t rows, int64_t cols, Scales sc, const uint16_t* lora_a,
+                             const uint16_t* lora_b, int r, float scale, uint16_t* out, int out_f16,
+                             hipStream_t s);
 
 }  // namespace nf4i

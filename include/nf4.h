@@ -52,7 +52,7 @@ typedef enum nf4_status {
   NF4_ERR_DEVICE = 7      /* the device is not gfx950, or a HIP call failed       */
 } nf4_status;
 
-typedef enum nf4_dtype { NF4_F32 = 0, NF4_BF16 = 1 } nf4_dtype;
+typedef enum nf4_dtype { NF4_F32 = 0, NF4_BF16 = 1, NF4_F16 = 2 } nf4_dtype;
 
 #define NF4_BLOCKSIZE 64
 #define NF4_BLOCKSIZE2 256
@@ -163,6 +163,24 @@ size_t nf4_gemm_workspace(int64_t m, int64_t rows, int32_t r);
 int nf4_gemm(const nf4_weight* w, const void* x, int64_t m, void* y,
              const void* lora_a, const void* lora_b, int32_t r, float lora_scale,
              void* workspace, size_t workspace_bytes, void* stream);
+
+/* LoRA merge -- tutorial page, "Merging LoRA Adapters After Fine-Tuning":
+ * after training the adapters are folded into one dense 16-bit copy of the
+ * base, which needs the base dequantized first (tool page, "Practical
+ * guidance and best practices": merging adds a rounding step).
+ *   out[n][k] = round( deq[n][k] + lora_scale * sum_j B[n][j] * A[j][k] )
+ *   w      : the NF4 weight [rows][cols] (either scale form); cols % 8 == 0.
+ *   lora_a : bf16 [r][cols], lora_b : bf16 [rows][r], 1 <= r <= 64, both
+ *            16-byte aligned.  lora_scale is finite (alpha / r).
+ *   out    : [rows][cols] of out_dtype (NF4_BF16 or NF4_F16), 16-byte
+ *            aligned, not overlapping any input.
+ * deq[n][k] is the float32 value nf4_dequantize writes.  The sum is formed in
+ * float64 with j ascending (exact for bf16 adapters unless its terms span
+ * more than about 37 binary orders), multiplied by lora_scale and added to
+ * deq[n][k] in float64, and the result is rounded once to nearest even into
+ * out_dtype (fp16 subnormals kept). */
+int nf4_lora_merge(const nf4_weight* w, const void* lora_a, const void* lora_b, int32_t r,
+                   float lora_scale, void* out, int out_dtype, void* stream);
 
 #ifdef __cplusplus
 }

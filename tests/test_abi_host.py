@@ -117,6 +117,16 @@ CASES = [
     ("gemm workspace null", lambda L: L.nf4_gemm(ctypes.byref(_w()), A, 4, A, A, A, 16, 2.0, None, 4096, None), nf4.NF4_ERR_WORKSPACE),
     ("gemm scale nan", lambda L: L.nf4_gemm(ctypes.byref(_w()), A, 4, A, A, A, 16, float("nan"), A, 4096, None), nf4.NF4_ERR_SIZE),
     ("gemm misaligned y", lambda L: L.nf4_gemm(ctypes.byref(_w()), A, 4, A + 2, None, None, 0, 0.0, None, 0, None), nf4.NF4_ERR_ALIGN),
+    ("merge null weight", lambda L: L.nf4_lora_merge(None, A, A, 16, 2.0, A, 1, None), nf4.NF4_ERR_NULL),
+    ("merge null a", lambda L: L.nf4_lora_merge(ctypes.byref(_w()), None, A, 16, 2.0, A, 1, None), nf4.NF4_ERR_NULL),
+    ("merge null out", lambda L: L.nf4_lora_merge(ctypes.byref(_w()), A, A, 16, 2.0, None, 1, None), nf4.NF4_ERR_NULL),
+    ("merge cols%8", lambda L: L.nf4_lora_merge(ctypes.byref(_w(cols=100)), A, A, 16, 2.0, A, 1, None), nf4.NF4_ERR_SIZE),
+    ("merge rank 0", lambda L: L.nf4_lora_merge(ctypes.byref(_w()), A, A, 0, 2.0, A, 1, None), nf4.NF4_ERR_SIZE),
+    ("merge rank 65", lambda L: L.nf4_lora_merge(ctypes.byref(_w()), A, A, 65, 2.0, A, 1, None), nf4.NF4_ERR_SIZE),
+    ("merge scale inf", lambda L: L.nf4_lora_merge(ctypes.byref(_w()), A, A, 16, float("inf"), A, 1, None), nf4.NF4_ERR_SIZE),
+    ("merge f32 out", lambda L: L.nf4_lora_merge(ctypes.byref(_w()), A, A, 16, 2.0, A, 0, None), nf4.NF4_ERR_DTYPE),
+    ("merge misaligned out", lambda L: L.nf4_lora_merge(ctypes.byref(_w()), A, A, 16, 2.0, A + 2, 2, None), nf4.NF4_ERR_ALIGN),
+    ("merge misaligned b", lambda L: L.nf4_lora_merge(ctypes.byref(_w()), A, A + 8, 16, 2.0, A, 1, None), nf4.NF4_ERR_ALIGN),
 ]
 
 
