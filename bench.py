@@ -293,7 +293,7 @@ def main():
     return 0
 
 
-LEGS = ("hbm", "gemv-decode", "gemv-mlp", "gemv-70b", "stack-70b", "gemm")
+LEGS = ("hbm", "gemv-decode", "gemv-mlp", "gemv-70b", "stack-70b", "gemm", "lora-merge")
 
 
 def extra_legs(torch, nf4, syn, dev, stream, EventTimer, only=None):
@@ -311,7 +311,49 @@ def extra_legs(torch, nf4, syn, dev, stream, EventTimer, only=None):
         res.update(leg_stack_70b(torch, nf4, syn, dev, stream, EventTimer))
     if only in (None, "gemm"):
         res.update(leg_gemm(torch, nf4, dev, stream, EventTimer, g))
+    if only in (None, "lora-merge"):
+        res.update(leg_lora_merge(torch, nf4, dev, stream, EventTimer, g))
     return res
+
+
+FP64_VECTOR_PEAK_TFLOPS = 78.6
+
+
+def leg_lora_merge(torch, nf4, dev, stream, EventTimer, g):
+    """The LoRA merge on the QLoRA shape: W 14336x4096 (NF4 + double quant),
+    r = 16, alpha = 32, merged into a dense bf16 copy (median of 20)."""
+    print("[bench] lora merge leg", file=sys.stderr, flush=True)
+    N, K, r = 14336, 4096, 16
+    g.manual_seed(4_000)
+    W = nf4.quantize_weight((torch.randn((N, K), generator=g, device=dev) * 0.02).to(torch.bfloat16),
+                            double_quant=True)
+    g.manual_seed(4_006)
+    A = (torch.randn((r, K), generator=g, device=dev) * 0.01).to(torch.bfloat16)
+    g.manual_seed(4_007)
+    B = (torch.randn((N, r), generator=g, device=dev) * 0.01).to(torch.bfloat16)
+    out = torch.empty((N, K), dtype=torch.bfloat16, device=dev)
+    for _ in range(3):
+        nf4.nf4_lora_merge(W, A, B, 2.0, out=out)
+    torch.cuda.synchronize()
+    t = EventTimer(torch, stream)
+    for _ in range(20):
+        s = t.start()
+        nf4.nf4_lora_merge(W, A, B, 2.0, out=out)
+        t.stop(s)
+    torch.cuda.synchronize()
+    us = t.median_us()
+    sb = step_bytes(N, K)
+    nbytes = sb["gemv"] - 2 * K - 2 * N + 2 * N * K + 2 * r * (N + K)  # NF4 + scales in, bf16 out, adapters
+    flops = 2.0 * r * N * K
+    del W, out
+    return {"lora_merge": {
+        "workload": "W 14336x4096 NF4+DQ + s.B.A (r=16, s=2) -> dense bf16, float64 rank-16 sums",
+        "us": round(us, 1),
+        "GBps": round(nbytes / (us * 1e-6) / 1e9, 1),
+        "frac_hbm_peak": round(nbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+        "fp64_TFLOPs": round(flops / (us * 1e-6) / 1e12, 2),
+        "frac_fp64_vector_peak": round(flops / (us * 1e-6) / 1e12 / FP64_VECTOR_PEAK_TFLOPS, 4),
+    }}
 
 
 def leg_stack_70b(torch, nf4, syn, dev, stream, EventTimer, layers=80, gemv_passes=20):

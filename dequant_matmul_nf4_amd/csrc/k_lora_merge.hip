@@ -19,9 +19,10 @@
 //
 // Layout: a workgroup of 256 threads covers kRows consecutive rows (grid x)
 // and 2048 columns (grid y); each thread owns 8 consecutive columns of those
-// rows (16 bytes of output per row).  For each j the thread loads A[j][8 columns] once and
-// updates its kRows x 8 float64 sums; B[n][j] is the same for the whole
-// workgroup.  The work is float64 arithmetic (r multiply-adds per output
+// rows (16 bytes of output per row).  For each j the thread loads
+// A[j][8 columns] once (one j ahead of its use) and updates its kRows x 8
+// float64 sums; the workgroup's kRows rows of B sit in LDS and are read as
+// broadcasts.  The work is float64 arithmetic (r multiply-adds per output
 // value) next to 0.52 bytes read and 2 bytes written per value.
 #include "nf4_device.h"
 
@@ -59,20 +60,30 @@ __global__ __launch_bounds__(kMergeThreads) void k_lora_merge(const uint8_t* __r
                                                               const uint16_t* __restrict__ lb, int r, float scale,
                                                               uint16_t* __restrict__ out, Codebook cb) {
   __shared__ float lv[16];
-  if (threadIdx.x < 16) lv[threadIdx.x] = cb.level[threadIdx.x];
-  __syncthreads();
+  __shared__ uint16_t bsh[kRows * 64];  // B[n0 + i][j] at i * 64 + j
   const int64_t k0 = static_cast<int64_t>(blockIdx.y) * kColsPerWg + 8 * static_cast<int64_t>(threadIdx.x);
   const int64_t n0 = static_cast<int64_t>(blockIdx.x) * kRows;
-  if (k0 >= cols) return;  // cols % 8 == 0: a thread's 8 columns are all in range or all out
   const int nr = static_cast<int>(rows - n0 < kRows ? rows - n0 : kRows);
+  if (threadIdx.x < 16) lv[threadIdx.x] = cb.level[threadIdx.x];
+  for (int t = threadIdx.x; t < kRows * r; t += kMergeThreads) {
+    const int i = t / r, j = t - (t / r) * r;
+    const int64_t n = n0 + (i < nr ? i : nr - 1);  // rows past the end repeat the last (never stored)
+    bsh[i * 64 + j] = lb[n * r + j];
+  }
+  __syncthreads();
+  if (k0 >= cols) return;  // cols % 8 == 0: a thread's 8 columns are all in range or all out
 
   double acc[kRows][8];
 #pragma unroll
   for (int i = 0; i < kRows; ++i)
 #pragma unroll
     for (int c = 0; c < 8; ++c) acc[i][c] = 0.0;
+  // A[j][8 columns] is loaded one j ahead of its use (clamped at the end)
+  const uint16_t* ap = la + k0;
+  uint4 a_next = *reinterpret_cast<const uint4*>(ap);
   for (int j = 0; j < r; ++j) {
-    const uint4 a4 = *reinterpret_cast<const uint4*>(la + static_cast<int64_t>(j) * cols + k0);
+    const uint4 a4 = a_next;
+    a_next = *reinterpret_cast<const uint4*>(ap + static_cast<int64_t>(j + 1 < r ? j + 1 : j) * cols);
     const uint32_t aw[4] = {a4.x, a4.y, a4.z, a4.w};
     double a[8];
 #pragma unroll
@@ -82,8 +93,7 @@ __global__ __launch_bounds__(kMergeThreads) void k_lora_merge(const uint8_t* __r
     }
 #pragma unroll
     for (int i = 0; i < kRows; ++i) {
-      const int64_t n = n0 + (i < nr ? i : nr - 1);  // rows past the end repeat the last (never stored)
-      const double b = static_cast<double>(__uint_as_float(static_cast<uint32_t>(lb[n * r + j]) << 16));
+      const double b = static_cast<double>(__uint_as_float(static_cast<uint32_t>(bsh[i * 64 + j]) << 16));
 #pragma unroll
       for (int c = 0; c < 8; ++c) acc[i][c] = fma(b, a[c], acc[i][c]);
     }
