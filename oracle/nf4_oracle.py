@@ -289,6 +289,32 @@ def matmul_ref(x: np.ndarray, w_deq: np.ndarray, lora_a=None, lora_b=None, lora_
     return y
 
 
+def backward_ref(dy: np.ndarray, w_deq: np.ndarray, x=None, lora_a=None, lora_b=None, lora_scale: float = 0.0):
+    """Gradients of Y = X . W^T + s . (X . A^T) . B^T with the base W frozen,
+    all in float64 ([TUT] "QLoRA: Fine-Tuning a 4-bit Model": the 4-bit base
+    stays frozen and the gradients flow through it to the adapters):
+
+        dX = dY . W + s . (dY . B) . A
+        dA = s . (dY . B)^T . X        dB = s . dY^T . (X . A^T)
+
+    dy: [M, N], w_deq: [N, K], x: [M, K], lora_a: [r, K], lora_b: [N, r].
+    Returns dX, and (dA, dB) when the adapters are given."""
+    dy64 = np.asarray(dy, dtype=np.float64)
+    dx = dy64 @ np.asarray(w_deq, dtype=np.float64)
+    if lora_a is None:
+        return dx, None, None
+    a64 = np.asarray(lora_a, dtype=np.float64)
+    b64 = np.asarray(lora_b, dtype=np.float64)
+    u = float(lora_scale) * (dy64 @ b64)
+    dx = dx + u @ a64
+    da = db = None
+    if x is not None:
+        x64 = np.asarray(x, dtype=np.float64)
+        da = u.T @ x64
+        db = float(lora_scale) * (dy64.T @ (x64 @ a64.T))
+    return dx, da, db
+
+
 def rel_frobenius(y, y_ref) -> float:
     y = np.asarray(y, dtype=np.float64)
     y_ref = np.asarray(y_ref, dtype=np.float64)

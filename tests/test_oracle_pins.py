@@ -486,3 +486,44 @@ def test_lora_merge_is_the_rounded_exact_value():
                 Fraction(float(b[n, j])) * Fraction(float(a[j, k])) for j in range(r))
             assert int(got_b[n, k]) == _bf16_bits_of(_round_exact(x, 8, -126), x < 0)
             assert int(got_h[n, k]) == _f16_bits_of(_round_exact(x, 11, -14), x < 0)
+
+
+# ------------------------------------------------------ NEXT-1 backward reference
+
+def test_backward_ref_is_the_gradient_of_the_forward():
+    """backward_ref against the forward reference by central differences
+    (the forward is linear in X, A and B, so the difference quotient of a
+    scalar loss <dY, Y> is exact up to float64 rounding), and against brute
+    force loops on a tiny case."""
+    rng = np.random.default_rng(21)
+    m, n, k, r, s = 3, 5, 4, 2, 1.5
+    x = rng.standard_normal((m, k))
+    w = rng.standard_normal((n, k))
+    a = rng.standard_normal((r, k))
+    b = rng.standard_normal((n, r))
+    dy = rng.standard_normal((m, n))
+    dx, da, db = oracle.backward_ref(dy, w, x, a, b, s)
+
+    def loss(xx, aa, bb):
+        return float(np.sum(dy * oracle.matmul_ref(xx, w, aa, bb, s)))
+
+    h = 1e-3
+    for arr, grad in ((x, dx), (a, da), (b, db)):
+        num = np.zeros_like(arr)
+        for idx in np.ndindex(arr.shape):
+            p, q = arr.copy(), arr.copy()
+            p[idx] += h
+            q[idx] -= h
+            args_p = [p if arr is t else t for t in (x, a, b)]
+            args_q = [q if arr is t else t for t in (x, a, b)]
+            num[idx] = (loss(*args_p) - loss(*args_q)) / (2 * h)
+        assert np.allclose(num, grad, rtol=1e-9, atol=1e-9)
+    # brute force dX
+    bf = np.zeros((m, k))
+    for i in range(m):
+        for kk in range(k):
+            bf[i, kk] = sum(dy[i, j] * w[j, kk] for j in range(n)) + s * sum(
+                dy[i, j] * b[j, t] * a[t, kk] for j in range(n) for t in range(r))
+    assert np.allclose(bf, dx, rtol=1e-12, atol=1e-12)
+    dx0, da0, db0 = oracle.backward_ref(dy, w)
+    assert da0 is None and db0 is None and np.allclose(dx0, dy @ w)
