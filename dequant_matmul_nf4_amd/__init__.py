@@ -23,7 +23,8 @@ BLOCKSIZE, BLOCKSIZE2 = 64, 256
 
 EXPORTS = (
     "nf4_last_error", "nf4_codebook", "nf4_quantize", "nf4_double_quant_workspace",
-    "nf4_double_quant", "nf4_dequantize", "nf4_gemv", "nf4_gemm_workspace", "nf4_gemm", "nf4_lora_merge",
+    "nf4_double_quant", "nf4_dequantize", "nf4_gemv", "nf4_gemm_workspace", "nf4_gemm", "nf4_gemm_dx_workspace",
+    "nf4_gemm_dx", "nf4_lora_merge",
 )
 
 
@@ -65,6 +66,8 @@ def lib() -> ctypes.CDLL:
         "nf4_gemv": (ctypes.c_int, [wp, vp, i64, vp, ctypes.c_int, vp]),
         "nf4_gemm_workspace": (sz, [i64, i64, i32]),
         "nf4_gemm": (ctypes.c_int, [wp, vp, i64, vp, vp, vp, i32, ctypes.c_float, vp, sz, vp]),
+        "nf4_gemm_dx_workspace": (sz, [i64, i64, i32]),
+        "nf4_gemm_dx": (ctypes.c_int, [wp, vp, i64, vp, vp, vp, i32, ctypes.c_float, vp, sz, vp]),
         "nf4_lora_merge": (ctypes.c_int, [wp, vp, vp, i32, ctypes.c_float, vp, ctypes.c_int, vp]),
     }
     for name, (res, args) in sig.items():
@@ -96,6 +99,10 @@ def nf4_double_quant_workspace(nblocks: int) -> int:
 
 def nf4_gemm_workspace(m: int, rows: int, r: int) -> int:
     return int(lib().nf4_gemm_workspace(m, rows, r))
+
+
+def nf4_gemm_dx_workspace(m: int, rows: int, r: int) -> int:
+    return int(lib().nf4_gemm_dx_workspace(m, rows, r))
 
 
 # ------------------------------------------------------------- torch glue
@@ -259,6 +266,34 @@ def nf4_gemm(w: NF4Weight, x, y=None, lora_a=None, lora_b=None, lora_scale: floa
     _check(lib().nf4_gemm(ctypes.byref(cs), _ptr(x2), m, _ptr(y), _ptr(lora_a), _ptr(lora_b), r,
                           float(lora_scale), _ptr(workspace), wsn, _stream(stream)))
     return y
+
+
+def nf4_gemm_dx(w: NF4Weight, dy, dx=None, lora_a=None, lora_b=None, lora_scale: float = 0.0,
+                workspace=None, stream=None):
+    """dx = dy . deq(W) + lora_scale . (dy . B) . A, bf16 in and out."""
+    torch = _torch()
+    dy2 = dy.reshape(-1, w.rows)
+    _need_cuda(dy2, lora_a, lora_b)
+    m = dy2.shape[0]
+    r = 0 if lora_a is None else lora_a.shape[0]
+    if dx is None:
+        dx = torch.empty((m, w.cols), dtype=torch.bfloat16, device=dy.device)
+    _need_cuda(dx)
+    for t in (dy2, dx, lora_a, lora_b):
+        if t is not None and t.dtype != torch.bfloat16:
+            raise TypeError("dy, dx, lora_a and lora_b must be bf16")
+    if dx.numel() != m * w.cols:
+        raise ValueError("dx has the wrong size")
+    if lora_a is not None and (tuple(lora_a.shape) != (r, w.cols) or lora_b is None or tuple(lora_b.shape) != (w.rows, r)):
+        raise ValueError("LoRA shapes must be A [r, cols] and B [rows, r]")
+    wsb = nf4_gemm_dx_workspace(m, w.rows, r)
+    if wsb and workspace is None:
+        workspace = torch.empty(wsb, dtype=torch.uint8, device=dy.device)
+    wsn = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    cs = w.c_struct()
+    _check(lib().nf4_gemm_dx(ctypes.byref(cs), _ptr(dy2), m, _ptr(dx), _ptr(lora_a), _ptr(lora_b), r,
+                             float(lora_scale), _ptr(workspace), wsn, _stream(stream)))
+    return dx
 
 
 def nf4_lora_merge(w: NF4Weight, lora_a, lora_b, lora_scale: float, out=None, out_dtype=None, stream=None):

@@ -210,6 +210,47 @@ int nf4_gemm(const nf4_weight* w, const void* x, int64_t m, void* y, const void*
                   "nf4_gemm");
 }
 
+size_t nf4_gemm_dx_workspace(int64_t m, int64_t rows, int32_t r) {
+  if (m < 1 || rows < 1 || r < 1 || r > 64) return 0;
+  const size_t bytes = nf4i::gemm_dx_workspace(m, rows, r);
+  return (bytes + 255) & ~size_t(255);
+}
+
+int nf4_gemm_dx(const nf4_weight* w, const void* dy, int64_t m, void* dx, const void* lora_a,
+                const void* lora_b, int32_t r, float lora_scale, void* workspace, size_t workspace_bytes,
+                void* stream) {
+  nf4i::Scales sc{};
+  int64_t n = 0;
+  if (int rc = check_weight(w, &sc, &n, "nf4_gemm_dx")) return rc;
+  if (!dy || !dx) return fail(NF4_ERR_NULL, "nf4_gemm_dx: dy and dx are required");
+  if (w->cols % 64)
+    return fail(NF4_ERR_SIZE, "nf4_gemm_dx: cols = %lld is not a multiple of 64", (long long)w->cols);
+  if (w->rows % 8) return fail(NF4_ERR_SIZE, "nf4_gemm_dx: rows = %lld is not a multiple of 8", (long long)w->rows);
+  if (m < 1 || m > (int64_t(1) << 31)) return fail(NF4_ERR_SIZE, "nf4_gemm_dx: m = %lld out of range", (long long)m);
+  if ((lora_a == nullptr) != (lora_b == nullptr))
+    return fail(NF4_ERR_NULL, "nf4_gemm_dx: lora_a and lora_b must both be NULL or both be set");
+  if (lora_a) {
+    if (r < 1 || r > 64) return fail(NF4_ERR_SIZE, "nf4_gemm_dx: LoRA rank r = %d out of range 1..64", (int)r);
+    if (!std::isfinite(lora_scale)) return fail(NF4_ERR_SIZE, "nf4_gemm_dx: lora_scale is not finite");
+    if (!aligned(lora_a, 16) || !aligned(lora_b, 16))
+      return fail(NF4_ERR_ALIGN, "nf4_gemm_dx: lora_a and lora_b must be 16-byte aligned");
+    const size_t need = nf4_gemm_dx_workspace(m, w->rows, r);
+    if (!workspace || workspace_bytes < need)
+      return fail(NF4_ERR_WORKSPACE, "nf4_gemm_dx: workspace needs %zu bytes", need);
+    if (!aligned(workspace, 256)) return fail(NF4_ERR_ALIGN, "nf4_gemm_dx: workspace must be 256-byte aligned");
+  } else if (r != 0) {
+    return fail(NF4_ERR_SIZE, "nf4_gemm_dx: r must be 0 without LoRA matrices");
+  }
+  if (!aligned(dy, 16) || !aligned(dx, 16))
+    return fail(NF4_ERR_ALIGN, "nf4_gemm_dx: dy and dx must be 16-byte aligned");
+  if (int rc = check_device()) return rc;
+  return launched(nf4i::launch_gemm_dx(w->packed, w->rows, w->cols, sc, static_cast<const uint16_t*>(dy), m,
+                                       static_cast<uint16_t*>(dx), static_cast<const uint16_t*>(lora_a),
+                                       static_cast<const uint16_t*>(lora_b), lora_a ? r : 0, lora_scale,
+                                       static_cast<uint16_t*>(workspace), as_stream(stream)),
+                  "nf4_gemm_dx");
+}
+
 int nf4_lora_merge(const nf4_weight* w, const void* lora_a, const void* lora_b, int32_t r, float lora_scale,
                    void* out, int out_dtype, void* stream) {
   nf4i::Scales sc{};

@@ -424,13 +424,15 @@ __global__ __launch_bounds__(kThreads) void k_gemm(GemmArgs a) {
   }
 }
 
+}  // namespace
+
 // u[m][.] = (hi(sT) | lo(sT) | 0) with T = x . A^T in float32, one
 // workgroup per row of x: the row's extra columns are zeroed, then each wave
 // computes rank entries j (lanes split K, shuffle reduction) and writes
 // hi = bf16(s T) at column j and lo = bf16(s T - hi) at column r_pad + j.
-__global__ __launch_bounds__(256) void k_lora_prep(const uint16_t* __restrict__ x, const uint16_t* __restrict__ la,
-                                                   int64_t cols, int r, int r_pad, int kl, float scale,
-                                                   uint16_t* __restrict__ u) {
+static __global__ __launch_bounds__(256) void k_lora_prep(const uint16_t* __restrict__ x,
+                                                          const uint16_t* __restrict__ la, int64_t cols, int r,
+                                                          int r_pad, int kl, float scale, uint16_t* __restrict__ u) {
   const int64_t m = blockIdx.x;
   uint16_t* urow = u + m * kl;
   if (threadIdx.x < kl) urow[threadIdx.x] = 0;
@@ -461,12 +463,19 @@ __global__ __launch_bounds__(256) void k_lora_prep(const uint16_t* __restrict__ 
   }
 }
 
-}  // namespace
-
 size_t gemm_lora_cols(int r) {
   if (r <= 0) return 0;
   const int r_pad = (r + 15) / 16 * 16;
   return static_cast<size_t>((2 * r_pad + kBK - 1) / kBK * kBK);
+}
+
+hipError_t launch_lora_u(const uint16_t* x, const uint16_t* a, int64_t m, int64_t len, int r, float scale,
+                         uint16_t* u, hipStream_t s) {
+  if (m > 0x7FFFFFFF) return hipErrorInvalidValue;
+  const int r_pad = (r + 15) / 16 * 16;
+  hipLaunchKernelGGL(k_lora_prep, dim3(static_cast<unsigned>(m)), dim3(256), 0, s, x, a, len, r, r_pad,
+                     static_cast<int>(gemm_lora_cols(r)), scale, u);
+  return hipSuccess;
 }
 
 hipError_t launch_gemm(const uint8_t* packed, int64_t rows, int64_t cols, Scales sc, const uint16_t* x,
@@ -481,9 +490,7 @@ hipError_t launch_gemm(const uint8_t* packed, int64_t rows, int64_t cols, Scales
     a.kl = static_cast<int>(gemm_lora_cols(r));
     a.u = u_ws;
     a.lb = lora_b;
-    if (m > 0x7FFFFFFF) return hipErrorInvalidValue;
-    hipLaunchKernelGGL(k_lora_prep, dim3(static_cast<unsigned>(m)), dim3(256), 0, s, x, lora_a, cols, r, a.r_pad,
-                       a.kl, lora_scale, u_ws);
+    if (hipError_t e = launch_lora_u(x, lora_a, m, cols, r, lora_scale, u_ws, s)) return e;
   }
   const int64_t tiles = ((rows + kBN - 1) / kBN) * ((m + kBM - 1) / kBM);
   const int64_t cus = device_cus();

@@ -67,10 +67,21 @@ hipError_t launch_gemv(const uint8_t* packed, int64_t rows, int64_t cols, Scales
 // Extra K columns the GEMM uses for a LoRA term of rank r (0 without one);
 // the workspace holds m rows of that many bf16 values.
 size_t gemm_lora_cols(int r);
+// u[i][.] = (bf16(s T[i][j]) for j < r | bf16(s T - hi) at r_pad + j | 0) with
+// T[i][j] = sum_k x[i][k] a[j][k] formed in float32, for the m rows of
+// x [m][len] and the r rows of a [r][len] (len % 8 == 0); each row of u holds
+// gemm_lora_cols(r) bf16 values, r_pad = r rounded up to 16.
+hipError_t launch_lora_u(const uint16_t* x, const uint16_t* a, int64_t m, int64_t len, int r, float scale,
+                         uint16_t* u, hipStream_t s);
 hipError_t launch_gemm(const uint8_t* packed, int64_t rows, int64_t cols, Scales sc,
                        const uint16_t* x, int64_t m, uint16_t* y, const uint16_t* lora_a,
                        const uint16_t* lora_b, int r, float lora_scale, uint16_t* u_ws,
                        hipStream_t s);
+// Extra reduction indices and workspace of the input-gradient GEMM.
+size_t gemm_dx_workspace(int64_t m, int64_t rows, int r);
+hipError_t launch_gemm_dx(const uint8_t* packed, int64_t rows, int64_t cols, Scales sc, const uint16_t* dy,
+                          int64_t m, uint16_t* dx, const uint16_t* lora_a, const uint16_t* lora_b, int r,
+                          float lora_scale, uint16_t* ws, hipStream_t s);
 hipError_t launch_lora_merge(const uint8_t* packed, int64_t rows, int64_t cols, Scales sc, const uint16_t* lora_a,
                              const uint16_t* lora_b, int r, float scale, uint16_t* out, int out_f16,
                              hipStream_t s);

@@ -164,6 +164,32 @@ int nf4_gemm(const nf4_weight* w, const void* x, int64_t m, void* y,
              const void* lora_a, const void* lora_b, int32_t r, float lora_scale,
              void* workspace, size_t workspace_bytes, void* stream);
 
+/* Bytes of device workspace nf4_gemm_dx needs for m rows of dy, a weight of
+ * `rows` rows and LoRA rank r (0 when r == 0). */
+size_t nf4_gemm_dx_workspace(int64_t m, int64_t rows, int32_t r);
+
+/* Input gradient through the frozen 4-bit base for QLoRA training (tutorial
+ * page "QLoRA: Fine-Tuning a 4-bit Model": the base stays frozen and the
+ * gradients pass through it to the low-rank adapters; tool page "How it
+ * works", Step 5: blocks are expanded to 16-bit for the matrix hardware):
+ *   dx = dy . deq(W) + lora_scale . (dy . B) . A
+ * the backward of nf4_gemm's y = x . deq(W)^T + lora_scale . (x . A^T) . B^T
+ * with respect to x.
+ *   w      : the NF4 weight [rows][cols] (either scale form); cols % 64 == 0,
+ *            rows % 8 == 0.
+ *   dy     : bf16 [m][rows], 16-byte aligned, 1 <= m <= 2^31.
+ *   dx     : bf16 [m][cols], 16-byte aligned, not overlapping dy.
+ *   lora_a : bf16 [r][cols] and lora_b : bf16 [rows][r], both NULL (then r
+ *            must be 0) or both set with 1 <= r <= 64; 16-byte aligned.
+ *   workspace: at least nf4_gemm_dx_workspace(m, rows, r) bytes, 256-byte
+ *            aligned (may be NULL when that is 0); overwritten.
+ * W is dequantized to bf16 exactly as nf4_dequantize does; products are
+ * accumulated in float32 and dx is rounded once to bf16.  The adapter term
+ * forms U = lora_scale . dy . B in float32 and carries it as two bf16 parts. */
+int nf4_gemm_dx(const nf4_weight* w, const void* dy, int64_t m, void* dx,
+                const void* lora_a, const void* lora_b, int32_t r, float lora_scale,
+                void* workspace, size_t workspace_bytes, void* stream);
+
 /* LoRA merge -- tutorial page, "Merging LoRA Adapters After Fine-Tuning":
  * after training the adapters are folded into one dense 16-bit copy of the
  * base, which needs the base dequantized first (tool page, "Practical

@@ -15,6 +15,7 @@ Workloads (weights are row-major [out_features, in_features]):
       bf16 ~ N(0, 0.02); X bf16 [M, K] ~ N(0, 1) for M in (1, 4, 16).
   C4  X bf16 [4096, 4096] ~ N(0, 1); W bf16 [14336, 4096] ~ N(0, 0.02);
       LoRA A bf16 [16, 4096], B bf16 [14336, 16] ~ N(0, 0.01); alpha 32.
+      Its backward takes dY bf16 [4096, 14336] ~ N(0, 1).
   C5  70B-shaped layer: q, o [8192, 8192]; k, v [1024, 8192]; gate, up
       [28672, 8192]; down [8192, 28672]; bf16 ~ N(0, 0.02).
 
@@ -23,7 +24,7 @@ standard deviation in float32, outliers multiplied by 20 in float32 at
 round(0.001 n) distinct positions drawn without replacement, then one
 round-to-nearest-even cast to bf16.  Seeds are 1000 * workload + tensor id
 (0 weight, 1/2 further MLP weights, 5 activations, 6 LoRA A, 7 LoRA B,
-9 outlier positions).  C5 is drawn on the device with torch generators seeded
+8 output gradients, 9 outlier positions).  C5 is drawn on the device with torch generators seeded
 5_000_000 + 10 * layer + matrix index (q, k, v, o, gate, up, down = 0..6).
 """
 
@@ -31,7 +32,7 @@ from __future__ import annotations
 
 import numpy as np
 
-SEED_W, SEED_W1, SEED_W2, SEED_X, SEED_A, SEED_B, SEED_OUTLIER = 0, 1, 2, 5, 6, 7, 9
+SEED_W, SEED_W1, SEED_W2, SEED_X, SEED_A, SEED_B, SEED_DY, SEED_OUTLIER = 0, 1, 2, 5, 6, 7, 8, 9
 
 C3_SHAPES = {"gate": (14336, 4096), "up": (14336, 4096), "down": (4096, 14336)}
 C5_SHAPES = {
@@ -115,6 +116,11 @@ def c4_inputs(m: int = 4096, n: int = 14336, k: int = 4096, r: int = 16):
         "alpha": 32.0,
         "r": r,
     }
+
+
+def c4_grad(m: int = 4096, n: int = 14336):
+    """The output gradient dY [m, n] of the C4 layer (bf16 ~ N(0, 1))."""
+    return to_bf16(normal_f32((m, n), 1.0, seed(4, SEED_DY)))
 
 
 def c5_weight_device(layer: int, name: str, device="cuda"):

@@ -66,3 +66,25 @@ def oracle_rows_dequant_bf16(w_rows_f32: np.ndarray, row_idx, cols: int, absmax_
         bits = oracle.dequantize(packed, cols, absmax=a, out="bf16")
         out[i] = oracle.bf16_bits_to_f32(bits)
     return out
+
+
+def oracle_blocks_dequant_bf16(w_f32: np.ndarray, block_cols, absmax_all: np.ndarray, dq: bool):
+    """Oracle bf16 dequantized values of whole 64-column blocks of a weight
+    [rows, cols] (cols % 64 == 0): returns [rows, len(block_cols) * 64], the
+    blocks in the order given.  Each block quantizes on its own; with double
+    quantization its scale comes from the oracle's double_quant over the
+    absmax of the whole matrix."""
+    rows, cols = w_f32.shape
+    bpr = cols // 64
+    bc = np.asarray(block_cols, dtype=np.int64)
+    sub = np.stack([w_f32[:, 64 * b:64 * b + 64] for b in bc], axis=1)  # [rows, nb, 64]
+    packed, absmax = oracle.quantize(np.ascontiguousarray(sub).reshape(-1))
+    if dq:
+        q, s2, mean = oracle.double_quant(absmax_all)
+        a_hat_all = oracle.dequant_scales(q, s2, mean)
+        idx = (np.arange(rows, dtype=np.int64)[:, None] * bpr + bc[None, :]).reshape(-1)
+        a = a_hat_all[idx]
+    else:
+        a = absmax
+    bits = oracle.dequantize(packed, sub.size, absmax=a, out="bf16")
+    return oracle.bf16_bits_to_f32(bits).reshape(rows, len(bc) * 64)

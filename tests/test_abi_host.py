@@ -56,6 +56,10 @@ def test_workspace_sizes(L):
     assert nf4.nf4_gemm_workspace(4096, 14336, 0) == 0
     assert nf4.nf4_gemm_workspace(4096, 14336, 16) >= 4096 * 32 * 2
     assert nf4.nf4_gemm_workspace(4096, 14336, 16) % 256 == 0
+    assert nf4.nf4_gemm_dx_workspace(4096, 14336, 0) == 0
+    # U (m x 2 r_pad bf16, rounded up to 64) and B transposed (r x rows bf16)
+    assert nf4.nf4_gemm_dx_workspace(4096, 14336, 16) >= (4096 * 64 + 16 * 14336) * 2
+    assert nf4.nf4_gemm_dx_workspace(4096, 14336, 16) % 256 == 0
 
 
 def test_struct_layout():
@@ -117,6 +121,21 @@ CASES = [
     ("gemm workspace null", lambda L: L.nf4_gemm(ctypes.byref(_w()), A, 4, A, A, A, 16, 2.0, None, 4096, None), nf4.NF4_ERR_WORKSPACE),
     ("gemm scale nan", lambda L: L.nf4_gemm(ctypes.byref(_w()), A, 4, A, A, A, 16, float("nan"), A, 4096, None), nf4.NF4_ERR_SIZE),
     ("gemm misaligned y", lambda L: L.nf4_gemm(ctypes.byref(_w()), A, 4, A + 2, None, None, 0, 0.0, None, 0, None), nf4.NF4_ERR_ALIGN),
+    ("dx null weight", lambda L: L.nf4_gemm_dx(None, A, 4, A, None, None, 0, 0.0, None, 0, None), nf4.NF4_ERR_NULL),
+    ("dx null dy", lambda L: L.nf4_gemm_dx(ctypes.byref(_w()), None, 4, A, None, None, 0, 0.0, None, 0, None), nf4.NF4_ERR_NULL),
+    ("dx null dx", lambda L: L.nf4_gemm_dx(ctypes.byref(_w()), A, 4, None, None, None, 0, 0.0, None, 0, None), nf4.NF4_ERR_NULL),
+    ("dx cols%64", lambda L: L.nf4_gemm_dx(ctypes.byref(_w(cols=96)), A, 4, A, None, None, 0, 0.0, None, 0, None), nf4.NF4_ERR_SIZE),
+    ("dx rows%8", lambda L: L.nf4_gemm_dx(ctypes.byref(_w(rows=12)), A, 4, A, None, None, 0, 0.0, None, 0, None), nf4.NF4_ERR_SIZE),
+    ("dx m=0", lambda L: L.nf4_gemm_dx(ctypes.byref(_w()), A, 0, A, None, None, 0, 0.0, None, 0, None), nf4.NF4_ERR_SIZE),
+    ("dx half lora", lambda L: L.nf4_gemm_dx(ctypes.byref(_w()), A, 4, A, None, A, 16, 2.0, A, WS, None), nf4.NF4_ERR_NULL),
+    ("dx rank 65", lambda L: L.nf4_gemm_dx(ctypes.byref(_w()), A, 4, A, A, A, 65, 2.0, A, WS, None), nf4.NF4_ERR_SIZE),
+    ("dx r without lora", lambda L: L.nf4_gemm_dx(ctypes.byref(_w()), A, 4, A, None, None, 2, 0.0, None, 0, None), nf4.NF4_ERR_SIZE),
+    ("dx scale inf", lambda L: L.nf4_gemm_dx(ctypes.byref(_w()), A, 4, A, A, A, 16, float("-inf"), A, WS, None), nf4.NF4_ERR_SIZE),
+    ("dx workspace small", lambda L: L.nf4_gemm_dx(ctypes.byref(_w()), A, 4, A, A, A, 16, 2.0, A, 64, None), nf4.NF4_ERR_WORKSPACE),
+    ("dx workspace null", lambda L: L.nf4_gemm_dx(ctypes.byref(_w()), A, 4, A, A, A, 16, 2.0, None, WS, None), nf4.NF4_ERR_WORKSPACE),
+    ("dx misaligned workspace", lambda L: L.nf4_gemm_dx(ctypes.byref(_w()), A, 4, A, A, A, 16, 2.0, A + 16, WS, None), nf4.NF4_ERR_ALIGN),
+    ("dx misaligned dy", lambda L: L.nf4_gemm_dx(ctypes.byref(_w()), A + 2, 4, A, None, None, 0, 0.0, None, 0, None), nf4.NF4_ERR_ALIGN),
+    ("dx misaligned a", lambda L: L.nf4_gemm_dx(ctypes.byref(_w()), A, 4, A, A + 8, A, 16, 2.0, A, WS, None), nf4.NF4_ERR_ALIGN),
     ("merge null weight", lambda L: L.nf4_lora_merge(None, A, A, 16, 2.0, A, 1, None), nf4.NF4_ERR_NULL),
     ("merge null a", lambda L: L.nf4_lora_merge(ctypes.byref(_w()), None, A, 16, 2.0, A, 1, None), nf4.NF4_ERR_NULL),
     ("merge null out", lambda L: L.nf4_lora_merge(ctypes.byref(_w()), A, A, 16, 2.0, None, 1, None), nf4.NF4_ERR_NULL),
