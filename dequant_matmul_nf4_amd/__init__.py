@@ -24,7 +24,7 @@ BLOCKSIZE, BLOCKSIZE2 = 64, 256
 EXPORTS = (
     "nf4_last_error", "nf4_codebook", "nf4_quantize", "nf4_double_quant_workspace",
     "nf4_double_quant", "nf4_dequantize", "nf4_gemv", "nf4_gemm_workspace", "nf4_gemm", "nf4_gemm_dx_workspace",
-    "nf4_gemm_dx", "nf4_lora_merge",
+    "nf4_gemm_dx", "nf4_lora_grads_workspace", "nf4_lora_grads", "nf4_lora_merge",
 )
 
 
@@ -68,6 +68,8 @@ def lib() -> ctypes.CDLL:
         "nf4_gemm": (ctypes.c_int, [wp, vp, i64, vp, vp, vp, i32, ctypes.c_float, vp, sz, vp]),
         "nf4_gemm_dx_workspace": (sz, [i64, i64, i32]),
         "nf4_gemm_dx": (ctypes.c_int, [wp, vp, i64, vp, vp, vp, i32, ctypes.c_float, vp, sz, vp]),
+        "nf4_lora_grads_workspace": (sz, [i64, i64, i64, i32]),
+        "nf4_lora_grads": (ctypes.c_int, [vp, vp, i64, i64, i64, vp, vp, i32, ctypes.c_float, vp, vp, vp, sz, vp]),
         "nf4_lora_merge": (ctypes.c_int, [wp, vp, vp, i32, ctypes.c_float, vp, ctypes.c_int, vp]),
     }
     for name, (res, args) in sig.items():
@@ -103,6 +105,10 @@ def nf4_gemm_workspace(m: int, rows: int, r: int) -> int:
 
 def nf4_gemm_dx_workspace(m: int, rows: int, r: int) -> int:
     return int(lib().nf4_gemm_dx_workspace(m, rows, r))
+
+
+def nf4_lora_grads_workspace(m: int, rows: int, cols: int, r: int) -> int:
+    return int(lib().nf4_lora_grads_workspace(m, rows, cols, r))
 
 
 # ------------------------------------------------------------- torch glue
@@ -294,6 +300,40 @@ def nf4_gemm_dx(w: NF4Weight, dy, dx=None, lora_a=None, lora_b=None, lora_scale:
     _check(lib().nf4_gemm_dx(ctypes.byref(cs), _ptr(dy2), m, _ptr(dx), _ptr(lora_a), _ptr(lora_b), r,
                              float(lora_scale), _ptr(workspace), wsn, _stream(stream)))
     return dx
+
+
+def nf4_lora_grads(x, dy, lora_a, lora_b, lora_scale: float, da=None, db=None, want=("da", "db"),
+                   workspace=None, stream=None):
+    """(dA, dB) of the adapters: dA = s (dy B)^T x [r, cols], dB = s dy^T (x A^T)
+    [rows, r], float32; a gradient not in `want` (and not given) is None."""
+    torch = _torch()
+    r, cols = lora_a.shape
+    rows = lora_b.shape[0]
+    x2 = x.reshape(-1, cols)
+    dy2 = dy.reshape(-1, rows)
+    _need_cuda(x2, dy2, lora_a, lora_b)
+    m = x2.shape[0]
+    if dy2.shape[0] != m or tuple(lora_b.shape) != (rows, r):
+        raise ValueError("shapes must be x [m, cols], dy [m, rows], A [r, cols], B [rows, r]")
+    for t in (x2, dy2, lora_a, lora_b):
+        if t.dtype != torch.bfloat16:
+            raise TypeError("x, dy, lora_a and lora_b must be bf16")
+    if da is None and "da" in want:
+        da = torch.empty((r, cols), dtype=torch.float32, device=x.device)
+    if db is None and "db" in want:
+        db = torch.empty((rows, r), dtype=torch.float32, device=x.device)
+    for t, shape in ((da, (r, cols)), (db, (rows, r))):
+        if t is not None:
+            _need_cuda(t)
+            if t.dtype != torch.float32 or t.numel() != shape[0] * shape[1]:
+                raise ValueError("da and db must be float32 [r, cols] and [rows, r]")
+    wsb = nf4_lora_grads_workspace(m, rows, cols, r)
+    if workspace is None:
+        workspace = torch.empty(max(wsb, 1), dtype=torch.uint8, device=x.device)
+    wsn = workspace.numel() * workspace.element_size()
+    _check(lib().nf4_lora_grads(_ptr(x2), _ptr(dy2), m, rows, cols, _ptr(lora_a), _ptr(lora_b), r,
+                                float(lora_scale), _ptr(da), _ptr(db), _ptr(workspace), wsn, _stream(stream)))
+    return da, db
 
 
 def nf4_lora_merge(w: NF4Weight, lora_a, lora_b, lora_scale: float, out=None, out_dtype=None, stream=None):

@@ -251,6 +251,38 @@ int nf4_gemm_dx(const nf4_weight* w, const void* dy, int64_t m, void* dx, const 
                   "nf4_gemm_dx");
 }
 
+size_t nf4_lora_grads_workspace(int64_t m, int64_t rows, int64_t cols, int32_t r) {
+  if (m < 1 || rows < 1 || cols < 1 || r < 1 || r > 64) return 0;
+  return nf4i::lora_grads_workspace(m, rows, cols, r);
+}
+
+int nf4_lora_grads(const void* x, const void* dy, int64_t m, int64_t rows, int64_t cols, const void* lora_a,
+                   const void* lora_b, int32_t r, float lora_scale, float* da, float* db, void* workspace,
+                   size_t workspace_bytes, void* stream) {
+  if (!x || !dy || !lora_a || !lora_b)
+    return fail(NF4_ERR_NULL, "nf4_lora_grads: x, dy, lora_a and lora_b are required");
+  if (!da && !db) return fail(NF4_ERR_NULL, "nf4_lora_grads: at least one of da and db is required");
+  if (m < 1 || m > (int64_t(1) << 31)) return fail(NF4_ERR_SIZE, "nf4_lora_grads: m = %lld out of range", (long long)m);
+  if (rows < 8 || rows > kMaxN || rows % 8 || cols < 8 || cols > kMaxN || cols % 8)
+    return fail(NF4_ERR_SIZE, "nf4_lora_grads: rows = %lld and cols = %lld must be positive multiples of 8",
+                (long long)rows, (long long)cols);
+  if (r < 1 || r > 64) return fail(NF4_ERR_SIZE, "nf4_lora_grads: LoRA rank r = %d out of range 1..64", (int)r);
+  if (!std::isfinite(lora_scale)) return fail(NF4_ERR_SIZE, "nf4_lora_grads: lora_scale is not finite");
+  if (!aligned(x, 16) || !aligned(dy, 16) || !aligned(lora_a, 16) || !aligned(lora_b, 16) || !aligned(da, 16) ||
+      !aligned(db, 16))
+    return fail(NF4_ERR_ALIGN, "nf4_lora_grads: x, dy, lora_a, lora_b, da and db must be 16-byte aligned");
+  const size_t need = nf4_lora_grads_workspace(m, rows, cols, r);
+  if (!workspace || workspace_bytes < need)
+    return fail(NF4_ERR_WORKSPACE, "nf4_lora_grads: workspace needs %zu bytes", need);
+  if (!aligned(workspace, 256)) return fail(NF4_ERR_ALIGN, "nf4_lora_grads: workspace must be 256-byte aligned");
+  if (int rc = check_device()) return rc;
+  return launched(nf4i::launch_lora_grads(static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(dy), m, rows,
+                                          cols, static_cast<const uint16_t*>(lora_a),
+                                          static_cast<const uint16_t*>(lora_b), r, lora_scale, da, db, workspace,
+                                          as_stream(stream)),
+                  "nf4_lora_grads");
+}
+
 int nf4_lora_merge(const nf4_weight* w, const void* lora_a, const void* lora_b, int32_t r, float lora_scale,
                    void* out, int out_dtype, void* stream) {
   nf4i::Scales sc{};

@@ -35,7 +35,8 @@
 // LoRA: the low-rank term is folded in as extra K columns,
 //   [x | s T_hi | s T_lo] . [deq(W) | B | B]^T  with T = x . A^T,
 // where s T is split into two bf16 parts (hi = bf16(sT), lo = bf16(sT - hi))
-// by k_lora_prep, so the adapter product keeps about 16 significant bits.
+// by the LoRA prep kernel, so the adapter product keeps about 16 significant
+// bits.
 // Those columns (2 r rounded up to a multiple of 64) run as one or two more
 // K steps with both operands staged in LDS.
 #include "nf4_device.h"
@@ -426,56 +427,10 @@ __global__ __launch_bounds__(kThreads) void k_gemm(GemmArgs a) {
 
 }  // namespace
 
-// u[m][.] = (hi(sT) | lo(sT) | 0) with T = x . A^T in float32, one
-// workgroup per row of x: the row's extra columns are zeroed, then each wave
-// computes rank entries j (lanes split K, shuffle reduction) and writes
-// hi = bf16(s T) at column j and lo = bf16(s T - hi) at column r_pad + j.
-static __global__ __launch_bounds__(256) void k_lora_prep(const uint16_t* __restrict__ x,
-                                                          const uint16_t* __restrict__ la, int64_t cols, int r,
-                                                          int r_pad, int kl, float scale, uint16_t* __restrict__ u) {
-  const int64_t m = blockIdx.x;
-  uint16_t* urow = u + m * kl;
-  if (threadIdx.x < kl) urow[threadIdx.x] = 0;
-  __syncthreads();
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const uint16_t* xr = x + m * cols;
-  for (int j = wave; j < r; j += 4) {
-    const uint16_t* ar = la + static_cast<int64_t>(j) * cols;
-    float s = 0.0f;
-    for (int64_t k = lane * 8; k < cols; k += 64 * 8) {
-      const uint4 xv = *reinterpret_cast<const uint4*>(xr + k);
-      const uint4 av = *reinterpret_cast<const uint4*>(ar + k);
-      const uint32_t xq[4] = {xv.x, xv.y, xv.z, xv.w};
-      const uint32_t aq[4] = {av.x, av.y, av.z, av.w};
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        s = fmaf(__uint_as_float(xq[i] << 16), __uint_as_float(aq[i] << 16), s);
-        s = fmaf(__uint_as_float(xq[i] & 0xFFFF0000u), __uint_as_float(aq[i] & 0xFFFF0000u), s);
-      }
-    }
-    s = wave_sum(s) * scale;
-    if (lane == 0) {
-      const __bf16 hi = static_cast<__bf16>(s);
-      const __bf16 lo = static_cast<__bf16>(s - static_cast<float>(hi));
-      urow[j] = __builtin_bit_cast(uint16_t, hi);
-      urow[r_pad + j] = __builtin_bit_cast(uint16_t, lo);
-    }
-  }
-}
-
 size_t gemm_lora_cols(int r) {
   if (r <= 0) return 0;
   const int r_pad = (r + 15) / 16 * 16;
   return static_cast<size_t>((2 * r_pad + kBK - 1) / kBK * kBK);
-}
-
-hipError_t launch_lora_u(const uint16_t* x, const uint16_t* a, int64_t m, int64_t len, int r, float scale,
-                         uint16_t* u, hipStream_t s) {
-  if (m > 0x7FFFFFFF) return hipErrorInvalidValue;
-  const int r_pad = (r + 15) / 16 * 16;
-  hipLaunchKernelGGL(k_lora_prep, dim3(static_cast<unsigned>(m)), dim3(256), 0, s, x, a, len, r, r_pad,
-                     static_cast<int>(gemm_lora_cols(r)), scale, u);
-  return hipSuccess;
 }
 
 hipError_t launch_gemm(const uint8_t* packed, int64_t rows, int64_t cols, Scales sc, const uint16_t* x,

@@ -262,21 +262,28 @@ __global__ __launch_bounds__(kThr) void k_gemm_dx(DxArgs a) {
   }
 }
 
-// Bt[j][n] = B[n][j], so that the prep reads both of its operands along n.
-__global__ __launch_bounds__(256) void k_transpose_b(const uint16_t* __restrict__ lb, int64_t rows, int r,
-                                                     uint16_t* __restrict__ bt) {
-  const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
-  if (i >= rows * r) return;
-  const int64_t n = i / r, j = i - n * r;
-  bt[j * rows + n] = lb[i];
-}
-
 // Elements of u before Bt in the workspace, rounded up to 256 bytes.
 int64_t u_elems(int64_t m, int r) {
   return (m * static_cast<int64_t>(gemm_lora_cols(r)) + 127) / 128 * 128;
 }
 
 }  // namespace
+
+// Bt[j][n] = B[n][j], so that the prep reads both of its operands along n.
+static __global__ __launch_bounds__(256) void k_transpose_b(const uint16_t* __restrict__ lb, int64_t rows, int r,
+                                                            uint16_t* __restrict__ bt) {
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (i >= rows * r) return;
+  const int64_t n = i / r, j = i - n * r;
+  bt[j * rows + n] = lb[i];
+}
+
+hipError_t launch_transpose_b(const uint16_t* b, int64_t rows, int r, uint16_t* bt, hipStream_t s) {
+  const int64_t nt = rows * r;
+  if ((nt + 255) / 256 > 0x7FFFFFFF) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(k_transpose_b, dim3(static_cast<unsigned>((nt + 255) / 256)), dim3(256), 0, s, b, rows, r, bt);
+  return hipSuccess;
+}
 
 size_t gemm_dx_workspace(int64_t m, int64_t rows, int r) {
   if (r <= 0) return 0;
@@ -290,7 +297,7 @@ hipError_t launch_gemm_dx(const uint8_t* packed, int64_t rows, int64_t cols, Sca
   a.packed = packed; a.rows = rows; a.cols = cols; a.sc = sc; a.dy = dy; a.m = m; a.dx = dx;
   a.cb = codebook();
   const int64_t tiles = ((m + kTm - 1) / kTm) * ((cols + kTk - 1) / kTk);
-  if (tiles > 0x7FFFFFFF || (rows * r + 255) / 256 > 0x7FFFFFFF) return hipErrorInvalidValue;
+  if (tiles > 0x7FFFFFFF) return hipErrorInvalidValue;
   if (r > 0) {
     a.r = r;
     a.r_pad = (r + 15) / 16 * 16;
@@ -298,9 +305,7 @@ hipError_t launch_gemm_dx(const uint8_t* packed, int64_t rows, int64_t cols, Sca
     a.la = lora_a;
     a.u = ws;
     uint16_t* bt = ws + u_elems(m, r);
-    const int64_t nt = rows * r;
-    hipLaunchKernelGGL(k_transpose_b, dim3(static_cast<unsigned>((nt + 255) / 256)), dim3(256), 0, s, lora_b, rows,
-                       r, bt);
+    if (hipError_t e = launch_transpose_b(lora_b, rows, r, bt, s)) return e;
     if (hipError_t e = launch_lora_u(dy, bt, m, rows, r, lora_scale, ws, s)) return e;
   }
   if (sc.absmax) hipLaunchKernelGGL(k_gemm_dx<false>, dim3(static_cast<unsigned>(tiles)), dim3(kThr), 0, s, a);

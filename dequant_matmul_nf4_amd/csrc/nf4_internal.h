@@ -73,6 +73,12 @@ size_t gemm_lora_cols(int r);
 // gemm_lora_cols(r) bf16 values, r_pad = r rounded up to 16.
 hipError_t launch_lora_u(const uint16_t* x, const uint16_t* a, int64_t m, int64_t len, int r, float scale,
                          uint16_t* u, hipStream_t s);
+// The same product kept in float32: t[i][j] = fl32(s T[i][j]) in rows of
+// r_pad floats, zero for j >= r.
+hipError_t launch_lora_t32(const uint16_t* x, const uint16_t* a, int64_t m, int64_t len, int r, float scale,
+                           float* t, hipStream_t s);
+// bt[j][n] = b[n][j] for b [rows][r] bf16.
+hipError_t launch_transpose_b(const uint16_t* b, int64_t rows, int r, uint16_t* bt, hipStream_t s);
 hipError_t launch_gemm(const uint8_t* packed, int64_t rows, int64_t cols, Scales sc,
                        const uint16_t* x, int64_t m, uint16_t* y, const uint16_t* lora_a,
                        const uint16_t* lora_b, int r, float lora_scale, uint16_t* u_ws,
@@ -82,6 +88,11 @@ size_t gemm_dx_workspace(int64_t m, int64_t rows, int r);
 hipError_t launch_gemm_dx(const uint8_t* packed, int64_t rows, int64_t cols, Scales sc, const uint16_t* dy,
                           int64_t m, uint16_t* dx, const uint16_t* lora_a, const uint16_t* lora_b, int r,
                           float lora_scale, uint16_t* ws, hipStream_t s);
+// LoRA gradients (float32 out): da [r][cols], db [rows][r].
+size_t lora_grads_workspace(int64_t m, int64_t rows, int64_t cols, int r);
+hipError_t launch_lora_grads(const uint16_t* x, const uint16_t* dy, int64_t m, int64_t rows, int64_t cols,
+                             const uint16_t* lora_a, const uint16_t* lora_b, int r, float scale, float* da,
+                             float* db, void* ws, hipStream_t s);
 hipError_t launch_lora_merge(const uint8_t* packed, int64_t rows, int64_t cols, Scales sc, const uint16_t* lora_a,
                              const uint16_t* lora_b, int r, float scale, uint16_t* out, int out_f16,
                              hipStream_t s);

@@ -190,6 +190,27 @@ int nf4_gemm_dx(const nf4_weight* w, const void* dy, int64_t m, void* dx,
                 const void* lora_a, const void* lora_b, int32_t r, float lora_scale,
                 void* workspace, size_t workspace_bytes, void* stream);
 
+/* Bytes of device workspace nf4_lora_grads needs (0 for invalid sizes). */
+size_t nf4_lora_grads_workspace(int64_t m, int64_t rows, int64_t cols, int32_t r);
+
+/* Gradients of the low-rank adapters on the frozen base (tutorial page
+ * "QLoRA: Fine-Tuning a 4-bit Model": only the adapters train and their
+ * output is multiplied by a scale factor).  For nf4_gemm's
+ * y = x . deq(W)^T + lora_scale . (x . A^T) . B^T:
+ *   da = lora_scale . (dy . B)^T . x        float32 [r][cols]
+ *   db = lora_scale . dy^T . (x . A^T)      float32 [rows][r]
+ *   x      : bf16 [m][cols], dy : bf16 [m][rows], 1 <= m <= 2^31;
+ *            rows and cols positive multiples of 8.
+ *   lora_a : bf16 [r][cols], lora_b : bf16 [rows][r], 1 <= r <= 64.
+ *   da, db : outputs; either may be NULL to skip it, not both.  Overwritten.
+ *   All arrays 16-byte aligned; workspace at least
+ *   nf4_lora_grads_workspace(m, rows, cols, r) bytes, 256-byte aligned.
+ * The thin products (dy . B and x . A^T) and every sum are formed in float32;
+ * results are deterministic (fixed summation order). */
+int nf4_lora_grads(const void* x, const void* dy, int64_t m, int64_t rows, int64_t cols,
+                   const void* lora_a, const void* lora_b, int32_t r, float lora_scale,
+                   float* da, float* db, void* workspace, size_t workspace_bytes, void* stream);
+
 /* LoRA merge -- tutorial page, "Merging LoRA Adapters After Fine-Tuning":
  * after training the adapters are folded into one dense 16-bit copy of the
  * base, which needs the base dequantized first (tool page, "Practical

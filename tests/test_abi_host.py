@@ -136,6 +136,17 @@ CASES = [
     ("dx misaligned workspace", lambda L: L.nf4_gemm_dx(ctypes.byref(_w()), A, 4, A, A, A, 16, 2.0, A + 16, WS, None), nf4.NF4_ERR_ALIGN),
     ("dx misaligned dy", lambda L: L.nf4_gemm_dx(ctypes.byref(_w()), A + 2, 4, A, None, None, 0, 0.0, None, 0, None), nf4.NF4_ERR_ALIGN),
     ("dx misaligned a", lambda L: L.nf4_gemm_dx(ctypes.byref(_w()), A, 4, A, A + 8, A, 16, 2.0, A, WS, None), nf4.NF4_ERR_ALIGN),
+    ("grads null x", lambda L: L.nf4_lora_grads(None, A, 4, 64, 64, A, A, 16, 2.0, A, A, A, WS, None), nf4.NF4_ERR_NULL),
+    ("grads null b", lambda L: L.nf4_lora_grads(A, A, 4, 64, 64, A, None, 16, 2.0, A, A, A, WS, None), nf4.NF4_ERR_NULL),
+    ("grads no outputs", lambda L: L.nf4_lora_grads(A, A, 4, 64, 64, A, A, 16, 2.0, None, None, A, WS, None), nf4.NF4_ERR_NULL),
+    ("grads m=0", lambda L: L.nf4_lora_grads(A, A, 0, 64, 64, A, A, 16, 2.0, A, A, A, WS, None), nf4.NF4_ERR_SIZE),
+    ("grads rows%8", lambda L: L.nf4_lora_grads(A, A, 4, 60, 64, A, A, 16, 2.0, A, A, A, WS, None), nf4.NF4_ERR_SIZE),
+    ("grads cols%8", lambda L: L.nf4_lora_grads(A, A, 4, 64, 68, A, A, 16, 2.0, A, A, A, WS, None), nf4.NF4_ERR_SIZE),
+    ("grads rank 0", lambda L: L.nf4_lora_grads(A, A, 4, 64, 64, A, A, 0, 2.0, A, A, A, WS, None), nf4.NF4_ERR_SIZE),
+    ("grads scale nan", lambda L: L.nf4_lora_grads(A, A, 4, 64, 64, A, A, 16, float("nan"), A, A, A, WS, None), nf4.NF4_ERR_SIZE),
+    ("grads misaligned da", lambda L: L.nf4_lora_grads(A, A, 4, 64, 64, A, A, 16, 2.0, A + 4, A, A, WS, None), nf4.NF4_ERR_ALIGN),
+    ("grads workspace small", lambda L: L.nf4_lora_grads(A, A, 4, 64, 64, A, A, 16, 2.0, A, A, A, 64, None), nf4.NF4_ERR_WORKSPACE),
+    ("grads misaligned workspace", lambda L: L.nf4_lora_grads(A, A, 4, 64, 64, A, A, 16, 2.0, A, A, A + 128, WS, None), nf4.NF4_ERR_ALIGN),
     ("merge null weight", lambda L: L.nf4_lora_merge(None, A, A, 16, 2.0, A, 1, None), nf4.NF4_ERR_NULL),
     ("merge null a", lambda L: L.nf4_lora_merge(ctypes.byref(_w()), None, A, 16, 2.0, A, 1, None), nf4.NF4_ERR_NULL),
     ("merge null out", lambda L: L.nf4_lora_merge(ctypes.byref(_w()), A, A, 16, 2.0, None, 1, None), nf4.NF4_ERR_NULL),
