@@ -293,7 +293,7 @@ def main():
     return 0
 
 
-LEGS = ("hbm", "gemv-decode", "gemv-mlp", "gemv-70b", "stack-70b", "gemm", "lora-merge")
+LEGS = ("hbm", "gemv-decode", "gemv-mlp", "gemv-70b", "stack-70b", "gemm", "qlora-backward", "lora-merge")
 
 
 def extra_legs(torch, nf4, syn, dev, stream, EventTimer, only=None):
@@ -311,9 +311,71 @@ def extra_legs(torch, nf4, syn, dev, stream, EventTimer, only=None):
         res.update(leg_stack_70b(torch, nf4, syn, dev, stream, EventTimer))
     if only in (None, "gemm"):
         res.update(leg_gemm(torch, nf4, dev, stream, EventTimer, g))
+    if only in (None, "qlora-backward"):
+        res.update(leg_qlora_backward(torch, nf4, dev, stream, EventTimer, g))
     if only in (None, "lora-merge"):
         res.update(leg_lora_merge(torch, nf4, dev, stream, EventTimer, g))
     return res
+
+
+def _median_call(torch, stream, EventTimer, fn, reps=30, warm=5):
+    for _ in range(warm):
+        fn()
+    torch.cuda.synchronize()
+    t = EventTimer(torch, stream)
+    for _ in range(reps):
+        s = t.start()
+        fn()
+        t.stop(s)
+    torch.cuda.synchronize()
+    return t.median_us()
+
+
+def leg_qlora_backward(torch, nf4, dev, stream, EventTimer, g):
+    """The backward of the QLoRA forward GEMM (X 4096x4096, NF4(DQ) W
+    14336x4096, LoRA r = 16, alpha = 32): the input gradient through the
+    frozen base, dX = dY.deq(W) + s.(dY.B).A, and the adapter gradients dA,
+    dB (medians of 30 calls)."""
+    print("[bench] qlora backward leg", file=sys.stderr, flush=True)
+    M, N, K, r = 4096, 14336, 4096, 16
+    s_l = 32.0 / r
+    g.manual_seed(4_005)
+    X = torch.randn((M, K), generator=g, device=dev).to(torch.bfloat16)
+    g.manual_seed(4_000)
+    W = nf4.quantize_weight((torch.randn((N, K), generator=g, device=dev) * 0.02).to(torch.bfloat16),
+                            double_quant=True)
+    g.manual_seed(4_006)
+    A = (torch.randn((r, K), generator=g, device=dev) * 0.01).to(torch.bfloat16)
+    g.manual_seed(4_007)
+    B = (torch.randn((N, r), generator=g, device=dev) * 0.01).to(torch.bfloat16)
+    g.manual_seed(4_008)
+    dY = torch.randn((M, N), generator=g, device=dev).to(torch.bfloat16)
+    dX = torch.empty((M, K), dtype=torch.bfloat16, device=dev)
+    dA = torch.empty((r, K), dtype=torch.float32, device=dev)
+    dB = torch.empty((N, r), dtype=torch.float32, device=dev)
+    ws_dx = torch.empty(max(nf4.nf4_gemm_dx_workspace(M, N, r), 1), dtype=torch.uint8, device=dev)
+    ws_g = torch.empty(max(nf4.nf4_lora_grads_workspace(M, N, K, r), 1), dtype=torch.uint8, device=dev)
+    us_dx = _median_call(torch, stream, EventTimer, lambda: nf4.nf4_gemm_dx(W, dY, dX, A, B, s_l, ws_dx))
+    us_g = _median_call(torch, stream, EventTimer,
+                        lambda: nf4.nf4_lora_grads(X, dY, A, B, s_l, da=dA, db=dB, workspace=ws_g))
+    fl_dx = 2.0 * M * N * K + 2.0 * M * N * r + 2.0 * M * r * K
+    tf = fl_dx / (us_dx * 1e-6) / 1e12
+    Wd = nf4.nf4_dequantize(W, out_dtype=torch.bfloat16)
+    us_lib = _median_call(torch, stream, EventTimer, lambda: torch.matmul(dY, Wd))
+    del Wd
+    return {"qlora_backward": {
+        "workload": "dY 4096x14336 bf16, NF4(DQ) W 14336x4096, LoRA r=16 alpha=32: dX, dA, dB",
+        "gemm_dx_us": round(us_dx, 1),
+        "gemm_dx_TFLOPs": round(tf, 1),
+        "gemm_dx_frac_mfma_bf16_peak": round(tf / MFMA_BF16_PEAK_TFLOPS, 4),
+        "lora_grads_us": round(us_g, 1),
+        "timing": "medians of 30 calls after 5 warm-ups (dX call includes its LoRA prep; grads include both thin products)",
+        "calibration_torch_matmul_bf16": {
+            "what": "torch.matmul (hipBLASLt) dY . W on the dequantized bf16 weight, no LoRA",
+            "us": round(us_lib, 1),
+            "TFLOPs": round(2.0 * M * N * K / (us_lib * 1e-6) / 1e12, 1),
+        },
+    }}
 
 
 FP64_VECTOR_PEAK_TFLOPS = 78.6
