@@ -39,29 +39,23 @@
 // bits.
 // Those columns (2 r rounded up to a multiple of 64) run as one or two more
 // K steps with both operands staged in LDS.
-#include "nf4_device.h"
+#include "gemm_tiles.h"
 
 namespace nf4i {
 namespace {
 
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-typedef float floatx16 __attribute__((ext_vector_type(16)));
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));  // native vector: stays in registers
+using gt::bf16_pair;
+using gt::bf16x8;
+using gt::floatx16;
+using gt::kThreads;
+using gt::lds_frag;
+using gt::u32x4;
 
-constexpr int kBM = 256, kBN = 256, kBK = 64;
+constexpr int kBM = gt::kTileM, kBN = gt::kTileN, kBK = gt::kStep;
 constexpr int kRowBytes = 144;                  // 64 bf16 + 16 bytes of padding
 constexpr int kTileBytes = 256 * kRowBytes;     // one operand tile in LDS
 constexpr int kPairSlots = 32;                  // copies of the level-pair table
-constexpr int kThreads = 256;                   // 4 waves
-constexpr int kXPieces = kBM * kBK * 2 / 16 / kThreads;  // 16-byte x pieces per thread and step (8)
-
-__device__ __forceinline__ bf16x8 lds_frag(const char* p) { return *reinterpret_cast<const bf16x8*>(p); }
-
-__device__ __forceinline__ uint32_t bf16_pair(float lo, float hi) {
-  const bf16x2 p = {static_cast<__bf16>(lo), static_cast<__bf16>(hi)};  // round to nearest even
-  return __builtin_bit_cast(uint32_t, p);
-}
+constexpr int kXPieces = gt::kActPieces;        // 16-byte x pieces per thread and step (8)
 
 struct GemmArgs {
   const uint8_t* packed;
@@ -94,35 +88,6 @@ __device__ __forceinline__ void fill_level_pairs(float2* tab, float2* base, cons
   for (int i = threadIdx.x; i < 256 * kPairSlots; i += blockDim.x) tab[i] = base[i / kPairSlots];
   __syncthreads();
 }
-
-// x tile of one K step by direct global-to-LDS loads: wave w's instruction i
-// fills tile rows 64 w + 8 i .. + 7 (1 KB); its lane l takes row
-// 64 w + 8 i + l / 8, LDS slot l % 8, i.e. the row's 16-byte piece
-// (l % 8) ^ ((row / 2) % 8).  Rows past the end of x re-read the last valid
-// one (they only feed outputs that are never stored).
-struct XPtrs {
-  const uint8_t* row0;    // the lane's row for i = 0, at column 0 (bytes)
-  int64_t stride;         // bytes between the rows of i and i + 1 (8 rows)
-  int i_max;              // last i whose row exists
-  uint32_t piece[kXPieces];  // byte offset of the lane's piece for each i
-};
-
-constexpr int kXRowBytes = kBK * 2;  // 128: swizzled x tile rows
-
-__device__ __forceinline__ void dma_x(const XPtrs& p, int64_t ks, char* stage, int wave) {
-  const uint8_t* b = p.row0 + ks * (kBK * 2);
-#pragma unroll
-  for (int i = 0; i < kXPieces; ++i) {
-    const int ii = i < p.i_max ? i : p.i_max;
-    __builtin_amdgcn_global_load_lds(b + ii * p.stride + p.piece[i],
-                                     (__attribute__((address_space(3))) void*)(stage + (wave * 8 + i) * 1024), 16,
-                                     0, 0);
-  }
-}
-
-// Waits for this wave's direct-to-LDS loads (and all other vector memory
-// loads); the barrier after it then covers every wave's.
-__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
 // The codes a lane expands in one K step: for its two W rows (j = 0, 1) the
 // 16 bytes of columns 32 h .. 32 h + 31, and the rows' block scale inputs.
@@ -197,26 +162,6 @@ __device__ __forceinline__ void block_scales(const WRegs& wr, float mean, float 
   }
 }
 
-// A fragments of 16-wide k step s: rows 32 i + lane % 32 of the swizzled x
-// tile, logical piece 4 h + s (h = lane / 32) at slot (4 h + s) ^ sw, where
-// sw = ((lane % 32) / 2) % 8 is the same for every i.
-__device__ __forceinline__ void read_a(const char* xa, int s, uint32_t sw, uint32_t h4, bf16x8 (&f)[8]) {
-  const char* p = xa + (((h4 + s) ^ sw) << 4);
-#pragma unroll
-  for (int i = 0; i < 8; ++i) f[i] = lds_frag(p + i * 32 * kXRowBytes);
-}
-
-// The MFMAs compute y^T tiles (W fragment as the A operand, x fragment as
-// B), so that each lane ends up holding 4 consecutive output columns of one
-// output row (the A and B fragment layouts are the same).
-__device__ __forceinline__ void mfma16(const bf16x8 (&af)[8], const bf16x8 (&bf)[2], floatx16 (&acc)[8][2]) {
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    acc[i][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bf[0], af[i], acc[i][0], 0, 0, 0);
-    acc[i][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bf[1], af[i], acc[i][1], 0, 0, 0);
-  }
-}
-
 // One LoRA step (64 extra K columns): the x side from u into xs, the W side
 // [B | B] (zero past the rank) into ws as rows of output columns; both then
 // feed the MFMAs as fragments.
@@ -288,20 +233,7 @@ __global__ __launch_bounds__(kThreads) void k_gemm(GemmArgs a) {
     const int64_t m0 = (tid / tiles_n) * kBM;
     const int64_t n0 = (tid % tiles_n) * kBN;
 
-    XPtrs xp;
-    {
-      const int64_t xr = m0 + wave * 64 + (lane >> 3);
-      const int64_t xrc = xr < a.m ? xr : a.m - 1;
-      xp.row0 = reinterpret_cast<const uint8_t*>(a.x + xrc * a.cols);
-      xp.stride = 8 * a.cols * 2;
-      const int64_t last = xr < a.m ? (a.m - 1 - xr) / 8 : 0;
-      xp.i_max = static_cast<int>(last < kXPieces - 1 ? last : kXPieces - 1);
-#pragma unroll
-      for (int i = 0; i < kXPieces; ++i) {
-        const uint32_t r = static_cast<uint32_t>(8 * i + (lane >> 3));  // tile row - 64 wave
-        xp.piece[i] = (((lane & 7) ^ ((r >> 1) & 7)) << 4);
-      }
-    }
+    const gt::ActPtrs xp = gt::make_act_ptrs(a.x, a.cols, a.m, m0, wave, lane);
     WPtrs wp;
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
@@ -312,12 +244,7 @@ __global__ __launch_bounds__(kThreads) void k_gemm(GemmArgs a) {
     }
 
     floatx16 acc[8][2];
-#pragma unroll
-    for (int i = 0; i < 8; ++i)
-#pragma unroll
-      for (int j = 0; j < 2; ++j)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
+    gt::zero_acc(acc);
 
     // K step k: MFMAs from x stage k % 2 and the codes of step k (wc), in
     // four 16-wide k steps s.  Software pipeline: while the MFMAs of s run,
@@ -328,7 +255,7 @@ __global__ __launch_bounds__(kThreads) void k_gemm(GemmArgs a) {
     // global loads of step k + 1 (clamped on the last step) go out at the top
     // of step k.
     WRegs wc, wnx;
-    dma_x(xp, 0, xs0, wave);
+    gt::dma_act(xp, 0, xs0, wave);
     load_w<kDQ>(wc, wp, a, 0);
     float sa[2];
     bf16x8 bf[2][2];
@@ -339,51 +266,51 @@ __global__ __launch_bounds__(kThreads) void k_gemm(GemmArgs a) {
     lookup_step(lk[0], wc.w, 0, tabc, slot);
     bf[0][0] = expand_frag(lk[0].l[0], sa[0]);
     bf[0][1] = expand_frag(lk[0].l[1], sa[1]);
-    wait_vmem();
+    gt::wait_vmem();
     __syncthreads();
     for (int64_t ks = 0; ks < nk; ++ks) {
       const int64_t kn = ks + 1 < nk ? ks + 1 : ks;
       // the next step's x tile goes straight to the other stage (last read
       // before the previous barrier) and its codes to registers
-      dma_x(xp, kn, (ks & 1) ? xs0 : xs1, wave);
+      gt::dma_act(xp, kn, (ks & 1) ? xs0 : xs1, wave);
       load_w<kDQ>(wnx, wp, a, kn);
       __builtin_amdgcn_sched_barrier(0);
-      const char* xa = ((ks & 1) ? xs1 : xs0) + (lane & 31) * kXRowBytes;
-      read_a(xa, 0, sw, h4, af[0]);
-      read_a(xa, 1, sw, h4, af[1]);
+      const char* xa = ((ks & 1) ? xs1 : xs0) + (lane & 31) * gt::kActRowBytes;
+      gt::read_act(xa, 0, sw, h4, af[0]);
+      gt::read_act(xa, 1, sw, h4, af[1]);
       lookup_step(lk[1], wc.w, 1, tabc, slot);
       __builtin_amdgcn_sched_barrier(0);
       // s = 0
-      mfma16(af[0], bf[0], acc);
+      gt::mfma16(af[0], bf[0], acc);
       bf[1][0] = expand_frag(lk[1].l[0], sa[0]);
       bf[1][1] = expand_frag(lk[1].l[1], sa[1]);
-      read_a(xa, 2, sw, h4, af[2]);
+      gt::read_act(xa, 2, sw, h4, af[2]);
       lookup_step(lk[2], wc.w, 2, tabc, slot);
       mfma_interleave();
       __builtin_amdgcn_sched_barrier(0);
       // s = 1
-      mfma16(af[1], bf[1], acc);
+      gt::mfma16(af[1], bf[1], acc);
       bf[0][0] = expand_frag(lk[2].l[0], sa[0]);
       bf[0][1] = expand_frag(lk[2].l[1], sa[1]);
-      read_a(xa, 3, sw, h4, af[0]);
+      gt::read_act(xa, 3, sw, h4, af[0]);
       lookup_step(lk[0], wc.w, 3, tabc, slot);
       mfma_interleave();
       __builtin_amdgcn_sched_barrier(0);
       // s = 2
-      mfma16(af[2], bf[0], acc);
+      gt::mfma16(af[2], bf[0], acc);
       bf[1][0] = expand_frag(lk[0].l[0], sa[0]);
       bf[1][1] = expand_frag(lk[0].l[1], sa[1]);
       mfma_interleave();
       __builtin_amdgcn_sched_barrier(0);
       // s = 3, with the next step's s = 0 expansion
-      mfma16(af[0], bf[1], acc);
+      gt::mfma16(af[0], bf[1], acc);
       block_scales<kDQ>(wnx, mean, sa);
       lookup_step(lk[1], wnx.w, 0, tabc, slot);
       bf[0][0] = expand_frag(lk[1].l[0], sa[0]);
       bf[0][1] = expand_frag(lk[1].l[1], sa[1]);
       mfma_interleave();
       __builtin_amdgcn_sched_barrier(0);
-      wait_vmem();
+      gt::wait_vmem();
       __syncthreads();
       wc = wnx;
     }
@@ -394,34 +321,7 @@ __global__ __launch_bounds__(kThreads) void k_gemm(GemmArgs a) {
       __syncthreads();
     }
 
-    // epilogue: of each 32 x 32 tile of y^T the lane holds element e at
-    // output column (e % 4) + 4 (lane / 32) + 8 (e / 4) and output row
-    // lane % 32: four consecutive columns per group of four e, written as one
-    // 8-byte store when the row holds them all and is 8-byte aligned
-    const bool vec = (a.rows & 3) == 0;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int64_t row = m0 + i * 32 + (lane & 31);
-      if (row >= a.m) continue;
-      uint16_t* yr = a.y + row * a.rows;
-#pragma unroll
-      for (int j = 0; j < 2; ++j) {
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const int64_t col = n0 + wave * 64 + j * 32 + 4 * (lane >> 5) + 8 * g;
-          const uint32_t p0 = bf16_pair(acc[i][j][4 * g], acc[i][j][4 * g + 1]);
-          const uint32_t p1 = bf16_pair(acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]);
-          if (vec && col + 3 < a.rows) {
-            *reinterpret_cast<uint2*>(yr + col) = make_uint2(p0, p1);
-          } else {
-            const uint16_t v[4] = {static_cast<uint16_t>(p0), static_cast<uint16_t>(p0 >> 16),
-                                   static_cast<uint16_t>(p1), static_cast<uint16_t>(p1 >> 16)};
-            for (int u = 0; u < 4; ++u)
-              if (col + u < a.rows) yr[col + u] = v[u];
-          }
-        }
-      }
-    }
+    gt::store_acc(acc, a.y, a.m, a.rows, m0, n0, wave, lane);
   }
 }
 

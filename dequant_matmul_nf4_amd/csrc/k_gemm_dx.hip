@@ -6,45 +6,52 @@
 //   dX = dY . deq(W) + s . (dY . B) . A          dY [m][rows], dX [m][cols]
 //
 // The reduction runs over the weight's rows, so W enters in the other
-// orientation than in the forward GEMM: its NF4 codes are expanded into LDS
-// transposed, as Wt[col][row], and both MFMA operands are then read as
-// 16-byte runs along the reduction index.
+// orientation than in the forward GEMM and has to be transposed on chip.
 //
 // Tiling: a workgroup of 4 waves computes a 256 (m) x 256 (col) tile of dX;
-// wave w owns columns [64 w, 64 w + 64) for all 256 rows of dY, 8 x 2 tiles
-// of v_mfma_f32_32x32x16_bf16 per 16-wide reduction step, computed transposed
-// (Wt fragment as A, dY fragment as B) so that each lane ends up with 4
-// consecutive output columns.  One step covers 64 weight rows:
-//  1. the dY tile (256 x 64 bf16), the raw codes (64 weight rows x 256
-//     columns, 8 KB) and the 64 x 4 block scales are written to LDS from
-//     registers (their global loads were issued during the previous step);
-//  2. each thread expands 8 weight rows x 8 columns: level x block scale,
-//     rounded once to bf16 -- the value nf4_dequantize writes -- and stores
-//     each column's 8 values as one 16-byte run of Wt;
-//  3. the MFMAs read dY and Wt fragments from LDS.
-// LDS rows are 144 bytes (64 bf16 + 16 bytes of padding), so fragment reads
-// of consecutive rows fall in distinct banks; in Wt the 16-byte run c of row
-// k sits at slot c ^ ((k / 16) % 8), which also spreads the expansion's
-// stores (lanes write rows 8 apart) over the banks without moving the
-// fragment reads of any 16 consecutive rows.
+// wave w owns columns [64 w, 64 w + 64) for all 256 rows of dY (the shared
+// tile machinery of the forward GEMM: 8 x 2 tiles of
+// v_mfma_f32_32x32x16_bf16, transposed so that a lane holds 4 consecutive
+// output columns).  A step covers 64 weight rows:
+//  - dY: the 256 x 64 tile goes to LDS by direct global-to-LDS loads (two
+//    stages, swizzled rows), issued one step ahead;
+//  - W: each wave expands its own 64 columns x 64 rows into a private Wt
+//    tile in LDS, Wt[col][row] (two buffers).  Lane (g, q) = (lane % 8,
+//    lane / 8) holds the codes of rows 8 g .. 8 g + 7 at columns
+//    8 q .. 8 q + 7 (one 4-byte load per row), looks up the level pair of
+//    each code byte (a 256-entry table in LDS, read one quarter step ahead of
+//    use), multiplies by the row's block scale and rounds once to bf16 -- the
+//    value nf4_dequantize writes -- and stores each column's 8 values as one
+//    16-byte run.  Runs of a Wt row are swizzled (run c of column k at slot
+//    c ^ ((k / 16) % 8), rows padded to 144 bytes), which keeps both these
+//    stores and the fragment reads free of bank conflicts.  Since the tile is
+//    private to its wave, no barrier separates the expansion from its use.
+//  - Software pipeline: while the MFMAs of step s run, the wave expands step
+//    s + 1 (its codes loaded during step s - 1) and loads the codes of step
+//    s + 2; the one barrier per step guards the dY stages.  The step's body
+//    is kept free of branches so that the expansion can be interleaved with
+//    the MFMAs.
+// A last partial step (rows % 64 != 0) loads its dY tile through registers,
+// zero past the end.
 //
 // The LoRA term is folded in as extra reduction indices,
 //   [dY | U_hi | U_lo] . [deq(W) ; A ; A]  with U = s . dY . B,
-// U split into two bf16 parts (hi = bf16(U), lo = bf16(U - hi)) by the same
-// prep kernel as the forward GEMM's (run on dY and B transposed), so the
-// adapter product keeps about 16 significant bits.
-#include "nf4_device.h"
+// U split into two bf16 parts (hi = bf16(U), lo = bf16(U - hi)) by the LoRA
+// prep kernel (run on dY and B transposed), so the adapter product keeps
+// about 16 significant bits.
+#include "gemm_tiles.h"
 
 namespace nf4i {
 namespace {
 
-typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
-typedef float floatx16_t __attribute__((ext_vector_type(16)));
+using gt::bf16x8;
+using gt::floatx16;
+using gt::kThreads;
+using gt::u32x4;
 
-constexpr int kTm = 256, kTk = 256, kStep = 64;
-constexpr int kRowB = 144;  // 64 bf16 (128 bytes) + 16 bytes of padding per LDS row
-constexpr int kThr = 256;
+constexpr int kTm = gt::kTileM, kTk = gt::kTileN, kStep = gt::kStep;
+constexpr int kWtRowB = 144;              // 64 bf16 + 16 bytes of padding
+constexpr int kWtBytes = 64 * kWtRowB;    // one wave's Wt tile: 64 columns x 64 rows
 
 struct DxArgs {
   const uint8_t* packed;
@@ -59,207 +66,282 @@ struct DxArgs {
   Codebook cb;
 };
 
-__device__ __forceinline__ uint32_t bf16_pair(float lo, float hi) {
-  const bf16x2_t p = {static_cast<__bf16>(lo), static_cast<__bf16>(hi)};  // round to nearest even
-  return __builtin_bit_cast(uint32_t, p);
+// Byte offset of run c (reduction indices 8 c .. 8 c + 7) of Wt row k.
+__device__ __forceinline__ uint32_t wt_off(int k, int c) {
+  return static_cast<uint32_t>(k * kWtRowB + 16 * (c ^ ((k >> 4) & 7)));
 }
 
-// Byte offset of the 16-byte run c (reduction indices 8 c .. 8 c + 7) of Wt row k.
-__device__ __forceinline__ int wt_off(int k, int c) { return k * kRowB + 16 * (c ^ ((k >> 4) & 7)); }
-
-// Global loads of one reduction step, held in registers until the LDS is free.
-struct StepRegs {
-  uint4 dy[8];    // piece t + 256 i: dY tile row (t + 256 i) / 8, 16-byte run (t + 256 i) % 8
-  uint4 code[2];  // piece t + 256 i: weight row (t + 256 i) / 8 of the step, 16 bytes (t + 256 i) % 8
-  float am;       // plain scale of (weight row t / 4, tile block t % 4)
+// What a lane loads for one step: the codes of its 8 rows and the scale
+// inputs of row `lane` of the step (block of the wave's 64 columns).
+struct CodeRegs {
+  uint32_t w[8];
+  float am;
   int q;
   float s2;
 };
 
+struct CodePtrs {
+  const uint8_t* c;    // the wave's first code byte in weight row 0 (the same in every lane)
+  uint32_t off;        // the lane's 4 bytes in row 8 g: 8 g row_bytes + 4 q
+  uint32_t row_bytes;  // cols / 2
+  int64_t kb;          // the wave's column block
+  int64_t nbr;         // blocks per row
+};
+
 template <bool kDQ>
-__device__ __forceinline__ void load_step(StepRegs& g, const DxArgs& a, int64_t m0, int64_t k0, int64_t n0) {
-  const int t = threadIdx.x;
+__device__ __forceinline__ void load_codes(CodeRegs& r, const CodePtrs& p, const DxArgs& a, int64_t ks, int g,
+                                           int lane) {
+  const int64_t n0 = ks * kStep;
+  if (n0 + kStep <= a.rows) {  // a whole step: no clamping
+    const uint8_t* b = p.c + n0 * p.row_bytes;
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int p = t + kThr * i;
-    const int64_t row = m0 + (p >> 3);
-    const int64_t rc = row < a.m ? row : a.m - 1;  // rows past the end: never stored
-    const int64_t n = n0 + 8 * (p & 7);           // rows % 8 == 0: a run is all in or all out
-    g.dy[i] = n < a.rows ? *reinterpret_cast<const uint4*>(a.dy + rc * a.rows + n) : make_uint4(0, 0, 0, 0);
-  }
-  const int64_t half_cols = a.cols / 2;
+    for (int r8 = 0; r8 < 8; ++r8) r.w[r8] = *reinterpret_cast<const uint32_t*>(b + p.off + r8 * p.row_bytes);
+  } else {  // rows past the end re-read the last one (they meet zero dY)
 #pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const int p = t + kThr * i;
-    int64_t wrow = n0 + (p >> 3);
-    wrow = wrow < a.rows ? wrow : a.rows - 1;     // meets zero dY: adds nothing
-    int64_t off = k0 / 2 + 16 * (p & 7);          // byte within the weight row
-    off = off + 16 <= half_cols ? off : half_cols - 16;  // columns past the end: never stored
-    g.code[i] = *reinterpret_cast<const uint4*>(a.packed + wrow * half_cols + off);
+    for (int r8 = 0; r8 < 8; ++r8) {
+      const int64_t n = n0 + 8 * g + r8 < a.rows ? n0 + 8 * g + r8 : a.rows - 1;
+      r.w[r8] = *reinterpret_cast<const uint32_t*>(p.c + n * p.row_bytes + 4 * (lane >> 3));
+    }
   }
-  int64_t wrow = n0 + (t >> 2);
-  wrow = wrow < a.rows ? wrow : a.rows - 1;
-  const int64_t nbr = a.cols / 64;
-  int64_t kb = k0 / 64 + (t & 3);
-  kb = kb < nbr ? kb : nbr - 1;
-  const int64_t b = wrow * nbr + kb;
+  const int64_t nl = n0 + lane < a.rows ? n0 + lane : a.rows - 1;
+  const int64_t b = nl * p.nbr + p.kb;
   if constexpr (kDQ) {
-    g.q = a.sc.q[b];
-    g.s2 = a.sc.absmax2[b >> 8];
+    r.q = a.sc.q[b];
+    r.s2 = a.sc.absmax2[b >> 8];
   } else {
-    g.am = a.sc.absmax[b];
+    r.am = a.sc.absmax[b];
   }
 }
 
 template <bool kDQ>
-__global__ __launch_bounds__(kThr) void k_gemm_dx(DxArgs a) {
-  __shared__ __align__(16) char dyt[kTm * kRowB];      // dY tile [m][64 reduction]
-  __shared__ __align__(16) char wt[kTk * kRowB];       // Wt tile [col][64 reduction], runs swizzled
-  __shared__ __align__(16) char codes[kStep * kRowB];  // raw codes [64 weight rows][128 bytes]
-  __shared__ float scl[kStep * 4];                     // scale of (weight row, tile block)
-  __shared__ float lv[16];
-  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
-  if (t < 16) lv[t] = a.cb.level[t];
+__device__ __forceinline__ float row_scale(const CodeRegs& r, float mean) {
+  if constexpr (kDQ) return div127(r.q) * r.s2 + mean;  // a_hat: three roundings (contraction is off)
+  else return r.am;
+}
+
+// The 256 level pairs of a code byte (element 2 j = high nibble first), in
+// kPairCopies interleaved copies: entry e of copy c at byte e * 64 + c * 8.
+// A lane reads copy lane % 8, which spreads the lookups of 8 lanes over all
+// 64 banks.  Ends with a barrier.
+constexpr int kPairCopies = 8;
+__device__ __forceinline__ void fill_pairs(float2* tab, const Codebook& cb) {
+  if (threadIdx.x < 256) {
+    const int e = threadIdx.x;
+    const float2 v = make_float2(cb.level[e >> 4], cb.level[e & 15]);
+#pragma unroll
+    for (int c = 0; c < kPairCopies; ++c) tab[e * kPairCopies + c] = v;
+  }
+  __syncthreads();
+}
+
+// Level pairs of code byte h of the lane's 8 rows: columns 2 h and 2 h + 1.
+__device__ __forceinline__ void lookup_quarter(float2 (&l)[8], const uint32_t (&w)[8], const char* tab, int h,
+                                               uint32_t slot) {
+#pragma unroll
+  for (int r8 = 0; r8 < 8; ++r8) {
+    const uint32_t e = __builtin_amdgcn_ubfe(w[r8], 8 * h, 8);
+    l[r8] = *reinterpret_cast<const float2*>(tab + ((e << 6) | slot));
+  }
+}
+
+// Expands columns 2 h, 2 h + 1 of the lane's 8 into Wt from their level pairs.
+__device__ __forceinline__ void expand_quarter(char* wt, const float2 (&l)[8], const float (&ah)[8], int h, int g,
+                                               int q) {
+  u32x4 o0, o1;
+#pragma unroll
+  for (int p = 0; p < 4; ++p) {
+    // fl32(level * a_hat), rounded once to bf16
+    o0[p] = gt::bf16_pair(l[2 * p].x * ah[2 * p], l[2 * p + 1].x * ah[2 * p + 1]);
+    o1[p] = gt::bf16_pair(l[2 * p].y * ah[2 * p], l[2 * p + 1].y * ah[2 * p + 1]);
+  }
+  *reinterpret_cast<u32x4*>(wt + wt_off(8 * q + 2 * h, g)) = o0;
+  *reinterpret_cast<u32x4*>(wt + wt_off(8 * q + 2 * h + 1, g)) = o1;
+}
+
+// Wt fragments of 16-wide step s for lane half h: logical run 4 h + s (the
+// activation fragments' order).
+__device__ __forceinline__ void read_wt(const char* wt, int s, int lane, bf16x8 (&f)[2]) {
+  const int h4 = (lane >> 5) * 4;
+#pragma unroll
+  for (int j = 0; j < 2; ++j) f[j] = gt::lds_frag(wt + wt_off(32 * j + (lane & 31), h4 + s));
+}
+
+// Spreads the work issued next to 16 MFMAs between them.
+__device__ __forceinline__ void mfma_interleave() {
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+    __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);  // VALU
+    __builtin_amdgcn_sched_group_barrier(0x080, 1, 0);  // LDS read or write
+  }
+}
+
+// dY tile of the last step when it is partial: loads through registers,
+// zero past rows (rows % 8 == 0, so a 16-byte piece is all in or all out),
+// stored where the direct loads would have put them.
+__device__ __forceinline__ void act_tail(const gt::ActPtrs& p, int64_t ks, int64_t rows, char* stage, int wave,
+                                         int lane) {
+  const uint8_t* b = p.base + ks * (kStep * 2);
+#pragma unroll
+  for (int i = 0; i < gt::kActPieces; ++i) {
+    const int64_t n = ks * kStep + 8 * gt::act_piece(i, lane);
+    u32x4 v = {0u, 0u, 0u, 0u};
+    if (n < rows) v = *reinterpret_cast<const u32x4*>(b + p.off[i]);
+    *reinterpret_cast<u32x4*>(stage + (wave * 8 + i) * 1024 + 16 * lane) = v;
+  }
+}
+
+template <bool kDQ>
+__global__ __launch_bounds__(kThreads) void k_gemm_dx(DxArgs a) {
+  __shared__ __align__(16) char stage0[gt::kActStageBytes], stage1[gt::kActStageBytes];
+  __shared__ __align__(16) char wts[4][2][kWtBytes];
+  __shared__ __align__(16) float scl[4][2][64];  // per wave: a_hat of the step's 64 rows
+  __shared__ __align__(16) float2 pairs[256 * kPairCopies];  // 16 KB
+  const int t = threadIdx.x, lane = t & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
+  const int g = lane & 7, q = lane >> 3;
+  const uint32_t slot = static_cast<uint32_t>(lane & 7) << 3;
+  const char* tab = reinterpret_cast<const char*>(pairs);
   const float mean = kDQ ? *a.sc.mean : 0.0f;
+
   const int64_t tiles_k = (a.cols + kTk - 1) / kTk;
-  const int64_t m0 = (static_cast<int64_t>(blockIdx.x) / tiles_k) * kTm;
-  const int64_t k0 = (static_cast<int64_t>(blockIdx.x) % tiles_k) * kTk;
+  const int64_t tiles = tiles_k * ((a.m + kTm - 1) / kTm);
+  int64_t tid = blockIdx.x;
+  // consecutive tiles (one dY row strip) on one XCD: dispatch deals workgroups round-robin over 8
+  if (tiles % 8 == 0) tid = (tid % 8) * (tiles / 8) + tid / 8;
+  const int64_t m0 = (tid / tiles_k) * kTm;
+  const int64_t k0 = (tid % tiles_k) * kTk;
   const int64_t nsteps = (a.rows + kStep - 1) / kStep;
+  const bool ragged = (a.rows % kStep) != 0;
 
-  floatx16_t acc[8][2];
-#pragma unroll
-  for (int i = 0; i < 8; ++i)
-#pragma unroll
-    for (int j = 0; j < 2; ++j)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
+  const gt::ActPtrs ap = gt::make_act_ptrs(a.dy, a.rows, a.m, m0, wave, lane);
+  CodePtrs cp;
+  {
+    const int64_t wc = k0 + 64 * wave;                      // the wave's first column
+    const int64_t wcc = wc < a.cols ? wc : a.cols - 64;     // columns past the end: never stored
+    cp.row_bytes = static_cast<uint32_t>(a.cols / 2);
+    cp.c = a.packed + wcc / 2;
+    cp.off = static_cast<uint32_t>(8 * g) * cp.row_bytes + 4 * q;
+    cp.nbr = a.cols / 64;
+    cp.kb = wcc / 64;
+  }
+  char* wt0 = wts[wave][0];
+  char* wt1 = wts[wave][1];
+  float* sc0 = scl[wave][0];
+  float* sc1 = scl[wave][1];
 
-  // Fragments of 16-wide step s: Wt rows 64 w + 32 j + lane % 32 and dY rows
-  // 32 i + lane % 32, each at reduction indices 16 s + 8 (lane / 32) .. + 7.
-  auto mfma_step = [&]() {
+  floatx16 acc[8][2];
+  gt::zero_acc(acc);
+  const uint32_t sw = ((lane & 31) >> 1) & 7, h4 = (lane >> 5) * 4;
+
+  // prologue: dY of step 0, Wt of step 0, codes of step 1
+  CodeRegs c1, c2;
+  if (ragged && nsteps == 1) act_tail(ap, 0, a.rows, stage0, wave, lane);
+  else gt::dma_act(ap, 0, stage0, wave);
+  load_codes<kDQ>(c1, cp, a, 0, g, lane);
+  load_codes<kDQ>(c2, cp, a, nsteps > 1 ? 1 : 0, g, lane);
+  fill_pairs(pairs, a.cb);
+  {
+    sc0[lane] = row_scale<kDQ>(c1, mean);
+    float ah[8];
+    const float4 a0 = *reinterpret_cast<const float4*>(sc0 + 8 * g);
+    const float4 a1 = *reinterpret_cast<const float4*>(sc0 + 8 * g + 4);
+    ah[0] = a0.x; ah[1] = a0.y; ah[2] = a0.z; ah[3] = a0.w; ah[4] = a1.x; ah[5] = a1.y; ah[6] = a1.z; ah[7] = a1.w;
+#pragma unroll
+    for (int h = 0; h < 4; ++h) {
+      float2 l[8];
+      lookup_quarter(l, c1.w, tab, h, slot);
+      expand_quarter(wt0, l, ah, h, g, q);
+    }
+  }
+  c1 = c2;
+  gt::wait_vmem();
+  __syncthreads();
+  // level pairs of quarter 0 of the next expansion, one quarter ahead of use
+  float2 lk[2][8];
+  lookup_quarter(lk[0], c1.w, tab, 0, slot);
+
+  for (int64_t ks = 0; ks < nsteps; ++ks) {
+    const int64_t kn = ks + 1 < nsteps ? ks + 1 : ks;
+    char* st_cur = (ks & 1) ? stage1 : stage0;
+    char* st_nxt = (ks & 1) ? stage0 : stage1;
+    char* wt_cur = (ks & 1) ? wt1 : wt0;
+    char* wt_nxt = (ks & 1) ? wt0 : wt1;
+    float* sc_nxt = (ks & 1) ? sc0 : sc1;
+    // the next step's dY tile (the stage was last read before the previous
+    // barrier); on the last step a harmless reload, so that the code below
+    // stays one basic block for the scheduler
+    if (ragged && kn == nsteps - 1) act_tail(ap, kn, a.rows, st_nxt, wave, lane);
+    else gt::dma_act(ap, kn, st_nxt, wave);
+    // codes of step ks + 2; a_hat of step ks + 1 to this wave's scale buffer
+    load_codes<kDQ>(c2, cp, a, ks + 2 < nsteps ? ks + 2 : kn, g, lane);
+    sc_nxt[lane] = row_scale<kDQ>(c1, mean);
+    float ah[8];
+    {
+      const float4 a0 = *reinterpret_cast<const float4*>(sc_nxt + 8 * g);
+      const float4 a1 = *reinterpret_cast<const float4*>(sc_nxt + 8 * g + 4);
+      ah[0] = a0.x; ah[1] = a0.y; ah[2] = a0.z; ah[3] = a0.w; ah[4] = a1.x; ah[5] = a1.y; ah[6] = a1.z; ah[7] = a1.w;
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    const char* xa = st_cur + (lane & 31) * gt::kActRowBytes;
+    bf16x8 af[2][8], bw[2][2];
+    gt::read_act(xa, 0, sw, h4, af[0]);
+    read_wt(wt_cur, 0, lane, bw[0]);
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
-      const int c = 2 * s + (lane >> 5);
-      bf16x8_t af[2], bfr[8];
-#pragma unroll
-      for (int j = 0; j < 2; ++j)
-        af[j] = *reinterpret_cast<const bf16x8_t*>(wt + wt_off(wave * 64 + j * 32 + (lane & 31), c));
-#pragma unroll
-      for (int i = 0; i < 8; ++i)
-        bfr[i] = *reinterpret_cast<const bf16x8_t*>(dyt + (i * 32 + (lane & 31)) * kRowB + 16 * c);
-#pragma unroll
-      for (int i = 0; i < 8; ++i)
-#pragma unroll
-        for (int j = 0; j < 2; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[j], bfr[i], acc[i][j], 0, 0, 0);
-    }
-  };
-
-  StepRegs g;
-  if (nsteps > 0) load_step<kDQ>(g, a, m0, k0, 0);
-  for (int64_t ns = 0; ns < nsteps; ++ns) {
-    __syncthreads();  // the previous step's MFMAs are done with dyt and wt
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int p = t + kThr * i;
-      *reinterpret_cast<uint4*>(dyt + (p >> 3) * kRowB + 16 * (p & 7)) = g.dy[i];
-    }
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int p = t + kThr * i;
-      *reinterpret_cast<uint4*>(codes + (p >> 3) * kRowB + 16 * (p & 7)) = g.code[i];
-    }
-    if constexpr (kDQ) scl[t] = div127(g.q) * g.s2 + mean;  // a_hat: three roundings (contraction is off)
-    else scl[t] = g.am;
-    __syncthreads();
-    // the next step's loads go out now and land while this step expands and multiplies
-    const int64_t nn = ns + 1 < nsteps ? ns + 1 : ns;
-    load_step<kDQ>(g, a, m0, k0, nn * kStep);
-    {
-      // weight rows 8 g8 .. 8 g8 + 7 of the step, tile columns 8 kg .. 8 kg + 7
-      const int g8 = t >> 5, kg = t & 31;
-      float v[8][8];
-#pragma unroll
-      for (int r8 = 0; r8 < 8; ++r8) {
-        const int wr = 8 * g8 + r8;
-        const uint32_t word = *reinterpret_cast<const uint32_t*>(codes + wr * kRowB + 4 * kg);
-        const float ah = scl[wr * 4 + (kg >> 3)];
-#pragma unroll
-        for (int c = 0; c < 8; ++c) {
-          const uint32_t code = (word >> (8 * (c >> 1) + ((c & 1) ? 0 : 4))) & 0xFu;  // high nibble first
-          v[r8][c] = lv[code] * ah;  // fl32(level * a_hat)
-        }
+      if (s < 3) {
+        lookup_quarter(lk[(s + 1) & 1], c1.w, tab, s + 1, slot);
+        gt::read_act(xa, s + 1, sw, h4, af[(s + 1) & 1]);
+        read_wt(wt_cur, s + 1, lane, bw[(s + 1) & 1]);
       }
-#pragma unroll
-      for (int c = 0; c < 8; ++c) {
-        const uint4 o = make_uint4(bf16_pair(v[0][c], v[1][c]), bf16_pair(v[2][c], v[3][c]),
-                                   bf16_pair(v[4][c], v[5][c]), bf16_pair(v[6][c], v[7][c]));
-        *reinterpret_cast<uint4*>(wt + wt_off(8 * kg + c, g8)) = o;
-      }
+      gt::mfma16(af[s & 1], bw[s & 1], acc);
+      expand_quarter(wt_nxt, lk[s & 1], ah, s, g, q);  // on the last step into a buffer never read
+      mfma_interleave();
+      __builtin_amdgcn_sched_barrier(0);
     }
+    c1 = c2;
+    gt::wait_vmem();
     __syncthreads();
-    mfma_step();
+    lookup_quarter(lk[0], c1.w, tab, 0, slot);
   }
 
   // LoRA: reduction indices of [U_hi | U_lo | 0] against [A ; A ; 0]
-  for (int64_t j0 = 0; j0 < a.kl; j0 += kStep) {
-    __syncthreads();
+  if (a.kl > 0) {
+    const gt::ActPtrs up = gt::make_act_ptrs(a.u, a.kl, a.m, m0, wave, lane);
+    for (int64_t j0 = 0; j0 < a.kl; j0 += kStep) {
+      gt::dma_act(up, j0 / kStep, stage0, wave);
+      // the wave's Wt: column k0 + 64 w + 8 q + c, run g holds A[j0 + 8 g + e][column], e = 0..7
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int p = t + kThr * i;
-      const int64_t row = m0 + (p >> 3);
-      const int64_t rc = row < a.m ? row : a.m - 1;
-      *reinterpret_cast<uint4*>(dyt + (p >> 3) * kRowB + 16 * (p & 7)) =
-          *reinterpret_cast<const uint4*>(a.u + rc * a.kl + j0 + 8 * (p & 7));
-    }
-    {
-      // thread t fills Wt row t (tile column k0 + t) with A[j][col] for the step's 64 indices
-      const int64_t col = k0 + t;
-      const int64_t cc = col < a.cols ? col : a.cols - 1;
-#pragma unroll
-      for (int jg = 0; jg < 8; ++jg) {
+      for (int c = 0; c < 8; ++c) {
+        const int64_t col = k0 + 64 * wave + 8 * q + c;
+        const int64_t cc = col < a.cols ? col : a.cols - 1;
         uint32_t h[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-          const int64_t jj = j0 + 8 * jg + e;
+          const int64_t jj = j0 + 8 * g + e;
           const int64_t ja = jj < a.r_pad ? jj : jj - a.r_pad;
           const bool live = jj < 2 * a.r_pad && ja < a.r;
           h[e] = live ? a.la[ja * a.cols + cc] : 0u;
         }
-        *reinterpret_cast<uint4*>(wt + wt_off(t, jg)) =
-            make_uint4(h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16), h[6] | (h[7] << 16));
+        const u32x4 o = {h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16), h[6] | (h[7] << 16)};
+        *reinterpret_cast<u32x4*>(wt0 + wt_off(8 * q + c, g)) = o;
       }
+      gt::wait_vmem();
+      __syncthreads();
+      const char* xa = stage0 + (lane & 31) * gt::kActRowBytes;
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        bf16x8 af[8], bw[2];
+        gt::read_act(xa, s, sw, h4, af);
+        read_wt(wt0, s, lane, bw);
+        gt::mfma16(af, bw, acc);
+      }
+      __syncthreads();
     }
-    __syncthreads();
-    mfma_step();
   }
 
-  // epilogue: of each 32 x 32 tile of dX^T the lane holds element e at output
-  // column (e % 4) + 4 (lane / 32) + 8 (e / 4) and output row lane % 32
-  const bool vec = (a.cols & 3) == 0;
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int64_t row = m0 + i * 32 + (lane & 31);
-    if (row >= a.m) continue;
-    uint16_t* dr = a.dx + row * a.cols;
-#pragma unroll
-    for (int j = 0; j < 2; ++j) {
-#pragma unroll
-      for (int gq = 0; gq < 4; ++gq) {
-        const int64_t col = k0 + wave * 64 + j * 32 + 4 * (lane >> 5) + 8 * gq;
-        const uint32_t p0 = bf16_pair(acc[i][j][4 * gq], acc[i][j][4 * gq + 1]);
-        const uint32_t p1 = bf16_pair(acc[i][j][4 * gq + 2], acc[i][j][4 * gq + 3]);
-        if (vec && col + 3 < a.cols) {
-          *reinterpret_cast<uint2*>(dr + col) = make_uint2(p0, p1);
-        } else {
-          const uint16_t vv[4] = {static_cast<uint16_t>(p0), static_cast<uint16_t>(p0 >> 16),
-                                  static_cast<uint16_t>(p1), static_cast<uint16_t>(p1 >> 16)};
-          for (int e = 0; e < 4; ++e)
-            if (col + e < a.cols) dr[col + e] = vv[e];
-        }
-      }
-    }
-  }
+  gt::store_acc(acc, a.dx, a.m, a.cols, m0, k0, wave, lane);
 }
 
 // Elements of u before Bt in the workspace, rounded up to 256 bytes.
@@ -308,8 +390,8 @@ hipError_t launch_gemm_dx(const uint8_t* packed, int64_t rows, int64_t cols, Sca
     if (hipError_t e = launch_transpose_b(lora_b, rows, r, bt, s)) return e;
     if (hipError_t e = launch_lora_u(dy, bt, m, rows, r, lora_scale, ws, s)) return e;
   }
-  if (sc.absmax) hipLaunchKernelGGL(k_gemm_dx<false>, dim3(static_cast<unsigned>(tiles)), dim3(kThr), 0, s, a);
-  else hipLaunchKernelGGL(k_gemm_dx<true>, dim3(static_cast<unsigned>(tiles)), dim3(kThr), 0, s, a);
+  if (sc.absmax) hipLaunchKernelGGL(k_gemm_dx<false>, dim3(static_cast<unsigned>(tiles)), dim3(kThreads), 0, s, a);
+  else hipLaunchKernelGGL(k_gemm_dx<true>, dim3(static_cast<unsigned>(tiles)), dim3(kThreads), 0, s, a);
   return hipGetLastError();
 }
 
