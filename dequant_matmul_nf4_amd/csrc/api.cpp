@@ -172,10 +172,8 @@ int nf4_gemv(const nf4_weight* w, const void* x, int64_t m, void* y, int y_dtype
 }
 
 size_t nf4_gemm_workspace(int64_t m, int64_t rows, int32_t r) {
-  (void)rows;
-  if (m < 1 || r < 1 || r > 64) return 0;
-  const size_t bytes = static_cast<size_t>(m) * nf4i::gemm_lora_cols(r) * sizeof(uint16_t);
-  return (bytes + 255) & ~size_t(255);
+  if (m < 1 || rows < 1 || r < 1 || r > 64) return 0;
+  return (nf4i::gemm_workspace(m, rows, r) + 255) & ~size_t(255);
 }
 
 int nf4_gemm(const nf4_weight* w, const void* x, int64_t m, void* y, const void* lora_a,
@@ -186,6 +184,7 @@ int nf4_gemm(const nf4_weight* w, const void* x, int64_t m, void* y, const void*
   if (int rc = check_weight(w, &sc, &n, "nf4_gemm")) return rc;
   if (!x || !y) return fail(NF4_ERR_NULL, "nf4_gemm: x and y are required");
   if (w->cols % 64) return fail(NF4_ERR_SIZE, "nf4_gemm: cols = %lld is not a multiple of 64", (long long)w->cols);
+  if (w->cols >= (int64_t(1) << 23)) return fail(NF4_ERR_SIZE, "nf4_gemm: cols = %lld out of range", (long long)w->cols);
   if (m < 1 || m > (int64_t(1) << 31)) return fail(NF4_ERR_SIZE, "nf4_gemm: m = %lld out of range", (long long)m);
   if ((lora_a == nullptr) != (lora_b == nullptr))
     return fail(NF4_ERR_NULL, "nf4_gemm: lora_a and lora_b must both be NULL or both be set");
@@ -226,6 +225,9 @@ int nf4_gemm_dx(const nf4_weight* w, const void* dy, int64_t m, void* dx, const 
   if (w->cols % 64)
     return fail(NF4_ERR_SIZE, "nf4_gemm_dx: cols = %lld is not a multiple of 64", (long long)w->cols);
   if (w->rows % 8) return fail(NF4_ERR_SIZE, "nf4_gemm_dx: rows = %lld is not a multiple of 8", (long long)w->rows);
+  if (w->rows >= (int64_t(1) << 23) || w->cols >= (int64_t(1) << 23))
+    return fail(NF4_ERR_SIZE, "nf4_gemm_dx: rows = %lld, cols = %lld out of range", (long long)w->rows,
+                (long long)w->cols);
   if (m < 1 || m > (int64_t(1) << 31)) return fail(NF4_ERR_SIZE, "nf4_gemm_dx: m = %lld out of range", (long long)m);
   if ((lora_a == nullptr) != (lora_b == nullptr))
     return fail(NF4_ERR_NULL, "nf4_gemm_dx: lora_a and lora_b must both be NULL or both be set");

@@ -67,6 +67,10 @@ hipError_t launch_gemv(const uint8_t* packed, int64_t rows, int64_t cols, Scales
 // Extra K columns the GEMM uses for a LoRA term of rank r (0 without one);
 // the workspace holds m rows of that many bf16 values.
 size_t gemm_lora_cols(int r);
+// Workspace bytes of the forward GEMM with LoRA rank r: u (m rows of
+// gemm_lora_cols(r) bf16, rounded up to 256 bytes), then (B | B | 0) as rows
+// rows of the same width.
+size_t gemm_workspace(int64_t m, int64_t rows, int r);
 // u[i][.] = (bf16(s T[i][j]) for j < r | bf16(s T - hi) at r_pad + j | 0) with
 // T[i][j] = sum_k x[i][k] a[j][k] formed in float32, for the m rows of
 // x [m][len] and the r rows of a [r][len] (len % 8 == 0); each row of u holds

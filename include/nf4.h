@@ -143,8 +143,9 @@ int nf4_dequantize(const nf4_weight* w, void* out, int out_dtype, void* stream);
 int nf4_gemv(const nf4_weight* w, const void* x, int64_t m, void* y, int y_dtype,
              void* stream);
 
-/* Bytes of device workspace nf4_gemm needs for m rows of x and LoRA rank r
- * (0 when r == 0): m rows of 2 r (rounded up to 64) bf16 values. */
+/* Bytes of device workspace nf4_gemm needs for m rows of x, a weight of
+ * `rows` rows and LoRA rank r (0 when r == 0): m + rows rows of 2 r (rounded
+ * up to 64) bf16 values. */
 size_t nf4_gemm_workspace(int64_t m, int64_t rows, int32_t r);
 
 /* Dequantize-into-LDS bf16 matrix-core GEMM for prefill and training, with an
@@ -152,7 +153,8 @@ size_t nf4_gemm_workspace(int64_t m, int64_t rows, int32_t r);
  * and tool page "Fine-tuning with adapters on a 4-bit model": a frozen 4-bit
  * base plus low-rank adapters whose output is multiplied by a scale factor):
  *   y = x . deq(W)^T + lora_scale . (x . A^T) . B^T
- *   x      : bf16 [m][cols], 16-byte aligned, m >= 1, cols % 64 == 0.
+ *   x      : bf16 [m][cols], 16-byte aligned, m >= 1, cols % 64 == 0,
+ *            cols < 2^23.
  *   y      : bf16 [m][rows], 16-byte aligned.
  *   lora_a : bf16 [r][cols] and lora_b : bf16 [rows][r], both NULL (then r
  *            must be 0) or both set with 1 <= r <= 64; 16-byte aligned.
@@ -176,7 +178,7 @@ size_t nf4_gemm_dx_workspace(int64_t m, int64_t rows, int32_t r);
  * the backward of nf4_gemm's y = x . deq(W)^T + lora_scale . (x . A^T) . B^T
  * with respect to x.
  *   w      : the NF4 weight [rows][cols] (either scale form); cols % 64 == 0,
- *            rows % 8 == 0.
+ *            rows % 8 == 0, rows and cols < 2^23.
  *   dy     : bf16 [m][rows], 16-byte aligned, 1 <= m <= 2^31.
  *   dx     : bf16 [m][cols], 16-byte aligned, not overlapping dy.
  *   lora_a : bf16 [r][cols] and lora_b : bf16 [rows][r], both NULL (then r
