@@ -5,7 +5,9 @@ computes.  Only the tests, the smoke check and the CPU-baseline leg of the
 benchmark may import it; the product path (the HIP library and its Python
 binding) never does, and the two share no code, tables or constants.
 
-Sources (web pages, cited by title and section):
+Sources (web pages, cited by title and section; plus the Open Compute
+Project's 8-bit floating point specification for the E4M3 format of the
+float8 second-level reading):
   [TOOL]  "bitsandbytes" (ozercemkelahmet.com/tools/bitsandbytes):
           "How it works" Steps 1-5, "How NF4 works", "Double quantization",
           "A worked example", "Memory arithmetic", "Practical guidance and
@@ -226,15 +228,113 @@ def double_quant(absmax: np.ndarray, blocksize2: int = BLOCKSIZE2):
     return q, s2, mean
 
 
-def dequant_scales(q: np.ndarray, absmax2: np.ndarray, mean, blocksize2: int = BLOCKSIZE2) -> np.ndarray:
+def dequant_scales(q: np.ndarray, absmax2: np.ndarray, mean, blocksize2: int = BLOCKSIZE2,
+                   kind: str = "int8") -> np.ndarray:
     """a_hat = fl32(fl32(fl32(q / 127) * s2) + mean): [TOOL] "A worked example"
-    (divide by 127, multiply by the scale) followed by adding the mean back."""
-    q = np.asarray(q, dtype=np.int8).reshape(-1)
+    (divide by 127, multiply by the scale) followed by adding the mean back.
+    kind="fp8": the first factor is fl32(e4m3(q) / 448) instead (see below)."""
     s2 = np.asarray(absmax2, dtype=np.float32).reshape(-1)
-    g = np.arange(q.size) // blocksize2
-    t = (q.astype(np.float32) / np.float32(127.0)).astype(np.float32)
+    if kind == "fp8":
+        codes = np.asarray(q).reshape(-1).view(np.uint8) if np.asarray(q).dtype != np.uint8 else np.asarray(q).reshape(-1)
+        t = e4m3_ratio_table()[codes.astype(np.int64)]
+    else:
+        q = np.asarray(q, dtype=np.int8).reshape(-1)
+        t = (q.astype(np.float32) / np.float32(127.0)).astype(np.float32)
+    g = np.arange(t.size) // blocksize2
     t = (t * s2[g]).astype(np.float32)
     return (t + np.float32(mean)).astype(np.float32)
+
+
+# ------------------------------------------- float8 second level (READING C18)
+#
+# [TUT] "How NF4 Works" says the scales go from float32 to float8.  The pages
+# name no 8-bit float format; the reading here is E4M3 as defined in the Open
+# Compute Project's 8-bit floating point specification (OFP8): 1 sign bit, 4
+# exponent bits with bias 7, 3 mantissa bits, subnormals, no infinities, the
+# all-ones exponent and mantissa pattern is NaN, largest finite value 448.
+# The step mirrors the int8 one: t = fl32(fl32(c / s2) * 448), the code is
+# the E4M3 value nearest to t (ties to the even mantissa), and dequantization
+# multiplies fl32(e4m3(q) / 448) by s2 and adds the mean back.
+
+E4M3_MAX = 448.0
+
+
+def e4m3_value(code: int) -> float:
+    """The value of an E4M3 code (NaN for the two NaN patterns)."""
+    code = int(code) & 0xFF
+    sign = -1.0 if code & 0x80 else 1.0
+    e = (code >> 3) & 0xF
+    m = code & 0x7
+    if e == 0xF and m == 0x7:
+        return float("nan")
+    if e == 0:
+        return sign * m * 2.0 ** -9          # subnormal: m/8 * 2^(1 - 7)
+    return sign * (1.0 + m / 8.0) * 2.0 ** (e - 7)
+
+
+def e4m3_encode(t: np.ndarray) -> np.ndarray:
+    """E4M3 code nearest to each float32 t with |t| <= 448, ties to the even
+    mantissa; the sign of t is kept (t = +0 gives code 0)."""
+    t = np.asarray(t, dtype=np.float32).reshape(-1)
+    finite = [(e4m3_value(c), c) for c in range(0x7F)]          # +0 .. 448, ascending
+    mags = np.array([v for v, _ in finite], dtype=np.float64)
+    out = np.empty(t.size, dtype=np.uint8)
+    for i, x in enumerate(t.astype(np.float64)):
+        a = abs(x)
+        if not a <= E4M3_MAX:
+            raise ValueError("e4m3_encode: |t| out of range")
+        k = int(np.searchsorted(mags, a))            # mags[k - 1] < a <= mags[k]
+        if k < mags.size and mags[k] == a:
+            c = k
+        else:
+            lo, hi = k - 1, k
+            dlo, dhi = a - mags[lo], mags[hi] - a
+            if dlo < dhi:
+                c = lo
+            elif dhi < dlo:
+                c = hi
+            else:
+                c = lo if (lo & 1) == 0 else hi     # even mantissa (codes alternate parity)
+        out[i] = c | (0x80 if x < 0 else 0)
+    return out
+
+
+def e4m3_ratio_table() -> np.ndarray:
+    """fl32(e4m3(q) / 448) for every code q (0 for the NaN codes, never produced)."""
+    tab = np.zeros(256, dtype=np.float32)
+    for c in range(256):
+        v = e4m3_value(c)
+        if v == v:
+            tab[c] = np.float32(v) / np.float32(E4M3_MAX)
+    return tab
+
+
+def f8_absmax_quantize(v: np.ndarray, blocksize: int):
+    """The float8 reading of the second level: per block s = max |v|,
+    t = fl32(fl32(v / s) * 448), q = e4m3_encode(t); s = 0 gives code 0.
+    Returns (q uint8, s float32)."""
+    v = np.asarray(v, dtype=np.float32).reshape(-1)
+    nb = -(-v.size // blocksize)
+    padded = np.zeros(nb * blocksize, dtype=np.float32)
+    padded[: v.size] = v
+    blocks = padded.reshape(nb, blocksize)
+    s = np.abs(blocks).max(axis=1).astype(np.float32)
+    safe = np.where(s > 0, s, np.float32(1.0)).astype(np.float32)
+    with np.errstate(under="ignore"):
+        t = (blocks / safe[:, None]).astype(np.float32) * np.float32(E4M3_MAX)
+    t = t.astype(np.float32)
+    t[s == 0] = 0.0
+    q = e4m3_encode(t.reshape(-1)).reshape(nb, blocksize)
+    return q.reshape(-1)[: v.size], s
+
+
+def double_quant_f8(absmax: np.ndarray, blocksize2: int = BLOCKSIZE2):
+    """Returns (qabsmax uint8 E4M3 codes [nb], absmax2 float32 [ceil(nb/256)], mean float32)."""
+    a = np.asarray(absmax, dtype=np.float32).reshape(-1)
+    mean = exact_mean_f32(a)
+    centred = (a - mean).astype(np.float32)
+    q, s2 = f8_absmax_quantize(centred, blocksize2)
+    return q, s2, mean
 
 
 # ------------------------------------------------------------- dequantization
@@ -251,17 +351,18 @@ def bf16_bits_to_f32(b: np.ndarray) -> np.ndarray:
 
 
 def dequantize(packed, n: int, absmax=None, qabsmax=None, absmax2=None, mean=None,
-               blocksize: int = BLOCKSIZE, blocksize2: int = BLOCKSIZE2, out: str = "f32"):
+               blocksize: int = BLOCKSIZE, blocksize2: int = BLOCKSIZE2, out: str = "f32", dq_kind: str = "int8"):
     """[TOOL] "How it works", Step 5: expand each code with its block's scale.
 
     w = fl32(level[code] * a_hat); for out="bf16" the float32 value is rounded
-    once to nearest even and the bf16 bit patterns (uint16) are returned."""
+    once to nearest even and the bf16 bit patterns (uint16) are returned.
+    dq_kind selects the second level's reading (int8 or fp8)."""
     codes = unpack(packed, n)
     lv = codebook()
     if absmax is not None:
         a_hat = np.asarray(absmax, dtype=np.float32).reshape(-1)
     else:
-        a_hat = dequant_scales(qabsmax, absmax2, mean, blocksize2)
+        a_hat = dequant_scales(qabsmax, absmax2, mean, blocksize2, kind=dq_kind)
     blk = np.arange(n) // blocksize
     w = (lv[codes] * a_hat[blk]).astype(np.float32)
     if out == "f32":

@@ -527,3 +527,112 @@ def test_backward_ref_is_the_gradient_of_the_forward():
     assert np.allclose(bf, dx, rtol=1e-12, atol=1e-12)
     dx0, da0, db0 = oracle.backward_ref(dy, w)
     assert da0 is None and db0 is None and np.allclose(dx0, dy @ w)
+
+
+# ------------------------------------------- float8 second level (reading C18)
+
+def test_e4m3_values_closed_forms_and_library_decode():
+    """Decoding: the landmarks of the format, strict order of the 127
+    non-negative finite codes, sign symmetry, and agreement with torch's
+    independent float8_e4m3fn conversion for every code."""
+    v = np.array([oracle.e4m3_value(c) for c in range(256)])
+    assert v[0x00] == 0.0 and v[0x01] == 2.0 ** -9 and v[0x07] == 7 * 2.0 ** -9
+    assert v[0x08] == 2.0 ** -6 and v[0x38] == 1.0 and v[0x7E] == 448.0
+    assert np.isnan(v[0x7F]) and np.isnan(v[0xFF])
+    assert np.all(np.diff(v[:0x7F]) > 0)
+    for c in range(0x7F):
+        assert v[c | 0x80] == -v[c]
+    torch = pytest.importorskip("torch")
+    tv = torch.arange(256, dtype=torch.uint8).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    ok = ~np.isnan(v)
+    assert np.array_equal(np.isnan(tv), np.isnan(v))
+    assert np.array_equal(tv[ok], v[ok])
+
+
+def _e4m3_nearest_exact(x: float) -> int:
+    """Brute force over all finite codes with exact rationals, ties to the even code."""
+    fx = Fraction(x)
+    best = None
+    for c in range(0x7F):
+        d = abs(abs(fx) - Fraction(oracle.e4m3_value(c)))
+        if best is None or d < best[0] or (d == best[0] and c % 2 == 0):
+            best = (d, c)
+    return best[1] | (0x80 if x < 0 else 0)
+
+
+def test_e4m3_encode_brute_force_and_ties():
+    rng = np.random.default_rng(18)
+    xs = np.concatenate([
+        rng.uniform(-448, 448, 300).astype(np.float32),
+        (rng.standard_normal(300) * 4).astype(np.float32),
+        rng.uniform(-2.0 ** -6, 2.0 ** -6, 200).astype(np.float32),   # subnormal range
+        np.float32([0.0, 448.0, -448.0, 2.0 ** -10, 3 * 2.0 ** -10, 2.0 ** -9]),
+    ]).astype(np.float32)
+    got = oracle.e4m3_encode(xs)
+    want = np.array([_e4m3_nearest_exact(float(x)) for x in xs], dtype=np.uint8)
+    assert np.array_equal(got, want)
+    # every midpoint between neighbouring codes is representable in fp32 and
+    # must go to the even code
+    mids, even = [], []
+    for c in range(0x7E):
+        m = (oracle.e4m3_value(c) + oracle.e4m3_value(c + 1)) / 2
+        assert float(np.float32(m)) == m
+        mids.append(m)
+        even.append(c if c % 2 == 0 else c + 1)
+    assert np.array_equal(oracle.e4m3_encode(np.float32(mids)), np.array(even, dtype=np.uint8))
+    assert np.array_equal(oracle.e4m3_encode(-np.float32(mids)), np.array(even, dtype=np.uint8) | 0x80)
+    # round trip of every finite code
+    vals = np.float32([oracle.e4m3_value(c) for c in range(0x7F)])
+    assert np.array_equal(oracle.e4m3_encode(vals), np.arange(0x7F, dtype=np.uint8))
+    torch = pytest.importorskip("torch")
+    tq = torch.from_numpy(xs).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert np.array_equal(got & 0x7F, tq & 0x7F)
+
+
+def test_e4m3_ratio_table_is_the_rounded_quotient():
+    tab = oracle.e4m3_ratio_table()
+    for c in range(256):
+        v = oracle.e4m3_value(c)
+        if v != v:
+            assert tab[c] == 0.0
+            continue
+        assert tab[c] == np.float32(rn32(Fraction(v) / 448))
+
+
+def test_f8_double_quant_invariants():
+    """Each group with s2 > 0 reaches the largest magnitude 448 (codes 0x7E /
+    0xFE); every a_hat is within half an E4M3 step (relative 2^-4, or 2^-10
+    absolute in the subnormal range, scaled by s2 / 448) plus fp32 roundings
+    of the scale; the mean is the exact one of the int8 reading."""
+    rng = np.random.default_rng(81)
+    a = np.abs(normal_f32((3 * 256 + 17,), 0.02, 81)).astype(np.float32)
+    a[5] *= 40.0
+    a[300] = 0.0
+    q, s2, mean = oracle.double_quant_f8(a)
+    _, _, mean_i8 = oracle.double_quant(a)
+    assert mean == mean_i8 and q.dtype == np.uint8
+    c = (a - mean).astype(np.float32)
+    a_hat = oracle.dequant_scales(q, s2, mean, kind="fp8")
+    for g in range(s2.size):
+        sl = slice(256 * g, min(256 * (g + 1), a.size))
+        assert s2[g] == np.abs(c[sl]).max()
+        if s2[g] > 0:
+            assert np.any((q[sl] & 0x7F) == 0x7E)
+        for i in range(sl.start, sl.stop):
+            err = abs(float(a_hat[i]) - float(a[i]))
+            bound = max(abs(float(c[i])) * 2.0 ** -4, float(s2[g]) / 448 * 2.0 ** -10) + 4e-7 * (abs(float(a[i])) + float(s2[g]))
+            assert err <= bound, (i, err, bound)
+    # hand check of one value: code 0x38 (1.0) means a_hat = fl32(fl32(s2 / 448) ... ) path
+    assert oracle.dequant_scales(np.uint8([0x38]), np.float32([448.0]), np.float32(0.5), kind="fp8")[0] == np.float32(1.5)
+
+
+def test_dequantize_with_f8_scales_is_the_per_element_product():
+    w = normal_f32((3000,), 0.02, 83)
+    p, a = oracle.quantize(w)
+    q, s2, mean = oracle.double_quant_f8(a)
+    got = oracle.dequantize(p, w.size, qabsmax=q, absmax2=s2, mean=mean, dq_kind="fp8")
+    a_hat = oracle.dequant_scales(q, s2, mean, kind="fp8")
+    codes = oracle.unpack(p, w.size)
+    lv = oracle.codebook()
+    for i in range(0, w.size, 7):
+        assert got[i] == np.float32(rn32(frac(lv[codes[i]]) * frac(a_hat[i // 64])))
