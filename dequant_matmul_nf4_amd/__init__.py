@@ -19,11 +19,12 @@ LIB_PATH = os.path.join(_HERE, "libnf4.so")
 
 NF4_OK, NF4_ERR_NULL, NF4_ERR_SIZE, NF4_ERR_BLOCKSIZE, NF4_ERR_ALIGN, NF4_ERR_DTYPE, NF4_ERR_WORKSPACE, NF4_ERR_DEVICE = range(8)
 NF4_F32, NF4_BF16, NF4_F16 = 0, 1, 2
+NF4_DQ_INT8, NF4_DQ_FP8 = 0, 1
 BLOCKSIZE, BLOCKSIZE2 = 64, 256
 
 EXPORTS = (
     "nf4_last_error", "nf4_codebook", "nf4_quantize", "nf4_double_quant_workspace",
-    "nf4_double_quant", "nf4_dequantize", "nf4_gemv", "nf4_gemm_workspace", "nf4_gemm", "nf4_gemm_dx_workspace",
+    "nf4_double_quant", "nf4_e4m3_ratio", "nf4_double_quant_f8", "nf4_dequantize", "nf4_gemv", "nf4_gemm_workspace", "nf4_gemm", "nf4_gemm_dx_workspace",
     "nf4_gemm_dx", "nf4_lora_grads_workspace", "nf4_lora_grads", "nf4_lora_merge",
 )
 
@@ -40,6 +41,7 @@ class nf4_weight(ctypes.Structure):
         ("packed", ctypes.c_void_p), ("rows", ctypes.c_int64), ("cols", ctypes.c_int64),
         ("blocksize", ctypes.c_int32), ("absmax", ctypes.c_void_p), ("qabsmax", ctypes.c_void_p),
         ("absmax2", ctypes.c_void_p), ("mean", ctypes.c_void_p), ("blocksize2", ctypes.c_int32),
+        ("dq_type", ctypes.c_int32),
     ]
 
 
@@ -62,6 +64,8 @@ def lib() -> ctypes.CDLL:
         "nf4_quantize": (ctypes.c_int, [vp, ctypes.c_int, i64, i32, vp, vp, vp]),
         "nf4_double_quant_workspace": (sz, [i64]),
         "nf4_double_quant": (ctypes.c_int, [vp, i64, i32, vp, vp, vp, vp, sz, vp]),
+        "nf4_double_quant_f8": (ctypes.c_int, [vp, i64, i32, vp, vp, vp, vp, sz, vp]),
+        "nf4_e4m3_ratio": (ctypes.c_int, [ctypes.POINTER(ctypes.c_float)]),
         "nf4_dequantize": (ctypes.c_int, [wp, vp, ctypes.c_int, vp]),
         "nf4_gemv": (ctypes.c_int, [wp, vp, i64, vp, ctypes.c_int, vp]),
         "nf4_gemm_workspace": (sz, [i64, i64, i32]),
@@ -92,6 +96,13 @@ def nf4_codebook():
     """The 16 NF4 levels (host call, needs no GPU) as a list of floats."""
     out = (ctypes.c_float * 16)()
     _check(lib().nf4_codebook(out))
+    return list(out)
+
+
+def nf4_e4m3_ratio():
+    """fl32(e4m3(q) / 448) for the 256 float8 codes (host call, needs no GPU)."""
+    out = (ctypes.c_float * 256)()
+    _check(lib().nf4_e4m3_ratio(out))
     return list(out)
 
 
@@ -155,6 +166,7 @@ class NF4Weight:
     qabsmax: "object" = None
     absmax2: "object" = None
     mean: "object" = None
+    dq_type: int = 0  # NF4_DQ_INT8 or NF4_DQ_FP8 (second-level codes)
 
     @property
     def double_quant(self) -> bool:
@@ -164,7 +176,7 @@ class NF4Weight:
         return nf4_weight(
             packed=_ptr(self.packed), rows=self.rows, cols=self.cols, blocksize=BLOCKSIZE,
             absmax=_ptr(self.absmax), qabsmax=_ptr(self.qabsmax), absmax2=_ptr(self.absmax2),
-            mean=_ptr(self.mean), blocksize2=BLOCKSIZE2,
+            mean=_ptr(self.mean), blocksize2=BLOCKSIZE2, dq_type=self.dq_type,
         )
 
 
@@ -184,15 +196,17 @@ def nf4_quantize(x, packed=None, absmax=None, stream=None):
     return packed, absmax
 
 
-def nf4_double_quant(absmax, qabsmax=None, absmax2=None, mean=None, workspace=None, stream=None):
-    """Double quantization of the fp32 scales: returns (qabsmax, absmax2, mean)."""
+def nf4_double_quant(absmax, qabsmax=None, absmax2=None, mean=None, workspace=None, stream=None, fp8=False):
+    """Double quantization of the fp32 scales: returns (qabsmax, absmax2, mean).
+    fp8=True: the float8 (E4M3) second level, codes as uint8."""
     torch = _torch()
     _need_cuda(absmax)
     if absmax.dtype != torch.float32:
         raise TypeError("absmax must be float32")
     nb = absmax.numel()
     dev = absmax.device
-    qabsmax = torch.empty(nb, dtype=torch.int8, device=dev) if qabsmax is None else qabsmax
+    if qabsmax is None:
+        qabsmax = torch.empty(nb, dtype=torch.uint8 if fp8 else torch.int8, device=dev)
     absmax2 = torch.empty((nb + 255) // 256, dtype=torch.float32, device=dev) if absmax2 is None else absmax2
     mean = torch.empty(1, dtype=torch.float32, device=dev) if mean is None else mean
     wsb = nf4_double_quant_workspace(nb)
@@ -201,19 +215,24 @@ def nf4_double_quant(absmax, qabsmax=None, absmax2=None, mean=None, workspace=No
     _need_cuda(qabsmax, absmax2, mean, workspace)
     if qabsmax.numel() < nb or absmax2.numel() < (nb + 255) // 256 or mean.numel() < 1:
         raise ValueError("output buffers too small")
-    _check(lib().nf4_double_quant(_ptr(absmax), nb, BLOCKSIZE2, _ptr(qabsmax), _ptr(absmax2), _ptr(mean),
-                                  _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream)))
+    fn = lib().nf4_double_quant_f8 if fp8 else lib().nf4_double_quant
+    _check(fn(_ptr(absmax), nb, BLOCKSIZE2, _ptr(qabsmax), _ptr(absmax2), _ptr(mean),
+              _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream)))
     return qabsmax, absmax2, mean
 
 
-def quantize_weight(w, double_quant: bool = True, stream=None) -> NF4Weight:
-    """nf4_quantize (+ nf4_double_quant) of a 2-D weight into an NF4Weight."""
+def quantize_weight(w, double_quant: bool = True, stream=None, dq_type: str = "int8") -> NF4Weight:
+    """nf4_quantize (+ nf4_double_quant, int8 or fp8 second level) of a 2-D
+    weight into an NF4Weight."""
     rows, cols = w.shape
     packed, absmax = nf4_quantize(w, stream=stream)
     if not double_quant:
         return NF4Weight(packed, rows, cols, absmax=absmax)
-    q, s2, mean = nf4_double_quant(absmax, stream=stream)
-    return NF4Weight(packed, rows, cols, qabsmax=q, absmax2=s2, mean=mean)
+    if dq_type not in ("int8", "fp8"):
+        raise ValueError("dq_type must be 'int8' or 'fp8'")
+    fp8 = dq_type == "fp8"
+    q, s2, mean = nf4_double_quant(absmax, stream=stream, fp8=fp8)
+    return NF4Weight(packed, rows, cols, qabsmax=q, absmax2=s2, mean=mean, dq_type=NF4_DQ_FP8 if fp8 else NF4_DQ_INT8)
 
 
 def nf4_dequantize(w: NF4Weight, out=None, out_dtype=None, stream=None):

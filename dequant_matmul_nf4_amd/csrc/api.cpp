@@ -76,7 +76,7 @@ int check_weight(const nf4_weight* w, nf4i::Scales* sc, int64_t* n_out, const ch
   const int64_t nb = (n + 63) / 64;
   if (w->absmax) {
     if (!aligned(w->absmax, 4)) return fail(NF4_ERR_ALIGN, "%s: absmax must be 4-byte aligned", who);
-    *sc = nf4i::Scales{w->absmax, nullptr, nullptr, nullptr};
+    *sc = nf4i::Scales{w->absmax, nullptr, nullptr, nullptr, 0};
   } else {
     if (!w->qabsmax || !w->absmax2 || !w->mean)
       return fail(NF4_ERR_NULL, "%s: absmax is NULL, so qabsmax, absmax2 and mean are required", who);
@@ -85,7 +85,9 @@ int check_weight(const nf4_weight* w, nf4i::Scales* sc, int64_t* n_out, const ch
     if (nb >= (int64_t(1) << 31)) return fail(NF4_ERR_SIZE, "%s: too many blocks for double quant", who);
     if (!aligned(w->absmax2, 4) || !aligned(w->mean, 4))
       return fail(NF4_ERR_ALIGN, "%s: absmax2 and mean must be 4-byte aligned", who);
-    *sc = nf4i::Scales{nullptr, w->qabsmax, w->absmax2, w->mean};
+    if (w->dq_type != NF4_DQ_INT8 && w->dq_type != NF4_DQ_FP8)
+      return fail(NF4_ERR_DTYPE, "%s: dq_type %d unknown", who, (int)w->dq_type);
+    *sc = nf4i::Scales{nullptr, w->qabsmax, w->absmax2, w->mean, w->dq_type == NF4_DQ_FP8 ? 1 : 0};
   }
   *n_out = n;
   return NF4_OK;
@@ -96,6 +98,30 @@ hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
 }  // namespace
 
 int nf4i::device_cus() { return t_cus; }
+
+namespace {
+
+int double_quant(const float* absmax, int64_t nblocks, int32_t blocksize2, int8_t* qabsmax, float* absmax2,
+                 float* mean, void* workspace, size_t workspace_bytes, void* stream, int f8, const char* who) {
+  if (!absmax || !qabsmax || !absmax2 || !mean)
+    return fail(NF4_ERR_NULL, "%s: absmax, qabsmax, absmax2 and mean are required", who);
+  if (nblocks < 1 || nblocks >= (int64_t(1) << 31))
+    return fail(NF4_ERR_SIZE, "%s: nblocks = %lld out of range", who, (long long)nblocks);
+  if (blocksize2 != NF4_BLOCKSIZE2)
+    return fail(NF4_ERR_BLOCKSIZE, "%s: blocksize2 %d unsupported (only 256)", who, (int)blocksize2);
+  if (!workspace || workspace_bytes < nf4i::kDqWorkspaceBytes)
+    return fail(NF4_ERR_WORKSPACE, "%s: workspace needs %zu bytes", who, nf4i::kDqWorkspaceBytes);
+  if (!aligned(absmax, 16) || !aligned(qabsmax, 16) || !aligned(workspace, 16))
+    return fail(NF4_ERR_ALIGN, "%s: absmax, qabsmax and workspace must be 16-byte aligned", who);
+  if (!aligned(absmax2, 4) || !aligned(mean, 4))
+    return fail(NF4_ERR_ALIGN, "%s: absmax2 and mean must be 4-byte aligned", who);
+  if (int rc = check_device()) return rc;
+  return launched(nf4i::launch_double_quant(absmax, nblocks, qabsmax, absmax2, mean,
+                                            static_cast<unsigned long long*>(workspace), f8, as_stream(stream)),
+                  who);
+}
+
+}  // namespace
 
 extern "C" {
 
@@ -124,25 +150,25 @@ size_t nf4_double_quant_workspace(int64_t nblocks) {
   return nf4i::kDqWorkspaceBytes;
 }
 
+int nf4_e4m3_ratio(float out[256]) {
+  if (!out) return fail(NF4_ERR_NULL, "nf4_e4m3_ratio: out is NULL");
+  constexpr nf4i::E4m3Ratio t = nf4i::make_e4m3_ratio();
+  for (int c = 0; c < 256; ++c) out[c] = t.v[c];
+  return ok();
+}
+
 int nf4_double_quant(const float* absmax, int64_t nblocks, int32_t blocksize2, int8_t* qabsmax,
                      float* absmax2, float* mean, void* workspace, size_t workspace_bytes,
                      void* stream) {
-  if (!absmax || !qabsmax || !absmax2 || !mean)
-    return fail(NF4_ERR_NULL, "nf4_double_quant: absmax, qabsmax, absmax2 and mean are required");
-  if (nblocks < 1 || nblocks >= (int64_t(1) << 31))
-    return fail(NF4_ERR_SIZE, "nf4_double_quant: nblocks = %lld out of range", (long long)nblocks);
-  if (blocksize2 != NF4_BLOCKSIZE2)
-    return fail(NF4_ERR_BLOCKSIZE, "nf4_double_quant: blocksize2 %d unsupported (only 256)", (int)blocksize2);
-  if (!workspace || workspace_bytes < nf4i::kDqWorkspaceBytes)
-    return fail(NF4_ERR_WORKSPACE, "nf4_double_quant: workspace needs %zu bytes", nf4i::kDqWorkspaceBytes);
-  if (!aligned(absmax, 16) || !aligned(qabsmax, 16) || !aligned(workspace, 16))
-    return fail(NF4_ERR_ALIGN, "nf4_double_quant: absmax, qabsmax and workspace must be 16-byte aligned");
-  if (!aligned(absmax2, 4) || !aligned(mean, 4))
-    return fail(NF4_ERR_ALIGN, "nf4_double_quant: absmax2 and mean must be 4-byte aligned");
-  if (int rc = check_device()) return rc;
-  return launched(nf4i::launch_double_quant(absmax, nblocks, qabsmax, absmax2, mean,
-                                            static_cast<unsigned long long*>(workspace), as_stream(stream)),
-                  "nf4_double_quant");
+  return double_quant(absmax, nblocks, blocksize2, qabsmax, absmax2, mean, workspace, workspace_bytes, stream, 0,
+                      "nf4_double_quant");
+}
+
+int nf4_double_quant_f8(const float* absmax, int64_t nblocks, int32_t blocksize2, uint8_t* qabsmax,
+                        float* absmax2, float* mean, void* workspace, size_t workspace_bytes,
+                        void* stream) {
+  return double_quant(absmax, nblocks, blocksize2, reinterpret_cast<int8_t*>(qabsmax), absmax2, mean, workspace,
+                      workspace_bytes, stream, 1, "nf4_double_quant_f8");
 }
 
 int nf4_dequantize(const nf4_weight* w, void* out, int out_dtype, void* stream) {

@@ -1,6 +1,9 @@
 // Double quantization of the block scales (bitsandbytes tool page, "Double
 // quantization", with the int8 scheme of its "A worked example": scale by 127,
 // round half away from zero).  The scales are first centred on their mean.
+// The float8 variant (tutorial page "bitsandbytes quantization tutorial:
+// 4-bit and 8-bit models", section "How NF4 Works": float32 to float8) scales
+// by 448 instead and stores the nearest E4M3 code.
 //
 // The mean must not depend on summation order, so the scales are summed
 // exactly: each float32 is an integer m * 2^p times 2^-149 (m < 2^24,
@@ -173,6 +176,21 @@ __device__ float dq_mean(const unsigned long long* __restrict__ ws, int nparts, 
   return mean_s;
 }
 
+// E4M3 code of t, |t| <= 448, nearest with ties to the even mantissa (the
+// float8 reading): subnormals (|t| < 2^-6) are multiples of 2^-9, rounded by
+// rintf on t * 2^9 (exact scaling); normal values round the float32
+// significand to 3 bits at bit 20 (a carry moves into the exponent).  448 is
+// the largest finite E4M3 value, so the NaN pattern is never produced.
+__device__ __forceinline__ uint32_t e4m3_rne(float t) {
+  const uint32_t sign = (__float_as_uint(t) >> 24) & 0x80u;
+  const float a = fabsf(t);
+  if (a < 0x1p-6f) return sign | static_cast<uint32_t>(rintf(a * 512.0f));  // 0..8; 8 is 2^-6 = code 0x08
+  const uint32_t b = __float_as_uint(a);
+  const uint32_t r = b + 0x7FFFFu + ((b >> 20) & 1u);
+  return sign | ((((r >> 23) - 127u + 7u) << 3) | ((r >> 20) & 7u));
+}
+
+template <bool kF8>
 __global__ __launch_bounds__(256) void k_dq_quant(const float* __restrict__ absmax, int64_t nb,
                                                   const unsigned long long* __restrict__ ws, int nparts,
                                                   float* __restrict__ mean_out, int8_t* __restrict__ q,
@@ -208,13 +226,18 @@ __global__ __launch_bounds__(256) void k_dq_quant(const float* __restrict__ absm
     if (s > 0.0f) {
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const float t = (c[j] / s) * 127.0f;
-        const float at = fabsf(t);
-        const float fl = floorf(at);
-        float r = fl + ((at - fl) >= 0.5f ? 1.0f : 0.0f);  // half away from zero
-        r = fminf(r, 127.0f);
-        const int qi = (t < 0.0f) ? -static_cast<int>(r) : static_cast<int>(r);
-        word |= (static_cast<uint32_t>(qi) & 0xFFu) << (8 * j);
+        if constexpr (kF8) {
+          const float t = (c[j] / s) * 448.0f;  // two roundings, as the int8 step
+          word |= e4m3_rne(t) << (8 * j);
+        } else {
+          const float t = (c[j] / s) * 127.0f;
+          const float at = fabsf(t);
+          const float fl = floorf(at);
+          float r = fl + ((at - fl) >= 0.5f ? 1.0f : 0.0f);  // half away from zero
+          r = fminf(r, 127.0f);
+          const int qi = (t < 0.0f) ? -static_cast<int>(r) : static_cast<int>(r);
+          word |= (static_cast<uint32_t>(qi) & 0xFFu) << (8 * j);
+        }
       }
     }
     if (i0 + 4 <= nb) {
@@ -230,14 +253,15 @@ __global__ __launch_bounds__(256) void k_dq_quant(const float* __restrict__ absm
 }  // namespace
 
 hipError_t launch_double_quant(const float* absmax, int64_t nb, int8_t* q, float* absmax2,
-                               float* mean, unsigned long long* ws, hipStream_t s) {
+                               float* mean, unsigned long long* ws, int f8, hipStream_t s) {
   int64_t want = (nb + 256 * kPerThread - 1) / (256 * kPerThread);
   int grid = static_cast<int>(want < kDqMaxGroups ? want : kDqMaxGroups);
   hipLaunchKernelGGL(k_dq_partial, dim3(grid), dim3(256), 0, s, absmax, nb, ws);
   const int64_t groups = (nb + 255) >> 8;
   want = (groups + 3) / 4;  // 4 waves per workgroup
   const int qgrid = static_cast<int>(want < 1024 ? want : 1024);
-  hipLaunchKernelGGL(k_dq_quant, dim3(qgrid), dim3(256), 0, s, absmax, nb, ws, grid, mean, q, absmax2);
+  if (f8) hipLaunchKernelGGL(k_dq_quant<true>, dim3(qgrid), dim3(256), 0, s, absmax, nb, ws, grid, mean, q, absmax2);
+  else hipLaunchKernelGGL(k_dq_quant<false>, dim3(qgrid), dim3(256), 0, s, absmax, nb, ws, grid, mean, q, absmax2);
   return hipGetLastError();
 }
 

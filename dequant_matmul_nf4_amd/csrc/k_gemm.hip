@@ -159,10 +159,10 @@ __device__ __forceinline__ void mfma_interleave() {
 }
 
 template <bool kDQ>
-__device__ __forceinline__ void block_scales(const WRegs& wr, float mean, float (&sa)[2]) {
+__device__ __forceinline__ void block_scales(const WRegs& wr, float mean, int f8, float (&sa)[2]) {
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
-    if constexpr (kDQ) sa[j] = (div127(wr.q[j]) * wr.s2[j]) + mean;  // a_hat, three roundings
+    if constexpr (kDQ) sa[j] = (code_ratio(wr.q[j], f8) * wr.s2[j]) + mean;  // a_hat, three roundings
     else sa[j] = wr.am[j];
   }
 }
@@ -223,7 +223,7 @@ __global__ __launch_bounds__(kThreads, kWgPerCu) void k_gemm(GemmArgs a) {
     Lookups lk[3];
     bf16x8 af[3][kMI];
     const uint32_t sw = ((lane & 31) >> 1) & 7, h4 = (lane >> 5) * 4;
-    block_scales<kDQ>(wc, mean, sa);
+    block_scales<kDQ>(wc, mean, a.sc.f8, sa);
     lookup_step<kCopies>(lk[0], wc.w, 0, tabc, slot);
     bf[0][0] = expand_frag(lk[0].l[0], sa[0]);
     bf[0][1] = expand_frag(lk[0].l[1], sa[1]);
@@ -263,7 +263,7 @@ __global__ __launch_bounds__(kThreads, kWgPerCu) void k_gemm(GemmArgs a) {
       __builtin_amdgcn_sched_barrier(0);
       // s = 3, with the next step's s = 0 expansion
       gt::mfma16(af[0], bf[1], acc);
-      block_scales<kDQ>(wnx, mean, sa);
+      block_scales<kDQ>(wnx, mean, a.sc.f8, sa);
       lookup_step<kCopies>(lk[1], wnx.w, 0, tabc, slot);
       bf[0][0] = expand_frag(lk[1].l[0], sa[0]);
       bf[0][1] = expand_frag(lk[1].l[1], sa[1]);

@@ -121,8 +121,8 @@ __device__ __forceinline__ void load_codes(CodeRegs& r, const CodePtrs& p, const
 }
 
 template <bool kDQ>
-__device__ __forceinline__ float row_scale(const CodeRegs& r, float mean) {
-  if constexpr (kDQ) return div127(r.q) * r.s2 + mean;  // a_hat: three roundings (contraction is off)
+__device__ __forceinline__ float row_scale(const CodeRegs& r, float mean, int f8) {
+  if constexpr (kDQ) return code_ratio(r.q, f8) * r.s2 + mean;  // a_hat: three roundings (contraction is off)
   else return r.am;
 }
 
@@ -246,7 +246,7 @@ __global__ __launch_bounds__(kDxThreads) void k_gemm_dx(DxArgs a) {
 
   // a_hat of the lane's 8 rows from the wave's scale buffer (written just before, same wave)
   auto scales_of = [&](const CodeRegs& c, float (&ah)[8]) {
-    scw[lane & 31] = row_scale<kDQ>(c, mean);
+    scw[lane & 31] = row_scale<kDQ>(c, mean, a.sc.f8);
     const float4 a0 = *reinterpret_cast<const float4*>(scw + 8 * g);
     const float4 a1 = *reinterpret_cast<const float4*>(scw + 8 * g + 4);
     ah[0] = a0.x; ah[1] = a0.y; ah[2] = a0.z; ah[3] = a0.w; ah[4] = a1.x; ah[5] = a1.y; ah[6] = a1.z; ah[7] = a1.w;

@@ -203,7 +203,7 @@ __device__ __forceinline__ void gemv_load(GemvItem<R>& it, const uint8_t* __rest
 
 template <int R, bool kDQ>
 __device__ __forceinline__ void gemv_compute(const GemvItem<R>& it, const uint32_t* __restrict__ xr, bool active,
-                                             const char* tab, uint32_t slot, float mean, float acc[R]) {
+                                             const char* tab, uint32_t slot, float mean, int f8, float acc[R]) {
 #pragma unroll
   for (int r = 0; r < R; ++r) {
     const uint32_t q[8] = {it.w[r][0].x, it.w[r][0].y, it.w[r][0].z, it.w[r][0].w,
@@ -225,7 +225,7 @@ __device__ __forceinline__ void gemv_compute(const GemvItem<R>& it, const uint32
       }
     }
     float a;
-    if constexpr (kDQ) a = (div127(it.q[r]) * it.s2[r]) + mean;  // a_hat
+    if constexpr (kDQ) a = (code_ratio(it.q[r], f8) * it.s2[r]) + mean;  // a_hat
     else a = it.am[r];
     acc[r] = fmaf(sh + sl, active ? a : 0.0f, acc[r]);
   }
@@ -272,7 +272,7 @@ __global__ __launch_bounds__(1024) void k_gemv_m1(const uint8_t* __restrict__ pa
     for (int r = 0; r < R; ++r) acc[r] = 0.0f;
     for (int64_t sg = 0; sg < nseg; ++sg) {
       if (rb != r_begin || sg != 0) gemv_load<R, kDQ, true>(it, packed, rows, nblk, rb, sg * 64 + lane, sc, x);
-      gemv_compute<R, kDQ>(it, it.x, sg * 64 + lane < nblk, smem, slot, mean, acc);
+      gemv_compute<R, kDQ>(it, it.x, sg * 64 + lane < nblk, smem, slot, mean, sc.f8, acc);
     }
 #pragma unroll
     for (int r = 0; r < R; ++r) {
@@ -394,8 +394,8 @@ __device__ __forceinline__ void row_load(RowItem& it, const uint8_t* packed, int
 // out[c] = sum_j on[j] ? a_hat_j * xinv[c][j] * sum_k level[code_k] * xh[c][j][k] : 0.
 template <int MC, bool kDQ>
 __device__ __forceinline__ void row_dot(const RowItem& it, const uint32_t (&xh)[MC][2][16], const char* tab,
-                                        uint32_t slot, float mean, const float (&xinv)[MC][2], const bool (&on)[2],
-                                        float (&out)[MC]) {
+                                        uint32_t slot, float mean, int f8, const float (&xinv)[MC][2],
+                                        const bool (&on)[2], float (&out)[MC]) {
 #pragma unroll
   for (int c = 0; c < MC; ++c) out[c] = 0.0f;
 #pragma unroll
@@ -408,7 +408,7 @@ __device__ __forceinline__ void row_dot(const RowItem& it, const uint32_t (&xh)[
       e[u] = *reinterpret_cast<const uint32_t*>(tab + addr);
     }
     float a;
-    if constexpr (kDQ) a = (div127(it.q[j]) * it.s2[j]) + mean;  // a_hat
+    if constexpr (kDQ) a = (code_ratio(it.q[j], f8) * it.s2[j]) + mean;  // a_hat
     else a = it.am[j];
 #pragma unroll
     for (int c = 0; c < MC; ++c) {
@@ -522,7 +522,7 @@ __global__ __launch_bounds__(kWaves * 64) void k_gemv_rows(const uint8_t* packed
       const int64_t i = i0 + u;
       if (i < n) {  // wave-uniform
         float v[MC];
-        row_dot<MC, kDQ>(it[u], xh, smem, slot, mean, xinv, on, v);
+        row_dot<MC, kDQ>(it[u], xh, smem, slot, mean, sc.f8, xinv, on, v);
 #pragma unroll
         for (int c = 0; c < MC; ++c) {
           const float t = wave_sum_to_last(v[c]);
@@ -778,7 +778,7 @@ __global__ __launch_bounds__(kWaves * 64) void k_gemv_mfma(const uint8_t* __rest
             float s2;
             if constexpr (kQ4) s2 = (h + j) >= it.cross ? it.s2hi : it.s2lo;
             else s2 = it.am[h + j];
-            a = (div127(it.q[h + j]) * s2) + mean;  // a_hat of weight row ln
+            a = (code_ratio(it.q[h + j], sc.f8) * s2) + mean;  // a_hat of weight row ln
           } else {
             a = it.am[h + j];
           }

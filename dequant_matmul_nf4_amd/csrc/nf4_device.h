@@ -33,11 +33,19 @@ __device__ __forceinline__ float div127(int q) {
   return fmaf(r, y, q0);
 }
 
+// The float8 reading's ratio table (make_e4m3_ratio in nf4_internal.h).
+static __device__ const E4m3Ratio kE4m3Ratio = make_e4m3_ratio();
+
+// The first factor of a_hat: q / 127 for an int8 code, e4m3(q) / 448 for a
+// float8 code (q's low byte).
+__device__ __forceinline__ float code_ratio(int q, int f8) { return f8 ? kE4m3Ratio.v[q & 0xFF] : div127(q); }
+
 // The scale of block b: either the stored fp32 absmax, or the double-quantized
-// form a_hat = fl32(fl32(fl32(q / 127) * s2) + mean), three separate roundings.
+// form a_hat = fl32(fl32(fl32(q / 127) * s2) + mean), three separate roundings
+// (q / 127 replaced by e4m3(q) / 448 for float8 codes).
 __device__ __forceinline__ float block_scale(const Scales& sc, int64_t b, float mean) {
   if (sc.absmax) return sc.absmax[b];
-  const float t = div127(sc.q[b]);
+  const float t = code_ratio(sc.q[b], sc.f8);
   const float u = t * sc.absmax2[b >> 8];
   return u + mean;
 }

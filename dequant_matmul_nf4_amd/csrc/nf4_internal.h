@@ -38,6 +38,33 @@ __host__ __device__ inline int lut_special_index(int t) {
   return (sign << 10) | (e << 2) | m2;
 }
 
+// The float8 reading of the second level (tutorial page "bitsandbytes
+// quantization tutorial: 4-bit and 8-bit models", section "How NF4 Works":
+// the scales go from float32 to float8): E4M3 codes as the Open Compute
+// Project's 8-bit floating point specification defines them (bias 7, three
+// mantissa bits, subnormals, largest finite 448).  Where the int8 reading
+// divides the code by 127, this one takes fl32(e4m3(q) / 448) from a table.
+// The double quotient is rounded once more to float32; it is either exact or
+// has a repeating binary expansion ((8 + m) / 7 times a power of two), so it
+// never falls on a float32 tie and the two roundings give the correctly
+// rounded quotient.
+constexpr double e4m3_value(int c) {
+  const double sign = (c & 0x80) ? -1.0 : 1.0;
+  const int e = (c >> 3) & 0xF, m = c & 7;
+  if (e == 0xF && m == 7) return 0.0;  // the NaN codes, never written
+  double p = 1.0;
+  for (int i = 0; i < (e == 0 ? 9 : (e < 7 ? 7 - e : 0)); ++i) p *= 0.5;
+  for (int i = 0; i < (e > 7 ? e - 7 : 0); ++i) p *= 2.0;
+  return e == 0 ? sign * m * p : sign * (1.0 + m / 8.0) * p;
+}
+struct E4m3Ratio {
+  float v[256];
+};
+constexpr E4m3Ratio make_e4m3_ratio() {
+  E4m3Ratio t{};
+  for (int c = 0; c < 256; ++c) t.v[c] = static_cast<float>(e4m3_value(c) / 448.0);
+  return t;
+}
 // Compute units of the current device (set by the front end's device check
 // before any launch; used to size persistent grids).
 int device_cus();
@@ -48,6 +75,7 @@ struct Scales {
   const int8_t* q;       // double-quantized scales when absmax is null
   const float* absmax2;
   const float* mean;
+  int f8;                // second level: 0 = int8 codes, 1 = float8 (E4M3) codes
 };
 
 // Workspace of the double-quant kernels: one row of partial digit sums per
@@ -59,7 +87,7 @@ constexpr size_t kDqWorkspaceBytes = kDqMaxGroups * kDqDigits * sizeof(unsigned 
 hipError_t launch_quantize(const void* x, int x_bf16, int64_t n, uint8_t* packed,
                            float* absmax, hipStream_t s);
 hipError_t launch_double_quant(const float* absmax, int64_t nb, int8_t* q, float* absmax2,
-                               float* mean, unsigned long long* ws, hipStream_t s);
+                               float* mean, unsigned long long* ws, int f8, hipStream_t s);
 hipError_t launch_dequantize(const uint8_t* packed, int64_t n, Scales sc, void* out,
                              int out_bf16, hipStream_t s);
 hipError_t launch_gemv(const uint8_t* packed, int64_t rows, int64_t cols, Scales sc,

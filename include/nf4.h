@@ -54,6 +54,9 @@ typedef enum nf4_status {
 
 typedef enum nf4_dtype { NF4_F32 = 0, NF4_BF16 = 1, NF4_F16 = 2 } nf4_dtype;
 
+/* Type of the double-quantized scale codes (nf4_weight.dq_type). */
+typedef enum nf4_dq_type { NF4_DQ_INT8 = 0, NF4_DQ_FP8 = 1 } nf4_dq_type;
+
 #define NF4_BLOCKSIZE 64
 #define NF4_BLOCKSIZE2 256
 
@@ -108,12 +111,32 @@ int nf4_double_quant(const float* absmax, int64_t nblocks, int32_t blocksize2,
                      int8_t* qabsmax, float* absmax2, float* mean,
                      void* workspace, size_t workspace_bytes, void* stream);
 
+/* The float8 reading of the second level -- tutorial page "How NF4 Works":
+ * the scales go from float32 to float8.  Same arguments and mean as
+ * nf4_double_quant; qabsmax receives E4M3 codes (Open Compute Project 8-bit
+ * floating point: bias 7, 3 mantissa bits, subnormals, largest finite 448):
+ * t = fl32(fl32(c / s2) * 448) and q = the E4M3 code nearest to t, ties to the
+ * even mantissa; q = 0 in a group whose s2 is 0.  A weight using these codes
+ * sets dq_type = NF4_DQ_FP8, and its scales are
+ * a_hat = fl32(fl32(fl32(e4m3(q) / 448) * s2) + mean). */
+/* [host] The 256 values fl32(e4m3(q) / 448) the float8 second level uses in
+ * place of q / 127 (0 for the two NaN codes, which are never written).
+ * Needs no GPU.  Returns NF4_ERR_NULL for a NULL out. */
+int nf4_e4m3_ratio(float out[256]);
+
+int nf4_double_quant_f8(const float* absmax, int64_t nblocks, int32_t blocksize2,
+                        uint8_t* qabsmax, float* absmax2, float* mean,
+                        void* workspace, size_t workspace_bytes, void* stream);
+
 /* [host] A quantized weight: a struct holding device pointers.  The logical
  * matrix W[rows][cols] is row-major, element i = r*cols + c, and blocks of 64
  * run along that order.  Exactly one scale form is given:
  *   absmax != NULL                      : plain fp32 scales (no double quant);
  *   absmax == NULL, qabsmax/absmax2/mean: double-quantized scales, and each
- *     block's scale is a_hat = fl32(fl32(fl32(q / 127) * s2) + mean). */
+ *     block's scale is a_hat = fl32(fl32(fl32(q / 127) * s2) + mean) for
+ *     dq_type NF4_DQ_INT8, or fl32(fl32(fl32(e4m3(q) / 448) * s2) + mean) for
+ *     NF4_DQ_FP8 (codes from nf4_double_quant_f8).  dq_type is ignored for
+ *     plain scales; a zero-initialised struct means int8. */
 typedef struct nf4_weight {
   const uint8_t* packed;    /* ceil(rows*cols/2) bytes, 16-byte aligned          */
   int64_t rows, cols;       /* rows >= 1, cols >= 1                              */
@@ -123,6 +146,7 @@ typedef struct nf4_weight {
   const float* absmax2;     /* ceil(nblocks/256) float32 when absmax == NULL     */
   const float* mean;        /* one float32 when absmax == NULL                   */
   int32_t blocksize2;       /* 256 when absmax == NULL                           */
+  int32_t dq_type;          /* nf4_dq_type of qabsmax when absmax == NULL        */
 } nf4_weight;
 
 /* Dequantization -- tool page "How it works", Step 5.

@@ -50,6 +50,13 @@ def test_codebook_bit_identical_to_oracle(L):
     assert np.array_equal(cb.view(np.uint32), oracle.codebook().view(np.uint32))
 
 
+def test_e4m3_ratio_bit_identical_to_oracle(L):
+    """The float8 second level's table (built at compile time in the library)
+    against the oracle's, which is pinned to exact rational quotients."""
+    tab = np.array(nf4.nf4_e4m3_ratio(), dtype=np.float32)
+    assert np.array_equal(tab.view(np.uint32), oracle.e4m3_ratio_table().view(np.uint32))
+
+
 def test_workspace_sizes(L):
     assert nf4.nf4_double_quant_workspace(1) >= 16 * 8
     assert nf4.nf4_double_quant_workspace(1 << 30) <= WS
@@ -65,6 +72,7 @@ def test_workspace_sizes(L):
 def test_struct_layout():
     assert ctypes.sizeof(nf4.nf4_weight) == 72
     assert nf4.nf4_weight.blocksize2.offset == 64
+    assert nf4.nf4_weight.dq_type.offset == 68
 
 
 # Fake but aligned device addresses: every call below fails validation on the
@@ -96,6 +104,12 @@ CASES = [
     ("dq workspace small", lambda L: L.nf4_double_quant(A, 10, 256, A, A2, A2, A, 8, None), nf4.NF4_ERR_WORKSPACE),
     ("dq workspace null", lambda L: L.nf4_double_quant(A, 10, 256, A, A2, A2, None, WS, None), nf4.NF4_ERR_WORKSPACE),
     ("dq misaligned q", lambda L: L.nf4_double_quant(A, 10, 256, A + 1, A2, A2, A, WS, None), nf4.NF4_ERR_ALIGN),
+    ("dq f8 null", lambda L: L.nf4_double_quant_f8(A, 10, 256, None, A2, A2, A, WS, None), nf4.NF4_ERR_NULL),
+    ("dq f8 blocksize2", lambda L: L.nf4_double_quant_f8(A, 10, 128, A, A2, A2, A, WS, None), nf4.NF4_ERR_BLOCKSIZE),
+    ("dq f8 workspace small", lambda L: L.nf4_double_quant_f8(A, 10, 256, A, A2, A2, A, 8, None), nf4.NF4_ERR_WORKSPACE),
+    ("dequant dq_type unknown", lambda L: L.nf4_dequantize(ctypes.byref(_w(absmax=None, qabsmax=A, absmax2=A2, mean=A2, dq_type=2)), A, 1, None), nf4.NF4_ERR_DTYPE),
+    ("gemv dq_type unknown", lambda L: L.nf4_gemv(ctypes.byref(_w(absmax=None, qabsmax=A, absmax2=A2, mean=A2, dq_type=-1)), A, 1, A, 1, None), nf4.NF4_ERR_DTYPE),
+    ("e4m3 ratio null", lambda L: L.nf4_e4m3_ratio(None), nf4.NF4_ERR_NULL),
     ("dequant null weight", lambda L: L.nf4_dequantize(None, A, 1, None), nf4.NF4_ERR_NULL),
     ("dequant null out", lambda L: L.nf4_dequantize(ctypes.byref(_w()), None, 1, None), nf4.NF4_ERR_NULL),
     ("dequant bad dtype", lambda L: L.nf4_dequantize(ctypes.byref(_w()), A, 3, None), nf4.NF4_ERR_DTYPE),
