@@ -574,12 +574,12 @@ def legs_gemv_pools(torch, nf4, dev, stream, EventTimer, g, only=None):
     """Larger decode GEMVs: the Llama-8B MLP (M = 1, 4, 16) and one 70B-shaped layer."""
     res = {}
 
-    def gemv_pool(shapes, reps, label, m=1):
+    def gemv_pool(shapes, reps, label, m=1, dq_type="int8"):
         Wl = []
         for i, (r_, c_) in enumerate(shapes):
             g.manual_seed(9_000 + i)
             w = (torch.randn((r_, c_), generator=g, device=dev) * 0.02).to(torch.bfloat16)
-            Wl.append(nf4.quantize_weight(w, double_quant=True))
+            Wl.append(nf4.quantize_weight(w, double_quant=True, dq_type=dq_type))
             del w
         xs = {c_: (torch.randn((m, c_), generator=g, device=dev)).to(torch.bfloat16) for _, c_ in shapes}
         ys = [torch.empty((m, r_), dtype=torch.bfloat16, device=dev) for r_, _ in shapes]
@@ -617,7 +617,28 @@ def legs_gemv_pools(torch, nf4, dev, stream, EventTimer, g, only=None):
         layer = [(8192, 8192), (1024, 8192), (1024, 8192), (8192, 8192), (28672, 8192), (28672, 8192),
                  (8192, 28672)]
         res["gemv_layer_70b"] = gemv_pool(layer, 10, "70B-shaped layer q,k,v,o,gate,up,down NF4+DQ, M=1 (442 MB)")
+        res["gemv_layer_70b_fp8_scales"] = gemv_pool(
+            layer, 10, "the same layer with float8 (E4M3) second-level scales, M=1", dq_type="fp8")
+        res["double_quant_70b_gate"] = leg_dq_kinds(torch, nf4, dev, stream, EventTimer, g)
     return res
+
+
+def leg_dq_kinds(torch, nf4, dev, stream, EventTimer, g):
+    """Double quantization of the 3.67 M scales of one 28672x8192 weight with
+    the int8 and the float8 second level (medians of 20 calls)."""
+    g.manual_seed(9_100)
+    w = (torch.randn((28672, 8192), generator=g, device=dev) * 0.02).to(torch.bfloat16)
+    _, absmax = nf4.nf4_quantize(w)
+    del w
+    nb = absmax.numel()
+    out = {}
+    for kind in ("int8", "fp8"):
+        q, s2, mean = nf4.nf4_double_quant(absmax, fp8=kind == "fp8")
+        ws = torch.empty(nf4.nf4_double_quant_workspace(nb), dtype=torch.uint8, device=dev)
+        us = _median_call(torch, stream, EventTimer,
+                          lambda: nf4.nf4_double_quant(absmax, q, s2, mean, ws, fp8=kind == "fp8"), reps=20)
+        out[kind] = {"us": round(us, 2), "GBps_algorithmic": round(nb * 5.016 / (us * 1e-6) / 1e9, 1)}
+    return {"workload": "scales of one 28672x8192 NF4 weight (3.67 M)", **out}
 
 
 def leg_gemm(torch, nf4, dev, stream, EventTimer, g):
