@@ -35,10 +35,23 @@ def test_graph_replays_match_eager():
         y1=torch.empty((1, rows), dtype=torch.float32, device="cuda"),
         y4=torch.empty((4, rows), dtype=torch.bfloat16, device="cuda"),
         ym=torch.empty((m, rows), dtype=torch.bfloat16, device="cuda"),
+        dx=torch.empty((m, cols), dtype=torch.bfloat16, device="cuda"),
+        da=torch.empty((r, cols), dtype=torch.float32, device="cuda"),
+        db=torch.empty((rows, r), dtype=torch.float32, device="cuda"),
+        merged=torch.empty((rows, cols), dtype=torch.bfloat16, device="cuda"),
+        q8=torch.empty(nb, dtype=torch.uint8, device="cuda"),
+        s28=torch.empty(-(-nb // 256), dtype=torch.float32, device="cuda"),
+        mean8=torch.empty(1, dtype=torch.float32, device="cuda"),
+        y8=torch.empty((1, rows), dtype=torch.float32, device="cuda"),
     )
+    dy = syn.to_bf16(syn.normal_f32((m, rows), 1.0, 96)).to("cuda")
     dq_ws = torch.empty(nf4.nf4_double_quant_workspace(nb), dtype=torch.uint8, device="cuda")
     mm_ws = torch.empty(nf4.nf4_gemm_workspace(m, rows, r), dtype=torch.uint8, device="cuda")
+    dx_ws = torch.empty(nf4.nf4_gemm_dx_workspace(m, rows, r), dtype=torch.uint8, device="cuda")
+    gr_ws = torch.empty(nf4.nf4_lora_grads_workspace(m, rows, cols, r), dtype=torch.uint8, device="cuda")
     W = nf4.NF4Weight(out["packed"], rows, cols, qabsmax=out["q"], absmax2=out["s2"], mean=out["mean"])
+    W8 = nf4.NF4Weight(out["packed"], rows, cols, qabsmax=out["q8"], absmax2=out["s28"], mean=out["mean8"],
+                       dq_type=nf4.NF4_DQ_FP8)
 
     def path():
         nf4.nf4_quantize(w, out["packed"], out["absmax"])
@@ -47,6 +60,11 @@ def test_graph_replays_match_eager():
         nf4.nf4_gemv(W, x1, out["y1"])
         nf4.nf4_gemv(W, xm[:4], out["y4"])
         nf4.nf4_gemm(W, xm, out["ym"], a, b, 2.0, mm_ws)
+        nf4.nf4_gemm_dx(W, dy, out["dx"], a, b, 2.0, dx_ws)
+        nf4.nf4_lora_grads(xm, dy, a, b, 2.0, da=out["da"], db=out["db"], workspace=gr_ws)
+        nf4.nf4_lora_merge(W, a, b, 2.0, out=out["merged"])
+        nf4.nf4_double_quant(out["absmax"], out["q8"], out["s28"], out["mean8"], dq_ws, fp8=True)
+        nf4.nf4_gemv(W8, x1, out["y8"])
 
     path()
     torch.cuda.synchronize()
