@@ -307,10 +307,12 @@ __global__ __launch_bounds__(1024) void k_gemv_m1(const uint8_t* __restrict__ pa
 //    a single byte permute, every lane in its own bank), and one
 //    v_dot2c_f32_f16 takes both products; fp16 keeps 11 significant bits of
 //    each level;
-//  - a ring of U rows of loads stays in flight: slot u is consumed and at once
-//    refilled with the row U places ahead, indices clamped so that no branch
-//    separates the loads from their use; the first U rows are requested before
-//    the table is built;
+//  - a ring of U + 1 register slots keeps U rows of loads in flight: each step
+//    first requests the row U places ahead into the slot the previous step
+//    used, then works on its own row (indices clamped so that no branch
+//    separates the loads from their use); the first U rows are requested
+//    before the table is built.  One row ahead measured fastest: deeper rings
+//    were slower on every shape tried;
 //  - each row's per-lane partial sum is reduced across the wave with DPP
 //    (total in lane 63) and parked in LDS per (row, segment); at the end the
 //    segments of each row are added in a fixed order, so the result does not
@@ -368,33 +370,51 @@ __device__ __forceinline__ void fill_half_table(uint32_t* tab, const Codebook& c
 struct RowItem {
   uint4 w[2];    // piece j: 16 bytes of codes at segment offset 1024 j + 16 lane
   float am[2];   // absmax of each piece's block (plain scales)
-  int q[2];      // int8 scale codes (double quant)
+  int q[2];      // second-level scale codes (double quant)
   float s2[2];   // second-level scales
 };
 
-// Loads of one row.  row_blk0 = row * nblk (wave-uniform); blk[j] is the
-// lane's block of piece j (already clamped into the matrix), half = lane & 1.
+// The lane's fixed offsets within any row: piece j's code bytes
+// (blk[j] * 32 + 16 * half) and its block (blk[j]).
+struct LaneOffs {
+  uint32_t code[2];
+  uint32_t blk[2];
+};
+
+// Loads of one row.  The row's first block row_blk0 = row * nblk is
+// wave-uniform, so each address is a uniform base plus the lane's 32-bit
+// offset (no 64-bit arithmetic per lane); the scale group of piece j is
+// (row_blk0 % 256 + blk[j]) / 256 groups past that of the row's first block.
 template <bool kDQ>
-__device__ __forceinline__ void row_load(RowItem& it, const uint8_t* packed, int64_t row_blk0, const int (&blk)[2],
-                                         int half, Scales sc) {
+__device__ __forceinline__ void row_load(RowItem& it, const uint8_t* packed, int64_t row_blk0, const LaneOffs& lo,
+                                         Scales sc) {
+  const uint8_t* crow = packed + row_blk0 * 32;
+  const uint32_t g0 = static_cast<uint32_t>(row_blk0 & 255);
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
-    const int64_t b = row_blk0 + blk[j];
-    it.w[j] = *reinterpret_cast<const uint4*>(packed + b * 32 + 16 * half);
+    it.w[j] = *reinterpret_cast<const uint4*>(crow + lo.code[j]);
     if constexpr (kDQ) {
-      it.q[j] = sc.q[b];
-      it.s2[j] = sc.absmax2[b >> 8];
+      it.q[j] = (sc.q + row_blk0)[lo.blk[j]];
+      it.s2[j] = (sc.absmax2 + (row_blk0 >> 8))[(g0 + lo.blk[j]) >> 8];
     } else {
-      it.am[j] = sc.absmax[b];
+      it.am[j] = (sc.absmax + row_blk0)[lo.blk[j]];
     }
   }
 }
 
+// First factor of a_hat: q / 127 for int8 codes, the E4M3 ratio table (copied
+// to LDS) for float8 codes.
+template <bool kF8>
+__device__ __forceinline__ float row_ratio(int q, const float* rtab) {
+  if constexpr (kF8) return rtab[q & 0xFF];
+  else return div127(q);
+}
+
 // Products of one row item with MC rows of x (the lookups are shared):
 // out[c] = sum_j on[j] ? a_hat_j * xinv[c][j] * sum_k level[code_k] * xh[c][j][k] : 0.
-template <int MC, bool kDQ>
+template <int MC, bool kDQ, bool kF8>
 __device__ __forceinline__ void row_dot(const RowItem& it, const uint32_t (&xh)[MC][2][16], const char* tab,
-                                        uint32_t slot, float mean, int f8, const float (&xinv)[MC][2],
+                                        uint32_t slot, float mean, const float* rtab, const float (&xinv)[MC][2],
                                         const bool (&on)[2], float (&out)[MC]) {
 #pragma unroll
   for (int c = 0; c < MC; ++c) out[c] = 0.0f;
@@ -408,7 +428,7 @@ __device__ __forceinline__ void row_dot(const RowItem& it, const uint32_t (&xh)[
       e[u] = *reinterpret_cast<const uint32_t*>(tab + addr);
     }
     float a;
-    if constexpr (kDQ) a = (code_ratio(it.q[j], f8) * it.s2[j]) + mean;  // a_hat
+    if constexpr (kDQ) a = (row_ratio<kF8>(it.q[j], rtab) * it.s2[j]) + mean;  // a_hat
     else a = it.am[j];
 #pragma unroll
     for (int c = 0; c < MC; ++c) {
@@ -454,13 +474,14 @@ struct RowsPlan {
 
 // MC rows of x per launch (x and y point at the first of them; the x rows
 // are cols apart, the y rows `rows` apart).
-template <int U, int kWaves, int MC, bool kDQ, bool kBf16Out>
+template <int U, int kWaves, int MC, bool kDQ, bool kF8, bool kBf16Out>
 __global__ __launch_bounds__(kWaves * 64) void k_gemv_rows(const uint8_t* packed, int64_t rows,
                                                            int64_t cols, Scales sc, const uint16_t* x,
                                                            void* __restrict__ y, Codebook cb, RowsPlan pl) {
   constexpr int kRowsWg = kRowsMaxWg / MC;
   __shared__ uint32_t tab[256 * 64];
   __shared__ float part[kRowsWg * kSegMax * MC];
+  __shared__ float rtab[kF8 ? 256 : 1];
   const char* smem = reinterpret_cast<const char*>(tab);
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -481,21 +502,25 @@ __global__ __launch_bounds__(kWaves * 64) void k_gemv_rows(const uint8_t* packed
                                                                                    : pl.seg_blocks);
   bool on[2];
   int blk[2];
+  LaneOffs lo;
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
     const int bj = 32 * j + (lane >> 1);
     on[j] = bj < seg_end;
     blk[j] = seg * pl.seg_blocks + (on[j] ? bj : seg_end - 1);
+    lo.blk[j] = static_cast<uint32_t>(blk[j]);
+    lo.code[j] = static_cast<uint32_t>(blk[j]) * 32u + 16u * static_cast<uint32_t>(half);
   }
   const int64_t row0 = gp < rows ? gp : rows - 1;
   const int64_t last = n > 0 ? row0 + (n - 1) * np : row0;  // loads are clamped to it
 
   // the first U rows, x of the lane's pieces (MC rows), then the table
-  RowItem it[U];
+  constexpr int S = U + 1;  // ring slots: U rows in flight plus the one in use
+  RowItem it[S];
 #pragma unroll
   for (int u = 0; u < U; ++u) {
     const int64_t r = row0 + u * np;
-    row_load<kDQ>(it[u], packed, (r < last ? r : last) * nblk, blk, half, sc);
+    row_load<kDQ>(it[u], packed, (r < last ? r : last) * nblk, lo, sc);
   }
   uint4 xv[MC][2][4];
 #pragma unroll
@@ -506,6 +531,8 @@ __global__ __launch_bounds__(kWaves * 64) void k_gemv_rows(const uint8_t* packed
 #pragma unroll
       for (int i = 0; i < 4; ++i) xv[c][j][i] = xp[i];
     }
+  if constexpr (kF8)
+    for (int i = threadIdx.x; i < 256; i += kWaves * 64) rtab[i] = kE4m3Ratio.v[i];
   fill_half_table<kWaves * 64>(tab, cb);  // ends with a barrier
 
   uint32_t xh[MC][2][16];
@@ -516,21 +543,25 @@ __global__ __launch_bounds__(kWaves * 64) void k_gemv_rows(const uint8_t* packed
     for (int j = 0; j < 2; ++j) x_piece_to_half(xv[c][j], xh[c][j], xinv[c][j]);
   const float mean = kDQ ? *sc.mean : 0.0f;
 
-  for (int64_t i0 = 0; i0 < n; i0 += U) {
+  // step i: request row i + U into the slot freed by step i - 1, then use
+  // row i; the loop is unrolled by the ring size so that every slot keeps its
+  // registers (no copies, each wait covers only the row about to be used)
+  for (int64_t i0 = 0; i0 < n; i0 += S) {
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
+    for (int u = 0; u < S; ++u) {
       const int64_t i = i0 + u;
+      const int64_t r = row0 + (i + U) * np;
+      row_load<kDQ>(it[(u + U) % S], packed, (r < last ? r : last) * nblk, lo, sc);
+      __builtin_amdgcn_sched_barrier(0);
       if (i < n) {  // wave-uniform
         float v[MC];
-        row_dot<MC, kDQ>(it[u], xh, smem, slot, mean, sc.f8, xinv, on, v);
+        row_dot<MC, kDQ, kF8>(it[u], xh, smem, slot, mean, rtab, xinv, on, v);
 #pragma unroll
         for (int c = 0; c < MC; ++c) {
           const float t = wave_sum_to_last(v[c]);
           if (lane == 63) part[((prt * kmax + i) * kSegMax + seg) * MC + c] = t;
         }
       }
-      const int64_t r = row0 + (i + U) * np;
-      row_load<kDQ>(it[u], packed, (r < last ? r : last) * nblk, blk, half, sc);
     }
   }
   __syncthreads();
@@ -564,19 +595,28 @@ RowsPlan rows_plan(int64_t rows, int64_t cols, int waves, int rows_wg) {
   return pl;
 }
 
-template <int U, int kWaves, int MC, bool kDQ>
+template <int U, int kWaves, int MC, bool kDQ, bool kF8>
 hipError_t launch_rows(const uint8_t* packed, int64_t rows, int64_t cols, Scales sc, const uint16_t* x, void* y,
                        int y_bf16, hipStream_t s) {
   const RowsPlan pl = rows_plan(rows, cols, kWaves, kRowsMaxWg / MC);
-  if (pl.nseg > kSegMax || pl.wpr < 1) return hipErrorInvalidValue;
+  if (pl.nseg > kSegMax || pl.wpr < 1 || (cols / 64) * 32 >= (int64_t{1} << 32)) return hipErrorInvalidValue;
   const int64_t g = pl.grid;
   const Codebook& cb = codebook();
   const dim3 gd(static_cast<unsigned>(g)), bd(64 * kWaves);
   if (y_bf16)
-    hipLaunchKernelGGL((k_gemv_rows<U, kWaves, MC, kDQ, true>), gd, bd, 0, s, packed, rows, cols, sc, x, y, cb, pl);
+    hipLaunchKernelGGL((k_gemv_rows<U, kWaves, MC, kDQ, kF8, true>), gd, bd, 0, s, packed, rows, cols, sc, x, y, cb, pl);
   else
-    hipLaunchKernelGGL((k_gemv_rows<U, kWaves, MC, kDQ, false>), gd, bd, 0, s, packed, rows, cols, sc, x, y, cb, pl);
+    hipLaunchKernelGGL((k_gemv_rows<U, kWaves, MC, kDQ, kF8, false>), gd, bd, 0, s, packed, rows, cols, sc, x, y, cb, pl);
   return hipGetLastError();
+}
+
+// The scale form of a launch: plain absmax, int8 or float8 second level.
+template <int U, int kWaves, int MC>
+hipError_t launch_rows_sc(const uint8_t* packed, int64_t rows, int64_t cols, Scales sc, const uint16_t* x, void* y,
+                          int y_bf16, hipStream_t s) {
+  if (sc.absmax) return launch_rows<U, kWaves, MC, false, false>(packed, rows, cols, sc, x, y, y_bf16, s);
+  if (sc.f8) return launch_rows<U, kWaves, MC, true, true>(packed, rows, cols, sc, x, y, y_bf16, s);
+  return launch_rows<U, kWaves, MC, true, false>(packed, rows, cols, sc, x, y, y_bf16, s);
 }
 
 // ---------------------------------------------------------------- m = 2..16
@@ -859,7 +899,6 @@ hipError_t launch_mfma(const uint8_t* packed, int64_t rows, int64_t cols, Scales
 }
 
 // Skinny products (m > 1): passes of up to 4 rows of x over W, 8 waves.
-template <bool kDQ>
 hipError_t launch_rows_multi(const uint8_t* packed, int64_t rows, int64_t cols, Scales sc, const uint16_t* x,
                              int64_t m, void* y, int y_bf16, hipStream_t s) {
   const size_t ysz = y_bf16 ? 2 : 4;
@@ -868,10 +907,10 @@ hipError_t launch_rows_multi(const uint8_t* packed, int64_t rows, int64_t cols, 
     const uint16_t* xc = x + c0 * cols;
     void* yc = static_cast<char*>(y) + c0 * rows * ysz;
     hipError_t e;
-    if (mc == 4) e = launch_rows<1, 8, 4, kDQ>(packed, rows, cols, sc, xc, yc, y_bf16, s);
-    else if (mc == 3) e = launch_rows<1, 8, 3, kDQ>(packed, rows, cols, sc, xc, yc, y_bf16, s);
-    else if (mc == 2) e = launch_rows<1, 8, 2, kDQ>(packed, rows, cols, sc, xc, yc, y_bf16, s);
-    else e = launch_rows<1, 8, 1, kDQ>(packed, rows, cols, sc, xc, yc, y_bf16, s);
+    if (mc == 4) e = launch_rows_sc<1, 8, 4>(packed, rows, cols, sc, xc, yc, y_bf16, s);
+    else if (mc == 3) e = launch_rows_sc<1, 8, 3>(packed, rows, cols, sc, xc, yc, y_bf16, s);
+    else if (mc == 2) e = launch_rows_sc<1, 8, 2>(packed, rows, cols, sc, xc, yc, y_bf16, s);
+    else e = launch_rows_sc<1, 8, 1>(packed, rows, cols, sc, xc, yc, y_bf16, s);
     if (e != hipSuccess) return e;
   }
   return hipSuccess;
@@ -908,13 +947,14 @@ hipError_t launch_gemv(const uint8_t* packed, int64_t rows, int64_t cols, Scales
   if (m == 1) {
     const int64_t nseg = (cols / 64 + 63) / 64;
     if (nseg == 1) {
-      // one column segment: two rows in flight per wave, 8 waves
-      return sc.absmax ? launch_rows<2, 8, 1, false>(packed, rows, cols, sc, x, y, y_bf16, s)
-                       : launch_rows<2, 8, 1, true>(packed, rows, cols, sc, x, y, y_bf16, s);
+      // one column segment: 8 waves
+      return launch_rows_sc<1, 8, 1>(packed, rows, cols, sc, x, y, y_bf16, s);
     }
     if (nseg <= kSegMax) {
-      return sc.absmax ? launch_rows<1, 16, 1, false>(packed, rows, cols, sc, x, y, y_bf16, s)
-                       : launch_rows<1, 16, 1, true>(packed, rows, cols, sc, x, y, y_bf16, s);
+      // 16 waves, or 8 where 16 would leave row parts without rows
+      if (nseg <= 8 && rows < device_cus() * (16 / nseg))
+        return launch_rows_sc<1, 8, 1>(packed, rows, cols, sc, x, y, y_bf16, s);
+      return launch_rows_sc<1, 16, 1>(packed, rows, cols, sc, x, y, y_bf16, s);
     }
     // wider than 16 segments (cols > 65536): one row group per wave
     const int64_t cus = device_cus();
@@ -935,8 +975,7 @@ hipError_t launch_gemv(const uint8_t* packed, int64_t rows, int64_t cols, Scales
                        : launch_mfma<true>(packed, rows, cols, sc, x, m, y, y_bf16, s);
     }
     if ((cols / 64 + 63) / 64 <= 8) {
-      return sc.absmax ? launch_rows_multi<false>(packed, rows, cols, sc, x, m, y, y_bf16, s)
-                       : launch_rows_multi<true>(packed, rows, cols, sc, x, m, y, y_bf16, s);
+      return launch_rows_multi(packed, rows, cols, sc, x, m, y, y_bf16, s);
     }
     if (y_bf16) hipLaunchKernelGGL((k_gemv<4, true>), grid, dim3(256), 0, s, packed, rows, cols, sc, x, mm, y, cb);
     else hipLaunchKernelGGL((k_gemv<4, false>), grid, dim3(256), 0, s, packed, rows, cols, sc, x, mm, y, cb);
