@@ -66,23 +66,35 @@ __device__ double digits_to_double(const uint32_t (&dig)[kDqDigits]) {
   return ldexp(static_cast<double>(mant), exp2);
 }
 
-// Adds the 256 threads' digit vectors held in vec (thread t sums digit
-// t % 12 over rows t / 12, t / 12 + 21, ..., then 12 threads finish) and
-// returns the total of digit t in threads t < 12.  Contains two barriers.
+// Adds the 256 threads' digit vectors held in vec and returns the total of
+// digit t in threads t < 12: first thread t < 192 adds digit t % 12 of rows
+// 16 c .. 16 c + 15 (c = t / 12), then 12 threads add the 16 chunk sums.
+// Each step issues all of its LDS reads before adding, so the sum costs two
+// LDS round trips rather than one per row.  Contains two barriers.
+constexpr int kSumChunks = 16;  // rows per chunk and number of chunks (16 x 16 = 256)
+
 __device__ __forceinline__ unsigned long long block_digit_sum(unsigned long long (*vec)[kDqDigits + 1],
                                                               unsigned long long (*tot)[kDqDigits]) {
-  constexpr int kChunks = 256 / kDqDigits;  // 21
   const int t = threadIdx.x;
-  if (t < kChunks * kDqDigits) {
+  if (t < kSumChunks * kDqDigits) {
     const int k = t % kDqDigits, c = t / kDqDigits;
+    unsigned long long v[kSumChunks];
+#pragma unroll
+    for (int i = 0; i < kSumChunks; ++i) v[i] = vec[kSumChunks * c + i][k];
     unsigned long long sum = 0ull;
-    for (int r = c; r < 256; r += kChunks) sum += vec[r][k];
+#pragma unroll
+    for (int i = 0; i < kSumChunks; ++i) sum += v[i];
     tot[c][k] = sum;
   }
   __syncthreads();
   unsigned long long sum = 0ull;
-  if (t < kDqDigits)
-    for (int c = 0; c < kChunks; ++c) sum += tot[c][t];
+  if (t < kDqDigits) {
+    unsigned long long v[kSumChunks];
+#pragma unroll
+    for (int c = 0; c < kSumChunks; ++c) v[c] = tot[c][t];
+#pragma unroll
+    for (int c = 0; c < kSumChunks; ++c) sum += v[c];
+  }
   __syncthreads();
   return sum;
 }
@@ -94,9 +106,8 @@ constexpr int kPerThread = 4;
 
 __global__ __launch_bounds__(256) void k_dq_partial(const float* __restrict__ absmax, int64_t nb,
                                                     unsigned long long* __restrict__ ws) {
-  constexpr int kChunks = 256 / kDqDigits;  // 21
   __shared__ unsigned long long vec[256][kDqDigits + 1];  // +1: spreads the banks
-  __shared__ unsigned long long tot[kChunks][kDqDigits];
+  __shared__ unsigned long long tot[kSumChunks][kDqDigits];
   const int t = threadIdx.x;
   unsigned long long acc[kDqDigits];
 #pragma unroll
@@ -133,9 +144,8 @@ __global__ __launch_bounds__(256) void k_dq_partial(const float* __restrict__ ab
 // propagates the carries, rounds and divides.  Returns the mean in every
 // thread.
 __device__ float dq_mean(const unsigned long long* __restrict__ ws, int nparts, int64_t nb) {
-  constexpr int kChunks = 256 / kDqDigits;
   __shared__ unsigned long long vec[256][kDqDigits + 1];
-  __shared__ unsigned long long tot[kChunks][kDqDigits];
+  __shared__ unsigned long long tot[kSumChunks][kDqDigits];
   __shared__ unsigned long long dsum[kDqDigits];
   __shared__ float mean_s;
   const int t = threadIdx.x;
