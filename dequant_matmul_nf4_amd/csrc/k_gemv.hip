@@ -702,12 +702,13 @@ __device__ __forceinline__ void seg_load(SegItem<kDQ>& it, const uint8_t* __rest
   }
 }
 
-template <int kWaves, bool kDQ, bool kQ4, bool kBf16Out>
+template <int kWaves, bool kDQ, bool kF8, bool kQ4, bool kBf16Out>
 __global__ __launch_bounds__(kWaves * 64) void k_gemv_mfma(const uint8_t* __restrict__ packed, int64_t rows,
                                                            int64_t cols, Scales sc, const uint16_t* __restrict__ x,
                                                            int m, void* __restrict__ y, Codebook cb, MfmaPlan pl) {
   __shared__ uint32_t tab[256 * 64];
   __shared__ float part[kPartTiles * 256];
+  __shared__ float rtab[kF8 ? 256 : 1];  // float8 ratio table
   const char* smem = reinterpret_cast<const char*>(tab);
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -720,6 +721,8 @@ __global__ __launch_bounds__(kWaves * 64) void k_gemv_mfma(const uint8_t* __rest
   const int64_t kmine = (static_cast<int64_t>(blockIdx.x) < ngroups) ? (ngroups - blockIdx.x + G - 1) / G : 0;
   const int64_t ngroups2 = (rows * nblk + 255) / 256;  // second-level scales
   const float mean = kDQ ? *sc.mean : 0.0f;
+  if constexpr (kF8)
+    for (int i = threadIdx.x; i < 256; i += kWaves * 64) rtab[i] = kE4m3Ratio.v[i];
   fill_half_table<kWaves * 64>(tab, cb);  // ends with a barrier
 
   for (int seg = wave; seg < pl.nseg; seg += kWaves) {
@@ -818,7 +821,7 @@ __global__ __launch_bounds__(kWaves * 64) void k_gemv_mfma(const uint8_t* __rest
             float s2;
             if constexpr (kQ4) s2 = (h + j) >= it.cross ? it.s2hi : it.s2lo;
             else s2 = it.am[h + j];
-            a = (code_ratio(it.q[h + j], sc.f8) * s2) + mean;  // a_hat of weight row ln
+            a = (row_ratio<kF8>(it.q[h + j], rtab) * s2) + mean;  // a_hat of weight row ln
           } else {
             a = it.am[h + j];
           }
@@ -886,14 +889,18 @@ hipError_t launch_mfma(const uint8_t* packed, int64_t rows, int64_t cols, Scales
   const bool q4 = pl.seg_blocks == kMfmaSeg && (cols / 64) % kMfmaSeg == 0 && (sa & (kDQ ? 3u : 15u)) == 0;
   if (q4) {
     if (y_bf16)
-      hipLaunchKernelGGL((k_gemv_mfma<kMfmaWaves, kDQ, true, true>), gd, bd, 0, s, packed, rows, cols, sc, x, mi, y, cb, pl);
+      { if (sc.f8) hipLaunchKernelGGL((k_gemv_mfma<kMfmaWaves, kDQ, kDQ, true, true>), gd, bd, 0, s, packed, rows, cols, sc, x, mi, y, cb, pl);
+      else hipLaunchKernelGGL((k_gemv_mfma<kMfmaWaves, kDQ, false, true, true>), gd, bd, 0, s, packed, rows, cols, sc, x, mi, y, cb, pl); }
     else
-      hipLaunchKernelGGL((k_gemv_mfma<kMfmaWaves, kDQ, true, false>), gd, bd, 0, s, packed, rows, cols, sc, x, mi, y, cb, pl);
+      { if (sc.f8) hipLaunchKernelGGL((k_gemv_mfma<kMfmaWaves, kDQ, kDQ, true, false>), gd, bd, 0, s, packed, rows, cols, sc, x, mi, y, cb, pl);
+      else hipLaunchKernelGGL((k_gemv_mfma<kMfmaWaves, kDQ, false, true, false>), gd, bd, 0, s, packed, rows, cols, sc, x, mi, y, cb, pl); }
   } else {
     if (y_bf16)
-      hipLaunchKernelGGL((k_gemv_mfma<kMfmaWaves, kDQ, false, true>), gd, bd, 0, s, packed, rows, cols, sc, x, mi, y, cb, pl);
+      { if (sc.f8) hipLaunchKernelGGL((k_gemv_mfma<kMfmaWaves, kDQ, kDQ, false, true>), gd, bd, 0, s, packed, rows, cols, sc, x, mi, y, cb, pl);
+      else hipLaunchKernelGGL((k_gemv_mfma<kMfmaWaves, kDQ, false, false, true>), gd, bd, 0, s, packed, rows, cols, sc, x, mi, y, cb, pl); }
     else
-      hipLaunchKernelGGL((k_gemv_mfma<kMfmaWaves, kDQ, false, false>), gd, bd, 0, s, packed, rows, cols, sc, x, mi, y, cb, pl);
+      { if (sc.f8) hipLaunchKernelGGL((k_gemv_mfma<kMfmaWaves, kDQ, kDQ, false, false>), gd, bd, 0, s, packed, rows, cols, sc, x, mi, y, cb, pl);
+      else hipLaunchKernelGGL((k_gemv_mfma<kMfmaWaves, kDQ, false, false, false>), gd, bd, 0, s, packed, rows, cols, sc, x, mi, y, cb, pl); }
   }
   return hipGetLastError();
 }
@@ -968,8 +975,14 @@ hipError_t launch_gemv(const uint8_t* packed, int64_t rows, int64_t cols, Scales
       else launch_m1<2, true>(packed, rows, cols, sc, x, y, y_bf16, 16, s);
     }
   } else {
-    // skinny products on the matrix cores; wider rows in passes of up to 4
-    // rows of x on the vector ALUs (8 waves, so nseg <= 8)
+    // m = 2 (and m <= 4 on large matrices): the streaming kernel with the x
+    // rows sharing each lookup, which measured faster there than the matrix
+    // cores (e.g. 28672x8192: 35 against 78 us at m = 2, 55 against 80 us at
+    // m = 4; at m = 4 on 14336x4096 and at m >= 8 the matrix cores win).
+    // Otherwise skinny products on the matrix cores; wider rows in passes of
+    // up to 4 rows of x on the vector ALUs (8 waves, so nseg <= 8)
+    const bool rows_first = m <= 2 || (m <= 4 && rows * cols >= (int64_t{1} << 27));
+    if (rows_first && (cols / 64 + 63) / 64 <= 8) return launch_rows_multi(packed, rows, cols, sc, x, m, y, y_bf16, s);
     if (mfma_plan(rows, cols).nseg <= kPartTiles) {
       return sc.absmax ? launch_mfma<false>(packed, rows, cols, sc, x, m, y, y_bf16, s)
                        : launch_mfma<true>(packed, rows, cols, sc, x, m, y, y_bf16, s);

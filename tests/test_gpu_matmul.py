@@ -77,7 +77,7 @@ def test_gemv_c2_full():
 
 
 @pytest.mark.parametrize("name", ["gate", "down"])
-@pytest.mark.parametrize("m", [1, 4, 16])
+@pytest.mark.parametrize("m", [1, 2, 4, 16])
 def test_gemv_c3_sampled_rows(name, m):
     say("gemv C3", name, "m", m)
     torch = need_gpu()
@@ -92,6 +92,29 @@ def test_gemv_c3_sampled_rows(name, m):
     sel = np.unique(np.concatenate([[0, rows - 1], rng.choice(rows, 192, replace=False)]))
     absmax_all = oracle.block_absmax(w_f32.reshape(-1))
     wdeq = oracle_rows_dequant_bf16(w_f32[sel], sel, cols, absmax_all, True)
+    ref = oracle.matmul_ref(syn.bf16_to_f32(x), wdeq)
+    e = oracle.rel_frobenius(_y_f64(y)[:, sel], ref)
+    say(f"  rel err {e:.2e}")
+    assert e <= MATMUL_RTOL
+
+
+@pytest.mark.parametrize("m", [3, 4])
+def test_gemv_skinny_streaming_path_large(m):
+    """m <= 4 on a matrix of at least 2^27 weights takes the streaming kernel
+    with the x rows sharing each lookup: sampled rows against the oracle, and
+    the result does not depend on the scale array's alignment."""
+    say("gemv skinny streaming path", m)
+    torch = need_gpu()
+    rows, cols = 16384, 8192
+    w = syn.normal_f32((rows, cols), 0.02, 31 + m)
+    x = syn.to_bf16(syn.normal_f32((m, cols), 1.0, 32))
+    W = nf4.quantize_weight(to_dev(w), double_quant=True)
+    y = nf4.nf4_gemv(W, x.to("cuda"), y_dtype=torch.float32)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(5)
+    sel = np.unique(np.concatenate([[0, rows - 1], rng.choice(rows, 128, replace=False)]))
+    absmax_all = oracle.block_absmax(w.reshape(-1))
+    wdeq = oracle_rows_dequant_bf16(w[sel], sel, cols, absmax_all, True)
     ref = oracle.matmul_ref(syn.bf16_to_f32(x), wdeq)
     e = oracle.rel_frobenius(_y_f64(y)[:, sel], ref)
     say(f"  rel err {e:.2e}")
