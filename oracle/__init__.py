@@ -9,5 +9,5 @@ from .nf4_oracle import (  # noqa: F401
     dequant_scales, f32_to_bf16_bits, bf16_bits_to_f32, dequantize, matmul_ref,
     rel_frobenius, storage_bytes, bits_per_param, f64_to_bf16_bits, f64_to_f16_bits,
     lora_merge, backward_ref, E4M3_MAX, e4m3_value, e4m3_encode, e4m3_ratio_table,
-    f8_absmax_quantize, double_quant_f8,
+    f8_absmax_quantize, double_quant_f8, FP4_ZERO, FP4_PRODUCED, e2m1_value, fp4_codebook,
 )

@@ -7,7 +7,8 @@ binding) never does, and the two share no code, tables or constants.
 
 Sources (web pages, cited by title and section; plus the Open Compute
 Project's 8-bit floating point specification for the E4M3 format of the
-float8 second-level reading):
+float8 second-level reading and its microscaling (MX) formats specification
+for the E2M1 format of the FP4 reading):
   [TOOL]  "bitsandbytes" (ozercemkelahmet.com/tools/bitsandbytes):
           "How it works" Steps 1-5, "How NF4 works", "Double quantization",
           "A worked example", "Memory arithmetic", "Practical guidance and
@@ -110,8 +111,11 @@ def block_absmax(x: np.ndarray, blocksize: int = BLOCKSIZE) -> np.ndarray:
     return padded.reshape(nb, blocksize).max(axis=1)
 
 
-def nearest_code(v: np.ndarray) -> np.ndarray:
+def nearest_code(v: np.ndarray, levels=None, allowed=None) -> np.ndarray:
     """[TOOL] "How it works", Step 3: index of the nearest code-book entry.
+
+    levels: the code book (default NF4); allowed: the codes that may be
+    chosen (default all; the FP4 reading leaves out its negative zero).
 
     READING: an exact tie between two levels goes to the level farther from
     zero (the only rounding rule the pages state, in "A worked example", rounds
@@ -119,13 +123,14 @@ def nearest_code(v: np.ndarray) -> np.ndarray:
     float32 numbers whose exponents differ by at most 29 is exact there, and
     when |v| is too small for that, the zero level wins by a wide margin, so
     the minimum and any tie are decided exactly."""
-    lv = codebook().astype(np.float64)
+    lv = (codebook() if levels is None else np.asarray(levels, dtype=np.float32)).astype(np.float64)
+    ok = np.ones(lv.size, dtype=bool) if allowed is None else np.asarray(allowed, dtype=bool)
     out = np.empty(v.size, dtype=np.uint8)
     flat = np.asarray(v, dtype=np.float32).reshape(-1)
     step = 1 << 18
     for s in range(0, flat.size, step):
         vv = flat[s : s + step].astype(np.float64)[:, None]
-        d = np.abs(vv - lv[None, :])
+        d = np.where(ok[None, :], np.abs(vv - lv[None, :]), np.inf)
         dmin = d.min(axis=1, keepdims=True)
         tied = d == dmin
         score = np.where(tied, np.abs(lv)[None, :], -1.0)
@@ -150,14 +155,14 @@ def normalize(x: np.ndarray, absmax: np.ndarray, blocksize: int = BLOCKSIZE) -> 
     return out.reshape(-1)[: x.size]
 
 
-def pack(codes: np.ndarray) -> np.ndarray:
+def pack(codes: np.ndarray, pad: int = 7) -> np.ndarray:
     """[TOOL] "How it works", Step 4: two 4-bit indices share one byte.
 
     READING: element 2j in the high nibble, element 2j+1 in the low nibble; an
-    odd count is completed with the zero level's index 7."""
+    odd count is completed with the zero level's index (7 for NF4, 0 for FP4)."""
     c = np.asarray(codes, dtype=np.uint8).reshape(-1)
     if c.size % 2:
-        c = np.concatenate([c, np.array([7], dtype=np.uint8)])
+        c = np.concatenate([c, np.array([pad], dtype=np.uint8)])
     return ((c[0::2] << 4) | c[1::2]).astype(np.uint8)
 
 
@@ -169,15 +174,56 @@ def unpack(packed: np.ndarray, n: int) -> np.ndarray:
     return c[:n]
 
 
-def quantize(x: np.ndarray, blocksize: int = BLOCKSIZE):
+def quantize(x: np.ndarray, blocksize: int = BLOCKSIZE, kind: str = "nf4"):
     """Steps 1-4: returns (packed uint8 [ceil(n/2)], absmax float32 [ceil(n/64)]).
 
     Inputs are float32 values (bf16 inputs are passed as their exact float32
-    widening)."""
+    widening).  kind="fp4" uses the FP4 code book (READING C19 below)."""
     x = np.asarray(x, dtype=np.float32).reshape(-1)
     absmax = block_absmax(x, blocksize)
+    if kind == "fp4":
+        codes = nearest_code(normalize(x, absmax, blocksize), fp4_codebook(), FP4_PRODUCED)
+        return pack(codes, pad=FP4_ZERO), absmax
+    if kind != "nf4":
+        raise ValueError(kind)
     codes = nearest_code(normalize(x, absmax, blocksize))
     return pack(codes), absmax
+
+
+# ------------------------------------------------- FP4 code book (READING C19)
+#
+# [TOOL] "What it is" lists FP4 beside NF4 among the 4-bit formats of the
+# quantized linear layers and its "Glossary" calls FP4 a 4-bit floating-point
+# data type; the page "Environment: Huggingface Transformers BitsAndBytes
+# Quantization Env" ("Description") names NF4/FP4 as the two 4-bit choices.
+# No values are given.  READING: the 4-bit float is the E2M1 element type of
+# the Open Compute Project's microscaling (MX) formats specification -- a sign
+# bit, two exponent bits with bias 1 and one mantissa bit, exponent field 0
+# subnormal (value m / 2) -- so the magnitudes are 0, 0.5, 1, 1.5, 2, 3, 4, 6.
+# The code book ("Glossary": the table of allowed values that indices point
+# to) is those values divided by 6, so that the block absmax maps to +-1 as
+# NF4's outermost levels do.  A code is the 4-bit pattern itself (sign in bit
+# 3).  Pattern 1000 (negative zero) decodes to -0 and is never produced:
+# quantization chooses among the other 15 codes, zero going to 0000, with the
+# same nearest rule (ties to the level farther from zero).  Everything else
+# (absmax per 64, normalisation, packing, double quantization, the consumers)
+# is the NF4 path with this code book.
+
+FP4_ZERO = 0
+FP4_PRODUCED = np.array([c != 8 for c in range(16)])
+
+
+def e2m1_value(code: int) -> float:
+    """Value of a 4-bit E2M1 pattern (sign, 2 exponent bits with bias 1, 1 mantissa bit)."""
+    sign = -1.0 if code & 8 else 1.0
+    e, m = (code >> 1) & 3, code & 1
+    mag = m / 2 if e == 0 else (1 + m / 2) * 2.0 ** (e - 1)
+    return sign * mag
+
+
+def fp4_codebook() -> np.ndarray:
+    """The 16 FP4 levels by code: e2m1_value(code) / 6 rounded once to float32."""
+    return np.array([e2m1_value(c) / 6.0 for c in range(16)], dtype=np.float32)
 
 
 # --------------------------------------------------------- double quantization
@@ -351,14 +397,16 @@ def bf16_bits_to_f32(b: np.ndarray) -> np.ndarray:
 
 
 def dequantize(packed, n: int, absmax=None, qabsmax=None, absmax2=None, mean=None,
-               blocksize: int = BLOCKSIZE, blocksize2: int = BLOCKSIZE2, out: str = "f32", dq_kind: str = "int8"):
+               blocksize: int = BLOCKSIZE, blocksize2: int = BLOCKSIZE2, out: str = "f32", dq_kind: str = "int8",
+               kind: str = "nf4"):
     """[TOOL] "How it works", Step 5: expand each code with its block's scale.
 
     w = fl32(level[code] * a_hat); for out="bf16" the float32 value is rounded
     once to nearest even and the bf16 bit patterns (uint16) are returned.
-    dq_kind selects the second level's reading (int8 or fp8)."""
+    dq_kind selects the second level's reading (int8 or fp8), kind the code
+    book (nf4 or fp4)."""
     codes = unpack(packed, n)
-    lv = codebook()
+    lv = fp4_codebook() if kind == "fp4" else codebook()
     if absmax is not None:
         a_hat = np.asarray(absmax, dtype=np.float32).reshape(-1)
     else:

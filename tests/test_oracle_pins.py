@@ -636,3 +636,86 @@ def test_dequantize_with_f8_scales_is_the_per_element_product():
     lv = oracle.codebook()
     for i in range(0, w.size, 7):
         assert got[i] == np.float32(rn32(frac(lv[codes[i]]) * frac(a_hat[i // 64])))
+
+
+# ------------------------------------------------- FP4 code book (READING C19)
+
+def test_e2m1_values_are_the_mx_element_table():
+    """The E2M1 element type of the OCP microscaling formats: magnitudes
+    0, 0.5, 1, 1.5, 2, 3, 4, 6 for the patterns 000..111, the sign in bit 3."""
+    table = [0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0]
+    for c in range(8):
+        assert oracle.e2m1_value(c) == table[c]
+        assert oracle.e2m1_value(c | 8) == -table[c]
+    assert math.copysign(1.0, oracle.e2m1_value(8)) == -1.0  # negative zero
+
+
+def test_fp4_codebook_closed_form_and_symmetry():
+    cb = oracle.fp4_codebook()
+    assert cb.dtype == np.float32 and cb.shape == (16,)
+    for c in range(16):
+        assert cb[c] == rn32(Fraction(oracle.e2m1_value(c)).limit_denominator(4) / 6)
+    assert cb[7] == np.float32(1.0) and cb[15] == np.float32(-1.0)
+    assert cb[0] == 0 and not np.signbit(cb[0]) and cb[8] == 0 and np.signbit(cb[8])
+    assert np.array_equal(cb[8:], -cb[:8])
+    assert not oracle.FP4_PRODUCED[8] and oracle.FP4_PRODUCED.sum() == 15
+
+
+def _brute_quantize_fp4(vals):
+    a = max(abs(frac(v)) for v in vals)
+    af = np.float32(float(a))
+    codes = []
+    for v in vals:
+        q = Fraction(0) if a == 0 else frac(rn32(frac(v) / a))
+        codes.append(nearest_level_exact(q, oracle.fp4_codebook()))
+    return codes, af
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_fp4_quantize_matches_brute_force_on_tiny_blocks(seed):
+    rng = np.random.default_rng(700 + seed)
+    size = int(rng.integers(2, 65))
+    kind = ["normal", "uniform", "wide"][seed % 3]
+    x = random_blocks_f32(size, 710 + seed, kinds=(kind,))
+    packed, absmax = oracle.quantize(x, kind="fp4")
+    codes = oracle.unpack(packed, x.size)
+    bcodes, ba = _brute_quantize_fp4(list(x))
+    assert absmax.shape == (1,) and absmax[0] == ba
+    assert list(codes) == bcodes
+    assert 8 not in bcodes  # the first of two equally near zeros is the positive one
+
+
+def test_fp4_levels_round_trip_and_sign_symmetry():
+    cb = oracle.fp4_codebook()
+    produced = [c for c in range(16) if c != 8]
+    for k in (-4, 0, 3):
+        s = np.float32(2.0 ** k)
+        block = (cb[produced] * s).astype(np.float32)
+        packed, absmax = oracle.quantize(block, kind="fp4")
+        assert absmax[0] == s
+        assert list(oracle.unpack(packed, block.size)) == produced
+        deq = oracle.dequantize(packed, block.size, absmax=absmax, kind="fp4")
+        assert np.array_equal(deq, block)
+    x = random_blocks_f32(640, 720)
+    p1, _ = oracle.quantize(x, kind="fp4")
+    p2, _ = oracle.quantize(-x, kind="fp4")
+    c1, c2 = oracle.unpack(p1, x.size), oracle.unpack(p2, x.size)
+    assert np.array_equal(np.where(c1 == 0, 0, c1 ^ 8), c2)
+
+
+def test_fp4_ties_go_away_from_zero_and_odd_tail_pads_with_zero():
+    cb = oracle.fp4_codebook()
+    order = sorted((c for c in range(16) if c != 8), key=lambda c: float(cb[c]))
+    ties = 0
+    for lo, hi in zip(order, order[1:]):
+        m = (frac(cb[lo]) + frac(cb[hi])) / 2
+        if Fraction(float(rn32(m))) != m:
+            continue
+        ties += 1
+        block = np.array([float(m), 1.0], dtype=np.float32)
+        packed, _ = oracle.quantize(block, kind="fp4")
+        code = oracle.unpack(packed, 2)[0]
+        assert code == (hi if m > 0 else lo)
+    assert ties >= 2  # at least the midpoints next to zero
+    packed, _ = oracle.quantize(np.array([1.0, -0.5, 0.25], dtype=np.float32), kind="fp4")
+    assert packed.size == 2 and packed[1] & 0xF == oracle.FP4_ZERO
