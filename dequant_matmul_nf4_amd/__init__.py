@@ -20,10 +20,11 @@ LIB_PATH = os.path.join(_HERE, "libnf4.so")
 NF4_OK, NF4_ERR_NULL, NF4_ERR_SIZE, NF4_ERR_BLOCKSIZE, NF4_ERR_ALIGN, NF4_ERR_DTYPE, NF4_ERR_WORKSPACE, NF4_ERR_DEVICE = range(8)
 NF4_F32, NF4_BF16, NF4_F16 = 0, 1, 2
 NF4_DQ_INT8, NF4_DQ_FP8 = 0, 1
+NF4_QT_NF4, NF4_QT_FP4 = 0, 1
 BLOCKSIZE, BLOCKSIZE2 = 64, 256
 
 EXPORTS = (
-    "nf4_last_error", "nf4_codebook", "nf4_quantize", "nf4_double_quant_workspace",
+    "nf4_last_error", "nf4_codebook", "nf4_codebook_fp4", "nf4_quantize", "nf4_quantize_fp4", "nf4_double_quant_workspace",
     "nf4_double_quant", "nf4_e4m3_ratio", "nf4_double_quant_f8", "nf4_dequantize", "nf4_gemv", "nf4_gemm_workspace", "nf4_gemm", "nf4_gemm_dx_workspace",
     "nf4_gemm_dx", "nf4_lora_grads_workspace", "nf4_lora_grads", "nf4_lora_merge",
 )
@@ -41,7 +42,7 @@ class nf4_weight(ctypes.Structure):
         ("packed", ctypes.c_void_p), ("rows", ctypes.c_int64), ("cols", ctypes.c_int64),
         ("blocksize", ctypes.c_int32), ("absmax", ctypes.c_void_p), ("qabsmax", ctypes.c_void_p),
         ("absmax2", ctypes.c_void_p), ("mean", ctypes.c_void_p), ("blocksize2", ctypes.c_int32),
-        ("dq_type", ctypes.c_int32),
+        ("dq_type", ctypes.c_int32), ("quant_type", ctypes.c_int32),
     ]
 
 
@@ -61,7 +62,9 @@ def lib() -> ctypes.CDLL:
     sig = {
         "nf4_last_error": (ctypes.c_char_p, []),
         "nf4_codebook": (ctypes.c_int, [ctypes.POINTER(ctypes.c_float)]),
+        "nf4_codebook_fp4": (ctypes.c_int, [ctypes.POINTER(ctypes.c_float)]),
         "nf4_quantize": (ctypes.c_int, [vp, ctypes.c_int, i64, i32, vp, vp, vp]),
+        "nf4_quantize_fp4": (ctypes.c_int, [vp, ctypes.c_int, i64, i32, vp, vp, vp]),
         "nf4_double_quant_workspace": (sz, [i64]),
         "nf4_double_quant": (ctypes.c_int, [vp, i64, i32, vp, vp, vp, vp, sz, vp]),
         "nf4_double_quant_f8": (ctypes.c_int, [vp, i64, i32, vp, vp, vp, vp, sz, vp]),
@@ -96,6 +99,13 @@ def nf4_codebook():
     """The 16 NF4 levels (host call, needs no GPU) as a list of floats."""
     out = (ctypes.c_float * 16)()
     _check(lib().nf4_codebook(out))
+    return list(out)
+
+
+def nf4_codebook_fp4():
+    """The 16 FP4 levels by code (E2M1 value / 6; host call, needs no GPU)."""
+    out = (ctypes.c_float * 16)()
+    _check(lib().nf4_codebook_fp4(out))
     return list(out)
 
 
@@ -167,6 +177,7 @@ class NF4Weight:
     absmax2: "object" = None
     mean: "object" = None
     dq_type: int = 0  # NF4_DQ_INT8 or NF4_DQ_FP8 (second-level codes)
+    quant_type: int = 0  # NF4_QT_NF4 or NF4_QT_FP4 (code book of the packed codes)
 
     @property
     def double_quant(self) -> bool:
@@ -176,12 +187,13 @@ class NF4Weight:
         return nf4_weight(
             packed=_ptr(self.packed), rows=self.rows, cols=self.cols, blocksize=BLOCKSIZE,
             absmax=_ptr(self.absmax), qabsmax=_ptr(self.qabsmax), absmax2=_ptr(self.absmax2),
-            mean=_ptr(self.mean), blocksize2=BLOCKSIZE2, dq_type=self.dq_type,
+            mean=_ptr(self.mean), blocksize2=BLOCKSIZE2, dq_type=self.dq_type, quant_type=self.quant_type,
         )
 
 
-def nf4_quantize(x, packed=None, absmax=None, stream=None):
-    """Blockwise NF4 quantization of all elements of x (float32 or bf16)."""
+def nf4_quantize(x, packed=None, absmax=None, stream=None, fp4=False):
+    """Blockwise NF4 quantization of all elements of x (float32 or bf16);
+    fp4=True: the same steps with the FP4 code book."""
     torch = _torch()
     _need_cuda(x)
     n = x.numel()
@@ -192,7 +204,8 @@ def nf4_quantize(x, packed=None, absmax=None, stream=None):
     _need_cuda(packed, absmax)
     if packed.numel() < (n + 1) // 2 or absmax.numel() < (n + 63) // 64:
         raise ValueError("output buffers too small")
-    _check(lib().nf4_quantize(_ptr(x), _dtype_code(x), n, BLOCKSIZE, _ptr(packed), _ptr(absmax), _stream(stream)))
+    fn = lib().nf4_quantize_fp4 if fp4 else lib().nf4_quantize
+    _check(fn(_ptr(x), _dtype_code(x), n, BLOCKSIZE, _ptr(packed), _ptr(absmax), _stream(stream)))
     return packed, absmax
 
 
@@ -221,18 +234,23 @@ def nf4_double_quant(absmax, qabsmax=None, absmax2=None, mean=None, workspace=No
     return qabsmax, absmax2, mean
 
 
-def quantize_weight(w, double_quant: bool = True, stream=None, dq_type: str = "int8") -> NF4Weight:
+def quantize_weight(w, double_quant: bool = True, stream=None, dq_type: str = "int8",
+                    quant_type: str = "nf4") -> NF4Weight:
     """nf4_quantize (+ nf4_double_quant, int8 or fp8 second level) of a 2-D
-    weight into an NF4Weight."""
+    weight into an NF4Weight; quant_type "fp4" uses the FP4 code book."""
+    if quant_type not in ("nf4", "fp4"):
+        raise ValueError("quant_type must be 'nf4' or 'fp4'")
+    qt = NF4_QT_FP4 if quant_type == "fp4" else NF4_QT_NF4
     rows, cols = w.shape
-    packed, absmax = nf4_quantize(w, stream=stream)
+    packed, absmax = nf4_quantize(w, stream=stream, fp4=qt == NF4_QT_FP4)
     if not double_quant:
-        return NF4Weight(packed, rows, cols, absmax=absmax)
+        return NF4Weight(packed, rows, cols, absmax=absmax, quant_type=qt)
     if dq_type not in ("int8", "fp8"):
         raise ValueError("dq_type must be 'int8' or 'fp8'")
     fp8 = dq_type == "fp8"
     q, s2, mean = nf4_double_quant(absmax, stream=stream, fp8=fp8)
-    return NF4Weight(packed, rows, cols, qabsmax=q, absmax2=s2, mean=mean, dq_type=NF4_DQ_FP8 if fp8 else NF4_DQ_INT8)
+    return NF4Weight(packed, rows, cols, qabsmax=q, absmax2=s2, mean=mean, dq_type=NF4_DQ_FP8 if fp8 else NF4_DQ_INT8,
+                     quant_type=qt)
 
 
 def nf4_dequantize(w: NF4Weight, out=None, out_dtype=None, stream=None):

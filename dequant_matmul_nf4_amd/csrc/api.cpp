@@ -76,7 +76,7 @@ int check_weight(const nf4_weight* w, nf4i::Scales* sc, int64_t* n_out, const ch
   const int64_t nb = (n + 63) / 64;
   if (w->absmax) {
     if (!aligned(w->absmax, 4)) return fail(NF4_ERR_ALIGN, "%s: absmax must be 4-byte aligned", who);
-    *sc = nf4i::Scales{w->absmax, nullptr, nullptr, nullptr, 0};
+    *sc = nf4i::Scales{w->absmax, nullptr, nullptr, nullptr, 0, 0};
   } else {
     if (!w->qabsmax || !w->absmax2 || !w->mean)
       return fail(NF4_ERR_NULL, "%s: absmax is NULL, so qabsmax, absmax2 and mean are required", who);
@@ -87,8 +87,11 @@ int check_weight(const nf4_weight* w, nf4i::Scales* sc, int64_t* n_out, const ch
       return fail(NF4_ERR_ALIGN, "%s: absmax2 and mean must be 4-byte aligned", who);
     if (w->dq_type != NF4_DQ_INT8 && w->dq_type != NF4_DQ_FP8)
       return fail(NF4_ERR_DTYPE, "%s: dq_type %d unknown", who, (int)w->dq_type);
-    *sc = nf4i::Scales{nullptr, w->qabsmax, w->absmax2, w->mean, w->dq_type == NF4_DQ_FP8 ? 1 : 0};
+    *sc = nf4i::Scales{nullptr, w->qabsmax, w->absmax2, w->mean, w->dq_type == NF4_DQ_FP8 ? 1 : 0, 0};
   }
+  if (w->quant_type != NF4_QT_NF4 && w->quant_type != NF4_QT_FP4)
+    return fail(NF4_ERR_DTYPE, "%s: quant_type %d unknown", who, (int)w->quant_type);
+  sc->fp4 = w->quant_type == NF4_QT_FP4 ? 1 : 0;
   *n_out = n;
   return NF4_OK;
 }
@@ -123,6 +126,22 @@ int double_quant(const float* absmax, int64_t nblocks, int32_t blocksize2, int8_
 
 }  // namespace
 
+namespace {
+
+int quantize(const void* x, int x_dtype, int64_t n, int32_t blocksize, uint8_t* packed, float* absmax,
+             void* stream, int fp4, const char* who) {
+  if (!x || !packed || !absmax) return fail(NF4_ERR_NULL, "%s: x, packed and absmax are required", who);
+  if (x_dtype != NF4_F32 && x_dtype != NF4_BF16) return fail(NF4_ERR_DTYPE, "%s: x_dtype %d unknown", who, x_dtype);
+  if (n < 1 || n >= kMaxN) return fail(NF4_ERR_SIZE, "%s: n = %lld out of range", who, (long long)n);
+  if (blocksize != NF4_BLOCKSIZE) return fail(NF4_ERR_BLOCKSIZE, "%s: blocksize %d unsupported (only 64)", who, (int)blocksize);
+  if (!aligned(x, 16) || !aligned(packed, 16)) return fail(NF4_ERR_ALIGN, "%s: x and packed must be 16-byte aligned", who);
+  if (!aligned(absmax, 4)) return fail(NF4_ERR_ALIGN, "%s: absmax must be 4-byte aligned", who);
+  if (int rc = check_device()) return rc;
+  return launched(nf4i::launch_quantize(x, x_dtype == NF4_BF16, n, packed, absmax, fp4, as_stream(stream)), who);
+}
+
+}  // namespace
+
 extern "C" {
 
 const char* nf4_last_error(void) { return g_err; }
@@ -133,16 +152,20 @@ int nf4_codebook(float out[16]) {
   return ok();
 }
 
+int nf4_codebook_fp4(float out[16]) {
+  if (!out) return fail(NF4_ERR_NULL, "nf4_codebook_fp4: out is NULL");
+  std::memcpy(out, nf4i::codebook(1).level, 16 * sizeof(float));
+  return ok();
+}
+
 int nf4_quantize(const void* x, int x_dtype, int64_t n, int32_t blocksize, uint8_t* packed,
                  float* absmax, void* stream) {
-  if (!x || !packed || !absmax) return fail(NF4_ERR_NULL, "nf4_quantize: x, packed and absmax are required");
-  if (x_dtype != NF4_F32 && x_dtype != NF4_BF16) return fail(NF4_ERR_DTYPE, "nf4_quantize: x_dtype %d unknown", x_dtype);
-  if (n < 1 || n >= kMaxN) return fail(NF4_ERR_SIZE, "nf4_quantize: n = %lld out of range", (long long)n);
-  if (blocksize != NF4_BLOCKSIZE) return fail(NF4_ERR_BLOCKSIZE, "nf4_quantize: blocksize %d unsupported (only 64)", (int)blocksize);
-  if (!aligned(x, 16) || !aligned(packed, 16)) return fail(NF4_ERR_ALIGN, "nf4_quantize: x and packed must be 16-byte aligned");
-  if (!aligned(absmax, 4)) return fail(NF4_ERR_ALIGN, "nf4_quantize: absmax must be 4-byte aligned");
-  if (int rc = check_device()) return rc;
-  return launched(nf4i::launch_quantize(x, x_dtype == NF4_BF16, n, packed, absmax, as_stream(stream)), "nf4_quantize");
+  return quantize(x, x_dtype, n, blocksize, packed, absmax, stream, 0, "nf4_quantize");
+}
+
+int nf4_quantize_fp4(const void* x, int x_dtype, int64_t n, int32_t blocksize, uint8_t* packed,
+                     float* absmax, void* stream) {
+  return quantize(x, x_dtype, n, blocksize, packed, absmax, stream, 1, "nf4_quantize_fp4");
 }
 
 size_t nf4_double_quant_workspace(int64_t nblocks) {

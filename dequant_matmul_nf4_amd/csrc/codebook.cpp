@@ -1,5 +1,10 @@
-// Host derivation of the NF4 code book and of the thresholds the quantizer
-// compares against.
+// Host derivation of the NF4 code book (and of the FP4 one) and of the
+// thresholds the quantizer compares against.
+//
+// FP4: the bitsandbytes tool page lists FP4 beside NF4 among the 4-bit formats
+// ("What it is") and calls it a 4-bit floating-point type ("Glossary"),
+// without values.  The reading used is the E2M1 element type of the Open
+// Compute Project's microscaling formats specification, divided by 6.
 //
 // Bitsandbytes tool page (ozercemkelahmet.com/tools/bitsandbytes), "How NF4
 // works": the 16 code values are placed so that each covers an equal share of
@@ -107,16 +112,48 @@ QuantLut build_lut(const Codebook& cb) {
   return lut;
 }
 
-}  // namespace
+// FP4 (the E2M1 reading): a 4-bit pattern is a sign bit, two exponent bits
+// with bias 1 and one mantissa bit, exponent field 0 being subnormal (m / 2);
+// the level is that value divided by 6, so the largest magnitude is 1.
+double e2m1(int code) {
+  const int e = (code >> 1) & 3, m = code & 1;
+  const double mag = e == 0 ? 0.5 * m : (1.0 + 0.5 * m) * std::ldexp(1.0, e - 1);
+  return (code & 8) ? -mag : mag;
+}
 
-const Codebook& codebook() {
-  static const Codebook cb = build();
+Codebook build_fp4() {
+  Codebook cb{};
+  for (int c = 0; c < 16; ++c) cb.level[c] = static_cast<float>(e2m1(c) / 6.0);
+  for (int i = 0; i < 16; ++i) cb.thresh[i] = INFINITY;  // unused: the quantizer uses the ascending form
   return cb;
 }
 
-const QuantLut& quant_lut() {
-  static const QuantLut lut = build_lut(codebook());
-  return lut;
+// The 15 producible FP4 levels in ascending order (index c <-> pattern
+// c >= 7 ? c - 7 : 15 - c), with a 16th entry equal to the last whose
+// threshold is never reached, so that the NF4 bucket construction applies.
+Codebook build_fp4_ascending() {
+  const Codebook by_code = build_fp4();
+  Codebook cb{};
+  for (int c = 0; c < 15; ++c) cb.level[c] = by_code.level[c >= 7 ? c - 7 : 15 - c];
+  cb.level[15] = cb.level[14];
+  for (int i = 0; i < 14; ++i) cb.thresh[i] = decision_threshold(cb.level[i], cb.level[i + 1]);
+  cb.thresh[14] = INFINITY;
+  cb.thresh[15] = INFINITY;
+  return cb;
+}
+
+}  // namespace
+
+const Codebook& codebook(int fp4) {
+  static const Codebook nf4 = build();
+  static const Codebook f4 = build_fp4();
+  return fp4 ? f4 : nf4;
+}
+
+const QuantLut& quant_lut(int fp4) {
+  static const QuantLut nf4 = build_lut(codebook(0));
+  static const QuantLut f4 = build_lut(build_fp4_ascending());
+  return fp4 ? f4 : nf4;
 }
 
 }  // namespace nf4i

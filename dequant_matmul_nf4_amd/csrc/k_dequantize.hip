@@ -71,7 +71,7 @@ hipError_t launch_dequantize(const uint8_t* packed, int64_t n, Scales sc, void* 
   const int64_t noct = (n + 7) >> 3;
   const int64_t want = (noct + 255) / 256;
   const int grid = static_cast<int>(want < 16384 ? want : 16384);
-  const Codebook& cb = codebook();
+  const Codebook& cb = codebook(sc.fp4);
   if (out_bf16)
     hipLaunchKernelGGL(k_dequantize<true>, dim3(grid), dim3(256), 0, s, packed, n, sc, out, cb);
   else

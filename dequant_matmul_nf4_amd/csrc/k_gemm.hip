@@ -333,7 +333,7 @@ hipError_t launch_gemm(const uint8_t* packed, int64_t rows, int64_t cols, Scales
                        float lora_scale, uint16_t* u_ws, hipStream_t s) {
   GemmArgs a{};
   a.packed = packed; a.rows = rows; a.cols = cols; a.sc = sc; a.x = x; a.m = m; a.y = y;
-  a.cb = codebook();
+  a.cb = codebook(sc.fp4);
   if (r > 0) {
     const int r_pad = (r + 15) / 16 * 16;
     a.kl = static_cast<int>(gemm_lora_cols(r));

@@ -387,7 +387,7 @@ hipError_t launch_gemm_dx(const uint8_t* packed, int64_t rows, int64_t cols, Sca
                           float lora_scale, uint16_t* ws, hipStream_t s) {
   DxArgs a{};
   a.packed = packed; a.rows = rows; a.cols = cols; a.sc = sc; a.dy = dy; a.m = m; a.dx = dx;
-  a.cb = codebook();
+  a.cb = codebook(sc.fp4);
   const int64_t tiles = ((m + kTm - 1) / kTm) * ((cols + kTk - 1) / kTk);
   if (tiles > 0x7FFFFFFF) return hipErrorInvalidValue;
   if (r > 0) {

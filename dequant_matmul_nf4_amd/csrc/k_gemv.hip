@@ -601,7 +601,7 @@ hipError_t launch_rows(const uint8_t* packed, int64_t rows, int64_t cols, Scales
   const RowsPlan pl = rows_plan(rows, cols, kWaves, kRowsMaxWg / MC);
   if (pl.nseg > kSegMax || pl.wpr < 1 || (cols / 64) * 32 >= (int64_t{1} << 32)) return hipErrorInvalidValue;
   const int64_t g = pl.grid;
-  const Codebook& cb = codebook();
+  const Codebook& cb = codebook(sc.fp4);
   const dim3 gd(static_cast<unsigned>(g)), bd(64 * kWaves);
   if (y_bf16)
     hipLaunchKernelGGL((k_gemv_rows<U, kWaves, MC, kDQ, kF8, true>), gd, bd, 0, s, packed, rows, cols, sc, x, y, cb, pl);
@@ -880,7 +880,7 @@ hipError_t launch_mfma(const uint8_t* packed, int64_t rows, int64_t cols, Scales
                        void* y, int y_bf16, hipStream_t s) {
   const MfmaPlan pl = mfma_plan(rows, cols);
   if (pl.nseg > kPartTiles) return hipErrorInvalidValue;
-  const Codebook& cb = codebook();
+  const Codebook& cb = codebook(sc.fp4);
   const dim3 gd(static_cast<unsigned>(pl.grid)), bd(64 * kMfmaWaves);
   const int mi = static_cast<int>(m);
   // whole 4-block segments at multiples of 4 blocks in every row, and scale
@@ -936,7 +936,7 @@ void launch_m1(const uint8_t* packed, int64_t rows, int64_t cols, Scales sc, con
   if (g < need) g = need;
   if (g < 1) g = 1;
   if (g > 0x7FFFFFFF) return;
-  const Codebook& cb = codebook();
+  const Codebook& cb = codebook(sc.fp4);
   const dim3 gd(static_cast<unsigned>(g)), b(static_cast<unsigned>(64 * wpg));
   if (y_bf16) hipLaunchKernelGGL((k_gemv_m1<R, kDQ, true>), gd, b, 0, s, packed, rows, cols, sc, x, y, cb);
   else hipLaunchKernelGGL((k_gemv_m1<R, kDQ, false>), gd, b, 0, s, packed, rows, cols, sc, x, y, cb);
@@ -949,7 +949,7 @@ hipError_t launch_gemv(const uint8_t* packed, int64_t rows, int64_t cols, Scales
   const int64_t groups = (rows + kRowsPerGroup - 1) / kRowsPerGroup;
   if (groups > 0x7FFFFFFF) return hipErrorInvalidValue;
   const dim3 grid(static_cast<unsigned>(groups));
-  const Codebook& cb = codebook();
+  const Codebook& cb = codebook(sc.fp4);
   const int mm = static_cast<int>(m);
   if (m == 1) {
     const int64_t nseg = (cols / 64 + 63) / 64;

@@ -130,7 +130,7 @@ hipError_t launch_lora_merge(const uint8_t* packed, int64_t rows, int64_t cols, 
   const int64_t gy = (cols + kColsPerWg - 1) / kColsPerWg;   // column chunks
   if (gx > (int64_t(1) << 24) || gy > 65535) return hipErrorInvalidValue;  // work-items fit 32 bits
   const dim3 grid(static_cast<unsigned>(gx), static_cast<unsigned>(gy));
-  const Codebook& cb = codebook();
+  const Codebook& cb = codebook(sc.fp4);
   if (out_f16)
     hipLaunchKernelGGL(k_lora_merge<true>, grid, dim3(kMergeThreads), 0, s, packed, rows, cols, sc, lora_a, lora_b,
                        r, scale, out, cb);

@@ -1,7 +1,9 @@
 // Blockwise NF4 quantization (bitsandbytes tool page, "How it works",
 // Steps 1-4): per block of 64 values, the largest |x| is the scale; each value
 // is divided by it and replaced by the index of the nearest NF4 level; two
-// indices are packed per byte, the first in the high nibble.
+// indices are packed per byte, the first in the high nibble.  The FP4 code book
+// (the tool page's "What it is" and "Glossary"; read as E2M1 / 6) takes the
+// same steps; its ascending level index is stored as the E2M1 pattern.
 //
 // Layout: each lane owns 16 consecutive values (two 16-byte bf16 loads or
 // four 16-byte fp32 loads) and writes 8 bytes of packed codes; 4 adjacent
@@ -62,6 +64,7 @@ __device__ __forceinline__ uint32_t code_of(float q, const uint2* lut) {
 
 // Quantizes one 16-value segment held by a lane (its quad holds the block)
 // and stores its 8 packed bytes and, from the quad's first lane, the absmax.
+template <bool kFp4>
 __device__ __forceinline__ void quantize_segment(const float v[kPerLane], int64_t sg, uint8_t* __restrict__ packed,
                                                  float* __restrict__ absmax, const uint2* lut, int64_t nbytes,
                                                  bool full) {
@@ -69,7 +72,8 @@ __device__ __forceinline__ void quantize_segment(const float v[kPerLane], int64_
 #pragma unroll
   for (int i = 0; i < kPerLane; ++i) a = fmaxf(a, fabsf(v[i]));
   a = quad_max(a);
-  uint32_t w0 = 0x77777777u, w1 = 0x77777777u;  // all-zero block: zero level everywhere
+  constexpr uint32_t kZero = kFp4 ? 0u : 0x77777777u;  // the zero level's code in every nibble
+  uint32_t w0 = kZero, w1 = kZero;  // all-zero block
   if (a > 0.0f) {
     uint32_t c[kPerLane];
     if (a >= 0x1p-98f && a < 0x1p126f) {
@@ -83,6 +87,11 @@ __device__ __forceinline__ void quantize_segment(const float v[kPerLane], int64_
     } else {
 #pragma unroll
       for (int i = 0; i < kPerLane; ++i) c[i] = code_of(v[i] / a, lut);
+    }
+    if constexpr (kFp4) {
+      // ascending index -> E2M1 pattern
+#pragma unroll
+      for (int i = 0; i < kPerLane; ++i) c[i] = c[i] >= 7u ? c[i] - 7u : 15u - c[i];
     }
     w0 = 0;
     w1 = 0;
@@ -108,7 +117,7 @@ __device__ __forceinline__ void quantize_segment(const float v[kPerLane], int64_
 // segments per iteration and issues both loads before using either; there
 // is no branch around any load.  A partial last block is done afterwards by
 // the first quad of workgroup 0 with guarded loads and stores.
-template <bool kBf16>
+template <bool kBf16, bool kFp4>
 __global__ __launch_bounds__(256) void k_quantize(const void* __restrict__ x, int64_t n,
                                                   uint8_t* __restrict__ packed,
                                                   float* __restrict__ absmax, QuantLut tab) {
@@ -129,8 +138,8 @@ __global__ __launch_bounds__(256) void k_quantize(const void* __restrict__ x, in
     float v0[kPerLane], v1[kPerLane];
     load16<kBf16>(x, sg0 * kPerLane, n, v0);
     load16<kBf16>(x, sg1c * kPerLane, n, v1);
-    quantize_segment(v0, sg0, packed, absmax, lut, nbytes, true);
-    if (sg1 < nseg) quantize_segment(v1, sg1, packed, absmax, lut, nbytes, true);
+    quantize_segment<kFp4>(v0, sg0, packed, absmax, lut, nbytes, true);
+    if (sg1 < nseg) quantize_segment<kFp4>(v1, sg1, packed, absmax, lut, nbytes, true);
   }
   if ((n & 63) && blockIdx.x == 0 && threadIdx.x < 4) {
     const int64_t sg = nseg + threadIdx.x;
@@ -141,13 +150,13 @@ __global__ __launch_bounds__(256) void k_quantize(const void* __restrict__ x, in
       if constexpr (kBf16) v[i] = e < n ? bf16_to_f32(static_cast<const uint16_t*>(x)[e]) : 0.0f;
       else v[i] = e < n ? static_cast<const float*>(x)[e] : 0.0f;
     }
-    quantize_segment(v, sg, packed, absmax, lut, nbytes, false);
+    quantize_segment<kFp4>(v, sg, packed, absmax, lut, nbytes, false);
   }
 }
 
 }  // namespace
 
-hipError_t launch_quantize(const void* x, int x_bf16, int64_t n, uint8_t* packed, float* absmax,
+hipError_t launch_quantize(const void* x, int x_bf16, int64_t n, uint8_t* packed, float* absmax, int fp4,
                            hipStream_t s) {
   // two segments per lane and one pass per lane: a loop would make the next
   // loads wait for the previous stores (their registers are reused)
@@ -155,11 +164,14 @@ hipError_t launch_quantize(const void* x, int x_bf16, int64_t n, uint8_t* packed
   const int64_t want = (nseg + 511) / 512;
   if (want > 0x7FFFFFFF) return hipErrorInvalidValue;
   const int grid = static_cast<int>(want < 1 ? 1 : want);
-  const QuantLut& tab = quant_lut();
-  if (x_bf16)
-    hipLaunchKernelGGL(k_quantize<true>, dim3(grid), dim3(256), 0, s, x, n, packed, absmax, tab);
-  else
-    hipLaunchKernelGGL(k_quantize<false>, dim3(grid), dim3(256), 0, s, x, n, packed, absmax, tab);
+  const QuantLut& tab = quant_lut(fp4);
+  if (fp4) {
+    if (x_bf16) hipLaunchKernelGGL((k_quantize<true, true>), dim3(grid), dim3(256), 0, s, x, n, packed, absmax, tab);
+    else hipLaunchKernelGGL((k_quantize<false, true>), dim3(grid), dim3(256), 0, s, x, n, packed, absmax, tab);
+  } else {
+    if (x_bf16) hipLaunchKernelGGL((k_quantize<true, false>), dim3(grid), dim3(256), 0, s, x, n, packed, absmax, tab);
+    else hipLaunchKernelGGL((k_quantize<false, false>), dim3(grid), dim3(256), 0, s, x, n, packed, absmax, tab);
+  }
   return hipGetLastError();
 }
 

@@ -15,8 +15,9 @@ struct Codebook {
   float thresh[16];  // thresh[15] = +inf, never reached by |v| <= 1
 };
 
-// Host derivation, computed once (thread-safe) at first use.
-const Codebook& codebook();
+// Host derivation, computed once (thread-safe) at first use.  fp4 = 1
+// selects the FP4 code book (levels by 4-bit E2M1 pattern).
+const Codebook& codebook(int fp4 = 0);
 
 // Bucket table of the quantizer's nearest-level search.  A normalized value
 // v in [-1, 1] falls in bucket (bits(v) >> 21): its sign, exponent and two
@@ -31,7 +32,10 @@ struct QuantLut {
   float thr[kLutSpecial];
   uint32_t base[kLutSpecial];
 };
-const QuantLut& quant_lut();
+// The quantizer's bucket table.  For FP4 it is built on the 15 producible
+// levels in ascending order (zero at index 7, like NF4); the kernel maps the
+// ascending index c to the E2M1 pattern (c >= 7 ? c - 7 : 15 - c).
+const QuantLut& quant_lut(int fp4 = 0);
 
 __host__ __device__ inline int lut_special_index(int t) {
   const int sign = t / 24, e = kLutFirstExp + (t % 24) / 4, m2 = t % 4;
@@ -76,6 +80,7 @@ struct Scales {
   const float* absmax2;
   const float* mean;
   int f8;                // second level: 0 = int8 codes, 1 = float8 (E4M3) codes
+  int fp4;               // code book: 0 = NF4, 1 = FP4
 };
 
 // Workspace of the double-quant kernels: one row of partial digit sums per
@@ -85,7 +90,7 @@ constexpr int kDqMaxGroups = 256;
 constexpr size_t kDqWorkspaceBytes = kDqMaxGroups * kDqDigits * sizeof(unsigned long long);
 
 hipError_t launch_quantize(const void* x, int x_bf16, int64_t n, uint8_t* packed,
-                           float* absmax, hipStream_t s);
+                           float* absmax, int fp4, hipStream_t s);
 hipError_t launch_double_quant(const float* absmax, int64_t nb, int8_t* q, float* absmax2,
                                float* mean, unsigned long long* ws, int f8, hipStream_t s);
 hipError_t launch_dequantize(const uint8_t* packed, int64_t n, Scales sc, void* out,

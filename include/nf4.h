@@ -57,6 +57,11 @@ typedef enum nf4_dtype { NF4_F32 = 0, NF4_BF16 = 1, NF4_F16 = 2 } nf4_dtype;
 /* Type of the double-quantized scale codes (nf4_weight.dq_type). */
 typedef enum nf4_dq_type { NF4_DQ_INT8 = 0, NF4_DQ_FP8 = 1 } nf4_dq_type;
 
+/* Code book of the 4-bit codes (nf4_weight.quant_type): NF4, or FP4 (tool
+ * page "What it is": 4-bit FP4 and NF4 formats; "Glossary": FP4 is a 4-bit
+ * floating-point type).  A zero-initialised weight descriptor means NF4. */
+typedef enum nf4_quant_type { NF4_QT_NF4 = 0, NF4_QT_FP4 = 1 } nf4_quant_type;
+
 #define NF4_BLOCKSIZE 64
 #define NF4_BLOCKSIZE2 256
 
@@ -71,6 +76,15 @@ const char* nf4_last_error(void);
  * quantile at delta.  Derived on the host in extended precision at first use.
  * Needs no GPU.  Returns NF4_ERR_NULL if out is NULL. */
 int nf4_codebook(float out[16]);
+
+/* [host] The 16 FP4 levels as float32, by code (the 4-bit pattern).  The pages
+ * name FP4 without values; the reading used is the E2M1 element type of the
+ * Open Compute Project microscaling formats specification (sign in bit 3, two
+ * exponent bits with bias 1, one mantissa bit, exponent field 0 subnormal:
+ * magnitudes 0, 0.5, 1, 1.5, 2, 3, 4, 6), divided by 6 so that the block
+ * absmax maps to +-1: out[c] = e2m1(c) / 6, out[7] = 1, out[15] = -1,
+ * out[8] = -0.  Needs no GPU.  Returns NF4_ERR_NULL if out is NULL. */
+int nf4_codebook_fp4(float out[16]);
 
 /* Blockwise NF4 quantization -- tool page "How it works", Steps 1-4.
  *   x       : n input values, x_dtype NF4_F32 or NF4_BF16; 16-byte aligned.
@@ -88,6 +102,15 @@ int nf4_codebook(float out[16]);
  * block whose absmax is 0 gets code 7 throughout. */
 int nf4_quantize(const void* x, int x_dtype, int64_t n, int32_t blocksize,
                  uint8_t* packed, float* absmax, void* stream);
+
+/* FP4 quantization: nf4_quantize's steps with the FP4 code book (see
+ * nf4_codebook_fp4).  Each code is the pattern of the FP4 level nearest to
+ * fl32(x / absmax) among the 15 patterns other than 1000 (negative zero),
+ * an exact tie going to the level farther from zero; zero is 0000, so an odd
+ * n ends in a low nibble 0 and a block whose absmax is 0 gets code 0
+ * throughout.  Arguments, layout and errors as nf4_quantize. */
+int nf4_quantize_fp4(const void* x, int x_dtype, int64_t n, int32_t blocksize,
+                     uint8_t* packed, float* absmax, void* stream);
 
 /* Bytes of device workspace nf4_double_quant needs (a small constant). */
 size_t nf4_double_quant_workspace(int64_t nblocks);
@@ -147,6 +170,7 @@ typedef struct nf4_weight {
   const float* mean;        /* one float32 when absmax == NULL                   */
   int32_t blocksize2;       /* 256 when absmax == NULL                           */
   int32_t dq_type;          /* nf4_dq_type of qabsmax when absmax == NULL        */
+  int32_t quant_type;       /* nf4_quant_type of the codes in packed             */
 } nf4_weight;
 
 /* Dequantization -- tool page "How it works", Step 5.

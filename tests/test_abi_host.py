@@ -70,9 +70,10 @@ def test_workspace_sizes(L):
 
 
 def test_struct_layout():
-    assert ctypes.sizeof(nf4.nf4_weight) == 72
+    assert ctypes.sizeof(nf4.nf4_weight) == 80
     assert nf4.nf4_weight.blocksize2.offset == 64
     assert nf4.nf4_weight.dq_type.offset == 68
+    assert nf4.nf4_weight.quant_type.offset == 72
 
 
 # Fake but aligned device addresses: every call below fails validation on the
@@ -108,6 +109,10 @@ CASES = [
     ("dq f8 blocksize2", lambda L: L.nf4_double_quant_f8(A, 10, 128, A, A2, A2, A, WS, None), nf4.NF4_ERR_BLOCKSIZE),
     ("dq f8 workspace small", lambda L: L.nf4_double_quant_f8(A, 10, 256, A, A2, A2, A, 8, None), nf4.NF4_ERR_WORKSPACE),
     ("dequant dq_type unknown", lambda L: L.nf4_dequantize(ctypes.byref(_w(absmax=None, qabsmax=A, absmax2=A2, mean=A2, dq_type=2)), A, 1, None), nf4.NF4_ERR_DTYPE),
+    ("dequant quant_type unknown", lambda L: L.nf4_dequantize(ctypes.byref(_w(quant_type=2)), A, 1, None), nf4.NF4_ERR_DTYPE),
+    ("gemv quant_type unknown", lambda L: L.nf4_gemv(ctypes.byref(_w(absmax=None, qabsmax=A, absmax2=A2, mean=A2, quant_type=-1)), A, 1, A, 1, None), nf4.NF4_ERR_DTYPE),
+    ("quantize_fp4 null", lambda L: L.nf4_quantize_fp4(None, 1, 64, 64, A, A, None), nf4.NF4_ERR_NULL),
+    ("quantize_fp4 blocksize", lambda L: L.nf4_quantize_fp4(A, 1, 64, 32, A, A, None), nf4.NF4_ERR_BLOCKSIZE),
     ("gemv dq_type unknown", lambda L: L.nf4_gemv(ctypes.byref(_w(absmax=None, qabsmax=A, absmax2=A2, mean=A2, dq_type=-1)), A, 1, A, 1, None), nf4.NF4_ERR_DTYPE),
     ("e4m3 ratio null", lambda L: L.nf4_e4m3_ratio(None), nf4.NF4_ERR_NULL),
     ("dequant null weight", lambda L: L.nf4_dequantize(None, A, 1, None), nf4.NF4_ERR_NULL),
@@ -184,3 +189,12 @@ def test_invalid_arguments_rejected_on_host(L, name, call, code):
 
 def test_codebook_null(L):
     assert L.nf4_codebook(None) == nf4.NF4_ERR_NULL
+
+
+def test_fp4_codebook_bit_identical_to_oracle():
+    """The library's FP4 code book (host call) equals the oracle's, bit for bit
+    (both derived independently from the E2M1 definition)."""
+    import numpy as np
+    import oracle
+    got = np.array(nf4.nf4_codebook_fp4(), dtype=np.float32)
+    assert np.array_equal(got.view(np.uint32), oracle.fp4_codebook().view(np.uint32))
