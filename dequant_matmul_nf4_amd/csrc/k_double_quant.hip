@@ -102,8 +102,19 @@ __device__ __forceinline__ unsigned long long block_digit_sum(unsigned long long
 // Digit sums of the workgroup's scales: each thread adds kPerThread scales
 // (all loads issued first) into registers, then the 256 threads' digit
 // vectors are added through LDS into the workgroup's row.
+//
+// A contribution lands in digits d and d + 1.  The scales of one weight
+// mostly share one or two exponent ranges, so each thread also keeps a
+// window of three digits starting at the digit d of its first nonzero scale
+// and adds a contribution there when d is the window's first or second digit
+// (three selects); any other contribution takes the selects over all 12
+// digits.  The window is added into the 12 digits at the end, so the sum is
+// the same integer either way.  The window pays off from about 8 scales per
+// thread (measured: 8192^2 weights 15.4 -> 14.6 us; at 4 per thread the
+// final fold costs more than it saves), so the launcher picks it by size.
 constexpr int kPerThread = 4;
 
+template <bool kWindow>
 __global__ __launch_bounds__(256) void k_dq_partial(const float* __restrict__ absmax, int64_t nb,
                                                     unsigned long long* __restrict__ ws) {
   __shared__ unsigned long long vec[256][kDqDigits + 1];  // +1: spreads the banks
@@ -112,6 +123,8 @@ __global__ __launch_bounds__(256) void k_dq_partial(const float* __restrict__ ab
   unsigned long long acc[kDqDigits];
 #pragma unroll
   for (int k = 0; k < kDqDigits; ++k) acc[k] = 0ull;
+  int base = -1;  // the window's first digit (placed by the first nonzero scale)
+  unsigned long long w0 = 0ull, w1 = 0ull, w2 = 0ull;
   const int64_t stride = static_cast<int64_t>(gridDim.x) * blockDim.x;
   for (int64_t i0 = static_cast<int64_t>(blockIdx.x) * blockDim.x + t; i0 < nb; i0 += kPerThread * stride) {
     float v[kPerThread];
@@ -125,12 +138,24 @@ __global__ __launch_bounds__(256) void k_dq_partial(const float* __restrict__ ab
       int d;
       uint32_t lo, hi;
       scale_to_digits(v[u], &d, &lo, &hi);
-      // a contribution lands in digit d (low 32 bits) and d + 1 (high bits);
-      // selects keep the indexing static
+      if (kWindow && base < 0 && (lo | hi) != 0u) base = d;
+      const int rel = d - base;  // a zero scale adds nothing wherever it goes
+      if (kWindow && (rel == 0 || rel == 1)) {
+        w0 += rel == 0 ? lo : 0u;
+        w1 += rel == 0 ? hi : lo;
+        w2 += rel == 0 ? 0u : hi;
+      } else {
+        // selects keep the indexing static
 #pragma unroll
-      for (int k = 0; k < kDqDigits; ++k)
-        acc[k] += static_cast<unsigned long long>((k == d ? lo : 0u)) + static_cast<unsigned long long>((k == d + 1 ? hi : 0u));
+        for (int k = 0; k < kDqDigits; ++k)
+          acc[k] += static_cast<unsigned long long>((k == d ? lo : 0u)) + static_cast<unsigned long long>((k == d + 1 ? hi : 0u));
+      }
     }
+  }
+  if constexpr (kWindow) {
+#pragma unroll
+    for (int k = 0; k < kDqDigits; ++k)
+      acc[k] += (k == base ? w0 : 0ull) + (k == base + 1 ? w1 : 0ull) + (k == base + 2 ? w2 : 0ull);
   }
 #pragma unroll
   for (int k = 0; k < kDqDigits; ++k) vec[t][k] = acc[k];
@@ -266,7 +291,10 @@ hipError_t launch_double_quant(const float* absmax, int64_t nb, int8_t* q, float
                                float* mean, unsigned long long* ws, int f8, hipStream_t s) {
   int64_t want = (nb + 256 * kPerThread - 1) / (256 * kPerThread);
   int grid = static_cast<int>(want < kDqMaxGroups ? want : kDqMaxGroups);
-  hipLaunchKernelGGL(k_dq_partial, dim3(grid), dim3(256), 0, s, absmax, nb, ws);
+  if (nb >= static_cast<int64_t>(grid) * 256 * 8)
+    hipLaunchKernelGGL(k_dq_partial<true>, dim3(grid), dim3(256), 0, s, absmax, nb, ws);
+  else
+    hipLaunchKernelGGL(k_dq_partial<false>, dim3(grid), dim3(256), 0, s, absmax, nb, ws);
   const int64_t groups = (nb + 255) >> 8;
   want = (groups + 3) / 4;  // 4 waves per workgroup
   const int qgrid = static_cast<int>(want < 1024 ? want : 1024);

@@ -259,3 +259,33 @@ def test_quantize_deterministic():
     torch.cuda.synchronize()
     assert torch.equal(p1, p2) and torch.equal(a1, a2)
     assert torch.equal(q1, q2) and torch.equal(s1, s2) and torch.equal(m1, m2)
+
+
+@pytest.mark.parametrize("kind", ["wide", "narrow_with_outliers", "with_zeros"])
+def test_double_quant_large_scale_arrays_bit_exact(kind):
+    """Scale arrays large enough (>= 8 per summing thread) for the partial-sum
+    kernel's three-digit window: scales spread over many exponent ranges
+    (most contributions fall outside any one window), scales in one range
+    with rare outliers, and runs of zero scales -- mean, codes and group
+    scales bit-exact against the oracle."""
+    say("double quant large", kind)
+    torch = need_gpu()
+    nb = 600_000
+    rng = np.random.default_rng({"wide": 41, "narrow_with_outliers": 42, "with_zeros": 43}[kind])
+    if kind == "wide":
+        a = np.exp2(rng.uniform(-100, 60, nb)) * rng.uniform(1, 2, nb)
+    elif kind == "narrow_with_outliers":
+        a = rng.uniform(0.04, 0.09, nb)
+        idx = rng.choice(nb, 50, replace=False)
+        a[idx] = np.exp2(rng.uniform(-120, 100, idx.size))
+    else:
+        a = rng.uniform(0.01, 0.5, nb)
+        a[rng.random(nb) < 0.3] = 0.0
+        a[:70_000] = 0.0
+    a = a.astype(np.float32)
+    q, s2, mean = nf4.nf4_double_quant(torch.from_numpy(a).to("cuda"))
+    torch.cuda.synchronize()
+    q_o, s2_o, mean_o = oracle.double_quant(a)
+    assert f32_bits(mean)[0] == np.float32(mean_o).view(np.uint32)
+    assert np.array_equal(q.cpu().numpy(), q_o)
+    assert np.array_equal(f32_bits(s2), s2_o.view(np.uint32))
