@@ -192,3 +192,52 @@ def test_lora_merge_fp4_bit_exact():
     deq = oracle.dequantize(p, w.size, qabsmax=q, absmax2=s2, mean=mean, kind="fp4").reshape(rows, cols)
     ref = oracle.lora_merge(deq, syn.bf16_to_f32(a), syn.bf16_to_f32(b), 2.0, "bf16")
     assert np.array_equal(bf16_bits(out), ref.reshape(rows, cols))
+
+
+def test_fp4_with_float8_second_level():
+    """FP4 codes with the float8 (E4M3) second level: the two readings are
+    independent, so the dequantized weights are the oracle's bit for bit and
+    the GEMV stays within the bound."""
+    say("fp4 + fp8 scales")
+    torch = need_gpu()
+    rows, cols = 257, 1024
+    w = syn.normal_f32((rows, cols), 0.02, 1600)
+    W = nf4.quantize_weight(to_dev(w), quant_type="fp4", dq_type="fp8")
+    d16 = nf4.nf4_dequantize(W, out_dtype=torch.bfloat16)
+    xb = syn.to_bf16(syn.normal_f32((1, cols), 1.0, 1601))
+    y = nf4.nf4_gemv(W, xb.to("cuda"), y_dtype=torch.float32)
+    torch.cuda.synchronize()
+    p, a = oracle.quantize(w.reshape(-1), kind="fp4")
+    q, s2, mean = oracle.double_quant_f8(a)
+    r16 = oracle.dequantize(p, w.size, qabsmax=q, absmax2=s2, mean=mean, out="bf16", dq_kind="fp8", kind="fp4")
+    assert np.array_equal(bf16_bits(d16).reshape(-1), r16)
+    ref = oracle.matmul_ref(syn.bf16_to_f32(xb), oracle.bf16_bits_to_f32(r16).reshape(rows, cols))
+    assert oracle.rel_frobenius(_f64(y), ref) <= MATMUL_RTOL
+
+
+@pytest.mark.parametrize("m", [1, 4])
+def test_fp4_gemv_large_sampled_rows(m):
+    """A 16384x8192 FP4 weight (the streaming kernel at m = 1 and m = 4):
+    all codes bit-exact, sampled output rows against the oracle."""
+    say("fp4 gemv large", m)
+    torch = need_gpu()
+    rows, cols = 16384, 8192
+    w = syn.normal_f32((rows, cols), 0.02, 1700 + m)
+    x = syn.to_bf16(syn.normal_f32((m, cols), 1.0, 1701))
+    W = nf4.quantize_weight(to_dev(w), quant_type="fp4")
+    y = nf4.nf4_gemv(W, x.to("cuda"), y_dtype=torch.float32)
+    torch.cuda.synchronize()
+    p, a = oracle.quantize(w.reshape(-1), kind="fp4")
+    assert np.array_equal(u8(W.packed), p)
+    q, s2, mean = oracle.double_quant(a)
+    a_hat = oracle.dequant_scales(q, s2, mean)
+    rng = np.random.default_rng(9)
+    sel = np.unique(np.concatenate([[0, rows - 1], rng.choice(rows, 96, replace=False)]))
+    codes = oracle.unpack(p, w.size).reshape(rows, cols)[sel]
+    blk = (sel[:, None] * cols + np.arange(cols)[None, :]) // 64
+    wdeq = (oracle.fp4_codebook()[codes] * a_hat[blk]).astype(np.float32)
+    wdeq = oracle.bf16_bits_to_f32(oracle.f32_to_bf16_bits(wdeq)).reshape(sel.size, cols)
+    ref = oracle.matmul_ref(syn.bf16_to_f32(x), wdeq)
+    e = oracle.rel_frobenius(_f64(y)[:, sel], ref)
+    say(f"  rel err {e:.2e}")
+    assert e <= MATMUL_RTOL
