@@ -158,16 +158,19 @@ __device__ __forceinline__ void mfma_interleave() {
   }
 }
 
-template <bool kDQ>
-__device__ __forceinline__ void block_scales(const WRegs& wr, float mean, int f8, float (&sa)[2]) {
+// The scale form is a template parameter (plain, int8, float8): a runtime
+// choice would put a global-memory table load behind a branch, and the wait
+// the compiler places after it would also wait for the next step's loads.
+template <bool kDQ, bool kF8>
+__device__ __forceinline__ void block_scales(const WRegs& wr, float mean, float (&sa)[2]) {
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
-    if constexpr (kDQ) sa[j] = (code_ratio(wr.q[j], f8) * wr.s2[j]) + mean;  // a_hat, three roundings
+    if constexpr (kDQ) sa[j] = (code_ratio(wr.q[j], kF8 ? 1 : 0) * wr.s2[j]) + mean;  // a_hat, three roundings
     else sa[j] = wr.am[j];
   }
 }
 
-template <bool kDQ>
+template <bool kDQ, bool kF8>
 __global__ __launch_bounds__(kThreads, kWgPerCu) void k_gemm(GemmArgs a) {
   __shared__ __align__(16) char xs0[kStageBytes], xs1[kStageBytes];
   __shared__ __align__(16) float2 tab[256 * kCopies];
@@ -223,7 +226,7 @@ __global__ __launch_bounds__(kThreads, kWgPerCu) void k_gemm(GemmArgs a) {
     Lookups lk[3];
     bf16x8 af[3][kMI];
     const uint32_t sw = ((lane & 31) >> 1) & 7, h4 = (lane >> 5) * 4;
-    block_scales<kDQ>(wc, mean, a.sc.f8, sa);
+    block_scales<kDQ, kF8>(wc, mean, sa);
     lookup_step<kCopies>(lk[0], wc.w, 0, tabc, slot);
     bf[0][0] = expand_frag(lk[0].l[0], sa[0]);
     bf[0][1] = expand_frag(lk[0].l[1], sa[1]);
@@ -263,7 +266,7 @@ __global__ __launch_bounds__(kThreads, kWgPerCu) void k_gemm(GemmArgs a) {
       __builtin_amdgcn_sched_barrier(0);
       // s = 3, with the next step's s = 0 expansion
       gt::mfma16(af[0], bf[1], acc);
-      block_scales<kDQ>(wnx, mean, a.sc.f8, sa);
+      block_scales<kDQ, kF8>(wnx, mean, sa);
       lookup_step<kCopies>(lk[1], wnx.w, 0, tabc, slot);
       bf[0][0] = expand_frag(lk[1].l[0], sa[0]);
       bf[0][1] = expand_frag(lk[1].l[1], sa[1]);
@@ -349,8 +352,9 @@ hipError_t launch_gemm(const uint8_t* packed, int64_t rows, int64_t cols, Scales
   const int64_t tiles = ((rows + kBN - 1) / kBN) * ((m + kBM - 1) / kBM);
   const int64_t slots = kWgPerCu * device_cus();  // resident workgroups
   const unsigned grid = static_cast<unsigned>(tiles < slots ? tiles : slots);
-  if (sc.absmax) hipLaunchKernelGGL(k_gemm<false>, dim3(grid), dim3(kThreads), 0, s, a);
-  else hipLaunchKernelGGL(k_gemm<true>, dim3(grid), dim3(kThreads), 0, s, a);
+  if (sc.absmax) hipLaunchKernelGGL((k_gemm<false, false>), dim3(grid), dim3(kThreads), 0, s, a);
+  else if (sc.f8) hipLaunchKernelGGL((k_gemm<true, true>), dim3(grid), dim3(kThreads), 0, s, a);
+  else hipLaunchKernelGGL((k_gemm<true, false>), dim3(grid), dim3(kThreads), 0, s, a);
   return hipGetLastError();
 }
 

@@ -120,9 +120,10 @@ __device__ __forceinline__ void load_codes(CodeRegs& r, const CodePtrs& p, const
   }
 }
 
-template <bool kDQ>
-__device__ __forceinline__ float row_scale(const CodeRegs& r, float mean, int f8) {
-  if constexpr (kDQ) return code_ratio(r.q, f8) * r.s2 + mean;  // a_hat: three roundings (contraction is off)
+// The scale form is a template parameter (see the forward GEMM).
+template <bool kDQ, bool kF8>
+__device__ __forceinline__ float row_scale(const CodeRegs& r, float mean) {
+  if constexpr (kDQ) return code_ratio(r.q, kF8 ? 1 : 0) * r.s2 + mean;  // a_hat: three roundings (contraction is off)
   else return r.am;
 }
 
@@ -197,7 +198,7 @@ __device__ __forceinline__ void act_tail(const gt::ActPtrs<kP>& p, int64_t ks, i
   }
 }
 
-template <bool kDQ>
+template <bool kDQ, bool kF8>
 __global__ __launch_bounds__(kDxThreads) void k_gemm_dx(DxArgs a) {
   __shared__ __align__(16) char stage0[kStageBytes], stage1[kStageBytes];
   __shared__ __align__(16) char wts[4][2][kWtBytes];
@@ -246,7 +247,7 @@ __global__ __launch_bounds__(kDxThreads) void k_gemm_dx(DxArgs a) {
 
   // a_hat of the lane's 8 rows from the wave's scale buffer (written just before, same wave)
   auto scales_of = [&](const CodeRegs& c, float (&ah)[8]) {
-    scw[lane & 31] = row_scale<kDQ>(c, mean, a.sc.f8);
+    scw[lane & 31] = row_scale<kDQ, kF8>(c, mean);
     const float4 a0 = *reinterpret_cast<const float4*>(scw + 8 * g);
     const float4 a1 = *reinterpret_cast<const float4*>(scw + 8 * g + 4);
     ah[0] = a0.x; ah[1] = a0.y; ah[2] = a0.z; ah[3] = a0.w; ah[4] = a1.x; ah[5] = a1.y; ah[6] = a1.z; ah[7] = a1.w;
@@ -400,8 +401,10 @@ hipError_t launch_gemm_dx(const uint8_t* packed, int64_t rows, int64_t cols, Sca
     if (hipError_t e = launch_transpose_b(lora_b, rows, r, bt, s)) return e;
     if (hipError_t e = launch_lora_u(dy, bt, m, rows, r, lora_scale, ws, s)) return e;
   }
-  if (sc.absmax) hipLaunchKernelGGL(k_gemm_dx<false>, dim3(static_cast<unsigned>(tiles)), dim3(kDxThreads), 0, s, a);
-  else hipLaunchKernelGGL(k_gemm_dx<true>, dim3(static_cast<unsigned>(tiles)), dim3(kDxThreads), 0, s, a);
+  const dim3 gd(static_cast<unsigned>(tiles)), bd(kDxThreads);
+  if (sc.absmax) hipLaunchKernelGGL((k_gemm_dx<false, false>), gd, bd, 0, s, a);
+  else if (sc.f8) hipLaunchKernelGGL((k_gemm_dx<true, true>), gd, bd, 0, s, a);
+  else hipLaunchKernelGGL((k_gemm_dx<true, false>), gd, bd, 0, s, a);
   return hipGetLastError();
 }
 
