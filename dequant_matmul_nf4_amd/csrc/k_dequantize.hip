@@ -4,18 +4,18 @@
 //
 // Layout: each lane expands one 32-bit word of packed codes (8 values) and
 // writes 16 bytes (bf16) or 32 bytes (fp32); the code book sits in LDS.
-#include "nf4_device.h"
+#include "scale_forms.h"
 
 namespace nf4i {
 namespace {
 
-template <bool kBf16Out>
+template <bool kBf16Out, bool kDQ, bool kF8>
 __global__ __launch_bounds__(256) void k_dequantize(const uint8_t* __restrict__ packed, int64_t n,
                                                     Scales sc, void* __restrict__ out, Codebook cb) {
   __shared__ float lv[16];
   if (threadIdx.x < 16) lv[threadIdx.x] = cb.level[threadIdx.x];
   __syncthreads();
-  const float mean = sc.absmax ? 0.0f : *sc.mean;
+  const float mean = kDQ ? *sc.mean : 0.0f;
   const int64_t noct = (n + 7) >> 3;
   const int64_t nbytes = (n + 1) >> 1;
   const int64_t stride = static_cast<int64_t>(gridDim.x) * blockDim.x;
@@ -30,7 +30,7 @@ __global__ __launch_bounds__(256) void k_dequantize(const uint8_t* __restrict__ 
         if (byte0 + j < nbytes)
           word = (word & ~(0xFFu << (8 * j))) | (static_cast<uint32_t>(packed[byte0 + j]) << (8 * j));
     }
-    const float a = block_scale(sc, (o * 8) >> 6, mean);
+    const float a = block_scale_t<kDQ, kF8>(sc, (o * 8) >> 6, mean);
     float v[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
@@ -72,10 +72,14 @@ hipError_t launch_dequantize(const uint8_t* packed, int64_t n, Scales sc, void* 
   const int64_t want = (noct + 255) / 256;
   const int grid = static_cast<int>(want < 16384 ? want : 16384);
   const Codebook& cb = codebook(sc.fp4);
-  if (out_bf16)
-    hipLaunchKernelGGL(k_dequantize<true>, dim3(grid), dim3(256), 0, s, packed, n, sc, out, cb);
-  else
-    hipLaunchKernelGGL(k_dequantize<false>, dim3(grid), dim3(256), 0, s, packed, n, sc, out, cb);
+  const dim3 gd(static_cast<unsigned>(grid)), bd(256);
+#define NF4_DEQ(B, D, F) hipLaunchKernelGGL((k_dequantize<B, D, F>), gd, bd, 0, s, packed, n, sc, out, cb)
+  if (out_bf16) {
+    if (sc.absmax) NF4_DEQ(true, false, false); else if (sc.f8) NF4_DEQ(true, true, true); else NF4_DEQ(true, true, false);
+  } else {
+    if (sc.absmax) NF4_DEQ(false, false, false); else if (sc.f8) NF4_DEQ(false, true, true); else NF4_DEQ(false, true, false);
+  }
+#undef NF4_DEQ
   return hipGetLastError();
 }
 

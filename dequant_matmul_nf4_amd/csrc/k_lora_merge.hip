@@ -24,7 +24,7 @@
 // float64 sums; the workgroup's kRows rows of B sit in LDS and are read as
 // broadcasts.  The work is float64 arithmetic (r multiply-adds per output
 // value) next to 0.52 bytes read and 2 bytes written per value.
-#include "nf4_device.h"
+#include "scale_forms.h"
 
 namespace nf4i {
 namespace {
@@ -53,7 +53,7 @@ __device__ __forceinline__ uint32_t to_16(double v, bool f16) {
   return f32_to_bf16(f);                                                   // nearest even
 }
 
-template <bool kF16Out>
+template <bool kF16Out, bool kDQ, bool kF8>
 __global__ __launch_bounds__(kMergeThreads) void k_lora_merge(const uint8_t* __restrict__ packed, int64_t rows,
                                                               int64_t cols, Scales sc,
                                                               const uint16_t* __restrict__ la,
@@ -99,14 +99,14 @@ __global__ __launch_bounds__(kMergeThreads) void k_lora_merge(const uint8_t* __r
     }
   }
 
-  const float mean = sc.absmax ? 0.0f : *sc.mean;
+  const float mean = kDQ ? *sc.mean : 0.0f;
   const double s = static_cast<double>(scale);
 #pragma unroll
   for (int i = 0; i < kRows; ++i) {
     if (i >= nr) break;
     const int64_t e0 = (n0 + i) * cols + k0;  // first of the 8 elements; e0 % 8 == 0
     const uint32_t word = *reinterpret_cast<const uint32_t*>(packed + e0 / 2);
-    const float ah = block_scale(sc, e0 >> 6, mean);
+    const float ah = block_scale_t<kDQ, kF8>(sc, e0 >> 6, mean);
     uint32_t h[8];
 #pragma unroll
     for (int c = 0; c < 8; ++c) {
@@ -131,12 +131,15 @@ hipError_t launch_lora_merge(const uint8_t* packed, int64_t rows, int64_t cols, 
   if (gx > (int64_t(1) << 24) || gy > 65535) return hipErrorInvalidValue;  // work-items fit 32 bits
   const dim3 grid(static_cast<unsigned>(gx), static_cast<unsigned>(gy));
   const Codebook& cb = codebook(sc.fp4);
-  if (out_f16)
-    hipLaunchKernelGGL(k_lora_merge<true>, grid, dim3(kMergeThreads), 0, s, packed, rows, cols, sc, lora_a, lora_b,
-                       r, scale, out, cb);
-  else
-    hipLaunchKernelGGL(k_lora_merge<false>, grid, dim3(kMergeThreads), 0, s, packed, rows, cols, sc, lora_a, lora_b,
-                       r, scale, out, cb);
+#define NF4_MERGE(H, D, F) \
+  hipLaunchKernelGGL((k_lora_merge<H, D, F>), grid, dim3(kMergeThreads), 0, s, packed, rows, cols, sc, lora_a, lora_b, \
+                     r, scale, out, cb)
+  if (out_f16) {
+    if (sc.absmax) NF4_MERGE(true, false, false); else if (sc.f8) NF4_MERGE(true, true, true); else NF4_MERGE(true, true, false);
+  } else {
+    if (sc.absmax) NF4_MERGE(false, false, false); else if (sc.f8) NF4_MERGE(false, true, true); else NF4_MERGE(false, true, false);
+  }
+#undef NF4_MERGE
   return hipGetLastError();
 }
 
