@@ -15,9 +15,12 @@ from dataclasses import dataclass
 from typing import Optional
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libnf4.so")
+# NF4_LIBRARY selects another build of the same library (the sanitizer build
+# of the host-only tests); by default the in-tree libnf4.so is loaded.
+LIB_PATH = os.environ.get("NF4_LIBRARY") or os.path.join(_HERE, "libnf4.so")
 
-NF4_OK, NF4_ERR_NULL, NF4_ERR_SIZE, NF4_ERR_BLOCKSIZE, NF4_ERR_ALIGN, NF4_ERR_DTYPE, NF4_ERR_WORKSPACE, NF4_ERR_DEVICE = range(8)
+(NF4_OK, NF4_ERR_NULL, NF4_ERR_SIZE, NF4_ERR_BLOCKSIZE, NF4_ERR_ALIGN, NF4_ERR_DTYPE, NF4_ERR_WORKSPACE, NF4_ERR_DEVICE,
+ NF4_ERR_INTERNAL) = range(9)
 NF4_F32, NF4_BF16, NF4_F16 = 0, 1, 2
 NF4_DQ_INT8, NF4_DQ_FP8 = 0, 1
 NF4_QT_NF4, NF4_QT_FP4 = 0, 1
@@ -145,6 +148,19 @@ def _stream(stream=None) -> int:
     return int(s.cuda_stream)
 
 
+def _alloc_on(stream, *shape_dtype_device):
+    """torch.empty(shape, dtype, device) for a tensor the library writes on
+    `stream`.  When that is not the current stream, the tensor is recorded on
+    it, so the caching allocator does not hand its memory to another
+    allocation before the work queued on `stream` has finished."""
+    torch = _torch()
+    shape, dtype, device = shape_dtype_device
+    t = torch.empty(shape, dtype=dtype, device=device)
+    if stream is not None and stream != torch.cuda.current_stream(t.device):
+        t.record_stream(stream)
+    return t
+
+
 def _ptr(t) -> Optional[int]:
     return None if t is None else int(t.data_ptr())
 
@@ -166,6 +182,12 @@ def _need_cuda(*ts):
             raise ValueError("tensors must be contiguous device tensors")
 
 
+def _same_device(dev, *ts):
+    for t in ts:
+        if t is not None and t.device != dev:
+            raise ValueError(f"tensor on {t.device}, expected {dev}")
+
+
 @dataclass
 class NF4Weight:
     """A quantized weight W[rows][cols]: packed codes plus one scale form."""
@@ -183,7 +205,45 @@ class NF4Weight:
     def double_quant(self) -> bool:
         return self.absmax is None
 
+    def check(self) -> None:
+        """Host-side check of the buffers against rows and cols: the C ABI
+        takes bare pointers, so a buffer shorter than the shape implies would
+        be read past its end on the device.  Raises ValueError or TypeError."""
+        torch = _torch()
+        if int(self.rows) < 1 or int(self.cols) < 1:
+            raise ValueError(f"bad shape {self.rows} x {self.cols}")
+        n = int(self.rows) * int(self.cols)
+        nb = -(-n // BLOCKSIZE)
+        need = [("packed", self.packed, (n + 1) // 2, (torch.uint8,))]
+        if self.absmax is not None:
+            need.append(("absmax", self.absmax, nb, (torch.float32,)))
+        else:
+            if self.qabsmax is None or self.absmax2 is None or self.mean is None:
+                raise ValueError("without absmax, qabsmax, absmax2 and mean are all required")
+            need += [("qabsmax", self.qabsmax, nb, (torch.int8, torch.uint8)),
+                     ("absmax2", self.absmax2, -(-nb // BLOCKSIZE2), (torch.float32,)),
+                     ("mean", self.mean, 1, (torch.float32,))]
+        dev = None
+        for name, t, count, dtypes in need:
+            if t.dtype not in dtypes:
+                raise TypeError(f"{name} has dtype {t.dtype}, expected one of {dtypes}")
+            if t.numel() < count:
+                raise ValueError(f"{name} holds {t.numel()} elements; a {self.rows} x {self.cols} weight needs {count}")
+            if not t.is_contiguous():
+                raise ValueError(f"{name} must be contiguous")
+            if dev is None:
+                dev = t.device
+            elif t.device != dev:
+                raise ValueError(f"{name} is on {t.device}, the packed codes on {dev}")
+        if dev is None or dev.type != "cuda":
+            raise ValueError("the weight's buffers must be device tensors")
+
+    @property
+    def device(self):
+        return self.packed.device
+
     def c_struct(self) -> nf4_weight:
+        self.check()
         return nf4_weight(
             packed=_ptr(self.packed), rows=self.rows, cols=self.cols, blocksize=BLOCKSIZE,
             absmax=_ptr(self.absmax), qabsmax=_ptr(self.qabsmax), absmax2=_ptr(self.absmax2),
@@ -198,10 +258,13 @@ def nf4_quantize(x, packed=None, absmax=None, stream=None, fp4=False):
     _need_cuda(x)
     n = x.numel()
     if packed is None:
-        packed = torch.empty((n + 1) // 2, dtype=torch.uint8, device=x.device)
+        packed = _alloc_on(stream, ((n + 1) // 2,), torch.uint8, x.device)
     if absmax is None:
-        absmax = torch.empty((n + 63) // 64, dtype=torch.float32, device=x.device)
+        absmax = _alloc_on(stream, ((n + 63) // 64,), torch.float32, x.device)
     _need_cuda(packed, absmax)
+    _same_device(x.device, packed, absmax)
+    if packed.dtype != torch.uint8 or absmax.dtype != torch.float32:
+        raise TypeError("packed must be uint8 and absmax float32")
     if packed.numel() < (n + 1) // 2 or absmax.numel() < (n + 63) // 64:
         raise ValueError("output buffers too small")
     fn = lib().nf4_quantize_fp4 if fp4 else lib().nf4_quantize
@@ -219,13 +282,16 @@ def nf4_double_quant(absmax, qabsmax=None, absmax2=None, mean=None, workspace=No
     nb = absmax.numel()
     dev = absmax.device
     if qabsmax is None:
-        qabsmax = torch.empty(nb, dtype=torch.uint8 if fp8 else torch.int8, device=dev)
-    absmax2 = torch.empty((nb + 255) // 256, dtype=torch.float32, device=dev) if absmax2 is None else absmax2
-    mean = torch.empty(1, dtype=torch.float32, device=dev) if mean is None else mean
+        qabsmax = _alloc_on(stream, (nb,), torch.uint8 if fp8 else torch.int8, dev)
+    absmax2 = _alloc_on(stream, ((nb + 255) // 256,), torch.float32, dev) if absmax2 is None else absmax2
+    mean = _alloc_on(stream, (1,), torch.float32, dev) if mean is None else mean
     wsb = nf4_double_quant_workspace(nb)
     if workspace is None:
-        workspace = torch.empty(wsb, dtype=torch.uint8, device=dev)
+        workspace = _alloc_on(stream, (wsb,), torch.uint8, dev)
     _need_cuda(qabsmax, absmax2, mean, workspace)
+    _same_device(dev, qabsmax, absmax2, mean, workspace)
+    if absmax2.dtype != torch.float32 or mean.dtype != torch.float32 or qabsmax.element_size() != 1:
+        raise TypeError("qabsmax must hold bytes, absmax2 and mean float32")
     if qabsmax.numel() < nb or absmax2.numel() < (nb + 255) // 256 or mean.numel() < 1:
         raise ValueError("output buffers too small")
     fn = lib().nf4_double_quant_f8 if fp8 else lib().nf4_double_quant
@@ -255,12 +321,13 @@ def quantize_weight(w, double_quant: bool = True, stream=None, dq_type: str = "i
 
 def nf4_dequantize(w: NF4Weight, out=None, out_dtype=None, stream=None):
     torch = _torch()
+    cs = w.c_struct()
     if out is None:
-        out = torch.empty((w.rows, w.cols), dtype=out_dtype or torch.bfloat16, device=w.packed.device)
+        out = _alloc_on(stream, (w.rows, w.cols), out_dtype or torch.bfloat16, w.device)
     _need_cuda(out)
+    _same_device(w.device, out)
     if out.numel() != w.rows * w.cols:
         raise ValueError("out has the wrong size")
-    cs = w.c_struct()
     _check(lib().nf4_dequantize(ctypes.byref(cs), _ptr(out), _dtype_code(out), _stream(stream)))
     return out
 
@@ -273,12 +340,13 @@ def nf4_gemv(w: NF4Weight, x, y=None, y_dtype=None, stream=None):
     if x2.dtype != torch.bfloat16:
         raise TypeError("x must be bf16")
     m = x2.shape[0]
+    cs = w.c_struct()
     if y is None:
-        y = torch.empty((m, w.rows), dtype=y_dtype or torch.bfloat16, device=x.device)
+        y = _alloc_on(stream, (m, w.rows), y_dtype or torch.bfloat16, x.device)
     _need_cuda(y)
+    _same_device(w.device, x2, y)
     if y.numel() != m * w.rows:
         raise ValueError("y has the wrong size")
-    cs = w.c_struct()
     _check(lib().nf4_gemv(ctypes.byref(cs), _ptr(x2), m, _ptr(y), _dtype_code(y), _stream(stream)))
     return y
 
@@ -291,8 +359,9 @@ def nf4_gemm(w: NF4Weight, x, y=None, lora_a=None, lora_b=None, lora_scale: floa
     _need_cuda(x2, lora_a, lora_b)
     m = x2.shape[0]
     r = 0 if lora_a is None else lora_a.shape[0]
+    cs = w.c_struct()
     if y is None:
-        y = torch.empty((m, w.rows), dtype=torch.bfloat16, device=x.device)
+        y = _alloc_on(stream, (m, w.rows), torch.bfloat16, x.device)
     _need_cuda(y)
     for t in (x2, y, lora_a, lora_b):
         if t is not None and t.dtype != torch.bfloat16:
@@ -303,9 +372,10 @@ def nf4_gemm(w: NF4Weight, x, y=None, lora_a=None, lora_b=None, lora_scale: floa
         raise ValueError("LoRA shapes must be A [r, cols] and B [rows, r]")
     wsb = nf4_gemm_workspace(m, w.rows, r)
     if wsb and workspace is None:
-        workspace = torch.empty(wsb, dtype=torch.uint8, device=x.device)
+        workspace = _alloc_on(stream, (wsb,), torch.uint8, x.device)
+    _need_cuda(workspace)
+    _same_device(w.device, x2, y, lora_a, lora_b, workspace)
     wsn = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    cs = w.c_struct()
     _check(lib().nf4_gemm(ctypes.byref(cs), _ptr(x2), m, _ptr(y), _ptr(lora_a), _ptr(lora_b), r,
                           float(lora_scale), _ptr(workspace), wsn, _stream(stream)))
     return y
@@ -319,8 +389,9 @@ def nf4_gemm_dx(w: NF4Weight, dy, dx=None, lora_a=None, lora_b=None, lora_scale:
     _need_cuda(dy2, lora_a, lora_b)
     m = dy2.shape[0]
     r = 0 if lora_a is None else lora_a.shape[0]
+    cs = w.c_struct()
     if dx is None:
-        dx = torch.empty((m, w.cols), dtype=torch.bfloat16, device=dy.device)
+        dx = _alloc_on(stream, (m, w.cols), torch.bfloat16, dy.device)
     _need_cuda(dx)
     for t in (dy2, dx, lora_a, lora_b):
         if t is not None and t.dtype != torch.bfloat16:
@@ -331,9 +402,10 @@ def nf4_gemm_dx(w: NF4Weight, dy, dx=None, lora_a=None, lora_b=None, lora_scale:
         raise ValueError("LoRA shapes must be A [r, cols] and B [rows, r]")
     wsb = nf4_gemm_dx_workspace(m, w.rows, r)
     if wsb and workspace is None:
-        workspace = torch.empty(wsb, dtype=torch.uint8, device=dy.device)
+        workspace = _alloc_on(stream, (wsb,), torch.uint8, dy.device)
+    _need_cuda(workspace)
+    _same_device(w.device, dy2, dx, lora_a, lora_b, workspace)
     wsn = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    cs = w.c_struct()
     _check(lib().nf4_gemm_dx(ctypes.byref(cs), _ptr(dy2), m, _ptr(dx), _ptr(lora_a), _ptr(lora_b), r,
                              float(lora_scale), _ptr(workspace), wsn, _stream(stream)))
     return dx
@@ -356,9 +428,9 @@ def nf4_lora_grads(x, dy, lora_a, lora_b, lora_scale: float, da=None, db=None, w
         if t.dtype != torch.bfloat16:
             raise TypeError("x, dy, lora_a and lora_b must be bf16")
     if da is None and "da" in want:
-        da = torch.empty((r, cols), dtype=torch.float32, device=x.device)
+        da = _alloc_on(stream, (r, cols), torch.float32, x.device)
     if db is None and "db" in want:
-        db = torch.empty((rows, r), dtype=torch.float32, device=x.device)
+        db = _alloc_on(stream, (rows, r), torch.float32, x.device)
     for t, shape in ((da, (r, cols)), (db, (rows, r))):
         if t is not None:
             _need_cuda(t)
@@ -366,7 +438,9 @@ def nf4_lora_grads(x, dy, lora_a, lora_b, lora_scale: float, da=None, db=None, w
                 raise ValueError("da and db must be float32 [r, cols] and [rows, r]")
     wsb = nf4_lora_grads_workspace(m, rows, cols, r)
     if workspace is None:
-        workspace = torch.empty(max(wsb, 1), dtype=torch.uint8, device=x.device)
+        workspace = _alloc_on(stream, (max(wsb, 1),), torch.uint8, x.device)
+    _need_cuda(workspace)
+    _same_device(x.device, dy2, lora_a, lora_b, da, db, workspace)
     wsn = workspace.numel() * workspace.element_size()
     _check(lib().nf4_lora_grads(_ptr(x2), _ptr(dy2), m, rows, cols, _ptr(lora_a), _ptr(lora_b), r,
                                 float(lora_scale), _ptr(da), _ptr(db), _ptr(workspace), wsn, _stream(stream)))
@@ -382,12 +456,13 @@ def nf4_lora_merge(w: NF4Weight, lora_a, lora_b, lora_scale: float, out=None, ou
         raise TypeError("lora_a and lora_b must be bf16")
     if tuple(lora_a.shape) != (r, w.cols) or tuple(lora_b.shape) != (w.rows, r):
         raise ValueError("LoRA shapes must be A [r, cols] and B [rows, r]")
+    cs = w.c_struct()
     if out is None:
-        out = torch.empty((w.rows, w.cols), dtype=out_dtype or torch.bfloat16, device=lora_a.device)
+        out = _alloc_on(stream, (w.rows, w.cols), out_dtype or torch.bfloat16, lora_a.device)
     _need_cuda(out)
+    _same_device(w.device, lora_a, lora_b, out)
     if out.numel() != w.rows * w.cols:
         raise ValueError("out has the wrong size")
-    cs = w.c_struct()
     _check(lib().nf4_lora_merge(ctypes.byref(cs), _ptr(lora_a), _ptr(lora_b), r, float(lora_scale), _ptr(out),
                                 _dtype_code(out), _stream(stream)))
     return out

@@ -136,8 +136,12 @@ int quantize(const void* x, int x_dtype, int64_t n, int32_t blocksize, uint8_t* 
   if (blocksize != NF4_BLOCKSIZE) return fail(NF4_ERR_BLOCKSIZE, "%s: blocksize %d unsupported (only 64)", who, (int)blocksize);
   if (!aligned(x, 16) || !aligned(packed, 16)) return fail(NF4_ERR_ALIGN, "%s: x and packed must be 16-byte aligned", who);
   if (!aligned(absmax, 4)) return fail(NF4_ERR_ALIGN, "%s: absmax must be 4-byte aligned", who);
+  const char* lut_err = "";
+  const nf4i::QuantLut* lut = nf4i::quant_lut(fp4, &lut_err);
+  if (!lut) return fail(NF4_ERR_INTERNAL, "%s: %s", who, lut_err);
   if (int rc = check_device()) return rc;
-  return launched(nf4i::launch_quantize(x, x_dtype == NF4_BF16, n, packed, absmax, fp4, as_stream(stream)), who);
+  return launched(nf4i::launch_quantize(x, x_dtype == NF4_BF16, n, packed, absmax, *lut, fp4, as_stream(stream)),
+                  who);
 }
 
 }  // namespace

@@ -21,7 +21,6 @@
 #include <cfloat>
 #include <cmath>
 #include <cstdio>
-#include <cstdlib>
 #include <cstring>
 
 #include "nf4_internal.h"
@@ -83,34 +82,51 @@ float from_bits(uint32_t u) {
   return f;
 }
 
+}  // namespace
+
 // Builds the bucket table and checks, for every one of the 2048 buckets, that
 // the bucket rule reproduces the threshold count at both ends of the bucket
-// (the count is monotone, so that covers every value inside).
-QuantLut build_lut(const Codebook& cb) {
+// (the count is monotone, so that covers every value inside).  A failed check
+// is reported through `err` (and the function returns false); the table is
+// then unusable and the quantizer refuses to run.
+bool build_lut(const Codebook& cb, QuantLut* out, char* err, size_t err_len) {
   QuantLut lut{};
   for (int b = 0; b < kLutBuckets; ++b) {
     const uint32_t sign = static_cast<uint32_t>(b) >> 10;
     const uint32_t lo_mag = static_cast<uint32_t>(b & 1023) << 21, hi_mag = lo_mag | 0x1FFFFFu;
-    if ((lo_mag >> 23) > 127 || (lo_mag >> 23) == 127 && lo_mag != 0x3F800000u) continue;  // |v| > 1 never occurs
+    if ((lo_mag >> 23) > 127 || ((lo_mag >> 23) == 127 && lo_mag != 0x3F800000u)) continue;  // |v| > 1 never occurs
     const uint32_t hi_bits = std::min(hi_mag, 0x3F800000u);
     const float lo_v = from_bits((sign << 31) | (sign ? hi_bits : lo_mag));  // smallest value in bucket
     const float hi_v = from_bits((sign << 31) | (sign ? lo_mag : hi_bits));  // largest value in bucket
     const uint32_t c_lo = count_code(lo_v, cb), c_hi = count_code(hi_v, cb);
     const int e = static_cast<int>(lo_mag >> 23);
-    if (c_hi > c_lo + 1) { std::fprintf(stderr, "nf4: bucket %d holds two thresholds\n", b); std::abort(); }
+    if (c_hi > c_lo + 1) {
+      std::snprintf(err, err_len, "quantizer table self-check: bucket %d holds two decision thresholds", b);
+      return false;
+    }
     if (e < kLutFirstExp) {
-      if (c_lo != 7 || c_hi != 7) { std::fprintf(stderr, "nf4: bucket %d below 2^-5 is not code 7\n", b); std::abort(); }
+      if (c_lo != 7 || c_hi != 7) {
+        std::snprintf(err, err_len, "quantizer table self-check: bucket %d below 2^-5 is not the zero level", b);
+        return false;
+      }
       continue;
     }
     int t = -1;
     for (int k = 0; k < kLutSpecial; ++k)
       if (lut_special_index(k) == b) t = k;
-    if (t < 0) { std::fprintf(stderr, "nf4: bucket %d missing from the table\n", b); std::abort(); }
+    if (t < 0) {
+      std::snprintf(err, err_len, "quantizer table self-check: bucket %d is missing from the table", b);
+      return false;
+    }
     lut.base[t] = c_lo;
     lut.thr[t] = (c_hi == c_lo) ? INFINITY : cb.thresh[c_lo];
   }
-  return lut;
+  *out = lut;
+  if (err_len) err[0] = '\0';
+  return true;
 }
+
+namespace {
 
 // FP4 (the E2M1 reading): a 4-bit pattern is a sign bit, two exponent bits
 // with bias 1 and one mantissa bit, exponent field 0 being subnormal (m / 2);
@@ -150,10 +166,31 @@ const Codebook& codebook(int fp4) {
   return fp4 ? f4 : nf4;
 }
 
-const QuantLut& quant_lut(int fp4) {
-  static const QuantLut nf4 = build_lut(codebook(0));
-  static const QuantLut f4 = build_lut(build_fp4_ascending());
-  return fp4 ? f4 : nf4;
+namespace {
+
+struct LutState {
+  QuantLut lut;
+  bool ok;
+  char err[160];
+};
+
+LutState make_lut_state(const Codebook& cb) {
+  LutState st{};
+  st.ok = build_lut(cb, &st.lut, st.err, sizeof st.err);
+  return st;
+}
+
+}  // namespace
+
+const QuantLut* quant_lut(int fp4, const char** err) {
+  static const LutState nf4 = make_lut_state(codebook(0));
+  static const LutState f4 = make_lut_state(build_fp4_ascending());
+  const LutState& st = fp4 ? f4 : nf4;
+  if (!st.ok) {
+    if (err) *err = st.err;
+    return nullptr;
+  }
+  return &st.lut;
 }
 
 }  // namespace nf4i

@@ -156,15 +156,14 @@ __global__ __launch_bounds__(256) void k_quantize(const void* __restrict__ x, in
 
 }  // namespace
 
-hipError_t launch_quantize(const void* x, int x_bf16, int64_t n, uint8_t* packed, float* absmax, int fp4,
-                           hipStream_t s) {
+hipError_t launch_quantize(const void* x, int x_bf16, int64_t n, uint8_t* packed, float* absmax,
+                           const QuantLut& tab, int fp4, hipStream_t s) {
   // two segments per lane and one pass per lane: a loop would make the next
   // loads wait for the previous stores (their registers are reused)
   const int64_t nseg = (n >> 6) * 4;
   const int64_t want = (nseg + 511) / 512;
   if (want > 0x7FFFFFFF) return hipErrorInvalidValue;
   const int grid = static_cast<int>(want < 1 ? 1 : want);
-  const QuantLut& tab = quant_lut(fp4);
   if (fp4) {
     if (x_bf16) hipLaunchKernelGGL((k_quantize<true, true>), dim3(grid), dim3(256), 0, s, x, n, packed, absmax, tab);
     else hipLaunchKernelGGL((k_quantize<false, true>), dim3(grid), dim3(256), 0, s, x, n, packed, absmax, tab);

@@ -34,8 +34,14 @@ struct QuantLut {
 };
 // The quantizer's bucket table.  For FP4 it is built on the 15 producible
 // levels in ascending order (zero at index 7, like NF4); the kernel maps the
-// ascending index c to the E2M1 pattern (c >= 7 ? c - 7 : 15 - c).
-const QuantLut& quant_lut(int fp4 = 0);
+// ascending index c to the E2M1 pattern (c >= 7 ? c - 7 : 15 - c).  Built and
+// self-checked once; returns nullptr (and the reason in *err) if the check
+// failed, in which case nothing may be quantized.
+const QuantLut* quant_lut(int fp4 = 0, const char** err = nullptr);
+// The construction behind quant_lut for any ascending code book: false (with
+// the reason in err) when some bucket holds two decision thresholds, a bucket
+// below 2^-5 is not the zero level, or a needed bucket has no table slot.
+bool build_lut(const Codebook& cb, QuantLut* out, char* err, size_t err_len);
 
 __host__ __device__ inline int lut_special_index(int t) {
   const int sign = t / 24, e = kLutFirstExp + (t % 24) / 4, m2 = t % 4;
@@ -90,7 +96,7 @@ constexpr int kDqMaxGroups = 256;
 constexpr size_t kDqWorkspaceBytes = kDqMaxGroups * kDqDigits * sizeof(unsigned long long);
 
 hipError_t launch_quantize(const void* x, int x_bf16, int64_t n, uint8_t* packed,
-                           float* absmax, int fp4, hipStream_t s);
+                           float* absmax, const QuantLut& tab, int fp4, hipStream_t s);
 hipError_t launch_double_quant(const float* absmax, int64_t nb, int8_t* q, float* absmax2,
                                float* mean, unsigned long long* ws, int f8, hipStream_t s);
 hipError_t launch_dequantize(const uint8_t* packed, int64_t n, Scales sc, void* out,

@@ -49,7 +49,8 @@ typedef enum nf4_status {
   NF4_ERR_ALIGN = 4,      /* a pointer is not aligned as documented               */
   NF4_ERR_DTYPE = 5,      /* unknown nf4_dtype, or a dtype the call does not take */
   NF4_ERR_WORKSPACE = 6,  /* workspace missing or smaller than the *_workspace()  */
-  NF4_ERR_DEVICE = 7      /* the device is not gfx950, or a HIP call failed       */
+  NF4_ERR_DEVICE = 7,     /* the device is not gfx950, or a HIP call failed       */
+  NF4_ERR_INTERNAL = 8    /* a self-check of the library's own host tables failed */
 } nf4_status;
 
 typedef enum nf4_dtype { NF4_F32 = 0, NF4_BF16 = 1, NF4_F16 = 2 } nf4_dtype;

@@ -198,3 +198,89 @@ def test_fp4_codebook_bit_identical_to_oracle():
     import oracle
     got = np.array(nf4.nf4_codebook_fp4(), dtype=np.float32)
     assert np.array_equal(got.view(np.uint32), oracle.fp4_codebook().view(np.uint32))
+
+
+# ------------------------------------------------- binding-side weight checks
+
+def _cpu_weight(rows, cols, dq=True, short=None, dtype_swap=None):
+    import torch
+    n = rows * cols
+    nb = -(-n // 64)
+    parts = dict(packed=torch.zeros((n + 1) // 2, dtype=torch.uint8))
+    if dq:
+        parts.update(qabsmax=torch.zeros(nb, dtype=torch.int8), absmax2=torch.zeros(-(-nb // 256), dtype=torch.float32),
+                     mean=torch.zeros(1, dtype=torch.float32))
+    else:
+        parts.update(absmax=torch.zeros(nb, dtype=torch.float32))
+    if short:
+        parts[short] = parts[short][:-1]
+    if dtype_swap:
+        name, dt = dtype_swap
+        parts[name] = parts[name].to(dt)
+    return nf4.NF4Weight(rows=rows, cols=cols, **parts)
+
+
+@pytest.mark.parametrize("short", ["packed", "qabsmax", "absmax2", "mean"])
+def test_weight_descriptor_rejects_short_buffers(short):
+    """The C ABI takes bare pointers and cannot see sizes, so the binding
+    checks every buffer of a weight against its rows and cols before a call."""
+    w = _cpu_weight(300, 128, dq=True, short=short)
+    with pytest.raises(ValueError, match=short):
+        w.check()
+
+
+def test_weight_descriptor_rejects_short_plain_absmax_and_wrong_dtypes():
+    import torch
+    with pytest.raises(ValueError, match="absmax"):
+        _cpu_weight(33, 192, dq=False, short="absmax").check()
+    with pytest.raises(TypeError, match="absmax2"):
+        _cpu_weight(33, 192, dq=True, dtype_swap=("absmax2", torch.float64)).check()
+    with pytest.raises(TypeError, match="packed"):
+        _cpu_weight(33, 192, dq=True, dtype_swap=("packed", torch.int16)).check()
+    with pytest.raises(ValueError, match="required"):
+        nf4.NF4Weight(torch.zeros(64, dtype=torch.uint8), 1, 128, qabsmax=torch.zeros(2, dtype=torch.int8)).check()
+
+
+def test_weight_descriptor_rejects_host_tensors_and_mixed_devices():
+    """Buffers of the right sizes on the host are still refused (the library
+    takes device pointers only): nothing reaches the C ABI."""
+    w = _cpu_weight(64, 64, dq=True)
+    with pytest.raises(ValueError, match="device tensors"):
+        w.check()
+    with pytest.raises(ValueError, match="device tensors"):
+        nf4.nf4_gemv(w, __import__("torch").zeros((1, 64), dtype=__import__("torch").bfloat16))
+
+
+def _build_lut_fn(L):
+    out = subprocess.run(["nm", "-D", "--defined-only", nf4.LIB_PATH], capture_output=True, text=True, check=True).stdout
+    name = next(ln.split()[-1] for ln in out.splitlines() if "9build_lut" in ln)
+    f = getattr(L, name)
+    f.restype = ctypes.c_bool
+    f.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_char_p, ctypes.c_size_t]
+    return f
+
+
+def test_quantizer_table_self_check_reports_instead_of_aborting(L):
+    """The quantizer's bucket table is built and checked on the host at first
+    use.  A code book that breaks the table's assumption (two decision
+    thresholds inside one bucket) makes the check return false with a reason;
+    it no longer ends the caller's process.  The real code books pass."""
+    f = _build_lut_fn(L)
+    lut = ctypes.create_string_buffer(48 * 8)
+    err = ctypes.create_string_buffer(160)
+
+    def codebook_struct(levels):
+        levels = np.asarray(levels, dtype=np.float32)
+        mids = (levels[:-1].astype(np.float64) + levels[1:]) / 2  # thresholds between neighbours
+        thresh = np.concatenate([mids.astype(np.float32), [np.inf]]).astype(np.float32)
+        return np.concatenate([levels, thresh]).astype(np.float32)
+
+    good = codebook_struct(oracle.codebook())
+    assert f(good.ctypes.data, ctypes.addressof(lut), err, 160)
+    assert err.value == b""
+    lv = oracle.codebook().copy()
+    lv[12], lv[13] = np.float32(0.3), np.float32(0.3001)   # thresholds 0.30005 and ~0.37: same bucket [0.25, 0.3125)
+    lv[11] = np.float32(0.26)
+    bad = codebook_struct(lv)
+    assert not f(bad.ctypes.data, ctypes.addressof(lut), err, 160)
+    assert b"two decision thresholds" in err.value
