@@ -29,7 +29,7 @@ BLOCKSIZE, BLOCKSIZE2 = 64, 256
 EXPORTS = (
     "nf4_last_error", "nf4_codebook", "nf4_codebook_fp4", "nf4_quantize", "nf4_quantize_fp4", "nf4_double_quant_workspace",
     "nf4_double_quant", "nf4_e4m3_ratio", "nf4_double_quant_f8", "nf4_dequantize", "nf4_gemv", "nf4_gemm_workspace", "nf4_gemm", "nf4_gemm_dx_workspace",
-    "nf4_gemm_dx", "nf4_lora_grads_workspace", "nf4_lora_grads", "nf4_lora_merge",
+    "nf4_gemm_dx", "nf4_lora_grads_workspace", "nf4_lora_grads", "nf4_lora_merge", "nf4_double_quant_noalloc",
 )
 
 
@@ -71,6 +71,7 @@ def lib() -> ctypes.CDLL:
         "nf4_double_quant_workspace": (sz, [i64]),
         "nf4_double_quant": (ctypes.c_int, [vp, i64, i32, vp, vp, vp, vp, sz, vp]),
         "nf4_double_quant_f8": (ctypes.c_int, [vp, i64, i32, vp, vp, vp, vp, sz, vp]),
+        "nf4_double_quant_noalloc": (ctypes.c_int, [vp, i64, i32, vp, vp, vp, vp]),
         "nf4_e4m3_ratio": (ctypes.c_int, [ctypes.POINTER(ctypes.c_float)]),
         "nf4_dequantize": (ctypes.c_int, [wp, vp, ctypes.c_int, vp]),
         "nf4_gemv": (ctypes.c_int, [wp, vp, i64, vp, ctypes.c_int, vp]),
@@ -297,6 +298,25 @@ def nf4_double_quant(absmax, qabsmax=None, absmax2=None, mean=None, workspace=No
     fn = lib().nf4_double_quant_f8 if fp8 else lib().nf4_double_quant
     _check(fn(_ptr(absmax), nb, BLOCKSIZE2, _ptr(qabsmax), _ptr(absmax2), _ptr(mean),
               _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream)))
+    return qabsmax, absmax2, mean
+
+
+def nf4_double_quant_noalloc(absmax, qabsmax, absmax2, mean, stream=None):
+    """nf4_double_quant (int8 second level) through the entry point that
+    allocates nothing: the outputs are the caller's and the partial sums use
+    the library's static device scratch.  Returns (qabsmax, absmax2, mean)."""
+    torch = _torch()
+    _need_cuda(absmax, qabsmax, absmax2, mean)
+    _same_device(absmax.device, qabsmax, absmax2, mean)
+    if absmax.dtype != torch.float32 or absmax2.dtype != torch.float32 or mean.dtype != torch.float32:
+        raise TypeError("absmax, absmax2 and mean must be float32")
+    if qabsmax.dtype != torch.int8:
+        raise TypeError("qabsmax must be int8")
+    nb = absmax.numel()
+    if qabsmax.numel() < nb or absmax2.numel() < (nb + 255) // 256 or mean.numel() < 1:
+        raise ValueError("output buffers too small")
+    _check(lib().nf4_double_quant_noalloc(_ptr(absmax), nb, BLOCKSIZE2, _ptr(qabsmax), _ptr(absmax2), _ptr(mean),
+                                          _stream(stream)))
     return qabsmax, absmax2, mean
 
 

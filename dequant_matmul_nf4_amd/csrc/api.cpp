@@ -98,6 +98,7 @@ int check_weight(const nf4_weight* w, nf4i::Scales* sc, int64_t* n_out, const ch
 
 hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
 
+
 }  // namespace
 
 int nf4i::device_cus() { return t_cus; }
@@ -189,6 +190,29 @@ int nf4_double_quant(const float* absmax, int64_t nblocks, int32_t blocksize2, i
                      void* stream) {
   return double_quant(absmax, nblocks, blocksize2, qabsmax, absmax2, mean, workspace, workspace_bytes, stream, 0,
                       "nf4_double_quant");
+}
+
+int nf4_double_quant_noalloc(const float* absmax, int64_t nblocks, int32_t blocksize2, int8_t* qabsmax,
+                             float* absmax2, float* mean, void* stream) {
+  const char* who = "nf4_double_quant_noalloc";
+  if (!absmax || !qabsmax || !absmax2 || !mean)
+    return fail(NF4_ERR_NULL, "%s: absmax, qabsmax, absmax2 and mean are required", who);
+  if (nblocks < 1 || nblocks >= (int64_t(1) << 31))
+    return fail(NF4_ERR_SIZE, "%s: nblocks = %lld out of range 1..2^31-1", who, (long long)nblocks);
+  if (blocksize2 != NF4_BLOCKSIZE2)
+    return fail(NF4_ERR_BLOCKSIZE, "%s: blocksize2 %d unsupported (only 256)", who, (int)blocksize2);
+  if (nf4_double_quant_workspace(nblocks) > nf4i::kDqScratchBytes)
+    return fail(NF4_ERR_SIZE, "%s: %lld scales need %zu bytes of scratch, more than the %zu held", who,
+                (long long)nblocks, nf4_double_quant_workspace(nblocks), nf4i::kDqScratchBytes);
+  if (!aligned(absmax, 16) || !aligned(qabsmax, 16))
+    return fail(NF4_ERR_ALIGN, "%s: absmax and qabsmax must be 16-byte aligned", who);
+  if (!aligned(absmax2, 4) || !aligned(mean, 4))
+    return fail(NF4_ERR_ALIGN, "%s: absmax2 and mean must be 4-byte aligned", who);
+  if (int rc = check_device()) return rc;
+  unsigned long long* ws = nullptr;
+  if (hipError_t e = nf4i::dq_scratch(&ws); e != hipSuccess)
+    return fail(NF4_ERR_DEVICE, "%s: scratch address lookup failed: %s", who, hipGetErrorString(e));
+  return launched(nf4i::launch_double_quant(absmax, nblocks, qabsmax, absmax2, mean, ws, 0, as_stream(stream)), who);
 }
 
 int nf4_double_quant_f8(const float* absmax, int64_t nblocks, int32_t blocksize2, uint8_t* qabsmax,

@@ -17,10 +17,19 @@
 //
 // Kernels: k_dq_partial (digit sums per workgroup), k_dq_quant (the mean,
 // then one wave per group of 256 scales).
+#include <mutex>
+
 #include "nf4_device.h"
 
 namespace nf4i {
 namespace {
+
+// Partial digit rows of the allocation-free entry point: one call's worth
+// (kDqMaxGroups rows of kDqDigits u64, 24 KiB) per device, alive until the
+// process ends.  Host code never passes this name to a kernel; it passes the
+// address dq_scratch() obtained for the current device.
+static __device__ __align__(256) unsigned long long scratch[kDqMaxGroups * kDqDigits];
+static_assert(sizeof(scratch) >= kDqWorkspaceBytes, "scratch holds the partial rows of any call");
 
 __device__ __forceinline__ void scale_to_digits(float a, int* d, uint32_t* lo, uint32_t* hi) {
   const uint32_t u = __float_as_uint(a) & 0x7FFFFFFFu;
@@ -286,6 +295,27 @@ __global__ __launch_bounds__(256) void k_dq_quant(const float* __restrict__ absm
 }
 
 }  // namespace
+
+hipError_t dq_scratch(unsigned long long** out) {
+  // device address of `scratch`, looked up once per device with that device
+  // current (each device holds its own copy of the array)
+  static std::mutex mu;
+  static void* addr[64];
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lk(mu);
+  if (!addr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (!p) return hipErrorInvalidSymbol;
+    addr[dev] = p;
+  }
+  *out = static_cast<unsigned long long*>(addr[dev]);
+  return hipSuccess;
+}
 
 hipError_t launch_double_quant(const float* absmax, int64_t nb, int8_t* q, float* absmax2,
                                float* mean, unsigned long long* ws, int f8, hipStream_t s) {

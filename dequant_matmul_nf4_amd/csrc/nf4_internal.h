@@ -99,6 +99,11 @@ hipError_t launch_quantize(const void* x, int x_bf16, int64_t n, uint8_t* packed
                            float* absmax, const QuantLut& tab, int fp4, hipStream_t s);
 hipError_t launch_double_quant(const float* absmax, int64_t nb, int8_t* q, float* absmax2,
                                float* mean, unsigned long long* ws, int f8, hipStream_t s);
+// Device address of the double quantization's static scratch on the current
+// device (kDqWorkspaceBytes or more, 256-byte aligned), for callers that
+// cannot allocate.  Looked up once per device.
+constexpr size_t kDqScratchBytes = kDqWorkspaceBytes;
+hipError_t dq_scratch(unsigned long long** out);
 hipError_t launch_dequantize(const uint8_t* packed, int64_t n, Scales sc, void* out,
                              int out_bf16, hipStream_t s);
 hipError_t launch_gemv(const uint8_t* packed, int64_t rows, int64_t cols, Scales sc,

@@ -135,6 +135,21 @@ int nf4_double_quant(const float* absmax, int64_t nblocks, int32_t blocksize2,
                      int8_t* qabsmax, float* absmax2, float* mean,
                      void* workspace, size_t workspace_bytes, void* stream);
 
+/* nf4_double_quant for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, hosts that forbid
+ * allocation): the same arguments, results and errors without the
+ * workspace.  The partial sums live in a static 24 KiB device array that the
+ * library holds on every device it runs on until the process ends; its
+ * address is looked up on the first call on a device.  Allocates nothing.
+ * nblocks is limited to 1 <= nblocks < 2^31 as for nf4_double_quant (the
+ * scratch needed does not grow with nblocks); a size outside that range is
+ * rejected with NF4_ERR_SIZE.  Every call on one device shares that array:
+ * calls that may overlap on one device (different streams with no ordering
+ * between them) race and must not be made; calls ordered on one stream are
+ * fine.  The array's contents on entry do not matter. */
+int nf4_double_quant_noalloc(const float* absmax, int64_t nblocks, int32_t blocksize2,
+                             int8_t* qabsmax, float* absmax2, float* mean, void* stream);
+
 /* The float8 reading of the second level -- tutorial page "How NF4 Works":
  * the scales go from float32 to float8.  Same arguments and mean as
  * nf4_double_quant; qabsmax receives E4M3 codes (Open Compute Project 8-bit

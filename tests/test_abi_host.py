@@ -105,6 +105,12 @@ CASES = [
     ("dq workspace small", lambda L: L.nf4_double_quant(A, 10, 256, A, A2, A2, A, 8, None), nf4.NF4_ERR_WORKSPACE),
     ("dq workspace null", lambda L: L.nf4_double_quant(A, 10, 256, A, A2, A2, None, WS, None), nf4.NF4_ERR_WORKSPACE),
     ("dq misaligned q", lambda L: L.nf4_double_quant(A, 10, 256, A + 1, A2, A2, A, WS, None), nf4.NF4_ERR_ALIGN),
+    ("dq noalloc null", lambda L: L.nf4_double_quant_noalloc(A, 10, 256, None, A2, A2, None), nf4.NF4_ERR_NULL),
+    ("dq noalloc nblocks 0", lambda L: L.nf4_double_quant_noalloc(A, 0, 256, A, A2, A2, None), nf4.NF4_ERR_SIZE),
+    ("dq noalloc nblocks 2^31", lambda L: L.nf4_double_quant_noalloc(A, 1 << 31, 256, A, A2, A2, None), nf4.NF4_ERR_SIZE),
+    ("dq noalloc blocksize2", lambda L: L.nf4_double_quant_noalloc(A, 10, 128, A, A2, A2, None), nf4.NF4_ERR_BLOCKSIZE),
+    ("dq noalloc misaligned absmax", lambda L: L.nf4_double_quant_noalloc(A + 4, 10, 256, A, A2, A2, None), nf4.NF4_ERR_ALIGN),
+    ("dq noalloc misaligned mean", lambda L: L.nf4_double_quant_noalloc(A, 10, 256, A, A2, A2 + 2, None), nf4.NF4_ERR_ALIGN),
     ("dq f8 null", lambda L: L.nf4_double_quant_f8(A, 10, 256, None, A2, A2, A, WS, None), nf4.NF4_ERR_NULL),
     ("dq f8 blocksize2", lambda L: L.nf4_double_quant_f8(A, 10, 128, A, A2, A2, A, WS, None), nf4.NF4_ERR_BLOCKSIZE),
     ("dq f8 workspace small", lambda L: L.nf4_double_quant_f8(A, 10, 256, A, A2, A2, A, 8, None), nf4.NF4_ERR_WORKSPACE),
