@@ -3,8 +3,9 @@ layer's seven weights are drawn on the device exactly as the bench's stack
 leg draws them (synthetic.c5_weight_device).  Quantization and double
 quantization are checked against the oracle bit for bit -- every block's
 absmax, every int8 code, group scale and the mean, and the packed codes of
-sampled blocks (each block quantizes on its own) -- and layer 0's decode GEMV
-on sampled rows within the matmul tolerance (bitsandbytes tool page, "How it
+sampled blocks (each block quantizes on its own), every packed byte of
+layer 0's 8192 x 8192 q projection -- and layer 0's decode GEMV on sampled
+rows within the matmul tolerance (bitsandbytes tool page, "How it
 works" and "Double quantization")."""
 
 from __future__ import annotations
@@ -75,3 +76,25 @@ def test_c5_layer0_gemv_sampled_rows():
         e = oracle.rel_frobenius(got, ref)
         say(f"  rel err {e:.2e}")
         assert e <= MATMUL_RTOL
+
+
+def test_c5_layer0_q_every_packed_byte():
+    """Every packed byte of one full 70B-shaped matrix (layer 0's q
+    projection, 8192 x 8192, 32 MiB of codes) against the oracle's
+    quantization of the whole matrix, with its absmax and double-quantized
+    scales."""
+    torch = need_gpu()
+    say("c5 layer 0 q: every packed byte")
+    w = syn.c5_weight_device(0, "q")
+    W = nf4.quantize_weight(w, double_quant=True)
+    _, absmax = nf4.nf4_quantize(w)
+    torch.cuda.synchronize()
+    wf = _host_f32(w)
+    del w
+    p_or, a_or = oracle.quantize(wf)
+    assert np.array_equal(W.packed.cpu().numpy(), p_or)
+    assert np.array_equal(absmax.cpu().numpy().view(np.uint32), a_or.view(np.uint32))
+    q_or, s2_or, mean_or = oracle.double_quant(a_or)
+    assert np.array_equal(W.qabsmax.cpu().numpy(), q_or)
+    assert np.array_equal(W.absmax2.cpu().numpy().view(np.uint32), s2_or.view(np.uint32))
+    assert np.float32(W.mean.item()).view(np.uint32) == np.float32(mean_or).view(np.uint32)

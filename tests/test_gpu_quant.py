@@ -289,3 +289,70 @@ def test_double_quant_large_scale_arrays_bit_exact(kind):
     assert f32_bits(mean)[0] == np.float32(mean_o).view(np.uint32)
     assert np.array_equal(q.cpu().numpy(), q_o)
     assert np.array_equal(f32_bits(s2), s2_o.view(np.uint32))
+
+
+def _threshold_inputs(levels_ascending: np.ndarray, seed: int) -> np.ndarray:
+    """Blocks whose absmax a has a random odd significand (so 1/a is not
+    exact and the kernel's reciprocal-based division has a residual to
+    correct) and whose other 63 values sit where fl32(x / a) lands within a
+    few ulps of a decision threshold (the midpoint of two neighbouring
+    levels): x = fl32(a * t) for t at -4 .. +4 ulps of each midpoint, and the
+    float32 neighbours of each such x.  The exponents of a span the range the
+    kernel divides by reciprocal (2^-98 <= a < 2^126) and both sides beyond
+    it, where it divides per value, including subnormal a.  Half of the blocks
+    hold -a as their largest magnitude."""
+    rng = np.random.default_rng(seed)
+    lv = levels_ascending.astype(np.float64)
+    mids = (lv[:-1] + lv[1:]) / 2
+    t = []
+    for m in mids:
+        c = np.float32(m)
+        for k in range(-4, 5):
+            v = c
+            for _ in range(abs(k)):
+                v = np.nextafter(v, np.float32(np.inf) if k > 0 else np.float32(-np.inf))
+            t.append(v)
+    t = np.array(t, dtype=np.float32)
+    exps = [-126, -120, -99, -98, -97, -60, -10, -1, 0, 1, 10, 60, 100, 124, 125, 126, 127]
+    avals = []
+    for e in exps:
+        for _ in range(6):
+            sig = 1.0 + (2 * int(rng.integers(0, 1 << 22)) + 1) * 2.0 ** -23
+            avals.append(np.float32(np.ldexp(sig, e)))
+    for e in (-130, -140, -148):  # subnormal a
+        avals.append(np.float32(np.ldexp(1.0 + (2 * int(rng.integers(0, 1 << 20)) + 1) * 2.0 ** -21, e)))
+    blocks = []
+    for i, a in enumerate(avals):
+        x = (np.float32(a) * t).astype(np.float32)
+        vals = np.concatenate([x, np.nextafter(x, np.float32(np.inf)), np.nextafter(x, np.float32(-np.inf))])
+        vals = vals[np.abs(vals) <= a]
+        for j in range(0, vals.size, 63):
+            body = np.zeros(63, dtype=np.float32)
+            part = vals[j:j + 63]
+            body[:part.size] = part
+            head = np.float32(-a) if (i + j // 63) % 2 else np.float32(a)
+            blocks.append(np.concatenate([[head], body]).astype(np.float32))
+    return np.concatenate(blocks)
+
+
+@pytest.mark.parametrize("kind", ["nf4", "fp4"])
+def test_quantize_division_near_every_threshold(kind):
+    """Bit-exact codes where the normalized value is within a few ulps of a
+    decision threshold, for scales that are not powers of two: a wrong last
+    bit in fl32(x / a) flips the code there."""
+    torch = need_gpu()
+    if kind == "nf4":
+        levels = oracle.codebook()
+    else:
+        lv = oracle.fp4_codebook()
+        levels = np.unique(lv[oracle.FP4_PRODUCED])
+    x = _threshold_inputs(levels, 11 if kind == "nf4" else 12)
+    say("quantize near thresholds", kind, "values", x.size)
+    xt = torch.from_numpy(x).to("cuda")
+    packed, absmax = nf4.nf4_quantize(xt, fp4=kind == "fp4")
+    torch.cuda.synchronize()
+    p_ref, a_ref = oracle.quantize(x, kind=kind)
+    _assert_quant_equal(packed, absmax, p_ref, a_ref)
+    # the sweep does reach both division paths and every threshold
+    a = np.abs(x.reshape(-1, 64)[:, 0])
+    assert ((a >= 2.0 ** -98) & (a < 2.0 ** 126)).any() and ((a < 2.0 ** -98) | (a >= 2.0 ** 126)).any()
