@@ -30,6 +30,7 @@ EXPORTS = (
     "nf4_last_error", "nf4_codebook", "nf4_codebook_fp4", "nf4_quantize", "nf4_quantize_fp4", "nf4_double_quant_workspace",
     "nf4_double_quant", "nf4_e4m3_ratio", "nf4_double_quant_f8", "nf4_dequantize", "nf4_gemv", "nf4_gemm_workspace", "nf4_gemm", "nf4_gemm_dx_workspace",
     "nf4_gemm_dx", "nf4_lora_grads_workspace", "nf4_lora_grads", "nf4_lora_merge", "nf4_double_quant_noalloc",
+    "nf4_gemv_batched",
 )
 
 
@@ -75,6 +76,7 @@ def lib() -> ctypes.CDLL:
         "nf4_e4m3_ratio": (ctypes.c_int, [ctypes.POINTER(ctypes.c_float)]),
         "nf4_dequantize": (ctypes.c_int, [wp, vp, ctypes.c_int, vp]),
         "nf4_gemv": (ctypes.c_int, [wp, vp, i64, vp, ctypes.c_int, vp]),
+        "nf4_gemv_batched": (ctypes.c_int, [wp, i32, ctypes.POINTER(vp), ctypes.POINTER(vp), ctypes.c_int, vp]),
         "nf4_gemm_workspace": (sz, [i64, i64, i32]),
         "nf4_gemm": (ctypes.c_int, [wp, vp, i64, vp, vp, vp, i32, ctypes.c_float, vp, sz, vp]),
         "nf4_gemm_dx_workspace": (sz, [i64, i64, i32]),
@@ -369,6 +371,31 @@ def nf4_gemv(w: NF4Weight, x, y=None, y_dtype=None, stream=None):
         raise ValueError("y has the wrong size")
     _check(lib().nf4_gemv(ctypes.byref(cs), _ptr(x2), m, _ptr(y), _dtype_code(y), _stream(stream)))
     return y
+
+
+def nf4_gemv_batched(ws, xs, ys=None, y_dtype=None, stream=None):
+    """ys[i] = xs[i] . deq(ws[i])^T at m = 1 for several weights in one launch;
+    xs[i] is bf16 [1, cols_i] (the same tensor may serve several weights).
+    Returns the list of outputs."""
+    torch = _torch()
+    ws, xs = list(ws), list(xs)
+    if len(ws) != len(xs) or not 1 <= len(ws) <= 8:
+        raise ValueError("ws and xs must be lists of the same length, 1 to 8")
+    structs = (nf4_weight * len(ws))(*[w.c_struct() for w in ws])
+    if ys is None:
+        ys = [_alloc_on(stream, (1, w.rows), y_dtype or torch.bfloat16, xs[i].device) for i, w in enumerate(ws)]
+    ys = list(ys)
+    for w, x, y in zip(ws, xs, ys):
+        _need_cuda(x, y)
+        _same_device(w.device, x, y)
+        if x.dtype != torch.bfloat16 or x.numel() != w.cols:
+            raise ValueError("each x must be bf16 with cols values (m = 1)")
+        if y.numel() != w.rows or y.dtype != ys[0].dtype:
+            raise ValueError("each y must hold rows values, all of one dtype")
+    xp = (ctypes.c_void_p * len(ws))(*[_ptr(x) for x in xs])
+    yp = (ctypes.c_void_p * len(ws))(*[_ptr(y) for y in ys])
+    _check(lib().nf4_gemv_batched(structs, len(ws), xp, yp, _dtype_code(ys[0]), _stream(stream)))
+    return ys
 
 
 def nf4_gemm(w: NF4Weight, x, y=None, lora_a=None, lora_b=None, lora_scale: float = 0.0,

@@ -98,6 +98,7 @@ int check_weight(const nf4_weight* w, nf4i::Scales* sc, int64_t* n_out, const ch
 
 hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
 
+const uint8_t* w_packed(const nf4_weight& w) { return w.packed; }
 
 }  // namespace
 
@@ -246,6 +247,33 @@ int nf4_gemv(const nf4_weight* w, const void* x, int64_t m, void* y, int y_dtype
   return launched(nf4i::launch_gemv(w->packed, w->rows, w->cols, sc, static_cast<const uint16_t*>(x), m, y,
                                     y_dtype == NF4_BF16, as_stream(stream)),
                   "nf4_gemv");
+}
+
+int nf4_gemv_batched(const nf4_weight* ws, int32_t count, const void* const* xs, void* const* ys, int y_dtype,
+                     void* stream) {
+  const char* who = "nf4_gemv_batched";
+  if (!ws || !xs || !ys) return fail(NF4_ERR_NULL, "%s: ws, xs and ys are required", who);
+  if (count < 1 || count > nf4i::kGemvBatchMax)
+    return fail(NF4_ERR_SIZE, "%s: count = %d out of range 1..%d", who, (int)count, nf4i::kGemvBatchMax);
+  if (y_dtype != NF4_F32 && y_dtype != NF4_BF16) return fail(NF4_ERR_DTYPE, "%s: y_dtype %d unknown", who, y_dtype);
+  nf4i::GemvJob jobs[nf4i::kGemvBatchMax];
+  for (int i = 0; i < count; ++i) {
+    nf4i::Scales sc{};
+    int64_t n = 0;
+    if (int rc = check_weight(&ws[i], &sc, &n, who)) return rc;
+    if (!xs[i] || !ys[i]) return fail(NF4_ERR_NULL, "%s: x and y of weight %d are required", who, i);
+    if (ws[i].cols % 64 || ws[i].cols > 65536)
+      return fail(NF4_ERR_SIZE, "%s: weight %d has cols = %lld (a multiple of 64 up to 65536 is required)", who, i,
+                  (long long)ws[i].cols);
+    if (!aligned(xs[i], 16) || !aligned(ys[i], 16))
+      return fail(NF4_ERR_ALIGN, "%s: x and y of weight %d must be 16-byte aligned", who, i);
+    if (i > 0 && ((sc.absmax == nullptr) != (jobs[0].sc.absmax == nullptr) || sc.f8 != jobs[0].sc.f8 ||
+                  sc.fp4 != jobs[0].sc.fp4))
+      return fail(NF4_ERR_DTYPE, "%s: weight %d has another scale form or code book than weight 0", who, i);
+    jobs[i] = nf4i::GemvJob{w_packed(ws[i]), ws[i].rows, ws[i].cols, sc, static_cast<const uint16_t*>(xs[i]), ys[i]};
+  }
+  if (int rc = check_device()) return rc;
+  return launched(nf4i::launch_gemv_batch(jobs, count, y_dtype == NF4_BF16, as_stream(stream)), who);
 }
 
 size_t nf4_gemm_workspace(int64_t m, int64_t rows, int32_t r) {

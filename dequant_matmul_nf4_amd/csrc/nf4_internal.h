@@ -108,6 +108,19 @@ hipError_t launch_dequantize(const uint8_t* packed, int64_t n, Scales sc, void* 
                              int out_bf16, hipStream_t s);
 hipError_t launch_gemv(const uint8_t* packed, int64_t rows, int64_t cols, Scales sc,
                        const uint16_t* x, int64_t m, void* y, int y_bf16, hipStream_t s);
+// One decode product of a batched launch: y = x . deq(W)^T at m = 1.
+constexpr int kGemvBatchMax = 8;
+struct GemvJob {
+  const uint8_t* packed;
+  int64_t rows, cols;
+  Scales sc;
+  const uint16_t* x;
+  void* y;
+};
+// Decode GEMV of up to kGemvBatchMax weights (all with the same scale form
+// and code book, cols % 64 == 0, cols <= 65536) in as few launches as the
+// kernel's x stage allows: consecutive jobs whose x fit together share one.
+hipError_t launch_gemv_batch(const GemvJob* jobs, int count, int y_bf16, hipStream_t s);
 // Extra K columns the GEMM uses for a LoRA term of rank r (0 without one);
 // the workspace holds m rows of that many bf16 values.
 size_t gemm_lora_cols(int r);

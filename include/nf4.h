@@ -207,6 +207,31 @@ int nf4_dequantize(const nf4_weight* w, void* out, int out_dtype, void* stream);
 int nf4_gemv(const nf4_weight* w, const void* x, int64_t m, void* y, int y_dtype,
              void* stream);
 
+/* Decode GEMV of several weights in one launch: ys[i] = xs[i] . deq(ws[i])^T
+ * for i < count, each at m = 1 (tool page "How it works", Step 5, as
+ * nf4_gemv).  One decode step multiplies the same token by every weight of a
+ * layer, and several of those products share their input (the attention
+ * projections, the MLP input projections); one launch streams all of them
+ * back to back with no drain of the chip between weights.
+ *   ws    : [host] array of count weight descriptors, 1 <= count <= 8, each
+ *           with cols % 64 == 0 and cols <= 65536, all with the same scale
+ *           form (plain, int8 or float8 second level) and code book.
+ *   xs    : [host] array of count device pointers, xs[i] bf16 [1][ws[i].cols],
+ *           16-byte aligned.  Weights whose x is the same pointer share one
+ *           staged copy of it.
+ *   ys    : [host] array of count device pointers, ys[i] [1][ws[i].rows] of
+ *           y_dtype (NF4_F32 or NF4_BF16), 16-byte aligned, not overlapping
+ *           each other or any input.
+ * Each ys[i] holds exactly the bits nf4_gemv(&ws[i], xs[i], 1, ys[i], ...)
+ * writes for cols <= 65536: the same levels rounded to fp16, the same x
+ * scaling, the same per-lane sums and the same fixed order of the segment
+ * sums.  The kernel stages the distinct x of a launch together, up to 40960
+ * values: a call whose weights need more makes several launches, each over
+ * the longest run of consecutive weights that fits (a weight wider than that
+ * alone takes nf4_gemv's kernel); results are the same. */
+int nf4_gemv_batched(const nf4_weight* ws, int32_t count, const void* const* xs, void* const* ys, int y_dtype,
+                     void* stream);
+
 /* Bytes of device workspace nf4_gemm needs for m rows of x, a weight of
  * `rows` rows and LoRA rank r (0 when r == 0): m + rows rows of 2 r (rounded
  * up to 64) bf16 values. */

@@ -185,6 +185,35 @@ CASES = [
 ]
 
 
+def _batch(L, ws, xs=None, ys=None, count=None, y_dtype=1):
+    arr = (nf4.nf4_weight * len(ws))(*ws)
+    xs = xs if xs is not None else [A] * len(ws)
+    ys = ys if ys is not None else [A2] * len(ws)
+    xp = (ctypes.c_void_p * len(xs))(*xs)
+    yp = (ctypes.c_void_p * len(ys))(*ys)
+    return L.nf4_gemv_batched(arr, len(ws) if count is None else count, xp, yp, y_dtype, None)
+
+
+def _dqw(**kw):
+    return _w(absmax=None, qabsmax=A, absmax2=A2, mean=A2, **kw)
+
+
+CASES += [
+    ("batched null ws", lambda L: L.nf4_gemv_batched(None, 1, (ctypes.c_void_p * 1)(A), (ctypes.c_void_p * 1)(A), 1, None), nf4.NF4_ERR_NULL),
+    ("batched count 0", lambda L: _batch(L, [_w()], count=0), nf4.NF4_ERR_SIZE),
+    ("batched count 9", lambda L: _batch(L, [_w()] * 9), nf4.NF4_ERR_SIZE),
+    ("batched bad dtype", lambda L: _batch(L, [_w()], y_dtype=2), nf4.NF4_ERR_DTYPE),
+    ("batched cols%64", lambda L: _batch(L, [_w(), _w(cols=96)]), nf4.NF4_ERR_SIZE),
+    ("batched cols>65536", lambda L: _batch(L, [_w(cols=65600)]), nf4.NF4_ERR_SIZE),
+    ("batched null x", lambda L: _batch(L, [_w(), _w()], xs=[A, None]), nf4.NF4_ERR_NULL),
+    ("batched misaligned y", lambda L: _batch(L, [_w(), _w()], ys=[A2, A2 + 4]), nf4.NF4_ERR_ALIGN),
+    ("batched mixed scale forms", lambda L: _batch(L, [_w(), _dqw()]), nf4.NF4_ERR_DTYPE),
+    ("batched mixed dq types", lambda L: _batch(L, [_dqw(), _dqw(dq_type=1)]), nf4.NF4_ERR_DTYPE),
+    ("batched mixed code books", lambda L: _batch(L, [_w(), _w(quant_type=1)]), nf4.NF4_ERR_DTYPE),
+    ("batched bad weight", lambda L: _batch(L, [_w(), _w(blocksize=32)]), nf4.NF4_ERR_BLOCKSIZE),
+]
+
+
 @pytest.mark.parametrize("name,call,code", CASES, ids=[c[0] for c in CASES])
 def test_invalid_arguments_rejected_on_host(L, name, call, code):
     rc = call(L)
