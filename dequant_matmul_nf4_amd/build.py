@@ -80,6 +80,34 @@ def build(verbose: bool = False, sanitize: bool = False) -> str:
     return lib
 
 
+CALIB = os.path.join(PKG, "calib")
+CALIB_LIB = os.path.join(PKG, "libnf4_calib.so")
+
+
+def build_calib(verbose: bool = False) -> str:
+    """The benchmark's calibration kernels (a plain streaming read), built
+    into their own library; the NF4 library does not contain them."""
+    os.makedirs(BUILD, exist_ok=True)
+    srcs = sorted(f for f in os.listdir(CALIB) if f.endswith(".hip"))
+    objs = []
+    for src in srcs:
+        obj = os.path.join(BUILD, "calib_" + src + ".o")
+        cmd = [hipcc(), "-x", "hip", *DEVICE, *COMMON, "-c", os.path.join(CALIB, src), "-o", obj]
+        r = subprocess.run(cmd, capture_output=True, text=True)
+        if r.returncode != 0:
+            raise RuntimeError(f"compile failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
+        objs.append(obj)
+    tmp = CALIB_LIB + ".tmp"
+    cmd = [hipcc(), "-shared", f"--offload-arch={ARCH}", "-fPIC", *objs, "-o", tmp]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"link failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
+    os.replace(tmp, CALIB_LIB)
+    if verbose:
+        print(f"built {CALIB_LIB}")
+    return CALIB_LIB
+
+
 def sanitizer_runtime() -> str:
     """The compiler's AddressSanitizer runtime (it carries the
     UndefinedBehaviorSanitizer handlers too), to preload into an
@@ -96,4 +124,6 @@ def sanitizer_runtime() -> str:
 
 if __name__ == "__main__":
     build(verbose=True, sanitize="--sanitize" in sys.argv[1:])
+    if "--sanitize" not in sys.argv[1:]:
+        build_calib(verbose=True)
     sys.exit(0)
