@@ -59,8 +59,8 @@ def parse():
 
 # HBM bytes of the dominant kernel as read by the FETCH_SIZE / WRITE_SIZE
 # counters (profiles/), kept only while the kernel's sources are unchanged.
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "k_gemv_rows_70b_layer_traffic.json")
-GEMV_SOURCES = ["k_gemv.hip", "nf4_device.h", "nf4_internal.h"]
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "k_gemv_batch_70b_layer_traffic.json")
+GEMV_SOURCES = ["k_gemv_batch.hip", "gemv_rows.h", "nf4_device.h", "nf4_internal.h"]
 
 
 def sources_digest(names) -> str:
@@ -206,18 +206,20 @@ def main():
     step_bytes_layer = sum(step_bytes(r, c)["gemv"] for r, c in shapes)
 
     # One step: the decode GEMV (m = 1) over the seven matrices of one stored
-    # layer, issued as a decode step issues them: q, k, v in one batched
-    # launch (they share the layer's input), o, gate and up in one batched
-    # launch (they share the MLP input), down; one HIP graph per layer.
-    # Consecutive steps take layers 37 apart, so no step finds its 442 MB in
-    # the 256 MB last-level cache.
+    # layer in one nf4_gemv_batched call (one launch), each matrix with its
+    # layer input (q, k, v: the attention input; o: the attention output;
+    # gate, up: the MLP input; down: the MLP hidden state); one HIP graph per
+    # layer.  Consecutive steps take layers 37 apart, so no step finds its
+    # 442 MB in the 256 MB last-level cache.  The decode-order form (four
+    # launches: o and down wait for the results before them in a real model)
+    # and seven single launches are measured beside it.
     xs = layer_inputs(torch, dev)
     ys = [torch.empty((1, r), dtype=torch.bfloat16, device=dev) for r, _ in shapes]
     L = len(store)
     print(f"[bench] capturing the decode GEMV of {L} stored layers", file=sys.stderr, flush=True)
     graphs = []
     for layer in range(L):
-        graphs.append(capture_layer_gemv(torch, nf4, store[layer], xs, ys, "decode"))
+        graphs.append(capture_layer_gemv(torch, nf4, store[layer], xs, ys, "one"))
     torch.cuda.synchronize()
     order = [(37 * k) % L for k in range(max(args.steps, args.warmup))]
 
@@ -262,14 +264,14 @@ def main():
                         "(groups of 256) in a persistent store; decode GEMV y = x.deq(W)^T at m=1 over the seven "
                         "matrices of one stored layer per step, a different layer each step",
             "layers": L,
-            "step": "nf4_gemv_batched on (q, k, v) with the attention input, on (o) with the attention output, "
-                    "on (gate, up) with the MLP input, on (down) with the MLP hidden state: four launches in one "
-                    "HIP graph per stored layer",
+            "step": "one nf4_gemv_batched call (one launch) over q, k, v, o, gate, up, down of one stored layer, "
+                    "each with its layer input (attention input for q, k, v; attention output for o; MLP input for "
+                    "gate, up; MLP hidden state for down), one HIP graph per stored layer",
             "bytes_per_step": step_bytes_layer,
             "bytes_per_weight": "0.5 codes + 1/64 int8 scale codes + 4/16384 group scales; plus x and y",
         },
         "roofline": {
-            "kernel": "k_gemv_batch (the four launches of a step)",
+            "kernel": "k_gemv_batch (one launch per step)",
             "bound": "hbm",
             "achieved": round(achieved, 1),
             "peak": HBM_PEAK_GBS,
@@ -357,8 +359,7 @@ def layer_gemv_variants(torch, nf4, store, xs, ys, stream, nbytes, passes=40):
     L = len(store)
     for form, what in (("single", "seven nf4_gemv launches"),
                        ("decode", "q|k|v, o, gate|up, down as four nf4_gemv_batched launches"),
-                       ("one", "one nf4_gemv_batched call over the seven: q..up in one launch, down (its 28672-value x "
-                               "does not fit the same stage) in a second")):
+                       ("one", "one nf4_gemv_batched call over the seven (one launch)")):
         layers = [(37 * k) % L for k in range(passes)]
         graphs = {l: capture_layer_gemv(torch, nf4, store[l], xs, ys, form) for l in sorted(set(layers))}
         for l in layers[:3]:
@@ -574,7 +575,7 @@ def leg_layer_gemv(torch, nf4, syn, dev, stream, EventTimer, layers=6, passes=12
     shapes = [syn.C5_SHAPES[name] for name in syn.C5_ORDER]
     xs = layer_inputs(torch, dev)
     ys = [torch.empty((1, r), dtype=torch.bfloat16, device=dev) for r, _ in shapes]
-    graphs = [capture_layer_gemv(torch, nf4, Ws, xs, ys, "decode") for Ws in store]
+    graphs = [capture_layer_gemv(torch, nf4, Ws, xs, ys, "one") for Ws in store]
     torch.cuda.synchronize()
     t = EventTimer(torch, stream)
     for k in range(passes):

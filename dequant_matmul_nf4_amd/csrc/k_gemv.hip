@@ -337,7 +337,7 @@ __global__ __launch_bounds__(kWaves * 64) void k_gemv_rows(const uint8_t* packed
   constexpr int kRowsWg = kRowsMaxWg / MC;
   __shared__ uint32_t tab[256 * 64];
   __shared__ float part[kRowsWg * kSegMax * MC];
-  __shared__ float rtab[kF8 ? 256 : 1];
+  __shared__ float rtab[kDQ ? 256 : 1];
   const char* smem = reinterpret_cast<const char*>(tab);
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -359,14 +359,7 @@ __global__ __launch_bounds__(kWaves * 64) void k_gemv_rows(const uint8_t* packed
   bool on[2];
   int blk[2];
   LaneOffs lo;
-#pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    const int bj = 32 * j + (lane >> 1);
-    on[j] = bj < seg_end;
-    blk[j] = seg * pl.seg_blocks + (on[j] ? bj : seg_end - 1);
-    lo.blk[j] = static_cast<uint32_t>(blk[j]);
-    lo.code[j] = static_cast<uint32_t>(blk[j]) * 32u + 16u * static_cast<uint32_t>(half);
-  }
+  make_lane_offs(seg * pl.seg_blocks, seg_end, lane, lo, on, blk);
   const int64_t row0 = gp < rows ? gp : rows - 1;
   const int64_t last = n > 0 ? row0 + (n - 1) * np : row0;  // loads are clamped to it
 
@@ -387,8 +380,7 @@ __global__ __launch_bounds__(kWaves * 64) void k_gemv_rows(const uint8_t* packed
 #pragma unroll
       for (int i = 0; i < 4; ++i) xv[c][j][i] = xp[i];
     }
-  if constexpr (kF8)
-    for (int i = threadIdx.x; i < 256; i += kWaves * 64) rtab[i] = kE4m3Ratio.v[i];
+  if constexpr (kDQ) fill_ratio_table<kF8>(rtab, kWaves * 64);
   fill_half_table<kWaves * 64>(tab, cb);  // ends with a barrier
 
   uint32_t xh[MC][2][16];
@@ -396,7 +388,9 @@ __global__ __launch_bounds__(kWaves * 64) void k_gemv_rows(const uint8_t* packed
 #pragma unroll
   for (int c = 0; c < MC; ++c)
 #pragma unroll
-    for (int j = 0; j < 2; ++j) x_piece_to_half(xv[c][j], xh[c][j], xinv[c][j]);
+    for (int j = 0; j < 2; ++j) x_half_block_to_half(xv[c][j], xh[c][j], xinv[c][j]);
+  float xsel[MC];
+  lane_x_scales<MC>(xinv, on, xsel);
   const float mean = kDQ ? *sc.mean : 0.0f;
 
   // step i: request row i + U into the slot freed by step i - 1, then use
@@ -411,7 +405,7 @@ __global__ __launch_bounds__(kWaves * 64) void k_gemv_rows(const uint8_t* packed
       __builtin_amdgcn_sched_barrier(0);
       if (i < n) {  // wave-uniform
         float v[MC];
-        row_dot<MC, kDQ, kF8>(it[u], xh, smem, slot, mean, rtab, xinv, on, v);
+        row_dot<MC, kDQ>(it[u], xh, smem, slot, mean, rtab, xsel, v);
 #pragma unroll
         for (int c = 0; c < MC; ++c) {
           const float t = wave_sum_to_last(v[c]);
@@ -494,6 +488,14 @@ hipError_t launch_rows_sc(const uint8_t* packed, int64_t rows, int64_t cols, Sca
 //    workgroup is p-th of its share); waves walk the workgroup's groups for
 //    each of their segments and park each (group, segment) partial tile in
 //    LDS; the segments are added in a fixed order at the end.
+// First factor of a_hat: q / 127 for int8 codes, the E4M3 ratio table (copied
+// to LDS) for float8 codes.
+template <bool kF8>
+__device__ __forceinline__ float row_ratio(int q, const float* rtab) {
+  if constexpr (kF8) return rtab[q & 0xFF];
+  else return div127(q);
+}
+
 constexpr int kPartTiles = 64;   // 16 x 16 float partial tiles per workgroup (64 KiB)
 constexpr int kMfmaSeg = 4;      // blocks per column segment (x kept in registers)
 constexpr int kMfmaWaves = 16;

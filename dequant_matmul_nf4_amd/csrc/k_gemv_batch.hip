@@ -17,10 +17,10 @@
 //  - a wave walks its rows of group 0, then of group 1, ..., and requests
 //    the next row one step ahead across the group boundaries, so the memory
 //    pipe does not drain between weights;
-//  - every x is converted to fp16 once per workgroup at the start (each
-//    32-value piece scaled by a power of two chosen from its largest |x|)
-//    into LDS, from where a wave takes its segment's values into registers
-//    when it enters a group;
+//  - a wave keeps the x values of its column segment in registers as fp16
+//    (each 64-value block scaled by a power of two chosen from its largest
+//    |x|); the x of its next group is requested together with that group's
+//    first row, one step before the wave needs it;
 //  - partial sums of every (row, segment) stay in LDS until the end, when
 //    each row's segments are added in a fixed order (results do not depend
 //    on timing) and written to that weight's y.
@@ -33,8 +33,6 @@ constexpr int kBWaves = 16;
 constexpr int kAhead = 1;          // rows requested ahead of the one in use
 constexpr int kSlots = kAhead + 1; // register slots of the row ring
 constexpr int kBPartMax = 2048;    // partial sums per workgroup (floats)
-constexpr int kBXWords = 20480;    // fp16 pairs of x in LDS (40960 values)
-constexpr int kBXPieces = 1280;    // 32-value pieces of x in LDS (their scales)
 
 struct BMat {
   const uint8_t* packed;
@@ -54,31 +52,21 @@ struct BGroup {
   int nseg, seg_blocks, wpr, kmax;
   int mat0, mat1;        // its weights
   int part0;             // first partial-sum slot (per workgroup)
-  int xword0, xpiece0;   // its x in LDS
 };
 
 struct BArgs {
   BMat mat[kGemvBatchMax];
   BGroup grp[kGemvBatchMax];
   int ngroups;
-  int npieces;           // 32-value pieces of x over all groups
   Codebook cb;
 };
 
 // The lane's piece offsets in a row segment of group G (as k_gemv_rows).
 __device__ __forceinline__ void lane_offsets(const BGroup& G, int seg, int lane, LaneOffs& lo, bool (&on)[2],
                                              int (&blk)[2]) {
-  const int half = lane & 1;
   const int seg_end = static_cast<int>(G.nblk - seg * G.seg_blocks < G.seg_blocks ? G.nblk - seg * G.seg_blocks
                                                                                   : G.seg_blocks);
-#pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    const int bj = 32 * j + (lane >> 1);
-    on[j] = bj < seg_end;
-    blk[j] = seg * G.seg_blocks + (on[j] ? bj : seg_end - 1);
-    lo.blk[j] = static_cast<uint32_t>(blk[j]);
-    lo.code[j] = static_cast<uint32_t>(blk[j]) * 32u + 16u * static_cast<uint32_t>(half);
-  }
+  make_lane_offs(seg * G.seg_blocks, seg_end, lane, lo, on, blk);
 }
 
 // A wave's walk over its rows (wave-uniform state, kept in scalar
@@ -163,9 +151,7 @@ template <bool kDQ, bool kF8, bool kBf16Out>
 __global__ __launch_bounds__(kBWaves * 64) void k_gemv_batch(BArgs a) {
   __shared__ uint32_t tab[256 * 64];
   __shared__ float part[kBPartMax];
-  __shared__ __align__(16) uint32_t xs[kBXWords];
-  __shared__ float xinvs[kBXPieces];
-  __shared__ float rtab[kF8 ? 256 : 1];
+  __shared__ float rtab[kDQ ? 256 : 1];
   __shared__ float means[kGemvBatchMax];
   const char* smem = reinterpret_cast<const char*>(tab);
   const int lane = threadIdx.x & 63;
@@ -189,13 +175,38 @@ __global__ __launch_bounds__(kBWaves * 64) void k_gemv_batch(BArgs a) {
   Scales sc_l = any ? mat_scales<kDQ>(a.mat[wl.m]) : Scales{};
   int m_l = wl.m;
 
+  // raw (bf16) x of the lane's two half blocks of a group's segment; xr_g is
+  // the group whose x it holds and that the compute walk has not entered yet
+  // (-1: none)
+  uint4 xr[2][4];
+  int xr_g = -1;
+  auto load_x = [&](uint4 (&dst)[2][4], int g, int seg) {
+    const BGroup& G = a.grp[g];
+    LaneOffs lo_;
+    bool on_[2];
+    int blk_[2];
+    lane_offsets(G, seg, lane, lo_, on_, blk_);
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const uint4* xp = reinterpret_cast<const uint4*>(G.x + static_cast<int64_t>(blk_[j]) * 64 + 32 * (lane & 1));
+#pragma unroll
+      for (int i = 0; i < 4; ++i) dst[j][i] = xp[i];
+    }
+  };
+
   // advances the load walk and requests its row into `dst` (past the wave's
-  // last row the last row is requested again: loads are never branched around)
+  // last row the last row is requested again: loads are never branched
+  // around); on entering a group it also requests that group's x, unless the
+  // x of an earlier group is still waiting to be used
   auto load_next = [&](RowItem& dst) {
     if (walk_next(wl, a, wave)) {
       bool on_[2];
       int blk_[2];
       lane_offsets(a.grp[wl.g], wl.seg, lane, lol, on_, blk_);
+      if (xr_g < 0) {
+        load_x(xr, wl.g, wl.seg);
+        xr_g = wl.g;
+      }
     }
     if (wl.m != m_l) {
       m_l = wl.m;
@@ -205,39 +216,25 @@ __global__ __launch_bounds__(kBWaves * 64) void k_gemv_batch(BArgs a) {
     row_load<kDQ>(dst, packed_l, wl.blk0, lol, sc_l);
   };
 
-  // the wave's first kAhead rows are requested before the tables are built
+  // the wave's first kAhead rows and its first x are requested before the
+  // tables are built
   RowItem it[kSlots];
   if (any) {
     row_load<kDQ>(it[0], packed_l, wl.blk0, lol, sc_l);
+    load_x(xr, wl.g, wl.seg);
+    xr_g = wl.g;
 #pragma unroll
     for (int r = 1; r < kAhead; ++r) load_next(it[r]);
   }
 
-  // x of every group to fp16 pairs in LDS, one 32-value piece per thread
-  for (int t = threadIdx.x; t < a.npieces; t += kBWaves * 64) {
-    int g = 0;
-#pragma unroll
-    for (int k = 1; k < kGemvBatchMax; ++k)
-      if (k < a.ngroups && t >= a.grp[k].xpiece0) g = k;
-    const int p = t - a.grp[g].xpiece0;
-    const uint4* xp = reinterpret_cast<const uint4*>(a.grp[g].x + 32 * static_cast<int64_t>(p));
-    const uint4 xv[4] = {xp[0], xp[1], xp[2], xp[3]};
-    uint32_t xh[16];
-    float xinv;
-    x_piece_to_half(xv, xh, xinv);
-    uint4* dst = reinterpret_cast<uint4*>(xs + a.grp[g].xword0 + 16 * p);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) dst[i] = make_uint4(xh[4 * i], xh[4 * i + 1], xh[4 * i + 2], xh[4 * i + 3]);
-    xinvs[a.grp[g].xpiece0 + p] = xinv;
-  }
   if (kDQ && static_cast<int>(threadIdx.x) < a.grp[a.ngroups - 1].mat1) means[threadIdx.x] = *a.mat[threadIdx.x].mean;
-  if constexpr (kF8)
-    for (int i = threadIdx.x; i < 256; i += kBWaves * 64) rtab[i] = kE4m3Ratio.v[i];
+  if constexpr (kDQ) fill_ratio_table<kF8>(rtab, kBWaves * 64);
   fill_half_table<kBWaves * 64>(tab, a.cb);  // ends with a barrier
 
   // state of the compute walk's group: x in registers, segment flags, slots
   uint32_t xh[1][2][16];
   float xinv[1][2];
+  float xsel[1];
   bool on[2];
   int part_row = 0, nseg_c = 1;  // part index of the current row, stride per row
   float mean_c = 0.0f;
@@ -247,17 +244,19 @@ __global__ __launch_bounds__(kBWaves * 64) void k_gemv_batch(BArgs a) {
     LaneOffs lo_;
     int blk[2];
     lane_offsets(G, wc.seg, lane, lo_, on, blk);
+    if (xr_g != wc.g) {
+      // this group's x was not requested ahead (the wave's rows of the group
+      // before it were too few): request it now
+      uint4 xn[2][4];
+      load_x(xn, wc.g, wc.seg);
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int piece = 2 * blk[j] + (lane & 1);
-      const uint4* src = reinterpret_cast<const uint4*>(xs + G.xword0 + 16 * piece);
+      for (int j = 0; j < 2; ++j) x_half_block_to_half(xn[j], xh[0][j], xinv[0][j]);
+    } else {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const uint4 w = src[i];
-        xh[0][j][4 * i] = w.x; xh[0][j][4 * i + 1] = w.y; xh[0][j][4 * i + 2] = w.z; xh[0][j][4 * i + 3] = w.w;
-      }
-      xinv[0][j] = xinvs[G.xpiece0 + piece];
+      for (int j = 0; j < 2; ++j) x_half_block_to_half(xr[j], xh[0][j], xinv[0][j]);
+      xr_g = -1;
     }
+    lane_x_scales<1>(xinv, on, xsel);
     nseg_c = G.nseg;
     part_row = G.part0 + (wc.prt * G.kmax) * G.nseg + wc.seg;
   };
@@ -280,7 +279,7 @@ __global__ __launch_bounds__(kBWaves * 64) void k_gemv_batch(BArgs a) {
           }
         }
         float v[1];
-        row_dot<1, kDQ, kF8>(it[u], xh, smem, slot, mean_c, rtab, xinv, on, v);
+        row_dot<1, kDQ>(it[u], xh, smem, slot, mean_c, rtab, xsel, v);
         const float t = wave_sum_to_last(v[0]);
         if (lane == 63) part[part_row] = t;
         part_row += nseg_c;
@@ -323,8 +322,7 @@ __global__ __launch_bounds__(kBWaves * 64) void k_gemv_batch(BArgs a) {
 
 // Groups the jobs by their x (same pointer and width), plans the groups for
 // a grid of one workgroup per compute unit (more if the partial sums would
-// not fit), and fills the kernel arguments.  Returns false if the jobs'
-// x do not fit the LDS stage together.
+// not fit), and fills the kernel arguments.
 bool plan_batch(const GemvJob* jobs, int count, BArgs& a, int& grid) {
   a = BArgs{};
   int order[kGemvBatchMax];
@@ -364,19 +362,12 @@ bool plan_batch(const GemvJob* jobs, int count, BArgs& a, int& grid) {
   }
   (void)order;
   a.ngroups = ng;
-  int words = 0, pieces = 0;
   for (int g = 0; g < ng; ++g) {
     BGroup& G = a.grp[g];
     G.nseg = static_cast<int>((G.nblk + 63) / 64);
     G.seg_blocks = static_cast<int>((G.nblk + G.nseg - 1) / G.nseg);
     G.wpr = kBWaves / G.nseg;
-    G.xword0 = words;
-    G.xpiece0 = pieces;
-    words += static_cast<int>(G.nblk * 32);
-    pieces += static_cast<int>(G.nblk * 2);
   }
-  a.npieces = pieces;
-  if (words > kBXWords || pieces > kBXPieces) return false;
   int64_t g = device_cus();
   for (;; ++g) {
     int64_t slots = 0;
@@ -403,30 +394,13 @@ hipError_t launch_batch_sc(const BArgs& a, int grid, int y_bf16, hipStream_t s) 
 
 hipError_t launch_gemv_batch(const GemvJob* jobs, int count, int y_bf16, hipStream_t s) {
   if (count < 1 || count > kGemvBatchMax) return hipErrorInvalidValue;
-  // greedy: each launch takes the longest run of the remaining jobs whose x
-  // fit the stage together; a job whose x alone does not fit (more than 40960
-  // values) takes the single-weight kernel, which computes the same bits
-  for (int start = 0; start < count;) {
-    BArgs a;
-    int grid = 0;
-    if (!plan_batch(jobs + start, 1, a, grid)) {
-      const GemvJob& j = jobs[start];
-      if (hipError_t e = launch_gemv(j.packed, j.rows, j.cols, j.sc, j.x, 1, j.y, y_bf16, s)) return e;
-      ++start;
-      continue;
-    }
-    int end = start + 1;
-    while (end < count && plan_batch(jobs + start, end + 1 - start, a, grid)) ++end;
-    if (!plan_batch(jobs + start, end - start, a, grid)) return hipErrorInvalidValue;
-    a.cb = codebook(jobs[start].sc.fp4);
-    hipError_t e;
-    if (jobs[start].sc.absmax) e = launch_batch_sc<false, false>(a, grid, y_bf16, s);
-    else if (jobs[start].sc.f8) e = launch_batch_sc<true, true>(a, grid, y_bf16, s);
-    else e = launch_batch_sc<true, false>(a, grid, y_bf16, s);
-    if (e != hipSuccess) return e;
-    start = end;
-  }
-  return hipSuccess;
+  BArgs a;
+  int grid = 0;
+  if (!plan_batch(jobs, count, a, grid)) return hipErrorInvalidValue;
+  a.cb = codebook(jobs[0].sc.fp4);
+  if (jobs[0].sc.absmax) return launch_batch_sc<false, false>(a, grid, y_bf16, s);
+  if (jobs[0].sc.f8) return launch_batch_sc<true, true>(a, grid, y_bf16, s);
+  return launch_batch_sc<true, false>(a, grid, y_bf16, s);
 }
 
 }  // namespace nf4i

@@ -118,8 +118,7 @@ struct GemvJob {
   void* y;
 };
 // Decode GEMV of up to kGemvBatchMax weights (all with the same scale form
-// and code book, cols % 64 == 0, cols <= 65536) in as few launches as the
-// kernel's x stage allows: consecutive jobs whose x fit together share one.
+// and code book, cols % 64 == 0, cols <= 65536) in one launch.
 hipError_t launch_gemv_batch(const GemvJob* jobs, int count, int y_bf16, hipStream_t s);
 // Extra K columns the GEMM uses for a LoRA term of rank r (0 without one);
 // the workspace holds m rows of that many bf16 values.

@@ -225,10 +225,7 @@ int nf4_gemv(const nf4_weight* w, const void* x, int64_t m, void* y, int y_dtype
  * Each ys[i] holds exactly the bits nf4_gemv(&ws[i], xs[i], 1, ys[i], ...)
  * writes for cols <= 65536: the same levels rounded to fp16, the same x
  * scaling, the same per-lane sums and the same fixed order of the segment
- * sums.  The kernel stages the distinct x of a launch together, up to 40960
- * values: a call whose weights need more makes several launches, each over
- * the longest run of consecutive weights that fits (a weight wider than that
- * alone takes nf4_gemv's kernel); results are the same. */
+ * sums.  One launch. */
 int nf4_gemv_batched(const nf4_weight* ws, int32_t count, const void* const* xs, void* const* ys, int y_dtype,
                      void* stream);
 

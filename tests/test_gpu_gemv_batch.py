@@ -84,19 +84,19 @@ def test_batched_single_weight_and_eight_weights():
     _run([(256 + 37 * i, 1024 * (1 + i % 3)) for i in range(8)], [i % 3 for i in range(8)], seed=12)
 
 
-def test_batched_x_larger_than_the_stage_splits_launches():
-    """Four distinct x of 16384 values each (65536 > 40960 staged values):
-    the call splits the weights over several launches, same results; a
-    weight whose x alone is wider than the stage (49152 values) takes the
-    single-weight kernel between batched launches."""
-    say("gemv batched: split over launches")
+def test_batched_wide_and_many_distinct_x():
+    """Four distinct x of 16384 values each, and a weight 49152 wide between
+    two narrow ones (each wave takes its x slice of every group from global
+    memory as it enters the group)."""
+    say("gemv batched: wide and many distinct x")
     _run([(300, 16384), (200, 16384), (100, 16384), (50, 16384)], [0, 1, 2, 3], seed=13)
     _run([(64, 1024), (100, 49152), (70, 2048)], [0, 1, 2], seed=14)
 
 
 def test_batched_70b_layer_bit_identical_to_single_launches():
     """The seven matrices of a 70B-shaped layer (drawn on the device exactly
-    as the benchmark draws them), with q, k, v, o, gate, up sharing one x:
+    as the benchmark draws them) in one call, with q, k, v, o, gate, up
+    sharing one x:
     every output bit-identical to nf4_gemv on the same weight; the q
     projection also against the oracle on every output."""
     torch = need_gpu()
