@@ -208,40 +208,40 @@ def main():
     # One step: the decode GEMV (m = 1) over the seven matrices of one stored
     # layer in one nf4_gemv_batched call (one launch), each matrix with its
     # layer input (q, k, v: the attention input; o: the attention output;
-    # gate, up: the MLP input; down: the MLP hidden state); one HIP graph per
-    # layer.  Consecutive steps take layers 37 apart, so no step finds its
-    # 442 MB in the 256 MB last-level cache.  The decode-order form (four
-    # launches: o and down wait for the results before them in a real model)
-    # and seven single launches are measured beside it.
+    # gate, up: the MLP input; down: the MLP hidden state).  Consecutive steps
+    # take layers 37 apart, so no step finds its 442 MB in the 256 MB
+    # last-level cache.  The warmup steps and the timed steps are one HIP
+    # graph each (W and K launches back to back), so the timed region holds
+    # the K launches and no host dispatch gap; HIP events on the stream the
+    # graph runs on bracket it.  The decode-order form (four launches: o and
+    # down wait for the results before them in a real model) and seven single
+    # launches are measured beside it.
     xs = layer_inputs(torch, dev)
     ys = [torch.empty((1, r), dtype=torch.bfloat16, device=dev) for r, _ in shapes]
     L = len(store)
-    print(f"[bench] capturing the decode GEMV of {L} stored layers", file=sys.stderr, flush=True)
-    graphs = []
-    for layer in range(L):
-        graphs.append(capture_layer_gemv(torch, nf4, store[layer], xs, ys, "one"))
-    torch.cuda.synchronize()
     order = [(37 * k) % L for k in range(max(args.steps, args.warmup))]
+    print(f"[bench] capturing {args.warmup} warmup and {args.steps} timed steps over {L} stored layers",
+          file=sys.stderr, flush=True)
+    warm = capture_layer_steps(torch, nf4, store, order[:args.warmup], xs, ys, "one")
+    timed = capture_layer_steps(torch, nf4, store, order[:args.steps], xs, ys, "one")
+    torch.cuda.synchronize()
 
     print("[bench] warmup", file=sys.stderr, flush=True)
-    for k in range(args.warmup):
-        graphs[order[k]].replay()
+    warm.replay()
     torch.cuda.synchronize()
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
     print(f"[bench] timing {args.steps} steps", file=sys.stderr, flush=True)
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for k in range(args.steps):
-        evs[k][0].record(stream)
-        graphs[order[k]].replay()
-        evs[k][1].record(stream)
+    ev0.record(stream)
+    timed.replay()
+    ev1.record(stream)
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
-    step_us = [1e3 * a.elapsed_time(b) for a, b in evs]
-    mean_us = sum(step_us) / len(step_us)
+    mean_us = 1e3 * ev0.elapsed_time(ev1) / args.steps
     value = step_bytes_layer * args.steps / elapsed / 1e9
     achieved = step_bytes_layer / (mean_us * 1e-6) / 1e9
-    del graphs
+    del warm, timed
     read_gbs = None
     out_variants = layer_gemv_variants(torch, nf4, store, xs, ys, stream, step_bytes_layer)
 
@@ -266,7 +266,7 @@ def main():
             "layers": L,
             "step": "one nf4_gemv_batched call (one launch) over q, k, v, o, gate, up, down of one stored layer, "
                     "each with its layer input (attention input for q, k, v; attention output for o; MLP input for "
-                    "gate, up; MLP hidden state for down), one HIP graph per stored layer",
+                    "gate, up; MLP hidden state for down); the K timed steps are one HIP graph of K launches",
             "bytes_per_step": step_bytes_layer,
             "bytes_per_weight": "0.5 codes + 1/64 int8 scale codes + 4/16384 group scales; plus x and y",
         },
@@ -280,7 +280,7 @@ def main():
             "traffic": measured_traffic(),
             "bytes_per_launch": step_bytes_layer,
             "avg_launch_us": round(mean_us, 3),
-            "timing": "HIP events around each step's graph on the stream it runs on, mean over the timed steps",
+            "timing": "HIP events on the graph's stream around the K timed launches, divided by K",
         },
     }
     out["stack_70b"] = stack
@@ -330,51 +330,56 @@ def layer_inputs(torch, dev):
 LAYER_X = ("attn", "attn", "attn", "o", "mlp", "mlp", "down")
 
 
-def capture_layer_gemv(torch, nf4, Ws, xs, ys, form):
-    """One layer's decode GEMV as a HIP graph.  form "decode": batched
-    launches over the matrices that share their input (q|k|v, o, gate|up,
-    down); "single": seven nf4_gemv launches; "one": one nf4_gemv_batched
-    call over all seven (it splits into as many launches as its x stage
-    needs)."""
+def layer_gemv_calls(nf4, Ws, xs, ys, form):
+    """One layer's decode GEMV.  form "decode": batched launches over the
+    matrices that share their input (q|k|v, o, gate|up, down); "single":
+    seven nf4_gemv launches; "one": one nf4_gemv_batched call (one launch)
+    over all seven."""
     xl = [xs[k] for k in LAYER_X]
+    if form == "single":
+        for W, x, y in zip(Ws, xl, ys):
+            nf4.nf4_gemv(W, x, y)
+    elif form == "one":
+        nf4.nf4_gemv_batched(Ws, xl, ys)
+    else:
+        for lo, hi in ((0, 3), (3, 4), (4, 6), (6, 7)):
+            nf4.nf4_gemv_batched(Ws[lo:hi], xl[lo:hi], ys[lo:hi])
 
+
+def capture_layer_steps(torch, nf4, store, layers, xs, ys, form):
+    """The decode GEMV of the stored layers `layers`, one after another, as
+    one HIP graph: the steps run back to back with no host dispatch between
+    them, as a serving loop's captured decode does."""
     def run():
-        if form == "single":
-            for W, x, y in zip(Ws, xl, ys):
-                nf4.nf4_gemv(W, x, y)
-        elif form == "one":
-            nf4.nf4_gemv_batched(Ws, xl, ys)
-        else:
-            for lo, hi in ((0, 3), (3, 4), (4, 6), (6, 7)):
-                nf4.nf4_gemv_batched(Ws[lo:hi], xl[lo:hi], ys[lo:hi])
+        for layer in layers:
+            layer_gemv_calls(nf4, store[layer], xs, ys, form)
 
     run()
     return capture_graph(torch, run)
 
 
 def layer_gemv_variants(torch, nf4, store, xs, ys, stream, nbytes, passes=40):
-    """The same layer GEMV issued three ways over the stored layers (median
-    of `passes` graph replays, a different layer each pass)."""
+    """The same layer GEMV issued three ways over the stored layers: one graph
+    of `passes` steps (a different layer each step) per form, timed with HIP
+    events around the replay; mean per step."""
     res = {}
     L = len(store)
+    layers = [(37 * k) % L for k in range(passes)]
     for form, what in (("single", "seven nf4_gemv launches"),
                        ("decode", "q|k|v, o, gate|up, down as four nf4_gemv_batched launches"),
                        ("one", "one nf4_gemv_batched call over the seven (one launch)")):
-        layers = [(37 * k) % L for k in range(passes)]
-        graphs = {l: capture_layer_gemv(torch, nf4, store[l], xs, ys, form) for l in sorted(set(layers))}
-        for l in layers[:3]:
-            graphs[l].replay()
+        graph = capture_layer_steps(torch, nf4, store, layers, xs, ys, form)
+        graph.replay()
         torch.cuda.synchronize()
         t = EventTimer(torch, stream)
-        for l in layers:
-            s = t.start()
-            graphs[l].replay()
-            t.stop(s)
+        s = t.start()
+        graph.replay()
+        t.stop(s)
         torch.cuda.synchronize()
-        med = t.median_us()
-        res[form] = {"what": what, "median_us": round(med, 2), "GBps": round(nbytes / (med * 1e-6) / 1e9, 1),
-                     "frac_hbm_peak": round(nbytes / (med * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}
-        del graphs
+        us = t.mean_us() / passes
+        res[form] = {"what": what, "us_per_step": round(us, 2), "GBps": round(nbytes / (us * 1e-6) / 1e9, 1),
+                     "frac_hbm_peak": round(nbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}
+        del graph
     return res
 
 
@@ -568,26 +573,25 @@ def build_stack_70b(torch, nf4, syn, dev, stream, EventTimer, layers=80):
 
 def leg_layer_gemv(torch, nf4, syn, dev, stream, EventTimer, layers=6, passes=12):
     """The headline step alone (for counter runs): a store of a few layers
-    (2.6 GB, far beyond the last-level cache) and the decode GEMV of one
-    layer per pass in the benchmark's launch form, a different layer each
-    pass."""
+    (2.6 GB, far beyond the last-level cache) and `passes` steps of the
+    decode GEMV in the benchmark's launch form as one graph, a different
+    layer each step."""
     store, _ = build_stack_70b(torch, nf4, syn, dev, stream, EventTimer, layers)
     shapes = [syn.C5_SHAPES[name] for name in syn.C5_ORDER]
     xs = layer_inputs(torch, dev)
     ys = [torch.empty((1, r), dtype=torch.bfloat16, device=dev) for r, _ in shapes]
-    graphs = [capture_layer_gemv(torch, nf4, Ws, xs, ys, "one") for Ws in store]
+    graph = capture_layer_steps(torch, nf4, store, [k % layers for k in range(passes)], xs, ys, "one")
     torch.cuda.synchronize()
     t = EventTimer(torch, stream)
-    for k in range(passes):
-        s = t.start()
-        graphs[k % len(store)].replay()
-        t.stop(s)
+    s = t.start()
+    graph.replay()
+    t.stop(s)
     torch.cuda.synchronize()
     nbytes = sum(step_bytes(r, c)["gemv"] for r, c in shapes)
-    med = t.median_us()
-    del graphs, store
-    return {"layer_gemv": {"layers": layers, "passes": passes, "median_us": round(med, 2),
-                           "GBps": round(nbytes / (med * 1e-6) / 1e9, 1)}}
+    us = t.mean_us() / passes
+    del graph, store
+    return {"layer_gemv": {"layers": layers, "passes": passes, "us_per_step": round(us, 2),
+                           "GBps": round(nbytes / (us * 1e-6) / 1e9, 1)}}
 
 
 def leg_stack_70b(torch, nf4, syn, dev, stream, EventTimer, layers=80, gemv_passes=20):
