@@ -415,10 +415,22 @@ def extra_legs(torch, nf4, syn, dev, stream, EventTimer, only=None):
     return res
 
 
-def _median_call(torch, stream, EventTimer, fn, reps=30, warm=5):
-    for _ in range(warm):
+def warm_up(torch, fn, calls=10, seconds=0.5):
+    """Runs fn at least `calls` times and for at least `seconds` of wall time
+    (the GPU's clock and power settle within a few hundred milliseconds of
+    sustained matrix-core load; timing starts after that)."""
+    t0 = time.perf_counter()
+    k = 0
+    while k < calls or time.perf_counter() - t0 < seconds:
         fn()
+        k += 1
+        if k % 10 == 0:
+            torch.cuda.synchronize()
     torch.cuda.synchronize()
+
+
+def _median_call(torch, stream, EventTimer, fn, reps=30, warm=5):
+    warm_up(torch, fn, calls=warm)
     t = EventTimer(torch, stream)
     for _ in range(reps):
         s = t.start()
@@ -466,7 +478,8 @@ def leg_qlora_backward(torch, nf4, dev, stream, EventTimer, g):
         "gemm_dx_TFLOPs": round(tf, 1),
         "gemm_dx_frac_mfma_bf16_peak": round(tf / MFMA_BF16_PEAK_TFLOPS, 4),
         "lora_grads_us": round(us_g, 1),
-        "timing": "medians of 30 calls after 5 warm-ups (dX call includes its LoRA prep; grads include both thin products)",
+        "timing": "medians of 30 calls after at least 5 warm-up calls and 0.5 s (dX call includes its LoRA prep; grads "
+                  "include both thin products)",
         "calibration_torch_matmul_bf16": {
             "what": "torch.matmul (hipBLASLt) dY . W on the dequantized bf16 weight, no LoRA",
             "us": round(us_lib, 1),
@@ -900,10 +913,8 @@ def leg_gemm(torch, nf4, dev, stream, EventTimer, g):
     B = (torch.randn((N, r), generator=g, device=dev) * 0.01).to(torch.bfloat16)
     Y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
     wsb = torch.empty(nf4.nf4_gemm_workspace(M, N, r), dtype=torch.uint8, device=dev)
-    # median of 50 event-timed calls after 10 warm-ups
-    for _ in range(10):
-        nf4.nf4_gemm(W, X, Y, A, B, 2.0, wsb)
-    torch.cuda.synchronize()
+    # 50 event-timed calls after at least 10 warm-up calls and 0.5 s
+    warm_up(torch, lambda: nf4.nf4_gemm(W, X, Y, A, B, 2.0, wsb))
     t = EventTimer(torch, stream)
     reps = 50
     for _ in range(reps):
@@ -926,16 +937,15 @@ def leg_gemm(torch, nf4, dev, stream, EventTimer, g):
         "TFLOPs": round(flops / (us_mean * 1e-6) / 1e12, 1),
         "TFLOPs_median": round(tf, 1),
         "frac_mfma_bf16_peak": round(flops / (us_mean * 1e-6) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
-        "timing": f"HIP events around each of {reps} calls (LoRA prep + GEMM) after 10 warm-ups; TFLOPs from the mean",
+        "timing": f"HIP events around each of {reps} calls (LoRA prep + GEMM) after at least 10 warm-up calls and "
+                  "0.5 s; TFLOPs from the mean",
         "no_lora": {"us": round(us_base, 1), "TFLOPs": round(fl_base / (us_base * 1e-6) / 1e12, 1),
                     "what": "nf4_gemm without adapters: the k_gemm launch alone, median of 50"},
     }
     # Calibration only (not part of the path): the vendor library's plain bf16
     # GEMM of the same shape on an already dequantized weight, no LoRA.
     Wd = nf4.nf4_dequantize(W, out_dtype=torch.bfloat16)
-    for _ in range(10):
-        torch.nn.functional.linear(X, Wd)
-    torch.cuda.synchronize()
+    warm_up(torch, lambda: torch.nn.functional.linear(X, Wd))
     t = EventTimer(torch, stream)
     for _ in range(reps):
         s = t.start()
