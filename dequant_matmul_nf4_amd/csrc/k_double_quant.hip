@@ -75,42 +75,82 @@ __device__ double digits_to_double(const uint32_t (&dig)[kDqDigits]) {
   return ldexp(static_cast<double>(mant), exp2);
 }
 
-// Adds the 256 threads' digit vectors held in vec and returns the total of
-// digit t in threads t < 12: first thread t < 192 adds digit t % 12 of rows
-// 16 c .. 16 c + 15 (c = t / 12), then 12 threads add the 16 chunk sums.
-// Each step issues all of its LDS reads before adding, so the sum costs two
-// LDS round trips rather than one per row.  Contains two barriers.
+// Both kernels run in workgroups of kThreads = 256 (small scale arrays: more
+// workgroups, so more of the chip pulls the few bytes) or 1024 threads (large
+// ones: fewer partial rows, so less for every quantizing workgroup to re-read).
+
+__device__ __forceinline__ unsigned long long wave_sum_u64(unsigned long long v) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, kWave);
+  return v;
+}
+
+// Adds the workgroup's digit vectors (acc in every thread) and returns the
+// total of digit t in threads t < 12.
+//  - 256 threads: the vectors go to LDS; thread t < 192 adds digit t % 12 of
+//    rows 16 c .. 16 c + 15 (c = t / 12), then 12 threads add the 16 chunk
+//    sums; each step issues all of its LDS reads before adding.
+//  - 1024 threads (too many rows for LDS): each wave adds its 64 lanes with
+//    cross-lane 64-bit adds, skipping a digit that is zero in all of its
+//    lanes (the scales of one weight touch two or three digits), and the 16
+//    wave sums of each digit are added through LDS.
+// Contains two barriers (256 threads) or one (1024).
 constexpr int kSumChunks = 16;  // rows per chunk and number of chunks (16 x 16 = 256)
 
-__device__ __forceinline__ unsigned long long block_digit_sum(unsigned long long (*vec)[kDqDigits + 1],
-                                                              unsigned long long (*tot)[kDqDigits]) {
+template <int kThreads>
+__device__ __forceinline__ unsigned long long block_digit_sum(const unsigned long long (&acc)[kDqDigits]) {
+  static_assert(kThreads == 256 || kThreads == 1024, "two workgroup sizes");
   const int t = threadIdx.x;
-  if (t < kSumChunks * kDqDigits) {
-    const int k = t % kDqDigits, c = t / kDqDigits;
-    unsigned long long v[kSumChunks];
-#pragma unroll
-    for (int i = 0; i < kSumChunks; ++i) v[i] = vec[kSumChunks * c + i][k];
-    unsigned long long sum = 0ull;
-#pragma unroll
-    for (int i = 0; i < kSumChunks; ++i) sum += v[i];
-    tot[c][k] = sum;
-  }
-  __syncthreads();
   unsigned long long sum = 0ull;
-  if (t < kDqDigits) {
-    unsigned long long v[kSumChunks];
+  if constexpr (kThreads == 256) {
+    __shared__ unsigned long long vec[256][kDqDigits + 1];  // +1: spreads the banks
+    __shared__ unsigned long long tot[kSumChunks][kDqDigits];
 #pragma unroll
-    for (int c = 0; c < kSumChunks; ++c) v[c] = tot[c][t];
+    for (int k = 0; k < kDqDigits; ++k) vec[t][k] = acc[k];
+    __syncthreads();
+    if (t < kSumChunks * kDqDigits) {
+      const int k = t % kDqDigits, c = t / kDqDigits;
+      unsigned long long v[kSumChunks];
 #pragma unroll
-    for (int c = 0; c < kSumChunks; ++c) sum += v[c];
+      for (int i = 0; i < kSumChunks; ++i) v[i] = vec[kSumChunks * c + i][k];
+      unsigned long long cs = 0ull;
+#pragma unroll
+      for (int i = 0; i < kSumChunks; ++i) cs += v[i];
+      tot[c][k] = cs;
+    }
+    __syncthreads();
+    if (t < kDqDigits) {
+      unsigned long long v[kSumChunks];
+#pragma unroll
+      for (int c = 0; c < kSumChunks; ++c) v[c] = tot[c][t];
+#pragma unroll
+      for (int c = 0; c < kSumChunks; ++c) sum += v[c];
+    }
+  } else {
+    constexpr int kWaves = kThreads / kWave;
+    __shared__ unsigned long long wsum[kWaves][kDqDigits];
+    const int lane = t & (kWave - 1), wave = t / kWave;
+#pragma unroll
+    for (int k = 0; k < kDqDigits; ++k) {
+      unsigned long long v = acc[k];
+      if (__any(v != 0ull)) v = wave_sum_u64(v);
+      if (lane == 0) wsum[wave][k] = v;
+    }
+    __syncthreads();
+    if (t < kDqDigits) {
+      unsigned long long v[kWaves];
+#pragma unroll
+      for (int w = 0; w < kWaves; ++w) v[w] = wsum[w][t];
+#pragma unroll
+      for (int w = 0; w < kWaves; ++w) sum += v[w];
+    }
   }
-  __syncthreads();
   return sum;
 }
 
-// Digit sums of the workgroup's scales: each thread adds kPerThread scales
-// (all loads issued first) into registers, then the 256 threads' digit
-// vectors are added through LDS into the workgroup's row.
+// Digit sums of the workgroup's scales: each thread adds its scales, read as
+// 16-byte vectors with kPartVec of them requested before any is used, into
+// registers; the workgroup's digit vectors are then added into its row.
 //
 // A contribution lands in digits d and d + 1.  The scales of one weight
 // mostly share one or two exponent ranges, so each thread also keeps a
@@ -119,89 +159,86 @@ __device__ __forceinline__ unsigned long long block_digit_sum(unsigned long long
 // (three selects); any other contribution takes the selects over all 12
 // digits.  The window is added into the 12 digits at the end, so the sum is
 // the same integer either way.  The window pays off from about 8 scales per
-// thread (measured: 8192^2 weights 15.4 -> 14.6 us; at 4 per thread the
-// final fold costs more than it saves), so the launcher picks it by size.
-constexpr int kPerThread = 4;
+// thread, so the launcher picks it by size.
+constexpr int kPartVec = 2;
 
-template <bool kWindow>
-__global__ __launch_bounds__(256) void k_dq_partial(const float* __restrict__ absmax, int64_t nb,
-                                                    unsigned long long* __restrict__ ws) {
-  __shared__ unsigned long long vec[256][kDqDigits + 1];  // +1: spreads the banks
-  __shared__ unsigned long long tot[kSumChunks][kDqDigits];
+template <int kThreads, bool kWindow>
+__global__ __launch_bounds__(kThreads) void k_dq_partial(const float* __restrict__ absmax, int64_t nb,
+                                                         unsigned long long* __restrict__ ws) {
   const int t = threadIdx.x;
   unsigned long long acc[kDqDigits];
 #pragma unroll
   for (int k = 0; k < kDqDigits; ++k) acc[k] = 0ull;
   int base = -1;  // the window's first digit (placed by the first nonzero scale)
   unsigned long long w0 = 0ull, w1 = 0ull, w2 = 0ull;
-  const int64_t stride = static_cast<int64_t>(gridDim.x) * blockDim.x;
-  for (int64_t i0 = static_cast<int64_t>(blockIdx.x) * blockDim.x + t; i0 < nb; i0 += kPerThread * stride) {
-    float v[kPerThread];
+  auto add = [&](float a) {
+    int d;
+    uint32_t lo, hi;
+    scale_to_digits(a, &d, &lo, &hi);
+    if (kWindow && base < 0 && (lo | hi) != 0u) base = d;
+    const int rel = d - base;  // a zero scale adds nothing wherever it goes
+    if (kWindow && (rel == 0 || rel == 1)) {
+      w0 += rel == 0 ? lo : 0u;
+      w1 += rel == 0 ? hi : lo;
+      w2 += rel == 0 ? 0u : hi;
+    } else {
+      // selects keep the indexing static
 #pragma unroll
-    for (int u = 0; u < kPerThread; ++u) {
+      for (int k = 0; k < kDqDigits; ++k)
+        acc[k] += static_cast<unsigned long long>((k == d ? lo : 0u)) + static_cast<unsigned long long>((k == d + 1 ? hi : 0u));
+    }
+  };
+  const int64_t n4 = nb >> 2;  // whole 16-byte vectors; absmax is 16-byte aligned
+  const float4* a4 = reinterpret_cast<const float4*>(absmax);
+  const int64_t stride = static_cast<int64_t>(gridDim.x) * kThreads;
+  for (int64_t i0 = static_cast<int64_t>(blockIdx.x) * kThreads + t; i0 < n4; i0 += kPartVec * stride) {
+    float4 v[kPartVec];
+#pragma unroll
+    for (int u = 0; u < kPartVec; ++u) {
       const int64_t i = i0 + u * stride;
-      v[u] = (i < nb) ? absmax[i] : 0.0f;
+      v[u] = (i < n4) ? a4[i] : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
     }
 #pragma unroll
-    for (int u = 0; u < kPerThread; ++u) {
-      int d;
-      uint32_t lo, hi;
-      scale_to_digits(v[u], &d, &lo, &hi);
-      if (kWindow && base < 0 && (lo | hi) != 0u) base = d;
-      const int rel = d - base;  // a zero scale adds nothing wherever it goes
-      if (kWindow && (rel == 0 || rel == 1)) {
-        w0 += rel == 0 ? lo : 0u;
-        w1 += rel == 0 ? hi : lo;
-        w2 += rel == 0 ? 0u : hi;
-      } else {
-        // selects keep the indexing static
-#pragma unroll
-        for (int k = 0; k < kDqDigits; ++k)
-          acc[k] += static_cast<unsigned long long>((k == d ? lo : 0u)) + static_cast<unsigned long long>((k == d + 1 ? hi : 0u));
-      }
+    for (int u = 0; u < kPartVec; ++u) {
+      add(v[u].x);
+      add(v[u].y);
+      add(v[u].z);
+      add(v[u].w);
     }
   }
+  // the last nb % 4 scales, in the first workgroup
+  if (blockIdx.x == 0 && t < static_cast<int>(nb & 3)) add(absmax[(n4 << 2) + t]);
   if constexpr (kWindow) {
 #pragma unroll
     for (int k = 0; k < kDqDigits; ++k)
       acc[k] += (k == base ? w0 : 0ull) + (k == base + 1 ? w1 : 0ull) + (k == base + 2 ? w2 : 0ull);
   }
-#pragma unroll
-  for (int k = 0; k < kDqDigits; ++k) vec[t][k] = acc[k];
-  __syncthreads();
-  const unsigned long long sum = block_digit_sum(vec, tot);
+  const unsigned long long sum = block_digit_sum<kThreads>(acc);
   if (t < kDqDigits) ws[blockIdx.x * kDqDigits + t] = sum;
 }
 
-// The mean from the partial rows (at most 256), in a workgroup of 256
-// threads: thread t loads row t, the rows are added per digit, and thread 0
-// propagates the carries, rounds and divides.  Returns the mean in every
-// thread.
+// The mean from the partial rows (at most 256, one per thread of the
+// workgroup at most): thread t < nparts loads row t, the rows are added per digit, and thread 0 propagates the carries,
+// rounds and divides.  Returns the mean in every thread.
+template <int kThreads>
 __device__ float dq_mean(const unsigned long long* __restrict__ ws, int nparts, int64_t nb) {
-  __shared__ unsigned long long vec[256][kDqDigits + 1];
-  __shared__ unsigned long long tot[kSumChunks][kDqDigits];
   __shared__ unsigned long long dsum[kDqDigits];
   __shared__ float mean_s;
   const int t = threadIdx.x;
-  {
-    unsigned long long row[kDqDigits];
-    if (t < nparts) {
-      const ulonglong2* p = reinterpret_cast<const ulonglong2*>(ws + t * kDqDigits);
+  unsigned long long row[kDqDigits];
+  if (t < nparts) {
+    const ulonglong2* p = reinterpret_cast<const ulonglong2*>(ws + t * kDqDigits);
 #pragma unroll
-      for (int k = 0; k < kDqDigits / 2; ++k) {
-        const ulonglong2 v = p[k];
-        row[2 * k] = v.x;
-        row[2 * k + 1] = v.y;
-      }
-    } else {
-#pragma unroll
-      for (int k = 0; k < kDqDigits; ++k) row[k] = 0ull;
+    for (int k = 0; k < kDqDigits / 2; ++k) {
+      const ulonglong2 v = p[k];
+      row[2 * k] = v.x;
+      row[2 * k + 1] = v.y;
     }
+  } else {
 #pragma unroll
-    for (int k = 0; k < kDqDigits; ++k) vec[t][k] = row[k];
+    for (int k = 0; k < kDqDigits; ++k) row[k] = 0ull;
   }
-  __syncthreads();
-  const unsigned long long s = block_digit_sum(vec, tot);
+  const unsigned long long s = block_digit_sum<kThreads>(row);
   if (t < kDqDigits) dsum[t] = s;
   __syncthreads();
   if (t == 0) {
@@ -234,16 +271,20 @@ __device__ __forceinline__ uint32_t e4m3_rne(float t) {
   return sign | ((((r >> 23) - 127u + 7u) << 3) | ((r >> 20) & 7u));
 }
 
-template <bool kF8>
-__global__ __launch_bounds__(256) void k_dq_quant(const float* __restrict__ absmax, int64_t nb,
-                                                  const unsigned long long* __restrict__ ws, int nparts,
-                                                  float* __restrict__ mean_out, int8_t* __restrict__ q,
-                                                  float* __restrict__ absmax2) {
-  const int lane = threadIdx.x & 63;
+// One wave per group of 256 scales; a wave's first kQuantPre groups are
+// requested before the mean is known, so their loads overlap the mean.
+constexpr int kQuantPre = 4;
+
+template <int kThreads, bool kF8>
+__global__ __launch_bounds__(kThreads) void k_dq_quant(const float* __restrict__ absmax, int64_t nb,
+                                                         const unsigned long long* __restrict__ ws, int nparts,
+                                                         float* __restrict__ mean_out, int8_t* __restrict__ q,
+                                                         float* __restrict__ absmax2) {
+  constexpr int kWaves = kThreads / kWave;
+  const int lane = threadIdx.x & (kWave - 1);
   const int64_t ngroups = (nb + 255) >> 8;
-  const int64_t wave = (static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x) >> 6;
-  const int64_t nwaves = (static_cast<int64_t>(gridDim.x) * blockDim.x) >> 6;
-  // the scales of the wave's first group are loaded before the mean is known
+  const int64_t wave = static_cast<int64_t>(blockIdx.x) * kWaves + threadIdx.x / kWave;
+  const int64_t nwaves = static_cast<int64_t>(gridDim.x) * kWaves;
   auto load4 = [&](int64_t g, float (&a)[4]) {
     const int64_t i0 = g * 256 + lane * 4;
     if (i0 + 4 <= nb) {
@@ -254,12 +295,7 @@ __global__ __launch_bounds__(256) void k_dq_quant(const float* __restrict__ absm
       for (int j = 0; j < 4; ++j) a[j] = (i0 + j < nb) ? absmax[i0 + j] : 0.0f;
     }
   };
-  float a[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-  if (wave < ngroups) load4(wave, a);
-  const float mu = dq_mean(ws, nparts, nb);
-  if (blockIdx.x == 0 && threadIdx.x == 0) *mean_out = mu;
-  for (int64_t g = wave; g < ngroups; g += nwaves) {
-    if (g != wave) load4(g, a);
+  auto quant_group = [&](int64_t g, const float (&a)[4], float mu) {
     const int64_t i0 = g * 256 + lane * 4;
     float c[4];
 #pragma unroll
@@ -291,6 +327,24 @@ __global__ __launch_bounds__(256) void k_dq_quant(const float* __restrict__ absm
         if (i0 + j < nb) q[i0 + j] = static_cast<int8_t>(word >> (8 * j));
     }
     if (lane == 0) absmax2[g] = s;
+  };
+  float a[kQuantPre][4];
+#pragma unroll
+  for (int p = 0; p < kQuantPre; ++p) {
+    const int64_t g = wave + p * nwaves;
+    if (g < ngroups) load4(g, a[p]);
+  }
+  const float mu = dq_mean<kThreads>(ws, nparts, nb);
+  if (blockIdx.x == 0 && threadIdx.x == 0) *mean_out = mu;
+#pragma unroll
+  for (int p = 0; p < kQuantPre; ++p) {
+    const int64_t g = wave + p * nwaves;
+    if (g < ngroups) quant_group(g, a[p], mu);
+  }
+  for (int64_t g = wave + kQuantPre * nwaves; g < ngroups; g += nwaves) {
+    float b[4];
+    load4(g, b);
+    quant_group(g, b, mu);
   }
 }
 
@@ -317,19 +371,39 @@ hipError_t dq_scratch(unsigned long long** out) {
   return hipSuccess;
 }
 
+namespace {
+
+template <int kThreads>
+void launch_dq(const float* absmax, int64_t nb, int8_t* q, float* absmax2, float* mean, unsigned long long* ws,
+               int f8, int per_thread, int max_qgrid, hipStream_t s) {
+  constexpr int kWaves = kThreads / kWave;
+  // at least per_thread scales per summing thread, at most kDqMaxGroups partial rows
+  int64_t want = (nb + kThreads * per_thread - 1) / (kThreads * per_thread);
+  const int grid = static_cast<int>(want < kDqMaxGroups ? want : kDqMaxGroups);
+  if (nb >= static_cast<int64_t>(grid) * kThreads * 8)
+    hipLaunchKernelGGL((k_dq_partial<kThreads, true>), dim3(grid), dim3(kThreads), 0, s, absmax, nb, ws);
+  else
+    hipLaunchKernelGGL((k_dq_partial<kThreads, false>), dim3(grid), dim3(kThreads), 0, s, absmax, nb, ws);
+  // one group per wave, up to max_qgrid workgroups (each re-reads the partial rows)
+  const int64_t groups = (nb + 255) >> 8;
+  want = (groups + kWaves - 1) / kWaves;
+  const int qgrid = static_cast<int>(want < max_qgrid ? want : max_qgrid);
+  if (f8)
+    hipLaunchKernelGGL((k_dq_quant<kThreads, true>), dim3(qgrid), dim3(kThreads), 0, s, absmax, nb, ws, grid, mean, q,
+                       absmax2);
+  else
+    hipLaunchKernelGGL((k_dq_quant<kThreads, false>), dim3(qgrid), dim3(kThreads), 0, s, absmax, nb, ws, grid, mean, q,
+                       absmax2);
+}
+
+}  // namespace
+
 hipError_t launch_double_quant(const float* absmax, int64_t nb, int8_t* q, float* absmax2,
                                float* mean, unsigned long long* ws, int f8, hipStream_t s) {
-  int64_t want = (nb + 256 * kPerThread - 1) / (256 * kPerThread);
-  int grid = static_cast<int>(want < kDqMaxGroups ? want : kDqMaxGroups);
-  if (nb >= static_cast<int64_t>(grid) * 256 * 8)
-    hipLaunchKernelGGL(k_dq_partial<true>, dim3(grid), dim3(256), 0, s, absmax, nb, ws);
+  if (nb >= (int64_t{1} << 21))
+    launch_dq<1024>(absmax, nb, q, absmax2, mean, ws, f8, 8, 256, s);
   else
-    hipLaunchKernelGGL(k_dq_partial<false>, dim3(grid), dim3(256), 0, s, absmax, nb, ws);
-  const int64_t groups = (nb + 255) >> 8;
-  want = (groups + 3) / 4;  // 4 waves per workgroup
-  const int qgrid = static_cast<int>(want < 1024 ? want : 1024);
-  if (f8) hipLaunchKernelGGL(k_dq_quant<true>, dim3(qgrid), dim3(256), 0, s, absmax, nb, ws, grid, mean, q, absmax2);
-  else hipLaunchKernelGGL(k_dq_quant<false>, dim3(qgrid), dim3(256), 0, s, absmax, nb, ws, grid, mean, q, absmax2);
+    launch_dq<256>(absmax, nb, q, absmax2, mean, ws, f8, 4, 1024, s);
   return hipGetLastError();
 }
 
