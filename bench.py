@@ -17,9 +17,11 @@ Extra legs (not part of `value`): the memory-system calibration (torch copy
 and sum, and a plain streaming-read kernel of our own), the 1024^2 round trip
 (microseconds), the 4096^2 quantize + double quant + GEMV composite and the
 GEMV alone over a pool of 4096^2 weights, the Llama-8B MLP GEMVs at m = 1, 4,
-16, the dequant-into-LDS GEMM of the QLoRA forward (X [4096, 4096] x NF4 W
-[14336, 4096] + LoRA r = 16, the GEMM roofline), its backward, the LoRA
-merge, and the double quantization with both second-level types.
+16, the dequantize-and-multiply matrix-core GEMM of the QLoRA forward
+(X [4096, 4096] x NF4 W [14336, 4096] + LoRA r = 16, the GEMM roofline), its
+backward, the LoRA merge, and the double quantization with both second-level
+types.  `--only layer-forms` compares the layer's decode GEMV as seven
+launches, four batched launches and one batched launch.
 `cpu_baseline` times the CPU oracle on a bounded sample of the same workload.
 """
 
@@ -243,7 +245,6 @@ def main():
     achieved = step_bytes_layer / (mean_us * 1e-6) / 1e9
     del warm, timed
     read_gbs = None
-    out_variants = layer_gemv_variants(torch, nf4, store, xs, ys, stream, step_bytes_layer)
 
     out = {
         "metric": METRIC,
@@ -284,7 +285,6 @@ def main():
         },
     }
     out["stack_70b"] = stack
-    out["gemv_layer_70b_launch_forms"] = out_variants
 
     if not args.no_extra:
         extra = extra_legs(torch, nf4, syn, dev, stream, EventTimer)
@@ -383,7 +383,7 @@ def layer_gemv_variants(torch, nf4, store, xs, ys, stream, nbytes, passes=40):
     return res
 
 
-LEGS = ("hbm", "c1", "c2-step", "gemv-decode", "gemv-mlp", "gemv-70b", "stack-70b", "layer-gemv", "gemm",
+LEGS = ("hbm", "c1", "c2-step", "gemv-decode", "gemv-mlp", "gemv-70b", "stack-70b", "layer-gemv", "layer-forms", "gemm",
         "qlora-backward", "lora-merge")
 
 
@@ -404,6 +404,8 @@ def extra_legs(torch, nf4, syn, dev, stream, EventTimer, only=None):
         res.update(legs_gemv_pools(torch, nf4, dev, stream, EventTimer, g, only))
     if only == "stack-70b":
         res.update(leg_stack_70b(torch, nf4, syn, dev, stream, EventTimer))
+    if only == "layer-forms":
+        res.update(leg_layer_forms(torch, nf4, syn, dev, stream, EventTimer))
     if only == "layer-gemv":
         res.update(leg_layer_gemv(torch, nf4, syn, dev, stream, EventTimer))
     if only in (None, "gemm"):
@@ -429,8 +431,8 @@ def warm_up(torch, fn, calls=10, seconds=0.5):
     torch.cuda.synchronize()
 
 
-def _median_call(torch, stream, EventTimer, fn, reps=30, warm=5):
-    warm_up(torch, fn, calls=warm)
+def _median_call(torch, stream, EventTimer, fn, reps=30, warm=5, warm_s=0.0):
+    warm_up(torch, fn, calls=warm, seconds=warm_s)
     t = EventTimer(torch, stream)
     for _ in range(reps):
         s = t.start()
@@ -464,13 +466,13 @@ def leg_qlora_backward(torch, nf4, dev, stream, EventTimer, g):
     dB = torch.empty((N, r), dtype=torch.float32, device=dev)
     ws_dx = torch.empty(max(nf4.nf4_gemm_dx_workspace(M, N, r), 1), dtype=torch.uint8, device=dev)
     ws_g = torch.empty(max(nf4.nf4_lora_grads_workspace(M, N, K, r), 1), dtype=torch.uint8, device=dev)
-    us_dx = _median_call(torch, stream, EventTimer, lambda: nf4.nf4_gemm_dx(W, dY, dX, A, B, s_l, ws_dx))
+    us_dx = _median_call(torch, stream, EventTimer, lambda: nf4.nf4_gemm_dx(W, dY, dX, A, B, s_l, ws_dx), warm_s=0.5)
     us_g = _median_call(torch, stream, EventTimer,
                         lambda: nf4.nf4_lora_grads(X, dY, A, B, s_l, da=dA, db=dB, workspace=ws_g))
     fl_dx = 2.0 * M * N * K + 2.0 * M * N * r + 2.0 * M * r * K
     tf = fl_dx / (us_dx * 1e-6) / 1e12
     Wd = nf4.nf4_dequantize(W, out_dtype=torch.bfloat16)
-    us_lib = _median_call(torch, stream, EventTimer, lambda: torch.matmul(dY, Wd))
+    us_lib = _median_call(torch, stream, EventTimer, lambda: torch.matmul(dY, Wd), warm_s=0.5)
     del Wd
     return {"qlora_backward": {
         "workload": "dY 4096x14336 bf16, NF4(DQ) W 14336x4096, LoRA r=16 alpha=32: dX, dA, dB",
@@ -605,6 +607,21 @@ def leg_layer_gemv(torch, nf4, syn, dev, stream, EventTimer, layers=6, passes=12
     del graph, store
     return {"layer_gemv": {"layers": layers, "passes": passes, "us_per_step": round(us, 2),
                            "GBps": round(nbytes / (us * 1e-6) / 1e9, 1)}}
+
+
+def leg_layer_forms(torch, nf4, syn, dev, stream, EventTimer, layers=6):
+    """The layer's decode GEMV issued three ways (seven single launches, the
+    decode order's four batched launches, one batched launch) over a store of
+    a few layers, a different layer each step.  Kept out of the default run,
+    whose kernel trace then holds the one-launch form alone."""
+    store, _ = build_stack_70b(torch, nf4, syn, dev, stream, EventTimer, layers)
+    shapes = [syn.C5_SHAPES[name] for name in syn.C5_ORDER]
+    xs = layer_inputs(torch, dev)
+    ys = [torch.empty((1, r), dtype=torch.bfloat16, device=dev) for r, _ in shapes]
+    nbytes = sum(step_bytes(r, c)["gemv"] for r, c in shapes)
+    res = layer_gemv_variants(torch, nf4, store, xs, ys, stream, nbytes)
+    del store
+    return {"gemv_layer_70b_launch_forms": {"layers": layers, **res}}
 
 
 def leg_stack_70b(torch, nf4, syn, dev, stream, EventTimer, layers=80, gemv_passes=20):
@@ -927,7 +944,7 @@ def leg_gemm(torch, nf4, dev, stream, EventTimer, g):
     tf = flops / (us * 1e-6) / 1e12
     us_mean = t.mean_us()
     # the base product alone: one k_gemm launch per call
-    us_base = _median_call(torch, stream, EventTimer, lambda: nf4.nf4_gemm(W, X, Y), reps=reps, warm=5)
+    us_base = _median_call(torch, stream, EventTimer, lambda: nf4.nf4_gemm(W, X, Y), reps=reps, warm=5, warm_s=0.5)
     fl_base = 2.0 * M * N * K
     res["gemm_qlora_forward"] = {
         "workload": "X 4096x4096 bf16 . NF4(DQ) W 14336x4096^T + LoRA r=16 alpha=32",
