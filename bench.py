@@ -302,6 +302,12 @@ def main():
                 "flops_per_launch": gemm["flops"],
                 "avg_launch_us": gemm["us_mean"],
             }
+            cal = gemm.get("calibration_torch_linear_bf16", {}).get("TFLOPs")
+            if cal:
+                # the vendor library's plain bf16 GEMM of the same shape: the
+                # measured-achievable matrix-core rate of this GPU here
+                out["roofline_gemm"]["measured_bf16_gemm_TFLOPs"] = cal
+                out["roofline_gemm"]["frac_of_measured_bf16_gemm"] = round(gemm["TFLOPs"] / cal, 4)
         out.update(extra)
     if read_gbs:
         out["roofline"]["measured_read_GBps"] = read_gbs
