@@ -74,13 +74,17 @@ def sources_digest(names) -> str:
     return h.hexdigest()
 
 
-def measured_traffic():
+GEMM_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "k_gemm_qlora_forward_traffic.json")
+GEMM_SOURCES = ["k_gemm.hip", "gemm_tiles.h", "nf4_device.h", "nf4_internal.h"]
+
+
+def measured_traffic(path=TRAFFIC_FILE, sources=GEMV_SOURCES):
     try:
-        with open(TRAFFIC_FILE) as f:
+        with open(path) as f:
             rec = json.load(f)
     except (OSError, ValueError):
         return None
-    if rec.get("sources_sha256") != sources_digest(GEMV_SOURCES):
+    if rec.get("sources_sha256") != sources_digest(sources):
         return None
     return rec.get("traffic_bytes_per_launch")
 
@@ -298,7 +302,7 @@ def main():
                 "peak": MFMA_BF16_PEAK_TFLOPS,
                 "unit": "TFLOP/s",
                 "frac": round(gemm["TFLOPs"] / MFMA_BF16_PEAK_TFLOPS, 4),
-                "traffic": None,
+                "traffic": measured_traffic(GEMM_TRAFFIC_FILE, GEMM_SOURCES),
                 "flops_per_launch": gemm["flops"],
                 "avg_launch_us": gemm["us_mean"],
             }
