@@ -660,10 +660,11 @@ def leg_stack_70b(torch, nf4, syn, dev, stream, EventTimer, layers=80, gemv_pass
 
 
 def stream_read_gbps(torch, dev, stream, EventTimer, nbytes=4 << 30):
-    """The best of a few launch shapes of the plain streaming-read kernel
-    (libnf4_calib.so, built beside the library) over a 4 GiB buffer: what
-    the memory system gives a read-only kernel here.  Returns GB/s and the
-    shape, or None when the calibration library is missing."""
+    """The best of a few launch shapes, with plain or non-temporal loads, of
+    the streaming-read kernel (libnf4_calib.so, built beside the library)
+    over a 4 GiB buffer: what the memory system gives a read-only kernel
+    here.  Returns GB/s and the shape, or None when the calibration library
+    is missing."""
     import ctypes
     path = os.path.join(ROOT, "dequant_matmul_nf4_amd", "libnf4_calib.so")
     if not os.path.exists(path):
@@ -671,26 +672,27 @@ def stream_read_gbps(torch, dev, stream, EventTimer, nbytes=4 << 30):
     L = ctypes.CDLL(path)
     f = L.nf4_calib_stream_read
     f.restype = ctypes.c_int
-    f.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_int, ctypes.c_uint32, ctypes.c_void_p,
-                  ctypes.c_void_p]
+    f.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_uint32,
+                  ctypes.c_void_p, ctypes.c_void_p]
     buf = torch.empty(nbytes // 4, dtype=torch.int32, device=dev).fill_(0x01010101)
     cus = torch.cuda.get_device_properties(dev).multi_processor_count
     out = torch.zeros(16 * cus, dtype=torch.int32, device=dev)
     best = None
     for per_cu in (2, 4, 8, 16):
         for unroll in (4, 8):
-            grid = per_cu * cus
+            for nt in (0, 1):
+                grid = per_cu * cus
 
-            def call():
-                rc = f(buf.data_ptr(), nbytes, grid, unroll, 0x5A5A5A5A, out.data_ptr(), stream.cuda_stream)
-                if rc != 0:
-                    raise RuntimeError(f"nf4_calib_stream_read failed: {rc}")
+                def call():
+                    rc = f(buf.data_ptr(), nbytes, grid, unroll, nt, 0x5A5A5A5A, out.data_ptr(), stream.cuda_stream)
+                    if rc != 0:
+                        raise RuntimeError(f"nf4_calib_stream_read failed: {rc}")
 
-            us = _median_call(torch, stream, EventTimer, call, reps=10, warm=2)
-            gbs = nbytes / (us * 1e-6) / 1e9
-            if best is None or gbs > best["GBps"]:
-                best = {"GBps": round(gbs, 1), "us": round(us, 1), "workgroups": grid, "threads": 512,
-                        "loads_in_flight_per_lane": unroll}
+                us = _median_call(torch, stream, EventTimer, call, reps=10, warm=2)
+                gbs = nbytes / (us * 1e-6) / 1e9
+                if best is None or gbs > best["GBps"]:
+                    best = {"GBps": round(gbs, 1), "us": round(us, 1), "workgroups": grid, "threads": 512,
+                            "loads_in_flight_per_lane": unroll, "nontemporal": bool(nt)}
     del buf, out
     return best
 
