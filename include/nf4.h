@@ -217,8 +217,8 @@ int nf4_gemv(const nf4_weight* w, const void* x, int64_t m, void* y, int y_dtype
  *           with cols % 64 == 0 and cols <= 65536, all with the same scale
  *           form (plain, int8 or float8 second level) and code book.
  *   xs    : [host] array of count device pointers, xs[i] bf16 [1][ws[i].cols],
- *           16-byte aligned.  Weights whose x is the same pointer share one
- *           staged copy of it.
+ *           16-byte aligned.  Weights whose x is the same pointer (and
+ *           width) are streamed as one group of rows.
  *   ys    : [host] array of count device pointers, ys[i] [1][ws[i].rows] of
  *           y_dtype (NF4_F32 or NF4_BF16), 16-byte aligned, not overlapping
  *           each other or any input.
@@ -234,8 +234,10 @@ int nf4_gemv_batched(const nf4_weight* ws, int32_t count, const void* const* xs,
  * up to 64) bf16 values. */
 size_t nf4_gemm_workspace(int64_t m, int64_t rows, int32_t r);
 
-/* Dequantize-into-LDS bf16 matrix-core GEMM for prefill and training, with an
- * optional fused LoRA term (tutorial page "QLoRA: Fine-Tuning a 4-bit Model"
+/* Dequantize-and-multiply bf16 matrix-core GEMM for prefill and training
+ * (the codes are expanded to bf16 straight into the matrix-core operands; no
+ * dequantized copy of W is written to memory), with an optional fused LoRA
+ * term (tutorial page "QLoRA: Fine-Tuning a 4-bit Model"
  * and tool page "Fine-tuning with adapters on a 4-bit model": a frozen 4-bit
  * base plus low-rank adapters whose output is multiplied by a scale factor):
  *   y = x . deq(W)^T + lora_scale . (x . A^T) . B^T
