@@ -21,23 +21,25 @@ from tests.gpu_common import check_full_product, need_gpu, say, to_dev
 pytestmark = pytest.mark.gpu
 
 
-def _oracle_f32(w: np.ndarray, dq: str) -> np.ndarray:
-    p, a = oracle.quantize(w.reshape(-1))
+def _oracle_f32(w: np.ndarray, dq: str, qt: str = "nf4") -> np.ndarray:
+    p, a = oracle.quantize(w.reshape(-1), kind=qt)
     if dq == "plain":
-        return oracle.dequantize(p, w.size, absmax=a, out="f32").reshape(w.shape)
+        return oracle.dequantize(p, w.size, absmax=a, out="f32", kind=qt).reshape(w.shape)
     if dq == "fp8":
         q, s2, mean = oracle.double_quant_f8(a)
-        return oracle.dequantize(p, w.size, qabsmax=q, absmax2=s2, mean=mean, out="f32", dq_kind="fp8").reshape(w.shape)
+        return oracle.dequantize(p, w.size, qabsmax=q, absmax2=s2, mean=mean, out="f32", dq_kind="fp8",
+                                 kind=qt).reshape(w.shape)
     q, s2, mean = oracle.double_quant(a)
-    return oracle.dequantize(p, w.size, qabsmax=q, absmax2=s2, mean=mean, out="f32").reshape(w.shape)
+    return oracle.dequantize(p, w.size, qabsmax=q, absmax2=s2, mean=mean, out="f32", kind=qt).reshape(w.shape)
 
 
-def _run(shapes, x_of, dq="int8", y_dtype="bf16", seed=0):
-    """Quantizes one weight per shape, multiplies them in one batched call
-    (weight i takes x number x_of[i]) and checks every output."""
+def _run(shapes, x_of, dq="int8", y_dtype="bf16", seed=0, qt="nf4"):
+    """Quantizes one weight per shape (code book qt), multiplies them in one
+    batched call (weight i takes x number x_of[i]) and checks every output."""
     torch = need_gpu()
     ws_np = [syn.normal_f32(sh, 0.02, 900 + seed + 17 * i) for i, sh in enumerate(shapes)]
-    Ws = [nf4.quantize_weight(to_dev(w), double_quant=dq != "plain", dq_type="fp8" if dq == "fp8" else "int8")
+    Ws = [nf4.quantize_weight(to_dev(w), double_quant=dq != "plain", dq_type="fp8" if dq == "fp8" else "int8",
+                              quant_type=qt)
           for w in ws_np]
     cols_of_x = {}
     for i, sh in enumerate(shapes):
@@ -54,7 +56,7 @@ def _run(shapes, x_of, dq="int8", y_dtype="bf16", seed=0):
         assert torch.equal(y, y1), f"weight {i}: batched and single launches differ"
         assert torch.equal(y, y2), f"weight {i}: not deterministic"
     for i, (w, y) in enumerate(zip(ws_np, ys)):
-        wdeq = _oracle_f32(w, dq)
+        wdeq = _oracle_f32(w, dq, qt)
         xf = syn.bf16_to_f32(xs_b[x_of[i]])
         ref = oracle.matmul_ref(xf, wdeq)
         sabs = np.abs(xf).astype(np.float64) @ np.abs(wdeq).astype(np.float64).T
@@ -76,6 +78,15 @@ def test_batched_shared_and_distinct_x_mixed_widths():
 def test_batched_scale_forms_and_outputs(dq, y_dtype):
     say("gemv batched:", dq, y_dtype)
     _run([(1000, 1024), (257, 2048), (33, 1024)], [0, 1, 0], dq=dq, y_dtype=y_dtype, seed=5)
+
+
+@pytest.mark.parametrize("dq", ["plain", "int8"])
+def test_batched_fp4_code_book(dq):
+    """Weights quantized with the FP4 code book (bitsandbytes tool page,
+    "What it is", read as the E2M1 levels): the batched launch takes the code
+    book from the weights, which must all share it."""
+    say("gemv batched: fp4", dq)
+    _run([(700, 2048), (129, 1024), (64, 2048)], [0, 1, 0], dq=dq, seed=21, qt="fp4")
 
 
 def test_batched_single_weight_and_eight_weights():
