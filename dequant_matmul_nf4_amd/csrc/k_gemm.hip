@@ -14,6 +14,12 @@
 // fragments and level lookups) are issued before the MFMAs of k step s, so
 // their latency is spent while the matrix cores run.
 //
+// Work units: the persistent workgroups take 256-row tiles round by round.
+// When the last round would leave compute units idle (its tiles number at
+// most half the workgroups), each of its tiles is cut into two 128-row halves
+// (MI = 4) taken by two workgroups: a half costs more than half a tile (its
+// weight tile is expanded for half as many rows) but the round ends sooner.
+//
 // Operands:
 //  - x: the (32 MI) x 64 tile is staged in LDS (two stages of 128-byte rows) by
 //    direct global-to-LDS loads (global_load_lds_dwordx4: each wave
@@ -73,6 +79,8 @@ struct GemmArgs {
   const uint16_t* u;     // LoRA columns of x: [m][kl] (s T hi | s T lo | 0), or null
   const uint16_t* bx;    // LoRA columns of W: [rows][kl] (B | B | 0)
   int kl;                // extra K (multiple of 64), 0 without LoRA
+  int64_t whole;         // work units 0 .. whole - 1: tile u, all 256 rows
+  int64_t units;         // units whole .. units - 1: tile whole + (u - whole) / 2, half (u - whole) % 2
   Codebook cb;
 };
 
@@ -147,14 +155,14 @@ __device__ __forceinline__ bf16x8 expand_frag(const float2 (&l)[4], float sa) {
 }
 
 // Spreads the work issued next to the MFMAs of one 16-wide k step between
-// them: per MFMA three VALU operations and one LDS access.
-template <int N>
+// them: per MFMA V VALU operations and L LDS accesses.
+template <int N, int V, int L>
 __device__ __forceinline__ void mfma_interleave() {
 #pragma unroll
   for (int i = 0; i < N; ++i) {
     __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
-    __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);  // VALU
-    __builtin_amdgcn_sched_group_barrier(0x080, 1, 0);  // LDS read or write
+    __builtin_amdgcn_sched_group_barrier(0x002, V, 0);  // VALU
+    __builtin_amdgcn_sched_group_barrier(0x080, L, 0);  // LDS read or write
   }
 }
 
@@ -168,6 +176,121 @@ __device__ __forceinline__ void block_scales(const WRegs& wr, float mean, float 
     if constexpr (kDQ) sa[j] = (code_ratio(wr.q[j], kF8 ? 1 : 0) * wr.s2[j]) + mean;  // a_hat, three roundings
     else sa[j] = wr.am[j];
   }
+}
+
+// One work unit: the (32 MI) x 256 tile of y at rows m0.., columns n0..
+// (MI = 8: a whole tile; MI = 4: half of one).  Every LDS stage read here is
+// read before a barrier that all waves pass before the unit returns.
+template <int MI, bool kDQ, bool kF8>
+__device__ __forceinline__ void gemm_unit(const GemmArgs& a, int64_t m0, int64_t n0, char* xs0, char* xs1,
+                                          const char* tabc, uint32_t slot, float mean, int wave, int lane) {
+  // Per MFMA: the expansion and lookups of the next 16-wide k step are the
+  // same for both tile heights, spread over 2 MI MFMAs.
+  constexpr int kV = MI == 8 ? 3 : 6, kL = MI == 8 ? 1 : 2;
+  const int64_t nk = a.cols / kBK;
+  const gt::ActPtrs<MI> xp = gt::make_act_ptrs<MI, 32 * MI>(a.x, a.cols, a.m, m0, wave, lane);
+  WPtrs wp;
+  int64_t nrow[2];
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int64_t n = n0 + wave * 64 + j * 32 + (lane & 31);
+    nrow[j] = n < a.rows ? n : a.rows - 1;  // rows past the end: never stored
+    wp.c[j] = a.packed + nrow[j] * (a.cols / 2) + (lane >> 5) * 16;
+    wp.blk[j] = nrow[j] * (a.cols / 64);
+  }
+
+  floatx16 acc[MI][2];
+  gt::zero_acc(acc);
+
+  // K step k: MFMAs from x stage k % 2 and the codes of step k (wc), in
+  // four 16-wide k steps s.  Software pipeline: while the MFMAs of s run,
+  // the wave expands the B fragments of s + 1 (looked up one k step
+  // earlier) and issues the LDS reads of s + 2; during s = 3 it expands
+  // the next step's s = 0, so that after the barrier the MFMAs can start at
+  // once.  The global loads of step k + 1 (clamped on the last step: x to
+  // the other stage, codes to registers) go out at the top of step k.
+  WRegs wc, wnx;
+  gt::dma_act(xp, 0, xs0, wave);
+  load_w<kDQ>(wc, wp, a, 0);
+  float sa[2];
+  bf16x8 bf[2][2];
+  Lookups lk[3];
+  bf16x8 af[3][MI];
+  const uint32_t sw = ((lane & 31) >> 1) & 7, h4 = (lane >> 5) * 4;
+  block_scales<kDQ, kF8>(wc, mean, sa);
+  lookup_step<kCopies>(lk[0], wc.w, 0, tabc, slot);
+  bf[0][0] = expand_frag(lk[0].l[0], sa[0]);
+  bf[0][1] = expand_frag(lk[0].l[1], sa[1]);
+  gt::wait_vmem();
+  __syncthreads();
+  for (int64_t ks = 0; ks < nk; ++ks) {
+    const int64_t kn = ks + 1 < nk ? ks + 1 : ks;
+    gt::dma_act(xp, kn, (ks & 1) ? xs0 : xs1, wave);  // the other stage was last read before the previous barrier
+    load_w<kDQ>(wnx, wp, a, kn);
+    __builtin_amdgcn_sched_barrier(0);
+    const char* xa = ((ks & 1) ? xs1 : xs0) + (lane & 31) * gt::kActRowBytes;
+    gt::read_act(xa, 0, sw, h4, af[0]);
+    gt::read_act(xa, 1, sw, h4, af[1]);
+    lookup_step<kCopies>(lk[1], wc.w, 1, tabc, slot);
+    __builtin_amdgcn_sched_barrier(0);
+    // s = 0
+    gt::mfma16(af[0], bf[0], acc);
+    bf[1][0] = expand_frag(lk[1].l[0], sa[0]);
+    bf[1][1] = expand_frag(lk[1].l[1], sa[1]);
+    gt::read_act(xa, 2, sw, h4, af[2]);
+    lookup_step<kCopies>(lk[2], wc.w, 2, tabc, slot);
+    mfma_interleave<2 * MI, kV, kL>();
+    __builtin_amdgcn_sched_barrier(0);
+    // s = 1
+    gt::mfma16(af[1], bf[1], acc);
+    bf[0][0] = expand_frag(lk[2].l[0], sa[0]);
+    bf[0][1] = expand_frag(lk[2].l[1], sa[1]);
+    gt::read_act(xa, 3, sw, h4, af[0]);
+    lookup_step<kCopies>(lk[0], wc.w, 3, tabc, slot);
+    mfma_interleave<2 * MI, kV, kL>();
+    __builtin_amdgcn_sched_barrier(0);
+    // s = 2
+    gt::mfma16(af[2], bf[0], acc);
+    bf[1][0] = expand_frag(lk[0].l[0], sa[0]);
+    bf[1][1] = expand_frag(lk[0].l[1], sa[1]);
+    mfma_interleave<2 * MI, kV, kL>();
+    __builtin_amdgcn_sched_barrier(0);
+    // s = 3, with the next step's s = 0 expansion
+    gt::mfma16(af[0], bf[1], acc);
+    block_scales<kDQ, kF8>(wnx, mean, sa);
+    lookup_step<kCopies>(lk[1], wnx.w, 0, tabc, slot);
+    bf[0][0] = expand_frag(lk[1].l[0], sa[0]);
+    bf[0][1] = expand_frag(lk[1].l[1], sa[1]);
+    mfma_interleave<2 * MI, kV, kL>();
+    __builtin_amdgcn_sched_barrier(0);
+    gt::wait_vmem();
+    __syncthreads();
+    wc = wnx;
+  }
+  if (a.kl > 0) {
+    // LoRA K steps: u through the x stage, [B | B | 0] rows straight into fragments
+    const gt::ActPtrs<MI> up = gt::make_act_ptrs<MI, 32 * MI>(a.u, a.kl, a.m, m0, wave, lane);
+    for (int64_t k0 = 0; k0 < a.kl; k0 += kBK) {
+      gt::dma_act(up, k0 / kBK, xs0, wave);  // xs0 was last read before the previous barrier
+      bf16x8 bl[4][2];
+#pragma unroll
+      for (int s4 = 0; s4 < 4; ++s4)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+          bl[s4][j] = *reinterpret_cast<const bf16x8*>(a.bx + nrow[j] * a.kl + k0 + h4 * 8 + 8 * s4);
+      gt::wait_vmem();
+      __syncthreads();
+      const char* xa = xs0 + (lane & 31) * gt::kActRowBytes;
+#pragma unroll
+      for (int s4 = 0; s4 < 4; ++s4) {
+        gt::read_act(xa, s4, sw, h4, af[0]);
+        gt::mfma16(af[0], bl[s4], acc);
+      }
+      __syncthreads();
+    }
+  }
+
+  gt::store_acc(acc, a.y, a.m, a.rows, m0, n0, wave, lane);
 }
 
 template <bool kDQ, bool kF8>
@@ -185,121 +308,24 @@ __global__ __launch_bounds__(kThreads, kWgPerCu) void k_gemm(GemmArgs a) {
   const float mean = kDQ ? *a.sc.mean : 0.0f;
   const int64_t tiles_n = (a.rows + kBN - 1) / kBN;
   const int64_t tiles = tiles_n * ((a.m + kBM - 1) / kBM);
-  const int64_t nk = a.cols / kBK;
 
-  // Persistent: the grid holds the resident workgroups and each takes tiles
+  // Persistent: the grid holds the resident workgroups and each takes units
   // blockIdx.x, blockIdx.x + gridDim.x, ...  Tile order: dispatch deals
   // workgroups round-robin over the 8 XCDs, so the workgroups of one XCD
   // that run at the same time get neighbouring tiles along N and share x rows.
-  for (int64_t tile = blockIdx.x; tile < tiles; tile += gridDim.x) {
+  for (int64_t u = blockIdx.x; u < a.units; u += gridDim.x) {
+    const bool half = u >= a.whole;
+    const int64_t tile = half ? a.whole + (u - a.whole) / 2 : u;
     int64_t tid = tile;
     if (tiles % 8 == 0) tid = (tile % 8) * (tiles / 8) + tile / 8;
     const int64_t m0 = (tid / tiles_n) * kBM;
     const int64_t n0 = (tid % tiles_n) * kBN;
-
-    const gt::ActPtrs<kMI> xp = gt::make_act_ptrs<kMI, kBM>(a.x, a.cols, a.m, m0, wave, lane);
-    WPtrs wp;
-    int64_t nrow[2];
-#pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int64_t n = n0 + wave * 64 + j * 32 + (lane & 31);
-      nrow[j] = n < a.rows ? n : a.rows - 1;  // rows past the end: never stored
-      wp.c[j] = a.packed + nrow[j] * (a.cols / 2) + (lane >> 5) * 16;
-      wp.blk[j] = nrow[j] * (a.cols / 64);
+    if (!half) {
+      gemm_unit<kMI, kDQ, kF8>(a, m0, n0, xs0, xs1, tabc, slot, mean, wave, lane);
+    } else {
+      const int64_t mh = m0 + ((u - a.whole) & 1) * (kBM / 2);
+      if (mh < a.m) gemm_unit<kMI / 2, kDQ, kF8>(a, mh, n0, xs0, xs1, tabc, slot, mean, wave, lane);
     }
-
-    floatx16 acc[kMI][2];
-    gt::zero_acc(acc);
-
-    // K step k: MFMAs from x stage k % 2 and the codes of step k (wc), in
-    // four 16-wide k steps s.  Software pipeline: while the MFMAs of s run,
-    // the wave expands the B fragments of s + 1 (looked up one k step
-    // earlier) and issues the LDS reads of s + 2; during s = 3 it expands
-    // the next step's s = 0, so that after the barrier the MFMAs can start at
-    // once.  The global loads of step k + 1 (clamped on the last step: x to
-    // the other stage, codes to registers) go out at the top of step k.
-    WRegs wc, wnx;
-    gt::dma_act(xp, 0, xs0, wave);
-    load_w<kDQ>(wc, wp, a, 0);
-    float sa[2];
-    bf16x8 bf[2][2];
-    Lookups lk[3];
-    bf16x8 af[3][kMI];
-    const uint32_t sw = ((lane & 31) >> 1) & 7, h4 = (lane >> 5) * 4;
-    block_scales<kDQ, kF8>(wc, mean, sa);
-    lookup_step<kCopies>(lk[0], wc.w, 0, tabc, slot);
-    bf[0][0] = expand_frag(lk[0].l[0], sa[0]);
-    bf[0][1] = expand_frag(lk[0].l[1], sa[1]);
-    gt::wait_vmem();
-    __syncthreads();
-    for (int64_t ks = 0; ks < nk; ++ks) {
-      const int64_t kn = ks + 1 < nk ? ks + 1 : ks;
-      gt::dma_act(xp, kn, (ks & 1) ? xs0 : xs1, wave);  // the other stage was last read before the previous barrier
-      load_w<kDQ>(wnx, wp, a, kn);
-      __builtin_amdgcn_sched_barrier(0);
-      const char* xa = ((ks & 1) ? xs1 : xs0) + (lane & 31) * gt::kActRowBytes;
-      gt::read_act(xa, 0, sw, h4, af[0]);
-      gt::read_act(xa, 1, sw, h4, af[1]);
-      lookup_step<kCopies>(lk[1], wc.w, 1, tabc, slot);
-      __builtin_amdgcn_sched_barrier(0);
-      // s = 0
-      gt::mfma16(af[0], bf[0], acc);
-      bf[1][0] = expand_frag(lk[1].l[0], sa[0]);
-      bf[1][1] = expand_frag(lk[1].l[1], sa[1]);
-      gt::read_act(xa, 2, sw, h4, af[2]);
-      lookup_step<kCopies>(lk[2], wc.w, 2, tabc, slot);
-      mfma_interleave<2 * kMI>();
-      __builtin_amdgcn_sched_barrier(0);
-      // s = 1
-      gt::mfma16(af[1], bf[1], acc);
-      bf[0][0] = expand_frag(lk[2].l[0], sa[0]);
-      bf[0][1] = expand_frag(lk[2].l[1], sa[1]);
-      gt::read_act(xa, 3, sw, h4, af[0]);
-      lookup_step<kCopies>(lk[0], wc.w, 3, tabc, slot);
-      mfma_interleave<2 * kMI>();
-      __builtin_amdgcn_sched_barrier(0);
-      // s = 2
-      gt::mfma16(af[2], bf[0], acc);
-      bf[1][0] = expand_frag(lk[0].l[0], sa[0]);
-      bf[1][1] = expand_frag(lk[0].l[1], sa[1]);
-      mfma_interleave<2 * kMI>();
-      __builtin_amdgcn_sched_barrier(0);
-      // s = 3, with the next step's s = 0 expansion
-      gt::mfma16(af[0], bf[1], acc);
-      block_scales<kDQ, kF8>(wnx, mean, sa);
-      lookup_step<kCopies>(lk[1], wnx.w, 0, tabc, slot);
-      bf[0][0] = expand_frag(lk[1].l[0], sa[0]);
-      bf[0][1] = expand_frag(lk[1].l[1], sa[1]);
-      mfma_interleave<2 * kMI>();
-      __builtin_amdgcn_sched_barrier(0);
-      gt::wait_vmem();
-      __syncthreads();
-      wc = wnx;
-    }
-    if (a.kl > 0) {
-      // LoRA K steps: u through the x stage, [B | B | 0] rows straight into fragments
-      const gt::ActPtrs<kMI> up = gt::make_act_ptrs<kMI, kBM>(a.u, a.kl, a.m, m0, wave, lane);
-      for (int64_t k0 = 0; k0 < a.kl; k0 += kBK) {
-        gt::dma_act(up, k0 / kBK, xs0, wave);  // xs0 was last read before the previous barrier
-        bf16x8 bl[4][2];
-#pragma unroll
-        for (int s4 = 0; s4 < 4; ++s4)
-#pragma unroll
-          for (int j = 0; j < 2; ++j)
-            bl[s4][j] = *reinterpret_cast<const bf16x8*>(a.bx + nrow[j] * a.kl + k0 + h4 * 8 + 8 * s4);
-        gt::wait_vmem();
-        __syncthreads();
-        const char* xa = xs0 + (lane & 31) * gt::kActRowBytes;
-#pragma unroll
-        for (int s4 = 0; s4 < 4; ++s4) {
-          gt::read_act(xa, s4, sw, h4, af[0]);
-          gt::mfma16(af[0], bl[s4], acc);
-        }
-        __syncthreads();
-      }
-    }
-
-    gt::store_acc(acc, a.y, a.m, a.rows, m0, n0, wave, lane);
   }
 }
 
@@ -351,7 +377,13 @@ hipError_t launch_gemm(const uint8_t* packed, int64_t rows, int64_t cols, Scales
   }
   const int64_t tiles = ((rows + kBN - 1) / kBN) * ((m + kBM - 1) / kBM);
   const int64_t slots = kWgPerCu * device_cus();  // resident workgroups
-  const unsigned grid = static_cast<unsigned>(tiles < slots ? tiles : slots);
+  // Tiles of the last round (all of them when they fill less than one): cut
+  // into halves when those fit in one round and the tiles have more than 128 rows.
+  const int64_t last = tiles - tiles / slots * slots;
+  const bool halve = last > 0 && 2 * last <= slots && m > kBM / 2;
+  a.whole = halve ? tiles - last : tiles;
+  a.units = halve ? tiles + last : tiles;
+  const unsigned grid = static_cast<unsigned>(a.units < slots ? a.units : slots);
   if (sc.absmax) hipLaunchKernelGGL((k_gemm<false, false>), dim3(grid), dim3(kThreads), 0, s, a);
   else if (sc.f8) hipLaunchKernelGGL((k_gemm<true, true>), dim3(grid), dim3(kThreads), 0, s, a);
   else hipLaunchKernelGGL((k_gemm<true, false>), dim3(grid), dim3(kThreads), 0, s, a);

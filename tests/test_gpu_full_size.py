@@ -97,10 +97,14 @@ def test_gemm_dx_c4_every_output():
     (2304, 8192, 256, 0),     # 9 x 32 = 288 tiles (a multiple of 8: XCD tile order), > one per CU
     (2341, 8292, 320, 16),    # 10 x 33 = 330 tiles, ragged M and N, plain tile order, LoRA
     (4608, 4096, 128, 7),     # 18 x 16 = 288 tiles, rank not a multiple of 16
+    (2048, 16384, 128, 0),    # 8 x 64 = 512 tiles: two whole rounds, no half tiles
+    (2048, 14592, 192, 16),   # 8 x 57 = 456 tiles: a last round of 200, too many to halve
 ])
 def test_gemm_persistent_tiles_every_output(m, rows, cols, r):
     """More tiles than compute units, so each persistent workgroup walks
-    several tiles and reuses its LDS across them; checked on every output."""
+    several tiles and reuses its LDS across them; checked on every output.
+    On 256 compute units the first three shapes end with a round of 32 or 74
+    tiles cut into 128-row halves; the last two keep every tile whole."""
     say("gemm persistent", m, rows, cols, "r", r)
     torch = need_gpu()
     w = syn.normal_f32((rows, cols), 0.02, 500 + rows)

@@ -1,7 +1,8 @@
 """GPU parity of nf4_gemv and nf4_gemm against the oracle's float64 product of
-its bf16-dequantized weights: relative Frobenius error <= 1e-2 (MATMUL_RTOL).
-The full-size workloads are checked on every output in
-test_gpu_full_size.py."""
+its bf16-dequantized weights: relative Frobenius error <= 1e-2 (MATMUL_RTOL);
+the GEMMs also per 128 x 256 output block (the half-tile work unit) and per
+element (gpu_common.check_full_product).  The full-size workloads are checked
+on every output in test_gpu_full_size.py."""
 
 from __future__ import annotations
 
@@ -11,7 +12,7 @@ import pytest
 import dequant_matmul_nf4_amd as nf4
 import oracle
 import synthetic as syn
-from tests.gpu_common import MATMUL_RTOL, need_gpu, oracle_rows_dequant_bf16, say, to_dev
+from tests.gpu_common import MATMUL_RTOL, check_full_product, need_gpu, oracle_rows_dequant_bf16, say, to_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -29,6 +30,24 @@ def _full_oracle_wdeq(w_f32: np.ndarray, dq: bool) -> np.ndarray:
 def _y_f64(y):
     import torch
     return y.detach().to(torch.float32).cpu().numpy().astype(np.float64)
+
+
+GEMM_UNIT = (128, 256)        # half-tile work unit of nf4_gemm (rows of x, rows of W)
+LORA_SPLIT_REL = 2.0 ** -16   # s T carried as two bf16 parts
+
+
+def _check_gemm(y, xb, wdeq, a=None, b=None, s=0.0, label="gemm"):
+    """Whole-output, per-block and per-element bounds against the oracle."""
+    xf = syn.bf16_to_f32(xb)
+    af = None if a is None else syn.bf16_to_f32(a)
+    bf = None if b is None else syn.bf16_to_f32(b)
+    ref = oracle.matmul_ref(xf, wdeq, af, bf, s)
+    sabs = np.abs(xf).astype(np.float64) @ np.abs(wdeq).astype(np.float64).T
+    if af is not None:
+        t = np.abs(xf).astype(np.float64) @ np.abs(af).astype(np.float64).T
+        sabs += abs(s) * (t @ np.abs(bf).astype(np.float64).T)
+    check_full_product(_y_f64(y), ref, sabs, terms=xf.shape[1] + 128, tile=GEMM_UNIT,
+                       w_rel=0.0 if a is None else LORA_SPLIT_REL, label=label)
 
 
 @pytest.mark.parametrize("rows,cols", [(1, 64), (5, 128), (33, 192), (1024, 1024), (300, 4096)])
@@ -232,6 +251,9 @@ def test_gemv_row_interleave_shapes(rows, cols, m):
 @pytest.mark.parametrize("lora", [0, 1, 16])
 @pytest.mark.parametrize("dq", [False, True])
 def test_gemm_small(m, rows, cols, lora, dq):
+    """Fewer tiles than compute units: with more than 128 rows of x each tile
+    is cut into two 128-row halves (m = 130: a second half of 2 rows; m = 300:
+    the second band's empty half is skipped); m <= 128 keeps whole tiles."""
     say("gemm", m, rows, cols, "lora", lora, "dq" if dq else "plain")
     torch = need_gpu()
     w = syn.normal_f32((rows, cols), 0.02, m + rows + cols)
@@ -246,12 +268,7 @@ def test_gemm_small(m, rows, cols, lora, dq):
     y = nf4.nf4_gemm(W, xb.to("cuda"), lora_a=None if a is None else a.to("cuda"),
                      lora_b=None if b is None else b.to("cuda"), lora_scale=s)
     torch.cuda.synchronize()
-    ref = oracle.matmul_ref(syn.bf16_to_f32(xb), _full_oracle_wdeq(w, dq),
-                            None if a is None else syn.bf16_to_f32(a),
-                            None if b is None else syn.bf16_to_f32(b), s)
-    e = oracle.rel_frobenius(_y_f64(y), ref)
-    say(f"  rel err {e:.2e}")
-    assert e <= MATMUL_RTOL
+    _check_gemm(y, xb, _full_oracle_wdeq(w, dq), a, b, s)
 
 
 @pytest.mark.parametrize("m,rows,cols,r", [(513, 300, 320, 64), (100, 260, 64, 33), (33, 257, 128, 17)])
@@ -267,19 +284,16 @@ def test_gemm_lora_ranks(m, rows, cols, r):
     W = nf4.quantize_weight(to_dev(w), double_quant=True)
     y = nf4.nf4_gemm(W, xb.to("cuda"), lora_a=a.to("cuda"), lora_b=b.to("cuda"), lora_scale=s)
     torch.cuda.synchronize()
-    ref = oracle.matmul_ref(syn.bf16_to_f32(xb), _full_oracle_wdeq(w, True), syn.bf16_to_f32(a),
-                            syn.bf16_to_f32(b), s)
-    e = oracle.rel_frobenius(_y_f64(y), ref)
-    say(f"  rel err {e:.2e}")
-    assert e <= MATMUL_RTOL
+    _check_gemm(y, xb, _full_oracle_wdeq(w, True), a, b, s)
 
 
 def test_gemm_lora_only_term_and_zero_b():
     """With B = 0 the LoRA path adds nothing; with a one-hot x the product
-    returns a dequantized column exactly rounded to bf16."""
+    returns a dequantized column exactly rounded to bf16 (192 rows of x: both
+    halves of a cut tile)."""
     say("gemm closed forms")
     torch = need_gpu()
-    rows, cols, m = 192, 256, 64
+    rows, cols, m = 192, 256, 192
     w = syn.normal_f32((rows, cols), 0.02, 12)
     W = nf4.quantize_weight(to_dev(w), double_quant=True)
     xb = syn.to_bf16(syn.normal_f32((m, cols), 1.0, 13)).to("cuda")
