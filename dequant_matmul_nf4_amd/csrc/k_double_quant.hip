@@ -149,7 +149,7 @@ __device__ __forceinline__ unsigned long long block_digit_sum(const unsigned lon
 }
 
 // Digit sums of the workgroup's scales: each thread adds its scales, read as
-// 16-byte vectors with kPartVec of them requested before any is used, into
+// 16-byte vectors with kVec of them requested before any is used, into
 // registers; the workgroup's digit vectors are then added into its row.
 //
 // A contribution lands in digits d and d + 1.  The scales of one weight
@@ -159,10 +159,9 @@ __device__ __forceinline__ unsigned long long block_digit_sum(const unsigned lon
 // (three selects); any other contribution takes the selects over all 12
 // digits.  The window is added into the 12 digits at the end, so the sum is
 // the same integer either way.  The window pays off from about 8 scales per
-// thread, so the launcher picks it by size.
-constexpr int kPartVec = 2;
-
-template <int kThreads, bool kWindow>
+// thread, so the launcher picks it by size.  kVec: 2 vectors in flight for
+// small arrays, 4 for large ones (16 scales per thread: one round trip).
+template <int kThreads, bool kWindow, int kVec>
 __global__ __launch_bounds__(kThreads) void k_dq_partial(const float* __restrict__ absmax, int64_t nb,
                                                          unsigned long long* __restrict__ ws) {
   const int t = threadIdx.x;
@@ -191,15 +190,15 @@ __global__ __launch_bounds__(kThreads) void k_dq_partial(const float* __restrict
   const int64_t n4 = nb >> 2;  // whole 16-byte vectors; absmax is 16-byte aligned
   const float4* a4 = reinterpret_cast<const float4*>(absmax);
   const int64_t stride = static_cast<int64_t>(gridDim.x) * kThreads;
-  for (int64_t i0 = static_cast<int64_t>(blockIdx.x) * kThreads + t; i0 < n4; i0 += kPartVec * stride) {
-    float4 v[kPartVec];
+  for (int64_t i0 = static_cast<int64_t>(blockIdx.x) * kThreads + t; i0 < n4; i0 += kVec * stride) {
+    float4 v[kVec];
 #pragma unroll
-    for (int u = 0; u < kPartVec; ++u) {
+    for (int u = 0; u < kVec; ++u) {
       const int64_t i = i0 + u * stride;
       v[u] = (i < n4) ? a4[i] : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
     }
 #pragma unroll
-    for (int u = 0; u < kPartVec; ++u) {
+    for (int u = 0; u < kVec; ++u) {
       add(v[u].x);
       add(v[u].y);
       add(v[u].z);
@@ -373,7 +372,7 @@ hipError_t dq_scratch(unsigned long long** out) {
 
 namespace {
 
-template <int kThreads>
+template <int kThreads, int kVec>
 void launch_dq(const float* absmax, int64_t nb, int8_t* q, float* absmax2, float* mean, unsigned long long* ws,
                int f8, int per_thread, int max_qgrid, hipStream_t s) {
   constexpr int kWaves = kThreads / kWave;
@@ -381,9 +380,9 @@ void launch_dq(const float* absmax, int64_t nb, int8_t* q, float* absmax2, float
   int64_t want = (nb + kThreads * per_thread - 1) / (kThreads * per_thread);
   const int grid = static_cast<int>(want < kDqMaxGroups ? want : kDqMaxGroups);
   if (nb >= static_cast<int64_t>(grid) * kThreads * 8)
-    hipLaunchKernelGGL((k_dq_partial<kThreads, true>), dim3(grid), dim3(kThreads), 0, s, absmax, nb, ws);
+    hipLaunchKernelGGL((k_dq_partial<kThreads, true, kVec>), dim3(grid), dim3(kThreads), 0, s, absmax, nb, ws);
   else
-    hipLaunchKernelGGL((k_dq_partial<kThreads, false>), dim3(grid), dim3(kThreads), 0, s, absmax, nb, ws);
+    hipLaunchKernelGGL((k_dq_partial<kThreads, false, kVec>), dim3(grid), dim3(kThreads), 0, s, absmax, nb, ws);
   // one group per wave, up to max_qgrid workgroups (each re-reads the partial rows)
   const int64_t groups = (nb + 255) >> 8;
   want = (groups + kWaves - 1) / kWaves;
@@ -401,9 +400,9 @@ void launch_dq(const float* absmax, int64_t nb, int8_t* q, float* absmax2, float
 hipError_t launch_double_quant(const float* absmax, int64_t nb, int8_t* q, float* absmax2,
                                float* mean, unsigned long long* ws, int f8, hipStream_t s) {
   if (nb >= (int64_t{1} << 21))
-    launch_dq<1024>(absmax, nb, q, absmax2, mean, ws, f8, 8, 256, s);
+    launch_dq<1024, 4>(absmax, nb, q, absmax2, mean, ws, f8, 16, 256, s);
   else
-    launch_dq<256>(absmax, nb, q, absmax2, mean, ws, f8, 4, 1024, s);
+    launch_dq<256, 2>(absmax, nb, q, absmax2, mean, ws, f8, 4, 1024, s);
   return hipGetLastError();
 }
 

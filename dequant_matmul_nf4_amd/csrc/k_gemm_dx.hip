@@ -256,7 +256,7 @@ __global__ __launch_bounds__(kDxThreads) void k_gemm_dx(DxArgs a) {
   // prologue: dY of step 0, Wt of step 0, codes of step 1
   CodeRegs c1, c2;
   if (ragged && nsteps == 1) act_tail(ap, 0, a.rows, stage0, wave, lane);
-  else gt::dma_act(ap, 0, stage0, wave);
+  else gt::dma_act_buf(ap, 0, stage0, wave);
   load_codes<kDQ>(c1, cp, a, 0, q);
   load_codes<kDQ>(c2, cp, a, nsteps > 1 ? 1 : 0, q);
   fill_pairs(pairs, a.cb);
@@ -288,7 +288,7 @@ __global__ __launch_bounds__(kDxThreads) void k_gemm_dx(DxArgs a) {
     // barrier); on the last step a harmless reload, so that the code below
     // stays one basic block for the scheduler
     if (ragged && kn == nsteps - 1) act_tail(ap, kn, a.rows, st_nxt, wave, lane);
-    else gt::dma_act(ap, kn, st_nxt, wave);
+    else gt::dma_act_buf(ap, kn, st_nxt, wave);
     load_codes<kDQ>(c2, cp, a, ks + 2 < nsteps ? ks + 2 : kn, q);
     float ah[8];
     scales_of(c1, ah);
@@ -321,7 +321,7 @@ __global__ __launch_bounds__(kDxThreads) void k_gemm_dx(DxArgs a) {
   if (a.kl > 0) {
     const gt::ActPtrs<kP> up = gt::make_act_ptrs<kP, kTm>(a.u, a.kl, a.m, m0, wave, lane);
     for (int64_t j0 = 0; j0 < a.kl; j0 += kStep) {
-      gt::dma_act(up, j0 / kStep, stage0, wave);
+      gt::dma_act_buf(up, j0 / kStep, stage0, wave);
       // quarter wq's Wt: column k0 + 64 wq + 4 q + c, run 4 wh + g holds A[j0 + 8 run + e][column]
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
