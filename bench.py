@@ -554,16 +554,17 @@ def leg_lora_merge(torch, nf4, dev, stream, EventTimer, g):
 def build_stack_70b(torch, nf4, syn, dev, stream, EventTimer, layers=80):
     """The 70B-shaped stack.  Layer by layer the seven bf16 weights (q, k, v,
     o, gate, up, down) are drawn on the device (untimed) and then quantized
-    and double-quantized into a persistent NF4 store (timed: one HIP graph of
-    the 7 x 3 launches per layer).  Returns the store and the stack's
-    figures."""
+    and double-quantized into a persistent NF4 store (timed: one HIP graph per
+    layer of seven nf4_quantize launches and one nf4_double_quant_batched call
+    over the seven scale arrays, two launches).  Returns the store and the
+    stack's figures."""
     layers = max(1, min(int(layers), 80))
     print(f"[bench] 70B stack: {layers} layers", file=sys.stderr, flush=True)
     LAYER_70B = [syn.C5_SHAPES[name] for name in syn.C5_ORDER]
     src = [torch.empty(sh, dtype=torch.bfloat16, device=dev) for sh in LAYER_70B]
     nbs = [r * c // 64 for r, c in LAYER_70B]
     absmax = [torch.empty(nb, dtype=torch.float32, device=dev) for nb in nbs]
-    dq_ws = torch.empty(nf4.nf4_double_quant_workspace(max(nbs)), dtype=torch.uint8, device=dev)
+    dq_ws = torch.empty(nf4.lib().nf4_double_quant_batched_workspace(len(nbs)), dtype=torch.uint8, device=dev)
     store, t = [], EventTimer(torch, stream)
     for layer in range(layers):
         Ws = []
@@ -576,7 +577,7 @@ def build_stack_70b(torch, nf4, syn, dev, stream, EventTimer, layers=80):
         def run():
             for w, W, am in zip(src, Ws, absmax):
                 nf4.nf4_quantize(w, W.packed, am)
-                nf4.nf4_double_quant(am, W.qabsmax, W.absmax2, W.mean, dq_ws)
+            nf4.nf4_double_quant_batched(absmax, outs=[(W.qabsmax, W.absmax2, W.mean) for W in Ws], workspace=dq_ws)
 
         graph = capture_graph(torch, run)
         graph.replay()  # first launch of the graph (upload), on the previous layer's data; untimed
@@ -603,7 +604,8 @@ def build_stack_70b(torch, nf4, syn, dev, stream, EventTimer, layers=80):
         "quantize_dq_algorithmic_GBps": round(alg_layer * layers / total_s / 1e9, 1),
         "quantize_dq_frac_hbm_peak": round(alg_layer * layers / total_s / 1e9 / HBM_PEAK_GBS, 4),
         "nf4_store_GB": round(layers * g_bytes / 1e9, 2),
-        "timing": "HIP events around each layer's graph (nf4_quantize + nf4_double_quant of the seven weights)",
+        "timing": "HIP events around each layer's graph: nf4_quantize of the seven weights, then one "
+                  "nf4_double_quant_batched call over their seven scale arrays",
     }
 
 

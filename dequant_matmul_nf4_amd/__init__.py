@@ -30,7 +30,7 @@ EXPORTS = (
     "nf4_last_error", "nf4_codebook", "nf4_codebook_fp4", "nf4_quantize", "nf4_quantize_fp4", "nf4_double_quant_workspace",
     "nf4_double_quant", "nf4_e4m3_ratio", "nf4_double_quant_f8", "nf4_dequantize", "nf4_gemv", "nf4_gemm_workspace", "nf4_gemm", "nf4_gemm_dx_workspace",
     "nf4_gemm_dx", "nf4_lora_grads_workspace", "nf4_lora_grads", "nf4_lora_merge", "nf4_double_quant_noalloc",
-    "nf4_gemv_batched",
+    "nf4_gemv_batched", "nf4_double_quant_batched_workspace", "nf4_double_quant_batched",
 )
 
 
@@ -38,6 +38,14 @@ class NF4Error(RuntimeError):
     def __init__(self, code: int, message: str):
         super().__init__(f"[{code}] {message}")
         self.code = code
+
+
+class nf4_dq_job(ctypes.Structure):
+    """Mirror of `struct nf4_dq_job` in include/nf4.h."""
+    _fields_ = [
+        ("absmax", ctypes.c_void_p), ("nblocks", ctypes.c_int64), ("qabsmax", ctypes.c_void_p),
+        ("absmax2", ctypes.c_void_p), ("mean", ctypes.c_void_p),
+    ]
 
 
 class nf4_weight(ctypes.Structure):
@@ -73,6 +81,8 @@ def lib() -> ctypes.CDLL:
         "nf4_double_quant": (ctypes.c_int, [vp, i64, i32, vp, vp, vp, vp, sz, vp]),
         "nf4_double_quant_f8": (ctypes.c_int, [vp, i64, i32, vp, vp, vp, vp, sz, vp]),
         "nf4_double_quant_noalloc": (ctypes.c_int, [vp, i64, i32, vp, vp, vp, vp]),
+        "nf4_double_quant_batched_workspace": (sz, [i32]),
+        "nf4_double_quant_batched": (ctypes.c_int, [ctypes.POINTER(nf4_dq_job), i32, i32, i32, vp, sz, vp]),
         "nf4_e4m3_ratio": (ctypes.c_int, [ctypes.POINTER(ctypes.c_float)]),
         "nf4_dequantize": (ctypes.c_int, [wp, vp, ctypes.c_int, vp]),
         "nf4_gemv": (ctypes.c_int, [wp, vp, i64, vp, ctypes.c_int, vp]),
@@ -301,6 +311,46 @@ def nf4_double_quant(absmax, qabsmax=None, absmax2=None, mean=None, workspace=No
     _check(fn(_ptr(absmax), nb, BLOCKSIZE2, _ptr(qabsmax), _ptr(absmax2), _ptr(mean),
               _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream)))
     return qabsmax, absmax2, mean
+
+
+def nf4_double_quant_batched(absmaxes, outs=None, workspace=None, stream=None, fp8=False):
+    """nf4_double_quant (fp8=True: nf4_double_quant_f8) of 1 to 8 scale arrays
+    in one pair of launches; each array's outputs are those of the single
+    call.  outs: optional list of (qabsmax, absmax2, mean) per array.
+    Returns the list of (qabsmax, absmax2, mean)."""
+    torch = _torch()
+    absmaxes = list(absmaxes)
+    if not 1 <= len(absmaxes) <= 8:
+        raise ValueError("1 to 8 scale arrays")
+    _need_cuda(*absmaxes)
+    dev = absmaxes[0].device
+    if outs is None:
+        outs = [(_alloc_on(stream, (a.numel(),), torch.uint8 if fp8 else torch.int8, dev),
+                 _alloc_on(stream, ((a.numel() + 255) // 256,), torch.float32, dev),
+                 _alloc_on(stream, (1,), torch.float32, dev)) for a in absmaxes]
+    outs = [tuple(o) for o in outs]
+    if len(outs) != len(absmaxes):
+        raise ValueError("one (qabsmax, absmax2, mean) per array")
+    for a, (q, s2, mu) in zip(absmaxes, outs):
+        if a.dtype != torch.float32:
+            raise TypeError("absmax must be float32")
+        _need_cuda(q, s2, mu)
+        _same_device(dev, a, q, s2, mu)
+        if s2.dtype != torch.float32 or mu.dtype != torch.float32 or q.element_size() != 1:
+            raise TypeError("qabsmax must hold bytes, absmax2 and mean float32")
+        if q.numel() < a.numel() or s2.numel() < (a.numel() + 255) // 256 or mu.numel() < 1:
+            raise ValueError("output buffers too small")
+    wsb = lib().nf4_double_quant_batched_workspace(len(absmaxes))
+    if workspace is None:
+        workspace = _alloc_on(stream, (wsb,), torch.uint8, dev)
+    _need_cuda(workspace)
+    _same_device(dev, workspace)
+    jobs = (nf4_dq_job * len(absmaxes))(*[nf4_dq_job(_ptr(a), a.numel(), _ptr(q), _ptr(s2), _ptr(mu))
+                                          for a, (q, s2, mu) in zip(absmaxes, outs)])
+    _check(lib().nf4_double_quant_batched(jobs, len(absmaxes), BLOCKSIZE2, NF4_DQ_FP8 if fp8 else NF4_DQ_INT8,
+                                          _ptr(workspace), workspace.numel() * workspace.element_size(),
+                                          _stream(stream)))
+    return outs
 
 
 def nf4_double_quant_noalloc(absmax, qabsmax, absmax2, mean, stream=None):

@@ -223,6 +223,43 @@ int nf4_double_quant_f8(const float* absmax, int64_t nblocks, int32_t blocksize2
                       workspace_bytes, stream, 1, "nf4_double_quant_f8");
 }
 
+size_t nf4_double_quant_batched_workspace(int32_t count) {
+  if (count < 1 || count > nf4i::kDqMaxJobs) return 0;
+  return static_cast<size_t>(count) * nf4i::kDqWorkspaceBytes;
+}
+
+int nf4_double_quant_batched(const nf4_dq_job* jobs, int32_t count, int32_t blocksize2, int32_t dq_type,
+                             void* workspace, size_t workspace_bytes, void* stream) {
+  const char* who = "nf4_double_quant_batched";
+  if (!jobs) return fail(NF4_ERR_NULL, "%s: jobs is NULL", who);
+  if (count < 1 || count > nf4i::kDqMaxJobs)
+    return fail(NF4_ERR_SIZE, "%s: count = %d out of range 1..%d", who, (int)count, nf4i::kDqMaxJobs);
+  if (blocksize2 != NF4_BLOCKSIZE2)
+    return fail(NF4_ERR_BLOCKSIZE, "%s: blocksize2 %d unsupported (only 256)", who, (int)blocksize2);
+  if (dq_type != NF4_DQ_INT8 && dq_type != NF4_DQ_FP8)
+    return fail(NF4_ERR_DTYPE, "%s: dq_type %d unknown", who, (int)dq_type);
+  const size_t need = nf4_double_quant_batched_workspace(count);
+  if (!workspace || workspace_bytes < need) return fail(NF4_ERR_WORKSPACE, "%s: workspace needs %zu bytes", who, need);
+  if (!aligned(workspace, 16)) return fail(NF4_ERR_ALIGN, "%s: workspace must be 16-byte aligned", who);
+  nf4i::DqJob dj[nf4i::kDqMaxJobs];
+  for (int i = 0; i < count; ++i) {
+    const nf4_dq_job& j = jobs[i];
+    if (!j.absmax || !j.qabsmax || !j.absmax2 || !j.mean)
+      return fail(NF4_ERR_NULL, "%s: array %d: absmax, qabsmax, absmax2 and mean are required", who, i);
+    if (j.nblocks < 1 || j.nblocks >= (int64_t(1) << 31))
+      return fail(NF4_ERR_SIZE, "%s: array %d: nblocks = %lld out of range", who, i, (long long)j.nblocks);
+    if (!aligned(j.absmax, 16) || !aligned(j.qabsmax, 16))
+      return fail(NF4_ERR_ALIGN, "%s: array %d: absmax and qabsmax must be 16-byte aligned", who, i);
+    if (!aligned(j.absmax2, 4) || !aligned(j.mean, 4))
+      return fail(NF4_ERR_ALIGN, "%s: array %d: absmax2 and mean must be 4-byte aligned", who, i);
+    dj[i] = nf4i::DqJob{j.absmax, j.nblocks, static_cast<int8_t*>(j.qabsmax), j.absmax2, j.mean};
+  }
+  if (int rc = check_device()) return rc;
+  return launched(nf4i::launch_double_quant_batch(dj, count, static_cast<unsigned long long*>(workspace),
+                                                  dq_type == NF4_DQ_FP8 ? 1 : 0, as_stream(stream)),
+                  who);
+}
+
 int nf4_dequantize(const nf4_weight* w, void* out, int out_dtype, void* stream) {
   nf4i::Scales sc{};
   int64_t n = 0;

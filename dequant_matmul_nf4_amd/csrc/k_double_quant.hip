@@ -16,7 +16,11 @@
 // float32 -- the same value in every workgroup, so no third launch is needed.
 //
 // Kernels: k_dq_partial (digit sums per workgroup), k_dq_quant (the mean,
-// then one wave per group of 256 scales).
+// then one wave per group of 256 scales).  For several scale arrays at once,
+// k_dq_partial_batch, k_dq_mean_batch (one workgroup per array: its mean,
+// written to the array's mean output) and k_dq_quant_batch (reads that mean)
+// do the same in three launches: each workgroup belongs to one array, found
+// from per-array workgroup offsets; each array has its own partial rows.
 #include <mutex>
 
 #include "nf4_device.h"
@@ -161,16 +165,20 @@ __device__ __forceinline__ unsigned long long block_digit_sum(const unsigned lon
 // the same integer either way.  The window pays off from about 8 scales per
 // thread, so the launcher picks it by size.  kVec: 2 vectors in flight for
 // small arrays, 4 for large ones (16 scales per thread: one round trip).
-template <int kThreads, bool kWindow, int kVec>
-__global__ __launch_bounds__(kThreads) void k_dq_partial(const float* __restrict__ absmax, int64_t nb,
-                                                         unsigned long long* __restrict__ ws) {
-  const int t = threadIdx.x;
+// Workgroup `blk` of `grid` summing workgroups over absmax[0, nb); its row
+// goes to ws[blk].
+// One thread's digit sums: 12 digits, plus (kWindow) the three-digit window.
+template <bool kWindow>
+struct DigitAcc {
   unsigned long long acc[kDqDigits];
-#pragma unroll
-  for (int k = 0; k < kDqDigits; ++k) acc[k] = 0ull;
   int base = -1;  // the window's first digit (placed by the first nonzero scale)
   unsigned long long w0 = 0ull, w1 = 0ull, w2 = 0ull;
-  auto add = [&](float a) {
+
+  __device__ __forceinline__ DigitAcc() {
+#pragma unroll
+    for (int k = 0; k < kDqDigits; ++k) acc[k] = 0ull;
+  }
+  __device__ __forceinline__ void add(float a) {
     int d;
     uint32_t lo, hi;
     scale_to_digits(a, &d, &lo, &hi);
@@ -186,11 +194,27 @@ __global__ __launch_bounds__(kThreads) void k_dq_partial(const float* __restrict
       for (int k = 0; k < kDqDigits; ++k)
         acc[k] += static_cast<unsigned long long>((k == d ? lo : 0u)) + static_cast<unsigned long long>((k == d + 1 ? hi : 0u));
     }
-  };
+  }
+  // The window added into the 12 digits: the same integer either way.
+  __device__ __forceinline__ void fold() {
+    if constexpr (kWindow) {
+#pragma unroll
+      for (int k = 0; k < kDqDigits; ++k)
+        acc[k] += (k == base ? w0 : 0ull) + (k == base + 1 ? w1 : 0ull) + (k == base + 2 ? w2 : 0ull);
+    }
+  }
+};
+
+template <int kThreads, bool kWindow, int kVec>
+__device__ __forceinline__ void dq_partial_body(const float* __restrict__ absmax, int64_t nb,
+                                                unsigned long long* __restrict__ ws, int blk, int grid) {
+  const int t = threadIdx.x;
+  DigitAcc<kWindow> da;
+  auto add = [&](float a) { da.add(a); };
   const int64_t n4 = nb >> 2;  // whole 16-byte vectors; absmax is 16-byte aligned
   const float4* a4 = reinterpret_cast<const float4*>(absmax);
-  const int64_t stride = static_cast<int64_t>(gridDim.x) * kThreads;
-  for (int64_t i0 = static_cast<int64_t>(blockIdx.x) * kThreads + t; i0 < n4; i0 += kVec * stride) {
+  const int64_t stride = static_cast<int64_t>(grid) * kThreads;
+  for (int64_t i0 = static_cast<int64_t>(blk) * kThreads + t; i0 < n4; i0 += kVec * stride) {
     float4 v[kVec];
 #pragma unroll
     for (int u = 0; u < kVec; ++u) {
@@ -206,14 +230,16 @@ __global__ __launch_bounds__(kThreads) void k_dq_partial(const float* __restrict
     }
   }
   // the last nb % 4 scales, in the first workgroup
-  if (blockIdx.x == 0 && t < static_cast<int>(nb & 3)) add(absmax[(n4 << 2) + t]);
-  if constexpr (kWindow) {
-#pragma unroll
-    for (int k = 0; k < kDqDigits; ++k)
-      acc[k] += (k == base ? w0 : 0ull) + (k == base + 1 ? w1 : 0ull) + (k == base + 2 ? w2 : 0ull);
-  }
-  const unsigned long long sum = block_digit_sum<kThreads>(acc);
-  if (t < kDqDigits) ws[blockIdx.x * kDqDigits + t] = sum;
+  if (blk == 0 && t < static_cast<int>(nb & 3)) add(absmax[(n4 << 2) + t]);
+  da.fold();
+  const unsigned long long sum = block_digit_sum<kThreads>(da.acc);
+  if (t < kDqDigits) ws[static_cast<int64_t>(blk) * kDqDigits + t] = sum;
+}
+
+template <int kThreads, bool kWindow, int kVec>
+__global__ __launch_bounds__(kThreads) void k_dq_partial(const float* __restrict__ absmax, int64_t nb,
+                                                         unsigned long long* __restrict__ ws) {
+  dq_partial_body<kThreads, kWindow, kVec>(absmax, nb, ws, blockIdx.x, gridDim.x);
 }
 
 // The mean from the partial rows (at most 256, one per thread of the
@@ -274,16 +300,19 @@ __device__ __forceinline__ uint32_t e4m3_rne(float t) {
 // requested before the mean is known, so their loads overlap the mean.
 constexpr int kQuantPre = 4;
 
-template <int kThreads, bool kF8>
-__global__ __launch_bounds__(kThreads) void k_dq_quant(const float* __restrict__ absmax, int64_t nb,
-                                                         const unsigned long long* __restrict__ ws, int nparts,
-                                                         float* __restrict__ mean_out, int8_t* __restrict__ q,
-                                                         float* __restrict__ absmax2) {
+// Workgroup `blk` of `grid` quantizing workgroups of one scale array: the
+// mean from the nparts partial rows at ws (written to mean_out by workgroup
+// 0), or, with kMeanGiven, read from mean_out, where an earlier launch put it.
+template <int kThreads, bool kF8, bool kMeanGiven = false>
+__device__ __forceinline__ void dq_quant_body(const float* __restrict__ absmax, int64_t nb,
+                                              const unsigned long long* __restrict__ ws, int nparts,
+                                              float* __restrict__ mean_out, int8_t* __restrict__ q,
+                                              float* __restrict__ absmax2, int blk, int grid) {
   constexpr int kWaves = kThreads / kWave;
   const int lane = threadIdx.x & (kWave - 1);
   const int64_t ngroups = (nb + 255) >> 8;
-  const int64_t wave = static_cast<int64_t>(blockIdx.x) * kWaves + threadIdx.x / kWave;
-  const int64_t nwaves = static_cast<int64_t>(gridDim.x) * kWaves;
+  const int64_t wave = static_cast<int64_t>(blk) * kWaves + threadIdx.x / kWave;
+  const int64_t nwaves = static_cast<int64_t>(grid) * kWaves;
   auto load4 = [&](int64_t g, float (&a)[4]) {
     const int64_t i0 = g * 256 + lane * 4;
     if (i0 + 4 <= nb) {
@@ -296,20 +325,36 @@ __global__ __launch_bounds__(kThreads) void k_dq_quant(const float* __restrict__
   };
   auto quant_group = [&](int64_t g, const float (&a)[4], float mu) {
     const int64_t i0 = g * 256 + lane * 4;
+    const bool full = (g + 1) * 256 <= nb;  // the same for the whole wave
     float c[4];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) c[j] = (i0 + j < nb) ? a[j] - mu : 0.0f;
+    for (int j = 0; j < 4; ++j) c[j] = (full || i0 + j < nb) ? a[j] - mu : 0.0f;
     float s = fmaxf(fmaxf(fabsf(c[0]), fabsf(c[1])), fmaxf(fabsf(c[2]), fabsf(c[3])));
     s = group_max<64>(s);
     uint32_t word = 0;
     if (s > 0.0f) {
+      // fl32(c / s) from one reciprocal per group: y = fl32(1 / s), q0 =
+      // fl32(c y), r = fma(-q0, s, c) (exact) and fma(r, y, q0) is the
+      // correctly rounded quotient (Markstein's theorem) while no
+      // intermediate underflows: for 2^-80 <= s < 2^126 that holds for
+      // |c / s| >= 2^-20, and below that the quotient only decides codes
+      // that are 0 either way (|t| < 127 * 2^-20 or 448 * 2^-20, far under
+      // half of the smallest nonzero code).  Other s: IEEE division per value.
+      const bool fast = s >= 0x1p-80f && s < 0x1p126f;  // the same for the whole wave
+      const float y = 1.0f / s;
+      auto quotient = [&](float cj) {
+        if (!fast) return cj / s;
+        const float q0 = cj * y;
+        const float r = fmaf(-q0, s, cj);
+        return fmaf(r, y, q0);
+      };
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         if constexpr (kF8) {
-          const float t = (c[j] / s) * 448.0f;  // two roundings, as the int8 step
+          const float t = quotient(c[j]) * 448.0f;  // two roundings, as the int8 step
           word |= e4m3_rne(t) << (8 * j);
         } else {
-          const float t = (c[j] / s) * 127.0f;
+          const float t = quotient(c[j]) * 127.0f;
           const float at = fabsf(t);
           const float fl = floorf(at);
           float r = fl + ((at - fl) >= 0.5f ? 1.0f : 0.0f);  // half away from zero
@@ -333,8 +378,13 @@ __global__ __launch_bounds__(kThreads) void k_dq_quant(const float* __restrict__
     const int64_t g = wave + p * nwaves;
     if (g < ngroups) load4(g, a[p]);
   }
-  const float mu = dq_mean<kThreads>(ws, nparts, nb);
-  if (blockIdx.x == 0 && threadIdx.x == 0) *mean_out = mu;
+  float mu;
+  if constexpr (kMeanGiven) {
+    mu = *mean_out;
+  } else {
+    mu = dq_mean<kThreads>(ws, nparts, nb);
+    if (blk == 0 && threadIdx.x == 0) *mean_out = mu;
+  }
 #pragma unroll
   for (int p = 0; p < kQuantPre; ++p) {
     const int64_t g = wave + p * nwaves;
@@ -345,6 +395,70 @@ __global__ __launch_bounds__(kThreads) void k_dq_quant(const float* __restrict__
     load4(g, b);
     quant_group(g, b, mu);
   }
+}
+
+template <int kThreads, bool kF8>
+__global__ __launch_bounds__(kThreads) void k_dq_quant(const float* __restrict__ absmax, int64_t nb,
+                                                         const unsigned long long* __restrict__ ws, int nparts,
+                                                         float* __restrict__ mean_out, int8_t* __restrict__ q,
+                                                         float* __restrict__ absmax2) {
+  dq_quant_body<kThreads, kF8>(absmax, nb, ws, nparts, mean_out, q, absmax2, blockIdx.x, gridDim.x);
+}
+
+// Several scale arrays in one pair of launches.  part0[j] and quant0[j] are
+// the first summing and quantizing workgroups of array j (part0[count] and
+// quant0[count] the totals); array j's partial rows are ws rows
+// part0[j] .. part0[j + 1] - 1.
+struct DqBatch {
+  int count;
+  const float* absmax[kDqMaxJobs];
+  int64_t nb[kDqMaxJobs];
+  int8_t* q[kDqMaxJobs];
+  float* absmax2[kDqMaxJobs];
+  float* mean[kDqMaxJobs];
+  int window[kDqMaxJobs];  // the summing kernel's digit window pays off (about 8 or more scales per thread)
+  int part0[kDqMaxJobs + 1];
+  int quant0[kDqMaxJobs + 1];
+};
+
+// The array a workgroup belongs to: the last j with first[j] <= blk.
+__device__ __forceinline__ int dq_job_of(const int (&first)[kDqMaxJobs + 1], int count, int blk) {
+  int j = 0;
+#pragma unroll
+  for (int k = 1; k < kDqMaxJobs; ++k) j = (k < count && first[k] <= blk) ? k : j;
+  return j;
+}
+
+constexpr int kDqBatchThreads = 1024;
+constexpr int kDqBatchVec = 4;
+constexpr int kDqBatchPerThread = 64;   // scales per summing thread (four vectors in flight at a time)
+
+__global__ __launch_bounds__(kDqBatchThreads) void k_dq_partial_batch(DqBatch b, unsigned long long* __restrict__ ws) {
+  const int blk = blockIdx.x;
+  const int j = dq_job_of(b.part0, b.count, blk);
+  const int local = blk - b.part0[j], grid = b.part0[j + 1] - b.part0[j];
+  unsigned long long* rows = ws + static_cast<int64_t>(b.part0[j]) * kDqDigits;
+  if (b.window[j]) dq_partial_body<kDqBatchThreads, true, kDqBatchVec>(b.absmax[j], b.nb[j], rows, local, grid);
+  else dq_partial_body<kDqBatchThreads, false, kDqBatchVec>(b.absmax[j], b.nb[j], rows, local, grid);
+}
+
+// One workgroup per array: the mean from its partial rows (at most
+// kDqMaxGroups, one per thread).
+__global__ __launch_bounds__(kDqMaxGroups) void k_dq_mean_batch(DqBatch b, const unsigned long long* __restrict__ ws) {
+  const int j = blockIdx.x;
+  const unsigned long long* rows = ws + static_cast<int64_t>(b.part0[j]) * kDqDigits;
+  const float mu = dq_mean<kDqMaxGroups>(rows, b.part0[j + 1] - b.part0[j], b.nb[j]);
+  if (threadIdx.x == 0) *b.mean[j] = mu;
+}
+
+// Sized so that every wave has at most kQuantPre groups, all requested at once.
+template <bool kF8>
+__global__ __launch_bounds__(kDqBatchThreads) void k_dq_quant_batch(DqBatch b) {
+  const int blk = blockIdx.x;
+  const int j = dq_job_of(b.quant0, b.count, blk);
+  const int local = blk - b.quant0[j], grid = b.quant0[j + 1] - b.quant0[j];
+  dq_quant_body<kDqBatchThreads, kF8, true>(b.absmax[j], b.nb[j], nullptr, 0, b.mean[j], b.q[j], b.absmax2[j], local,
+                                            grid);
 }
 
 }  // namespace
@@ -403,6 +517,43 @@ hipError_t launch_double_quant(const float* absmax, int64_t nb, int8_t* q, float
     launch_dq<1024, 4>(absmax, nb, q, absmax2, mean, ws, f8, 16, 256, s);
   else
     launch_dq<256, 2>(absmax, nb, q, absmax2, mean, ws, f8, 4, 1024, s);
+  return hipGetLastError();
+}
+
+hipError_t launch_double_quant_batch(const DqJob* jobs, int count, unsigned long long* ws, int f8, hipStream_t s) {
+  if (count < 1 || count > kDqMaxJobs) return hipErrorInvalidValue;
+  DqBatch b{};
+  b.count = count;
+  int parts = 0, quants = 0;
+  for (int j = 0; j < count; ++j) {
+    const int64_t nb = jobs[j].nblocks;
+    b.absmax[j] = jobs[j].absmax;
+    b.nb[j] = nb;
+    b.q[j] = jobs[j].q;
+    b.absmax2[j] = jobs[j].absmax2;
+    b.mean[j] = jobs[j].mean;
+    // summing workgroups: about kDqBatchPerThread scales per thread, at most kDqMaxGroups rows
+    const int64_t pw = (nb + int64_t{kDqBatchThreads} * kDqBatchPerThread - 1) /
+                       (int64_t{kDqBatchThreads} * kDqBatchPerThread);
+    const int g = static_cast<int>(pw < kDqMaxGroups ? pw : kDqMaxGroups);
+    b.window[j] = nb >= static_cast<int64_t>(g) * kDqBatchThreads * 8 ? 1 : 0;
+    // quantizing workgroups: at most kQuantPre groups of 256 scales per wave
+    const int64_t groups = (nb + 255) >> 8;
+    const int64_t per_wg = int64_t{kDqBatchThreads / kWave} * kQuantPre;
+    const int qg = static_cast<int>((groups + per_wg - 1) / per_wg);  // nb < 2^31: at most 2^13
+    b.part0[j] = parts;
+    b.quant0[j] = quants;
+    parts += g;
+    quants += qg;
+  }
+  for (int j = count; j <= kDqMaxJobs; ++j) {
+    b.part0[j] = parts;
+    b.quant0[j] = quants;
+  }
+  hipLaunchKernelGGL(k_dq_partial_batch, dim3(parts), dim3(kDqBatchThreads), 0, s, b, ws);
+  hipLaunchKernelGGL(k_dq_mean_batch, dim3(count), dim3(kDqMaxGroups), 0, s, b, ws);
+  if (f8) hipLaunchKernelGGL(k_dq_quant_batch<true>, dim3(quants), dim3(kDqBatchThreads), 0, s, b);
+  else hipLaunchKernelGGL(k_dq_quant_batch<false>, dim3(quants), dim3(kDqBatchThreads), 0, s, b);
   return hipGetLastError();
 }
 

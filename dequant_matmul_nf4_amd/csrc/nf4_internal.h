@@ -99,6 +99,19 @@ hipError_t launch_quantize(const void* x, int x_bf16, int64_t n, uint8_t* packed
                            float* absmax, const QuantLut& tab, int fp4, hipStream_t s);
 hipError_t launch_double_quant(const float* absmax, int64_t nb, int8_t* q, float* absmax2,
                                float* mean, unsigned long long* ws, int f8, hipStream_t s);
+// Several scale arrays (at most kDqMaxJobs) in one pair of launches; ws holds
+// kDqWorkspaceBytes per array.  Each array's results are those of
+// launch_double_quant on it alone (its mean is an exact sum, whatever the
+// split of the work).
+constexpr int kDqMaxJobs = 8;
+struct DqJob {
+  const float* absmax;
+  int64_t nblocks;
+  int8_t* q;
+  float* absmax2;
+  float* mean;
+};
+hipError_t launch_double_quant_batch(const DqJob* jobs, int count, unsigned long long* ws, int f8, hipStream_t s);
 // Device address of the double quantization's static scratch on the current
 // device (kDqWorkspaceBytes or more, 256-byte aligned), for callers that
 // cannot allocate.  Looked up once per device.

@@ -167,6 +167,34 @@ int nf4_double_quant_f8(const float* absmax, int64_t nblocks, int32_t blocksize2
                         uint8_t* qabsmax, float* absmax2, float* mean,
                         void* workspace, size_t workspace_bytes, void* stream);
 
+/* One scale array of a batched double quantization (device pointers). */
+typedef struct nf4_dq_job {
+  const float* absmax;  /* nblocks float32 scales, 16-byte aligned            */
+  int64_t nblocks;      /* 1 <= nblocks < 2^31                                 */
+  void* qabsmax;        /* out: nblocks int8 (or E4M3) codes, 16-byte aligned  */
+  float* absmax2;       /* out: ceil(nblocks / 256) float32, 4-byte aligned    */
+  float* mean;          /* out: one float32                                    */
+} nf4_dq_job;
+
+/* Bytes of device workspace nf4_double_quant_batched needs for `count`
+ * arrays (24 KiB per array; 0 for count outside 1..8). */
+size_t nf4_double_quant_batched_workspace(int32_t count);
+
+/* The double quantization of the tool page's "Double quantization" section
+ * for 1 to 8 scale arrays at once (for instance the seven weights of one
+ * transformer layer), in one pair of launches instead of one pair per
+ * array.  dq_type NF4_DQ_INT8 gives each array exactly the outputs of
+ * nf4_double_quant on it alone, NF4_DQ_FP8 those of nf4_double_quant_f8:
+ * each array has its own exact mean and its own groups of 256.
+ *   jobs     : count host structs (the struct itself is read on the host).
+ *   workspace: at least nf4_double_quant_batched_workspace(count) bytes,
+ *              16-byte aligned; its contents on entry do not matter.
+ * Outputs of different arrays must not overlap.  Errors as
+ * nf4_double_quant, checked for every array before anything is launched;
+ * NF4_ERR_SIZE for count outside 1..8, NF4_ERR_DTYPE for another dq_type. */
+int nf4_double_quant_batched(const nf4_dq_job* jobs, int32_t count, int32_t blocksize2, int32_t dq_type,
+                             void* workspace, size_t workspace_bytes, void* stream);
+
 /* [host] A quantized weight: a struct holding device pointers.  The logical
  * matrix W[rows][cols] is row-major, element i = r*cols + c, and blocks of 64
  * run along that order.  Exactly one scale form is given:

@@ -214,6 +214,39 @@ CASES += [
 ]
 
 
+def _dqj(**kw):
+    f = dict(absmax=A, nblocks=10, qabsmax=A, absmax2=A2, mean=A2)
+    f.update(kw)
+    return nf4.nf4_dq_job(**f)
+
+
+def _dqb(L, jobs, count=None, blocksize2=256, dq_type=0, ws=A, wsb=8 * WS, stream=None):
+    arr = (nf4.nf4_dq_job * max(len(jobs), 1))(*jobs)
+    return L.nf4_double_quant_batched(arr, len(jobs) if count is None else count, blocksize2, dq_type, ws, wsb, stream)
+
+
+CASES += [
+    ("dq batched null jobs", lambda L: L.nf4_double_quant_batched(None, 1, 256, 0, A, 8 * WS, None), nf4.NF4_ERR_NULL),
+    ("dq batched count 0", lambda L: _dqb(L, [_dqj()], count=0), nf4.NF4_ERR_SIZE),
+    ("dq batched count 9", lambda L: _dqb(L, [_dqj()] * 9), nf4.NF4_ERR_SIZE),
+    ("dq batched blocksize2", lambda L: _dqb(L, [_dqj()], blocksize2=128), nf4.NF4_ERR_BLOCKSIZE),
+    ("dq batched dq_type", lambda L: _dqb(L, [_dqj()], dq_type=2), nf4.NF4_ERR_DTYPE),
+    ("dq batched workspace small", lambda L: _dqb(L, [_dqj(), _dqj()], wsb=L.nf4_double_quant_batched_workspace(2) - 1), nf4.NF4_ERR_WORKSPACE),
+    ("dq batched workspace null", lambda L: _dqb(L, [_dqj()], ws=None), nf4.NF4_ERR_WORKSPACE),
+    ("dq batched misaligned workspace", lambda L: _dqb(L, [_dqj()], ws=A + 8), nf4.NF4_ERR_ALIGN),
+    ("dq batched null mean", lambda L: _dqb(L, [_dqj(), _dqj(mean=None)]), nf4.NF4_ERR_NULL),
+    ("dq batched nblocks 0", lambda L: _dqb(L, [_dqj(), _dqj(nblocks=0)]), nf4.NF4_ERR_SIZE),
+    ("dq batched nblocks 2^31", lambda L: _dqb(L, [_dqj(nblocks=1 << 31)]), nf4.NF4_ERR_SIZE),
+    ("dq batched misaligned q", lambda L: _dqb(L, [_dqj(), _dqj(qabsmax=A + 1)]), nf4.NF4_ERR_ALIGN),
+    ("dq batched misaligned absmax2", lambda L: _dqb(L, [_dqj(absmax2=A2 + 2)]), nf4.NF4_ERR_ALIGN),
+]
+
+
+def test_dq_batched_workspace_size(L):
+    one = L.nf4_double_quant_workspace(1)
+    assert [L.nf4_double_quant_batched_workspace(c) for c in (0, 1, 7, 8, 9)] == [0, one, 7 * one, 8 * one, 0]
+
+
 @pytest.mark.parametrize("name,call,code", CASES, ids=[c[0] for c in CASES])
 def test_invalid_arguments_rejected_on_host(L, name, call, code):
     rc = call(L)
