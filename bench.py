@@ -555,9 +555,9 @@ def build_stack_70b(torch, nf4, syn, dev, stream, EventTimer, layers=80):
     """The 70B-shaped stack.  Layer by layer the seven bf16 weights (q, k, v,
     o, gate, up, down) are drawn on the device (untimed) and then quantized
     and double-quantized into a persistent NF4 store (timed: one HIP graph per
-    layer of seven nf4_quantize launches and one nf4_double_quant_batched call
-    over the seven scale arrays, two launches).  Returns the store and the
-    stack's figures."""
+    layer of one nf4_quantize_batched launch over the seven weights and one
+    nf4_double_quant_batched call over their seven scale arrays).  Returns the
+    store and the stack's figures."""
     layers = max(1, min(int(layers), 80))
     print(f"[bench] 70B stack: {layers} layers", file=sys.stderr, flush=True)
     LAYER_70B = [syn.C5_SHAPES[name] for name in syn.C5_ORDER]
@@ -575,8 +575,7 @@ def build_stack_70b(torch, nf4, syn, dev, stream, EventTimer, layers=80):
                                     mean=torch.empty(1, dtype=torch.float32, device=dev)))
 
         def run():
-            for w, W, am in zip(src, Ws, absmax):
-                nf4.nf4_quantize(w, W.packed, am)
+            nf4.nf4_quantize_batched(src, outs=[(W.packed, am) for W, am in zip(Ws, absmax)])
             nf4.nf4_double_quant_batched(absmax, outs=[(W.qabsmax, W.absmax2, W.mean) for W in Ws], workspace=dq_ws)
 
         graph = capture_graph(torch, run)
@@ -604,8 +603,8 @@ def build_stack_70b(torch, nf4, syn, dev, stream, EventTimer, layers=80):
         "quantize_dq_algorithmic_GBps": round(alg_layer * layers / total_s / 1e9, 1),
         "quantize_dq_frac_hbm_peak": round(alg_layer * layers / total_s / 1e9 / HBM_PEAK_GBS, 4),
         "nf4_store_GB": round(layers * g_bytes / 1e9, 2),
-        "timing": "HIP events around each layer's graph: nf4_quantize of the seven weights, then one "
-                  "nf4_double_quant_batched call over their seven scale arrays",
+        "timing": "HIP events around each layer's graph: one nf4_quantize_batched call over the seven weights, "
+                  "then one nf4_double_quant_batched call over their seven scale arrays",
     }
 
 

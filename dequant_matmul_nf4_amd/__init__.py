@@ -30,7 +30,7 @@ EXPORTS = (
     "nf4_last_error", "nf4_codebook", "nf4_codebook_fp4", "nf4_quantize", "nf4_quantize_fp4", "nf4_double_quant_workspace",
     "nf4_double_quant", "nf4_e4m3_ratio", "nf4_double_quant_f8", "nf4_dequantize", "nf4_gemv", "nf4_gemm_workspace", "nf4_gemm", "nf4_gemm_dx_workspace",
     "nf4_gemm_dx", "nf4_lora_grads_workspace", "nf4_lora_grads", "nf4_lora_merge", "nf4_double_quant_noalloc",
-    "nf4_gemv_batched", "nf4_double_quant_batched_workspace", "nf4_double_quant_batched",
+    "nf4_gemv_batched", "nf4_double_quant_batched_workspace", "nf4_double_quant_batched", "nf4_quantize_batched",
 )
 
 
@@ -38,6 +38,11 @@ class NF4Error(RuntimeError):
     def __init__(self, code: int, message: str):
         super().__init__(f"[{code}] {message}")
         self.code = code
+
+
+class nf4_quantize_job(ctypes.Structure):
+    """Mirror of `struct nf4_quantize_job` in include/nf4.h."""
+    _fields_ = [("x", ctypes.c_void_p), ("n", ctypes.c_int64), ("packed", ctypes.c_void_p), ("absmax", ctypes.c_void_p)]
 
 
 class nf4_dq_job(ctypes.Structure):
@@ -81,6 +86,7 @@ def lib() -> ctypes.CDLL:
         "nf4_double_quant": (ctypes.c_int, [vp, i64, i32, vp, vp, vp, vp, sz, vp]),
         "nf4_double_quant_f8": (ctypes.c_int, [vp, i64, i32, vp, vp, vp, vp, sz, vp]),
         "nf4_double_quant_noalloc": (ctypes.c_int, [vp, i64, i32, vp, vp, vp, vp]),
+        "nf4_quantize_batched": (ctypes.c_int, [ctypes.POINTER(nf4_quantize_job), i32, ctypes.c_int, i32, i32, vp]),
         "nf4_double_quant_batched_workspace": (sz, [i32]),
         "nf4_double_quant_batched": (ctypes.c_int, [ctypes.POINTER(nf4_dq_job), i32, i32, i32, vp, sz, vp]),
         "nf4_e4m3_ratio": (ctypes.c_int, [ctypes.POINTER(ctypes.c_float)]),
@@ -311,6 +317,43 @@ def nf4_double_quant(absmax, qabsmax=None, absmax2=None, mean=None, workspace=No
     _check(fn(_ptr(absmax), nb, BLOCKSIZE2, _ptr(qabsmax), _ptr(absmax2), _ptr(mean),
               _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream)))
     return qabsmax, absmax2, mean
+
+
+def nf4_quantize_batched(xs, outs=None, stream=None, fp4=False):
+    """nf4_quantize (fp4=True: nf4_quantize_fp4) of 1 to 8 tensors of one dtype
+    in one launch; each tensor's outputs are those of the single call.
+    outs: optional list of (packed, absmax) per tensor.  Returns the list of
+    (packed, absmax)."""
+    torch = _torch()
+    xs = list(xs)
+    if not 1 <= len(xs) <= 8:
+        raise ValueError("1 to 8 tensors")
+    _need_cuda(*xs)
+    dt = xs[0].dtype
+    if dt not in (torch.float32, torch.bfloat16) or any(x.dtype != dt for x in xs):
+        raise TypeError("all tensors float32, or all bf16")
+    for x in xs:
+        if not x.is_contiguous():
+            raise ValueError("tensors must be contiguous")
+    dev = xs[0].device
+    if outs is None:
+        outs = [(_alloc_on(stream, ((x.numel() + 1) // 2,), torch.uint8, dev),
+                 _alloc_on(stream, ((x.numel() + 63) // 64,), torch.float32, dev)) for x in xs]
+    outs = [tuple(o) for o in outs]
+    if len(outs) != len(xs):
+        raise ValueError("one (packed, absmax) per tensor")
+    for x, (p, a) in zip(xs, outs):
+        _need_cuda(p, a)
+        _same_device(dev, x, p, a)
+        if p.dtype != torch.uint8 or a.dtype != torch.float32:
+            raise TypeError("packed must be uint8 and absmax float32")
+        if p.numel() < (x.numel() + 1) // 2 or a.numel() < (x.numel() + 63) // 64:
+            raise ValueError("output buffers too small")
+    jobs = (nf4_quantize_job * len(xs))(*[nf4_quantize_job(_ptr(x), x.numel(), _ptr(p), _ptr(a))
+                                          for x, (p, a) in zip(xs, outs)])
+    _check(lib().nf4_quantize_batched(jobs, len(xs), NF4_BF16 if dt == torch.bfloat16 else NF4_F32, BLOCKSIZE,
+                                      NF4_QT_FP4 if fp4 else NF4_QT_NF4, _stream(stream)))
+    return outs
 
 
 def nf4_double_quant_batched(absmaxes, outs=None, workspace=None, stream=None, fp8=False):

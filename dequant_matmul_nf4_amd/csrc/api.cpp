@@ -174,6 +174,34 @@ int nf4_quantize_fp4(const void* x, int x_dtype, int64_t n, int32_t blocksize, u
   return quantize(x, x_dtype, n, blocksize, packed, absmax, stream, 1, "nf4_quantize_fp4");
 }
 
+int nf4_quantize_batched(const nf4_quantize_job* jobs, int32_t count, int x_dtype, int32_t blocksize,
+                         int32_t quant_type, void* stream) {
+  const char* who = "nf4_quantize_batched";
+  if (!jobs) return fail(NF4_ERR_NULL, "%s: jobs is NULL", who);
+  if (count < 1 || count > nf4i::kQuantMaxJobs)
+    return fail(NF4_ERR_SIZE, "%s: count = %d out of range 1..%d", who, (int)count, nf4i::kQuantMaxJobs);
+  if (x_dtype != NF4_F32 && x_dtype != NF4_BF16) return fail(NF4_ERR_DTYPE, "%s: x_dtype %d unknown", who, x_dtype);
+  if (blocksize != NF4_BLOCKSIZE) return fail(NF4_ERR_BLOCKSIZE, "%s: blocksize %d unsupported (only 64)", who, (int)blocksize);
+  if (quant_type != NF4_QT_NF4 && quant_type != NF4_QT_FP4)
+    return fail(NF4_ERR_DTYPE, "%s: quant_type %d unknown", who, (int)quant_type);
+  nf4i::QuantJob qj[nf4i::kQuantMaxJobs];
+  for (int i = 0; i < count; ++i) {
+    const nf4_quantize_job& j = jobs[i];
+    if (!j.x || !j.packed || !j.absmax) return fail(NF4_ERR_NULL, "%s: tensor %d: x, packed and absmax are required", who, i);
+    if (j.n < 1 || j.n >= kMaxN) return fail(NF4_ERR_SIZE, "%s: tensor %d: n = %lld out of range", who, i, (long long)j.n);
+    if (!aligned(j.x, 16) || !aligned(j.packed, 16))
+      return fail(NF4_ERR_ALIGN, "%s: tensor %d: x and packed must be 16-byte aligned", who, i);
+    if (!aligned(j.absmax, 4)) return fail(NF4_ERR_ALIGN, "%s: tensor %d: absmax must be 4-byte aligned", who, i);
+    qj[i] = nf4i::QuantJob{j.x, j.n, j.packed, j.absmax};
+  }
+  const int fp4 = quant_type == NF4_QT_FP4 ? 1 : 0;
+  const char* lut_err = "";
+  const nf4i::QuantLut* lut = nf4i::quant_lut(fp4, &lut_err);
+  if (!lut) return fail(NF4_ERR_INTERNAL, "%s: %s", who, lut_err);
+  if (int rc = check_device()) return rc;
+  return launched(nf4i::launch_quantize_batch(qj, count, x_dtype == NF4_BF16, *lut, fp4, as_stream(stream)), who);
+}
+
 size_t nf4_double_quant_workspace(int64_t nblocks) {
   (void)nblocks;
   return nf4i::kDqWorkspaceBytes;

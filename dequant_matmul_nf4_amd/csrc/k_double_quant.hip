@@ -421,21 +421,13 @@ struct DqBatch {
   int quant0[kDqMaxJobs + 1];
 };
 
-// The array a workgroup belongs to: the last j with first[j] <= blk.
-__device__ __forceinline__ int dq_job_of(const int (&first)[kDqMaxJobs + 1], int count, int blk) {
-  int j = 0;
-#pragma unroll
-  for (int k = 1; k < kDqMaxJobs; ++k) j = (k < count && first[k] <= blk) ? k : j;
-  return j;
-}
-
 constexpr int kDqBatchThreads = 1024;
 constexpr int kDqBatchVec = 4;
 constexpr int kDqBatchPerThread = 64;   // scales per summing thread (four vectors in flight at a time)
 
 __global__ __launch_bounds__(kDqBatchThreads) void k_dq_partial_batch(DqBatch b, unsigned long long* __restrict__ ws) {
   const int blk = blockIdx.x;
-  const int j = dq_job_of(b.part0, b.count, blk);
+  const int j = batch_item_of<kDqMaxJobs>(b.part0, b.count, blk);
   const int local = blk - b.part0[j], grid = b.part0[j + 1] - b.part0[j];
   unsigned long long* rows = ws + static_cast<int64_t>(b.part0[j]) * kDqDigits;
   if (b.window[j]) dq_partial_body<kDqBatchThreads, true, kDqBatchVec>(b.absmax[j], b.nb[j], rows, local, grid);
@@ -455,7 +447,7 @@ __global__ __launch_bounds__(kDqMaxGroups) void k_dq_mean_batch(DqBatch b, const
 template <bool kF8>
 __global__ __launch_bounds__(kDqBatchThreads) void k_dq_quant_batch(DqBatch b) {
   const int blk = blockIdx.x;
-  const int j = dq_job_of(b.quant0, b.count, blk);
+  const int j = batch_item_of<kDqMaxJobs>(b.quant0, b.count, blk);
   const int local = blk - b.quant0[j], grid = b.quant0[j + 1] - b.quant0[j];
   dq_quant_body<kDqBatchThreads, kF8, true>(b.absmax[j], b.nb[j], nullptr, 0, b.mean[j], b.q[j], b.absmax2[j], local,
                                             grid);

@@ -113,26 +113,28 @@ __device__ __forceinline__ void quantize_segment(const float v[kPerLane], int64_
   if ((threadIdx.x & 3) == 0) absmax[sg >> 2] = a;
 }
 
-// Main loop over the blocks that hold 64 values: each lane takes two
-// segments per iteration and issues both loads before using either; there
-// is no branch around any load.  A partial last block is done afterwards by
-// the first quad of workgroup 0 with guarded loads and stores.
-template <bool kBf16, bool kFp4>
-__global__ __launch_bounds__(256) void k_quantize(const void* __restrict__ x, int64_t n,
-                                                  uint8_t* __restrict__ packed,
-                                                  float* __restrict__ absmax, QuantLut tab) {
-  __shared__ uint2 lut[kLutBuckets];
+// The bucket table in LDS (ends with a barrier).
+__device__ __forceinline__ void fill_lut(uint2* lut, const QuantLut& tab) {
   for (int i = threadIdx.x; i < kLutBuckets; i += blockDim.x) lut[i] = make_uint2(0x7F800000u, 7u);
   __syncthreads();
   if (threadIdx.x < kLutSpecial)
     lut[lut_special_index(threadIdx.x)] = make_uint2(__float_as_uint(tab.thr[threadIdx.x]), tab.base[threadIdx.x]);
   __syncthreads();
+}
 
+// Workgroup `blk` of `grid` over one tensor.  Main loop over the blocks that
+// hold 64 values: each lane takes two segments per iteration and issues both
+// loads before using either; there is no branch around any load.  A partial
+// last block is done afterwards by the first quad of workgroup 0 with
+// guarded loads and stores.
+template <bool kBf16, bool kFp4>
+__device__ __forceinline__ void quantize_body(const void* __restrict__ x, int64_t n, uint8_t* __restrict__ packed,
+                                              float* __restrict__ absmax, const uint2* lut, int blk, int grid) {
   const int64_t nfull = n >> 6;
   const int64_t nseg = nfull * 4;
   const int64_t nbytes = (n + 1) >> 1;
-  const int64_t stride = static_cast<int64_t>(gridDim.x) * blockDim.x;
-  for (int64_t sg0 = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; sg0 < nseg; sg0 += 2 * stride) {
+  const int64_t stride = static_cast<int64_t>(grid) * blockDim.x;
+  for (int64_t sg0 = static_cast<int64_t>(blk) * blockDim.x + threadIdx.x; sg0 < nseg; sg0 += 2 * stride) {
     const int64_t sg1 = sg0 + stride;
     const int64_t sg1c = sg1 < nseg ? sg1 : sg0;  // clamped: the load is always issued
     float v0[kPerLane], v1[kPerLane];
@@ -141,7 +143,7 @@ __global__ __launch_bounds__(256) void k_quantize(const void* __restrict__ x, in
     quantize_segment<kFp4>(v0, sg0, packed, absmax, lut, nbytes, true);
     if (sg1 < nseg) quantize_segment<kFp4>(v1, sg1, packed, absmax, lut, nbytes, true);
   }
-  if ((n & 63) && blockIdx.x == 0 && threadIdx.x < 4) {
+  if ((n & 63) && blk == 0 && threadIdx.x < 4) {
     const int64_t sg = nseg + threadIdx.x;
     float v[kPerLane];
 #pragma unroll
@@ -154,22 +156,85 @@ __global__ __launch_bounds__(256) void k_quantize(const void* __restrict__ x, in
   }
 }
 
+template <bool kBf16, bool kFp4>
+__global__ __launch_bounds__(256) void k_quantize(const void* __restrict__ x, int64_t n,
+                                                  uint8_t* __restrict__ packed,
+                                                  float* __restrict__ absmax, QuantLut tab) {
+  __shared__ uint2 lut[kLutBuckets];
+  fill_lut(lut, tab);
+  quantize_body<kBf16, kFp4>(x, n, packed, absmax, lut, blockIdx.x, gridDim.x);
+}
+
+// Several tensors in one launch: wg0[j] is the first workgroup of tensor j
+// (wg0[count] the total).
+struct QuantBatch {
+  int count;
+  const void* x[kQuantMaxJobs];
+  int64_t n[kQuantMaxJobs];
+  uint8_t* packed[kQuantMaxJobs];
+  float* absmax[kQuantMaxJobs];
+  int wg0[kQuantMaxJobs + 1];
+};
+
+template <bool kBf16, bool kFp4>
+__global__ __launch_bounds__(256) void k_quantize_batch(QuantBatch b, QuantLut tab) {
+  __shared__ uint2 lut[kLutBuckets];
+  fill_lut(lut, tab);
+  const int blk = blockIdx.x;
+  const int j = batch_item_of<kQuantMaxJobs>(b.wg0, b.count, blk);
+  quantize_body<kBf16, kFp4>(b.x[j], b.n[j], b.packed[j], b.absmax[j], lut, blk - b.wg0[j], b.wg0[j + 1] - b.wg0[j]);
+}
+
+}  // namespace
+
+namespace {
+// two segments per lane and one pass per lane: a loop would make the next
+// loads wait for the previous stores (their registers are reused)
+int64_t quantize_grid(int64_t n) {
+  const int64_t nseg = (n >> 6) * 4;
+  const int64_t want = (nseg + 511) / 512;
+  return want < 1 ? 1 : want;
+}
 }  // namespace
 
 hipError_t launch_quantize(const void* x, int x_bf16, int64_t n, uint8_t* packed, float* absmax,
                            const QuantLut& tab, int fp4, hipStream_t s) {
-  // two segments per lane and one pass per lane: a loop would make the next
-  // loads wait for the previous stores (their registers are reused)
-  const int64_t nseg = (n >> 6) * 4;
-  const int64_t want = (nseg + 511) / 512;
+  const int64_t want = quantize_grid(n);
   if (want > 0x7FFFFFFF) return hipErrorInvalidValue;
-  const int grid = static_cast<int>(want < 1 ? 1 : want);
+  const int grid = static_cast<int>(want);
   if (fp4) {
     if (x_bf16) hipLaunchKernelGGL((k_quantize<true, true>), dim3(grid), dim3(256), 0, s, x, n, packed, absmax, tab);
     else hipLaunchKernelGGL((k_quantize<false, true>), dim3(grid), dim3(256), 0, s, x, n, packed, absmax, tab);
   } else {
     if (x_bf16) hipLaunchKernelGGL((k_quantize<true, false>), dim3(grid), dim3(256), 0, s, x, n, packed, absmax, tab);
     else hipLaunchKernelGGL((k_quantize<false, false>), dim3(grid), dim3(256), 0, s, x, n, packed, absmax, tab);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_quantize_batch(const QuantJob* jobs, int count, int x_bf16, const QuantLut& tab, int fp4,
+                                 hipStream_t s) {
+  if (count < 1 || count > kQuantMaxJobs) return hipErrorInvalidValue;
+  QuantBatch b{};
+  b.count = count;
+  int64_t total = 0;
+  for (int j = 0; j < count; ++j) {
+    b.x[j] = jobs[j].x;
+    b.n[j] = jobs[j].n;
+    b.packed[j] = jobs[j].packed;
+    b.absmax[j] = jobs[j].absmax;
+    b.wg0[j] = static_cast<int>(total);
+    total += quantize_grid(jobs[j].n);
+    if (total > 0x7FFFFFFF) return hipErrorInvalidValue;
+  }
+  for (int j = count; j <= kQuantMaxJobs; ++j) b.wg0[j] = static_cast<int>(total);
+  const dim3 grid(static_cast<unsigned>(total));
+  if (fp4) {
+    if (x_bf16) hipLaunchKernelGGL((k_quantize_batch<true, true>), grid, dim3(256), 0, s, b, tab);
+    else hipLaunchKernelGGL((k_quantize_batch<false, true>), grid, dim3(256), 0, s, b, tab);
+  } else {
+    if (x_bf16) hipLaunchKernelGGL((k_quantize_batch<true, false>), grid, dim3(256), 0, s, b, tab);
+    else hipLaunchKernelGGL((k_quantize_batch<false, false>), grid, dim3(256), 0, s, b, tab);
   }
   return hipGetLastError();
 }

@@ -65,6 +65,17 @@ __device__ __forceinline__ float group_max(float v) {
   return v;
 }
 
+// Batched launches: the item (weight or scale array) a workgroup belongs to,
+// the last j < count with first[j] <= blk (first[] holds each item's first
+// workgroup, ascending).
+template <int N>
+__device__ __forceinline__ int batch_item_of(const int (&first)[N + 1], int count, int blk) {
+  int j = 0;
+#pragma unroll
+  for (int k = 1; k < N; ++k) j = (k < count && first[k] <= blk) ? k : j;
+  return j;
+}
+
 __device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, kWave);

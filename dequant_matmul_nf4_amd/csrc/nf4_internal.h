@@ -97,6 +97,17 @@ constexpr size_t kDqWorkspaceBytes = kDqMaxGroups * kDqDigits * sizeof(unsigned 
 
 hipError_t launch_quantize(const void* x, int x_bf16, int64_t n, uint8_t* packed,
                            float* absmax, const QuantLut& tab, int fp4, hipStream_t s);
+// Several tensors (at most kQuantMaxJobs, one input dtype and code book) in
+// one launch; each tensor's codes and absmax are those of launch_quantize.
+constexpr int kQuantMaxJobs = 8;
+struct QuantJob {
+  const void* x;
+  int64_t n;
+  uint8_t* packed;
+  float* absmax;
+};
+hipError_t launch_quantize_batch(const QuantJob* jobs, int count, int x_bf16, const QuantLut& tab, int fp4,
+                                 hipStream_t s);
 hipError_t launch_double_quant(const float* absmax, int64_t nb, int8_t* q, float* absmax2,
                                float* mean, unsigned long long* ws, int f8, hipStream_t s);
 // Several scale arrays (at most kDqMaxJobs) in one pair of launches; ws holds

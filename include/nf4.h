@@ -113,6 +113,26 @@ int nf4_quantize(const void* x, int x_dtype, int64_t n, int32_t blocksize,
 int nf4_quantize_fp4(const void* x, int x_dtype, int64_t n, int32_t blocksize,
                      uint8_t* packed, float* absmax, void* stream);
 
+/* One tensor of a batched quantization (device pointers). */
+typedef struct nf4_quantize_job {
+  const void* x;    /* n values (x_dtype of the call), 16-byte aligned      */
+  int64_t n;        /* 1 <= n < 2^40                                         */
+  uint8_t* packed;  /* out: ceil(n/2) bytes, 16-byte aligned                 */
+  float* absmax;    /* out: ceil(n/64) float32, 4-byte aligned               */
+} nf4_quantize_job;
+
+/* The blockwise quantization of the tool page's "How it works", Steps 1-4,
+ * for 1 to 8 tensors (for instance the seven weights of one transformer
+ * layer) in one launch instead of one per tensor.  All tensors share
+ * x_dtype and the code book: quant_type NF4_QT_NF4 gives each tensor exactly
+ * the outputs of nf4_quantize on it alone, NF4_QT_FP4 those of
+ * nf4_quantize_fp4.  jobs: count host structs.  Outputs of different
+ * tensors must not overlap.  Errors as nf4_quantize, checked for every
+ * tensor before anything is launched; NF4_ERR_SIZE for count outside 1..8,
+ * NF4_ERR_DTYPE for another quant_type. */
+int nf4_quantize_batched(const nf4_quantize_job* jobs, int32_t count, int x_dtype, int32_t blocksize,
+                         int32_t quant_type, void* stream);
+
 /* Bytes of device workspace nf4_double_quant needs (a small constant). */
 size_t nf4_double_quant_workspace(int64_t nblocks);
 

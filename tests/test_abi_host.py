@@ -242,6 +242,32 @@ CASES += [
 ]
 
 
+def _qj(**kw):
+    f = dict(x=A, n=128, packed=A, absmax=A2)
+    f.update(kw)
+    return nf4.nf4_quantize_job(**f)
+
+
+def _qb(L, jobs, count=None, x_dtype=1, blocksize=64, quant_type=0):
+    arr = (nf4.nf4_quantize_job * max(len(jobs), 1))(*jobs)
+    return L.nf4_quantize_batched(arr, len(jobs) if count is None else count, x_dtype, blocksize, quant_type, None)
+
+
+CASES += [
+    ("quantize batched null jobs", lambda L: L.nf4_quantize_batched(None, 1, 1, 64, 0, None), nf4.NF4_ERR_NULL),
+    ("quantize batched count 0", lambda L: _qb(L, [_qj()], count=0), nf4.NF4_ERR_SIZE),
+    ("quantize batched count 9", lambda L: _qb(L, [_qj()] * 9), nf4.NF4_ERR_SIZE),
+    ("quantize batched dtype", lambda L: _qb(L, [_qj()], x_dtype=5), nf4.NF4_ERR_DTYPE),
+    ("quantize batched blocksize", lambda L: _qb(L, [_qj()], blocksize=128), nf4.NF4_ERR_BLOCKSIZE),
+    ("quantize batched quant_type", lambda L: _qb(L, [_qj()], quant_type=2), nf4.NF4_ERR_DTYPE),
+    ("quantize batched null packed", lambda L: _qb(L, [_qj(), _qj(packed=None)]), nf4.NF4_ERR_NULL),
+    ("quantize batched n 0", lambda L: _qb(L, [_qj(), _qj(n=0)]), nf4.NF4_ERR_SIZE),
+    ("quantize batched n 2^40", lambda L: _qb(L, [_qj(n=1 << 40)]), nf4.NF4_ERR_SIZE),
+    ("quantize batched misaligned x", lambda L: _qb(L, [_qj(), _qj(x=A + 2)]), nf4.NF4_ERR_ALIGN),
+    ("quantize batched misaligned absmax", lambda L: _qb(L, [_qj(absmax=A2 + 2)]), nf4.NF4_ERR_ALIGN),
+]
+
+
 def test_dq_batched_workspace_size(L):
     one = L.nf4_double_quant_workspace(1)
     assert [L.nf4_double_quant_batched_workspace(c) for c in (0, 1, 7, 8, 9)] == [0, one, 7 * one, 8 * one, 0]
