@@ -434,6 +434,30 @@ def quantize_weight(w, double_quant: bool = True, stream=None, dq_type: str = "i
                      quant_type=qt)
 
 
+def quantize_weights(ws, double_quant: bool = True, stream=None, dq_type: str = "int8",
+                     quant_type: str = "nf4") -> list:
+    """quantize_weight for 1 to 8 2-D weights of one dtype (for instance the
+    seven weights of a transformer layer) through one nf4_quantize_batched
+    launch and one nf4_double_quant_batched call; each NF4Weight holds
+    exactly what quantize_weight gives for that weight."""
+    if quant_type not in ("nf4", "fp4"):
+        raise ValueError("quant_type must be 'nf4' or 'fp4'")
+    if dq_type not in ("int8", "fp8"):
+        raise ValueError("dq_type must be 'int8' or 'fp8'")
+    ws = list(ws)
+    if any(w.dim() != 2 for w in ws):
+        raise ValueError("weights must be 2-D")
+    qt = NF4_QT_FP4 if quant_type == "fp4" else NF4_QT_NF4
+    codes = nf4_quantize_batched(ws, stream=stream, fp4=qt == NF4_QT_FP4)
+    if not double_quant:
+        return [NF4Weight(p, w.shape[0], w.shape[1], absmax=a, quant_type=qt) for w, (p, a) in zip(ws, codes)]
+    fp8 = dq_type == "fp8"
+    scales = nf4_double_quant_batched([a for _, a in codes], stream=stream, fp8=fp8)
+    return [NF4Weight(p, w.shape[0], w.shape[1], qabsmax=q, absmax2=s2, mean=mu,
+                      dq_type=NF4_DQ_FP8 if fp8 else NF4_DQ_INT8, quant_type=qt)
+            for w, (p, _), (q, s2, mu) in zip(ws, codes, scales)]
+
+
 def nf4_dequantize(w: NF4Weight, out=None, out_dtype=None, stream=None):
     torch = _torch()
     cs = w.c_struct()

@@ -74,3 +74,25 @@ def test_batched_70b_layer_weights():
         assert torch.equal(q, W.qabsmax), name
         assert torch.equal(s2.view(torch.int32), W.absmax2.view(torch.int32)), name
         assert torch.equal(mu.view(torch.int32), W.mean.view(torch.int32)), name
+
+
+@pytest.mark.parametrize("qt,dq", [("nf4", "int8"), ("fp4", "fp8"), ("nf4", None)])
+def test_quantize_weights_matches_quantize_weight(qt, dq):
+    """The binding's quantize_weights (the two batched calls) against
+    quantize_weight on each of three weights of different shapes."""
+    torch = need_gpu()
+    say("quantize_weights", qt, dq)
+    shapes = [(300, 1024), (64, 64), (1024, 4160)]
+    ws = [_x(torch, r * c, 50 + i, torch.bfloat16).reshape(r, c) for i, (r, c) in enumerate(shapes)]
+    got = nf4.quantize_weights(ws, double_quant=dq is not None, dq_type=dq or "int8", quant_type=qt)
+    ref = [nf4.quantize_weight(w, double_quant=dq is not None, dq_type=dq or "int8", quant_type=qt) for w in ws]
+    torch.cuda.synchronize()
+    for a, b in zip(got, ref):
+        assert (a.rows, a.cols, a.dq_type, a.quant_type) == (b.rows, b.cols, b.dq_type, b.quant_type)
+        assert torch.equal(a.packed, b.packed)
+        for f in ("absmax", "qabsmax", "absmax2", "mean"):
+            x, y = getattr(a, f), getattr(b, f)
+            assert (x is None) == (y is None), f
+            if x is not None:
+                assert torch.equal(x.view(torch.uint8), y.view(torch.uint8)), f
+
