@@ -471,19 +471,20 @@ hipError_t launch_rows_sc(const uint8_t* packed, int64_t rows, int64_t cols, Sca
 
 // ---------------------------------------------------------------- m = 2..16
 //
-// Skinny products on the matrix cores: v_mfma_f32_16x16x32_f16 with x (its
-// m <= 16 rows, padded with zeros) as the A operand and the NF4 levels of 16
-// weight rows as the B operand, D[x row][weight row].
-//  - B needs no arithmetic: a byte of codes indexes the fp16 level-pair table
-//    (one permute, one LDS read) and the pair is already an operand word.
-//    The two MFMAs of a 64-block start from zero; the block's scale (one per
-//    weight row, i.e. per lane column of D) is then applied with 4 FMAs.
-//  - k order inside a block: lane group g = lane / 16 takes codes
-//    16 g .. 16 g + 15 (bytes 8 g .. 8 g + 7), the first 8 for the first MFMA
-//    and the rest for the second, for both operands.
-//  - x: a wave owns a column segment of at most 8 blocks and keeps it in
-//    registers as fp16, each x row scaled by a power of two chosen from its
-//    largest |x| in the segment (undone on the segment's partial sums).
+// Skinny products on the matrix cores: v_mfma_f32_16x16x32_bf16 with x (its
+// m <= 16 rows; rows past m repeat row m - 1 and are never stored) as the A
+// operand and 16 weight rows as the B operand, D[x row][weight row].
+//  - B is the dequantized weight rounded once to bf16, bf16(fl32(level * a))
+//    with a the block's scale, as the GEMM expands it: a byte of codes
+//    indexes a table of fp32 level pairs (one permute, one LDS read), both
+//    levels are multiplied by a and the pair is rounded to one operand word.
+//    With the scale inside the operand an MFMA may span two blocks, so a lane
+//    loads 16 contiguous code bytes and a wave instruction reads 64 bytes of
+//    each of its 16 rows.
+//  - k order of a 4-block segment: lane group g = lane / 16 takes, for
+//    h = 0, 1, codes 32 (g % 2) .. + 31 of block 2 h + g / 2 (code bytes
+//    16 (g % 2) .. + 15), 8 per MFMA, and x the same columns, so that x
+//    needs no conversion.
 //  - Weight rows go in groups of 16, interleaved over the grid (group p of a
 //    workgroup is p-th of its share); waves walk the workgroup's groups for
 //    each of their segments and park each (group, segment) partial tile in
@@ -500,7 +501,6 @@ constexpr int kPartTiles = 64;   // 16 x 16 float partial tiles per workgroup (6
 constexpr int kMfmaSeg = 4;      // blocks per column segment (x kept in registers)
 constexpr int kMfmaWaves = 16;
 
-typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
 typedef float floatx4 __attribute__((ext_vector_type(4)));
 
 struct MfmaPlan {
@@ -510,18 +510,29 @@ struct MfmaPlan {
   int kmax;          // row groups per workgroup, at most
 };
 
-// The loads of one (row group, segment): for weight row n = lane % 16, the 8
-// code bytes 8 g .. 8 g + 7 of each of the segment's blocks and the blocks'
-// scale inputs.  kQ4: the segment is 4 blocks starting at a multiple of 4 in
-// the flattened block order, so the 4 int8 codes (or 4 absmax) are one
-// aligned load and the group scales are the two that can occur.
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ uint32_t sk_bf16_pair(float lo, float hi) {
+  const bf16x2_t p = {static_cast<__bf16>(lo), static_cast<__bf16>(hi)};
+  return __builtin_bit_cast(uint32_t, p);
+}
+
+// The loads of one (row group, segment): for weight row ln = lane % 16 the
+// 16 code bytes 16 (g % 2) .. + 15 of blocks 2 h + g / 2 (h = 0, 1) of the
+// segment and those blocks' scale inputs, kept as loaded until they are used.
+// kQ4: the segment is 4 blocks starting at a multiple of 4 in the flattened
+// block order, so the 4 int8 codes (or 4 absmax) are one aligned load and the
+// group scales are the two that can occur.
 template <bool kDQ>
 struct SegItem {
-  uint2 c[kMfmaSeg];
-  float am[kMfmaSeg];
-  int q[kMfmaSeg];
+  uint4 c[2];
+  uint32_t q4;    // kQ4, double quant: the segment's 4 int8 codes
+  float4 a4;      // kQ4, plain scales: the segment's 4 absmax
+  int q[2];       // otherwise, per h: int8 code and group scale, or absmax
+  float am[2];
   float s2lo, s2hi;
-  int cross;   // blocks j >= cross of the segment use s2hi
+  int cross;      // blocks j >= cross of the segment use s2hi
 };
 
 template <bool kDQ, bool kQ4>
@@ -529,32 +540,31 @@ __device__ __forceinline__ void seg_load(SegItem<kDQ>& it, const uint8_t* __rest
                                          int64_t row, int64_t b0, int nb, int g, Scales sc, int64_t ngroups2) {
   const int64_t rb = row * nblk + b0;
 #pragma unroll
-  for (int j = 0; j < kMfmaSeg; ++j) {
-    const int64_t b = rb + (j < nb ? j : nb - 1);
-    it.c[j] = *reinterpret_cast<const uint2*>(packed + b * 32 + 8 * g);
+  for (int h = 0; h < 2; ++h) {
+    const int pj = 2 * h + (g >> 1);
+    const int64_t b = rb + (pj < nb ? pj : nb - 1);
+    it.c[h] = *reinterpret_cast<const uint4*>(packed + b * 32 + 16 * (g & 1));
   }
   if constexpr (kQ4) {
     if constexpr (kDQ) {
-      const uint32_t q4 = *reinterpret_cast<const uint32_t*>(sc.q + rb);
-#pragma unroll
-      for (int j = 0; j < kMfmaSeg; ++j) it.q[j] = static_cast<int>(static_cast<int8_t>(q4 >> (8 * j)));
+      it.q4 = *reinterpret_cast<const uint32_t*>(sc.q + rb);
       const int64_t g0 = rb >> 8;
       it.s2lo = sc.absmax2[g0];
       it.s2hi = sc.absmax2[g0 + 1 < ngroups2 ? g0 + 1 : g0];
       it.cross = 256 - static_cast<int>(rb & 255);
     } else {
-      const float4 a4 = *reinterpret_cast<const float4*>(sc.absmax + rb);
-      it.am[0] = a4.x; it.am[1] = a4.y; it.am[2] = a4.z; it.am[3] = a4.w;
+      it.a4 = *reinterpret_cast<const float4*>(sc.absmax + rb);
     }
   } else {
 #pragma unroll
-    for (int j = 0; j < kMfmaSeg; ++j) {
-      const int64_t b = rb + (j < nb ? j : nb - 1);
+    for (int h = 0; h < 2; ++h) {
+      const int pj = 2 * h + (g >> 1);
+      const int64_t b = rb + (pj < nb ? pj : nb - 1);
       if constexpr (kDQ) {
-        it.q[j] = sc.q[b];
-        it.am[j] = sc.absmax2[b >> 8];  // the block's group scale
+        it.q[h] = sc.q[b];
+        it.am[h] = sc.absmax2[b >> 8];
       } else {
-        it.am[j] = sc.absmax[b];
+        it.am[h] = sc.absmax[b];
       }
     }
   }
@@ -564,134 +574,115 @@ template <int kWaves, bool kDQ, bool kF8, bool kQ4, bool kBf16Out>
 __global__ __launch_bounds__(kWaves * 64) void k_gemv_mfma(const uint8_t* __restrict__ packed, int64_t rows,
                                                            int64_t cols, Scales sc, const uint16_t* __restrict__ x,
                                                            int m, void* __restrict__ y, Codebook cb, MfmaPlan pl) {
-  __shared__ uint32_t tab[256 * 64];
+  __shared__ __align__(16) float2 tab[256 * 32];
   __shared__ float part[kPartTiles * 256];
-  __shared__ float rtab[kF8 ? 256 : 1];  // float8 ratio table
+  __shared__ float rtab[kF8 ? 256 : 1];
   const char* smem = reinterpret_cast<const char*>(tab);
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int g = lane >> 4;       // lane group
-  const int ln = lane & 15;      // x row (A) / weight row in the group (B, D column)
-  const uint32_t slot = static_cast<uint32_t>(lane) << 2;
+  const int g = lane >> 4;
+  const int ln = lane & 15;
+  const uint32_t slot = static_cast<uint32_t>(lane & 31) << 3;
   const int64_t nblk = cols / 64;
   const int64_t ngroups = (rows + 15) / 16;
   const int64_t G = gridDim.x;
   const int64_t kmine = (static_cast<int64_t>(blockIdx.x) < ngroups) ? (ngroups - blockIdx.x + G - 1) / G : 0;
-  const int64_t ngroups2 = (rows * nblk + 255) / 256;  // second-level scales
+  const int64_t ngroups2 = (rows * nblk + 255) / 256;
   const float mean = kDQ ? *sc.mean : 0.0f;
   if constexpr (kF8)
     for (int i = threadIdx.x; i < 256; i += kWaves * 64) rtab[i] = kE4m3Ratio.v[i];
-  fill_half_table<kWaves * 64>(tab, cb);  // ends with a barrier
+  {
+    // the 256 fp32 level pairs (element 2j = high nibble first), 32 copies:
+    // entry e of copy c at byte 256 e + 8 c, a lane reads copy lane % 32
+    const int e = threadIdx.x & 255;
+    const int pp = threadIdx.x >> 8;
+    constexpr int kParts = kWaves * 64 / 256;
+    float l0 = cb.level[0], l1 = cb.level[0];
+#pragma unroll
+    for (int i = 1; i < 16; ++i) {
+      l0 = ((e >> 4) == i) ? cb.level[i] : l0;
+      l1 = ((e & 15) == i) ? cb.level[i] : l1;
+    }
+    const float2 v = make_float2(l0, l1);
+#pragma unroll
+    for (int j = 0; j < 32 / kParts; ++j) tab[e * 32 + ((j * kParts + pp + e) & 31)] = v;
+  }
+  __syncthreads();
 
   for (int seg = wave; seg < pl.nseg; seg += kWaves) {
     const int64_t b0 = static_cast<int64_t>(seg) * pl.seg_blocks;
     const int nb = static_cast<int>(nblk - b0 < pl.seg_blocks ? nblk - b0 : pl.seg_blocks);
-    // x of the segment: lane (row ln, group g) takes columns 16 g .. 16 g + 15
-    // of each block, as fp16 pairs scaled by 2^k(ln)
-    uint32_t xh[kMfmaSeg][8];
-    float xinv_d[4];
+    // x of the segment as the A operand: lane (row ln, group g) holds, for
+    // h = 0, 1, columns 32 (g % 2) .. + 31 of block 2 h + g / 2
+    uint4 xv[2][4];
     {
-      uint4 xv[kMfmaSeg][2];
-      const bool live = ln < m;
-      const uint16_t* xr = x + static_cast<int64_t>(live ? ln : 0) * cols;
+      // rows past m repeat row m - 1: a row of A only reaches the same row of D,
+      // and those rows are never stored
+      const uint16_t* xr = x + static_cast<int64_t>(ln < m ? ln : m - 1) * cols;
 #pragma unroll
-      for (int j = 0; j < kMfmaSeg; ++j) {
-        const int64_t blk = b0 + (j < nb ? j : nb - 1);
-        const uint4* p = reinterpret_cast<const uint4*>(xr + blk * 64 + 16 * g);
-        xv[j][0] = live ? p[0] : make_uint4(0, 0, 0, 0);
-        xv[j][1] = live ? p[1] : make_uint4(0, 0, 0, 0);
+      for (int h = 0; h < 2; ++h) {
+        const int pj = 2 * h + (g >> 1);
+        const int64_t blk = b0 + (pj < nb ? pj : nb - 1);
+        const uint4* p = reinterpret_cast<const uint4*>(xr + blk * 64 + 32 * (g & 1));
+#pragma unroll
+        for (int u = 0; u < 4; ++u) xv[h][u] = p[u];
       }
-      uint32_t mx = 0;
-#pragma unroll
-      for (int j = 0; j < kMfmaSeg; ++j) {
-        const uint32_t w[8] = {xv[j][0].x, xv[j][0].y, xv[j][0].z, xv[j][0].w,
-                               xv[j][1].x, xv[j][1].y, xv[j][1].z, xv[j][1].w};
-        uint32_t mj = 0;
-#pragma unroll
-        for (int i = 0; i < 8; ++i) mj = max(mj, max(w[i] & 0x7FFF0000u, (w[i] << 16) & 0x7FFF0000u));
-        mx = j < nb ? max(mx, mj) : mx;  // clamped blocks repeat the last one
-      }
-      // largest |x| of row ln over the four lane groups
-      mx = max(mx, static_cast<uint32_t>(__shfl_xor(static_cast<int>(mx), 16, kWave)));
-      mx = max(mx, static_cast<uint32_t>(__shfl_xor(static_cast<int>(mx), 32, kWave)));
-      int k = 14 - (static_cast<int>(mx >> 23) - 127);
-      k = k < -126 ? -126 : (k > 126 ? 126 : k);
-      const float sc2 = __uint_as_float(static_cast<uint32_t>(127 + k) << 23);
-      const float xinv = __uint_as_float(static_cast<uint32_t>(127 - k) << 23);
-#pragma unroll
-      for (int j = 0; j < kMfmaSeg; ++j) {
-        const uint32_t w[8] = {xv[j][0].x, xv[j][0].y, xv[j][0].z, xv[j][0].w,
-                               xv[j][1].x, xv[j][1].y, xv[j][1].z, xv[j][1].w};
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          const float lo = __uint_as_float(w[i] << 16) * sc2;  // exact: a power of two
-          const float hi = __uint_as_float(w[i] & 0xFFFF0000u) * sc2;
-          xh[j][i] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(lo, hi));
-        }
-      }
-      // D rows held by this lane are x rows 4 g + i
-#pragma unroll
-      for (int i = 0; i < 4; ++i) xinv_d[i] = __shfl(xinv, 4 * g + i, kWave);
     }
-
     // groups in order, the loads of group gi + 1 issued before group gi is
     // multiplied (clamped to the last group, whose loads are then repeated)
     auto load_group = [&](SegItem<kDQ>& it, int64_t gi) {
       const int64_t gl = gi < kmine ? gi : (kmine > 0 ? kmine - 1 : 0);
       const int64_t grp = blockIdx.x + gl * G;
-      const int64_t rowc = grp * 16 + ln < rows ? grp * 16 + ln : rows - 1;  // past the end: never stored
+      const int64_t rowc = grp * 16 + ln < rows ? grp * 16 + ln : rows - 1;
       seg_load<kDQ, kQ4>(it, packed, nblk, rowc, b0, nb, g, sc, ngroups2);
     };
+    // per h: the lane's block scale, its 16 lookups, then 4 MFMAs whose B
+    // words are the level pairs times the scale, each rounded once to bf16
     auto mult_group = [&](const SegItem<kDQ>& it, int64_t gi) {
-      floatx4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
-      // two halves of four blocks: all lookups, then all MFMAs, then the
-      // scaling, so that the LDS and MFMA latencies overlap; blocks past the
-      // segment's end (clamped loads) get scale 0
+      floatx4 acc[2];
 #pragma unroll
-      for (int h = 0; h < kMfmaSeg; h += 4) {
-        uint32_t bw[4][8];
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-#pragma unroll
-          for (int u = 0; u < 8; ++u) {
-            // codes 16 g .. 16 g + 7 (bytes 8 g .. 8 g + 3) then 16 g + 8 .. + 15
-            const uint32_t word = u < 4 ? it.c[h + j].x : it.c[h + j].y;
-            const uint32_t addr = __builtin_amdgcn_perm(word, slot, 0x0C0C0000u | ((4u + (u & 3)) << 8));
-            bw[j][u] = *reinterpret_cast<const uint32_t*>(smem + addr);
-          }
-        floatx4 d[4];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const uint4 b0w = make_uint4(bw[j][0], bw[j][1], bw[j][2], bw[j][3]);
-          const uint4 b1w = make_uint4(bw[j][4], bw[j][5], bw[j][6], bw[j][7]);
-          const uint4 a0w = make_uint4(xh[h + j][0], xh[h + j][1], xh[h + j][2], xh[h + j][3]);
-          const uint4 a1w = make_uint4(xh[h + j][4], xh[h + j][5], xh[h + j][6], xh[h + j][7]);
-          const floatx4 zero = {0.0f, 0.0f, 0.0f, 0.0f};
-          d[j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8_t, a0w),
-                                                       __builtin_bit_cast(half8_t, b0w), zero, 0, 0, 0);
-          d[j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8_t, a1w),
-                                                       __builtin_bit_cast(half8_t, b1w), d[j], 0, 0, 0);
-        }
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          float a;
-          if constexpr (kDQ) {
-            float s2;
-            if constexpr (kQ4) s2 = (h + j) >= it.cross ? it.s2hi : it.s2lo;
-            else s2 = it.am[h + j];
-            a = (row_ratio<kF8>(it.q[h + j], rtab) * s2) + mean;  // a_hat of weight row ln
+      for (int h = 0; h < 2; ++h) {
+        const int pj = 2 * h + (g >> 1);
+        float a;
+        if constexpr (kDQ) {
+          int q;
+          float s2;
+          if constexpr (kQ4) {
+            q = static_cast<int>(static_cast<int8_t>(it.q4 >> (8 * pj)));
+            s2 = pj >= it.cross ? it.s2hi : it.s2lo;
           } else {
-            a = it.am[h + j];
+            q = it.q[h];
+            s2 = it.am[h];
           }
-          a = (h + j < nb) ? a : 0.0f;
+          a = (row_ratio<kF8>(q, rtab) * s2) + mean;
+        } else if constexpr (kQ4) {
+          a = pj == 0 ? it.a4.x : pj == 1 ? it.a4.y : pj == 2 ? it.a4.z : it.a4.w;
+        } else {
+          a = it.am[h];
+        }
+        a = pj < nb ? a : 0.0f;  // clamped loads past the segment's end
+        float2 l[4][4];
 #pragma unroll
-          for (int i = 0; i < 4; ++i) acc[i] = fmaf(d[j][i], a, acc[i]);
+        for (int u = 0; u < 4; ++u)
+#pragma unroll
+          for (int bb = 0; bb < 4; ++bb) {
+            const uint32_t word = u == 0 ? it.c[h].x : u == 1 ? it.c[h].y : u == 2 ? it.c[h].z : it.c[h].w;
+            const uint32_t addr = __builtin_amdgcn_perm(word, slot, 0x0C0C0000u | ((4u + bb) << 8));
+            l[u][bb] = *reinterpret_cast<const float2*>(smem + addr);
+          }
+        acc[h] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const uint4 bw = make_uint4(sk_bf16_pair(l[u][0].x * a, l[u][0].y * a), sk_bf16_pair(l[u][1].x * a, l[u][1].y * a),
+                                      sk_bf16_pair(l[u][2].x * a, l[u][2].y * a), sk_bf16_pair(l[u][3].x * a, l[u][3].y * a));
+          acc[h] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, xv[h][u]),
+                                                           __builtin_bit_cast(bf16x8_t, bw), acc[h], 0, 0, 0);
         }
       }
       // partial tile of (group gi, segment): element (x row 4 g + i, weight row ln)
       float* pt = part + (gi * pl.nseg + seg) * 256;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) pt[(4 * g + i) * 16 + ln] = acc[i] * xinv_d[i];
+      for (int i = 0; i < 4; ++i) pt[(4 * g + i) * 16 + ln] = acc[0][i] + acc[1][i];
     };
     SegItem<kDQ> ia, ib;
     load_group(ia, 0);
@@ -710,10 +701,10 @@ __global__ __launch_bounds__(kWaves * 64) void k_gemv_mfma(const uint8_t* __rest
     const int wn = static_cast<int>(t & 15);
     const int64_t row = (blockIdx.x + gi * G) * 16 + wn;
     if (xm >= m || row >= rows) continue;
-    float s = 0.0f;
-    for (int sg = 0; sg < pl.nseg; ++sg) s += part[(gi * pl.nseg + sg) * 256 + xm * 16 + wn];
-    if constexpr (kBf16Out) static_cast<uint16_t*>(y)[xm * rows + row] = static_cast<uint16_t>(f32_to_bf16(s));
-    else static_cast<float*>(y)[xm * rows + row] = s;
+    float sum = 0.0f;
+    for (int sg = 0; sg < pl.nseg; ++sg) sum += part[(gi * pl.nseg + sg) * 256 + xm * 16 + wn];
+    if constexpr (kBf16Out) static_cast<uint16_t*>(y)[xm * rows + row] = static_cast<uint16_t>(f32_to_bf16(sum));
+    else static_cast<float*>(y)[xm * rows + row] = sum;
   }
 }
 

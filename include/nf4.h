@@ -248,10 +248,17 @@ int nf4_dequantize(const nf4_weight* w, void* out, int out_dtype, void* stream);
  *   y : [m][rows] of y_dtype (NF4_F32 or NF4_BF16), 16-byte aligned.
  * Products are accumulated in float32; no dequantized copy of W is written
  * to memory (tool page "How it works", Step 5: the expanded copy is
- * temporary).  For m == 1 and cols <= 65536 the levels enter the products
- * rounded to fp16 (11 significant bits, relative error <= 2^-11) and x
- * exactly (scaled by a power of two per 64-block), and the block scale is
- * applied once per block in float32; otherwise the float32 levels are used. */
+ * temporary).  What enters the products depends on the path:
+ *  - m <= 2, and m <= 4 on matrices of at least 2^27 weights, with
+ *    cols <= 65536 (m == 1) or cols <= 32768 (m > 1): the levels rounded to
+ *    fp16 (11 significant bits, relative error <= 2^-11) and x exactly
+ *    (scaled by a power of two per 64-block); the block scale is applied
+ *    once per block in float32;
+ *  - any other m <= 16 with cols <= 16384 (the matrix cores): the weight
+ *    rounded once to bf16 after scaling, bf16(fl32(level * a_hat)), exactly
+ *    as nf4_gemm takes it, and x exactly;
+ *  - wider rows: the float32 levels (m > 1), or each level as a pair of bf16
+ *    parts (16 significant bits, m == 1). */
 int nf4_gemv(const nf4_weight* w, const void* x, int64_t m, void* y, int y_dtype,
              void* stream);
 

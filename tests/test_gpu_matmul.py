@@ -188,6 +188,51 @@ def test_gemv_skinny_scale_load_forms(m, dq):
     assert err <= MATMUL_RTOL, err
 
 
+def _oracle_wdeq_kind(w_f32: np.ndarray, dq, kind: str) -> np.ndarray:
+    """The oracle's bf16 dequantized weight (as float32) for a second-level
+    reading dq (None, "int8" or "fp8") and a code book kind ("nf4", "fp4")."""
+    p, a = oracle.quantize(w_f32.reshape(-1), kind=kind)
+    if dq is None:
+        bits = oracle.dequantize(p, w_f32.size, absmax=a, out="bf16", kind=kind)
+    else:
+        q, s2, mean = oracle.double_quant_f8(a) if dq == "fp8" else oracle.double_quant(a)
+        bits = oracle.dequantize(p, w_f32.size, qabsmax=q, absmax2=s2, mean=mean, out="bf16", dq_kind=dq, kind=kind)
+    return oracle.bf16_bits_to_f32(bits).reshape(w_f32.shape)
+
+
+@pytest.mark.parametrize("rows,cols,m,dq,kind", [
+    (16, 64, 16, "int8", "nf4"),      # one group, one block: a segment of 1 block
+    (33, 192, 7, "fp8", "fp4"),       # a segment of 3 blocks, ragged last group
+    (777, 1088, 16, None, "nf4"),     # 17 blocks a row: block-by-block scale loads
+    (1000, 4160, 5, "int8", "nf4"),   # 65 blocks a row, ragged rows
+    (520, 4096, 8, None, "fp4"),      # plain absmax, one 16-byte load per segment
+    (1040, 4096, 12, "int8", "fp4"),
+    (2064, 2048, 16, "fp8", "nf4"),
+])
+def test_gemv_skinny_matrix_cores_every_output(rows, cols, m, dq, kind):
+    """For 5 <= m <= 16 the product runs on the matrix cores with the weight
+    rounded once to bf16 after scaling, bf16(fl32(level * a_hat)), as the GEMM
+    expands it (so that an MFMA may span two blocks).  Every output is checked
+    against the oracle's float64 product with its bf16 dequantized weight, with
+    no weight term in the per-element bound: only the float32 sums and the
+    output rounding."""
+    say("gemv skinny matrix cores", rows, cols, "m", m, dq, kind)
+    torch = need_gpu()
+    w = syn.normal_f32((rows, cols), 0.02, 17 * rows + cols)
+    xb = syn.to_bf16(syn.normal_f32((m, cols), 1.0, 5 + m))
+    W = nf4.quantize_weight(to_dev(w), double_quant=dq is not None, dq_type=dq or "int8", quant_type=kind)
+    y32 = nf4.nf4_gemv(W, xb.to("cuda"), y_dtype=torch.float32)
+    yb = nf4.nf4_gemv(W, xb.to("cuda"))
+    torch.cuda.synchronize()
+    wdeq = _oracle_wdeq_kind(w, dq, kind)
+    xf = syn.bf16_to_f32(xb)
+    ref = oracle.matmul_ref(xf, wdeq)
+    sabs = np.abs(xf).astype(np.float64) @ np.abs(wdeq).astype(np.float64).T
+    check_full_product(_y_f64(yb), ref, sabs, terms=cols, tile=(16, 16), label="bf16 out")
+    bound = cols * 2.0 ** -24 * sabs + 1e-30
+    assert float((np.abs(_y_f64(y32) - ref) / bound).max()) <= 1.0
+
+
 def test_gemv_x_dynamic_range():
     """x spanning 2^-60 .. 2^60 within and across blocks, and an all-zero
     block: the per-block power-of-two scaling of x keeps the decode GEMV
