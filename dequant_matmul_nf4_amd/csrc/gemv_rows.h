@@ -27,12 +27,21 @@ __device__ __forceinline__ float wave_sum_to_last(float v) {
   return v;
 }
 
+// A workgroup barrier for LDS data only: this wave's LDS accesses complete,
+// then s_barrier.  __syncthreads() also waits for every global load in flight
+// (its workgroup-scope fence), which would drain the rows a kernel requested
+// before building its tables.  The memory clobber keeps the compiler from
+// moving memory accesses across it.
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
 // 256 fp16 level pairs (element 2j = high nibble in the low half), one copy
 // per lane slot: entry e occupies 64 consecutive words.  Each thread builds the
 // pair of entry threadIdx % 256 in registers and writes its share of the 64
 // copies with 16-byte stores, starting at a chunk rotated by the entry so that
-// 16 consecutive lanes cover every bank.  Ends with a barrier.
-template <int kThreads>
+// 16 consecutive lanes cover every bank.  Ends with a barrier: __syncthreads,
+// or with kLdsBarrier the LDS-only barrier above, which leaves the caller's
+// global loads in flight.
+template <int kThreads, bool kLdsBarrier = false>
 __device__ __forceinline__ void fill_half_table(uint32_t* tab, const Codebook& cb) {
   static_assert(kThreads % 256 == 0 && kThreads <= 1024, "whole entries per pass");
   constexpr int kParts = kThreads / 256;
@@ -52,7 +61,8 @@ __device__ __forceinline__ void fill_half_table(uint32_t* tab, const Codebook& c
     const int c = (j * kParts + p + e) & 15;
     *reinterpret_cast<uint4*>(tab + e * 64 + 4 * c) = v4;
   }
-  __syncthreads();
+  if constexpr (kLdsBarrier) lds_barrier();
+  else __syncthreads();
 }
 
 struct RowItem {

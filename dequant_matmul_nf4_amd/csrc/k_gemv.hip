@@ -363,14 +363,11 @@ __global__ __launch_bounds__(kWaves * 64) void k_gemv_rows(const uint8_t* packed
   const int64_t row0 = gp < rows ? gp : rows - 1;
   const int64_t last = n > 0 ? row0 + (n - 1) * np : row0;  // loads are clamped to it
 
-  // the first U rows, x of the lane's pieces (MC rows), then the table
+  // x of the lane's pieces (MC rows), the first U rows, then the tables.  x
+  // goes first: its conversion, which the compiler may place before the
+  // tables' barrier, then waits for x alone, and the barrier waits for LDS
+  // only, so the rows stay in flight while the tables are built.
   constexpr int S = U + 1;  // ring slots: U rows in flight plus the one in use
-  RowItem it[S];
-#pragma unroll
-  for (int u = 0; u < U; ++u) {
-    const int64_t r = row0 + u * np;
-    row_load<kDQ>(it[u], packed, (r < last ? r : last) * nblk, lo, sc);
-  }
   uint4 xv[MC][2][4];
 #pragma unroll
   for (int c = 0; c < MC; ++c)
@@ -380,8 +377,14 @@ __global__ __launch_bounds__(kWaves * 64) void k_gemv_rows(const uint8_t* packed
 #pragma unroll
       for (int i = 0; i < 4; ++i) xv[c][j][i] = xp[i];
     }
+  RowItem it[S];
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const int64_t r = row0 + u * np;
+    row_load<kDQ>(it[u], packed, (r < last ? r : last) * nblk, lo, sc);
+  }
   if constexpr (kDQ) fill_ratio_table<kF8>(rtab, kWaves * 64);
-  fill_half_table<kWaves * 64>(tab, cb);  // ends with a barrier
+  fill_half_table<kWaves * 64, true>(tab, cb);  // ends with the LDS-only barrier
 
   uint32_t xh[MC][2][16];
   float xinv[MC][2];
