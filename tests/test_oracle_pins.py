@@ -277,7 +277,6 @@ def test_mean_is_the_correctly_rounded_exact_mean():
             a[:10] = np.float32(1e-30)     # wide dynamic range: naive sums lose bits
             a[10] = np.float32(3e4)
         exact = sum((Fraction(float(v)) for v in a), Fraction(0))
-        want = rn32(Fraction(rn64(exact)) / a.size)
         want = rn32(Fraction(rn64(Fraction(rn64(exact)) / a.size)))
         assert oracle.exact_mean_f32(a) == want
 
