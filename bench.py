@@ -868,6 +868,49 @@ def leg_gemv_decode(torch, nf4, syn, dev, stream, EventTimer, g):
     return res
 
 
+def gemv_mlp_batched(torch, nf4, dev, stream, EventTimer, g, reps=10, triples=6):
+    """The Llama-8B MLP decode step at m = 1 as a caller would issue it: gate
+    and up (which share x) in one nf4_gemv_batched launch, then down; six
+    distinct weight triples per pass, as the single-call leg."""
+    shapes = [(14336, 4096), (14336, 4096), (4096, 14336)]
+    Wt = []
+    for t in range(triples):
+        ws = []
+        for i, (r_, c_) in enumerate(shapes):
+            g.manual_seed(9_000 + 3 * t + i)
+            w = (torch.randn((r_, c_), generator=g, device=dev) * 0.02).to(torch.bfloat16)
+            ws.append(nf4.quantize_weight(w, double_quant=True))
+            del w
+        Wt.append(ws)
+    x_in = torch.randn((1, 4096), generator=g, device=dev).to(torch.bfloat16)
+    x_h = torch.randn((1, 14336), generator=g, device=dev).to(torch.bfloat16)
+    ys = [[torch.empty((1, r_), dtype=torch.bfloat16, device=dev) for r_, _ in shapes] for _ in range(triples)]
+
+    def run():
+        for ws, yy in zip(Wt, ys):
+            nf4.nf4_gemv_batched(ws[:2], [x_in, x_in], yy[:2])
+            nf4.nf4_gemv(ws[2], x_h, yy[2])
+
+    run()
+    torch.cuda.synchronize()
+    graph = capture_graph(torch, run)
+    graph.replay()
+    torch.cuda.synchronize()
+    t = EventTimer(torch, stream)
+    s = t.start()
+    for _ in range(reps):
+        graph.replay()
+    t.stop(s)
+    torch.cuda.synchronize()
+    total_us = t.mean_us() / reps
+    nbytes = triples * sum(step_bytes(r_, c_)["gemv"] for r_, c_ in shapes)
+    del Wt
+    return {"workload": "Llama-8B MLP at m=1, 6 distinct triples (545 MB) per pass: gate and up in one nf4_gemv_batched "
+                        "launch (they share x), then down", "m": 1, "us_per_pass": round(total_us, 2),
+            "GBps": round(nbytes / (total_us * 1e-6) / 1e9, 1),
+            "frac_hbm_peak": round(nbytes / (total_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}
+
+
 def legs_gemv_pools(torch, nf4, dev, stream, EventTimer, g, only=None):
     """Larger decode GEMVs: the Llama-8B MLP (M = 1, 4, 16) and one 70B-shaped layer."""
     res = {}
@@ -911,6 +954,7 @@ def legs_gemv_pools(torch, nf4, dev, stream, EventTimer, g, only=None):
         res["gemv_mlp_8b"] = gemv_pool(mlp, 10, label + ", M=1")
         res["gemv_mlp_8b_m4"] = gemv_pool(mlp, 10, label + ", M=4", m=4)
         res["gemv_mlp_8b_m16"] = gemv_pool(mlp, 10, label + ", M=16", m=16)
+        res["gemv_mlp_8b_batched"] = gemv_mlp_batched(torch, nf4, dev, stream, EventTimer, g, reps=10)
     if only in (None, "gemv-70b"):
         layer = [(8192, 8192), (1024, 8192), (1024, 8192), (8192, 8192), (28672, 8192), (28672, 8192),
                  (8192, 28672)]
