@@ -961,6 +961,7 @@ def legs_gemv_pools(torch, nf4, dev, stream, EventTimer, g, only=None):
         res["gemv_layer_70b"] = gemv_pool(layer, 10, "70B-shaped layer q,k,v,o,gate,up,down NF4+DQ, M=1 (442 MB)")
         res["gemv_layer_70b_fp8_scales"] = gemv_pool(
             layer, 10, "the same layer with float8 (E4M3) second-level scales, M=1", dq_type="fp8")
+        res["gemv_layer_70b_m16"] = gemv_pool(layer, 10, "the same layer at M=16 (seven nf4_gemv calls)", m=16)
         res["double_quant_70b_gate"] = leg_dq_kinds(torch, nf4, dev, stream, EventTimer, g)
     return res
 

@@ -491,7 +491,10 @@ hipError_t launch_rows_sc(const uint8_t* packed, int64_t rows, int64_t cols, Sca
 //  - Weight rows go in groups of 16, interleaved over the grid (group p of a
 //    workgroup is p-th of its share); waves walk the workgroup's groups for
 //    each of their segments and park each (group, segment) partial tile in
-//    LDS; the segments are added in a fixed order at the end.
+//    LDS; the segments are added in a fixed order at the end.  Where those
+//    tiles do not fit (wide rows: more than 64 per workgroup), each wave adds
+//    its segments, in order, into one tile per (group, wave) instead, and the
+//    16 waves' tiles are added in a fixed order at the end.
 // First factor of a_hat: q / 127 for int8 codes, the E4M3 ratio table (copied
 // to LDS) for float8 codes.
 template <bool kF8>
@@ -503,6 +506,7 @@ __device__ __forceinline__ float row_ratio(int q, const float* rtab) {
 constexpr int kPartTiles = 64;   // 16 x 16 float partial tiles per workgroup (64 KiB)
 constexpr int kMfmaSeg = 4;      // blocks per column segment (x kept in registers)
 constexpr int kMfmaWaves = 16;
+constexpr int kMfmaMaxGroups = kPartTiles / kMfmaWaves;  // row groups per workgroup with (group, wave) tiles
 
 typedef float floatx4 __attribute__((ext_vector_type(4)));
 
@@ -511,6 +515,7 @@ struct MfmaPlan {
   int nseg;          // column segments
   int seg_blocks;    // blocks per segment (<= kMfmaSeg)
   int kmax;          // row groups per workgroup, at most
+  int accum;         // tiles per (group, wave), summed over the wave's segments (else per (group, segment))
 };
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
@@ -573,7 +578,7 @@ __device__ __forceinline__ void seg_load(SegItem<kDQ>& it, const uint8_t* __rest
   }
 }
 
-template <int kWaves, bool kDQ, bool kF8, bool kQ4, bool kBf16Out>
+template <int kWaves, bool kDQ, bool kF8, bool kQ4, bool kBf16Out, bool kAccum>
 __global__ __launch_bounds__(kWaves * 64) void k_gemv_mfma(const uint8_t* __restrict__ packed, int64_t rows,
                                                            int64_t cols, Scales sc, const uint16_t* __restrict__ x,
                                                            int m, void* __restrict__ y, Codebook cb, MfmaPlan pl) {
@@ -610,6 +615,10 @@ __global__ __launch_bounds__(kWaves * 64) void k_gemv_mfma(const uint8_t* __rest
 #pragma unroll
     for (int j = 0; j < 32 / kParts; ++j) tab[e * 32 + ((j * kParts + pp + e) & 31)] = v;
   }
+  // (group, wave) tiles start at zero: a wave adds each of its segments
+  if constexpr (kAccum)
+    for (int i = threadIdx.x; i < kPartTiles * 64; i += kWaves * 64)
+      reinterpret_cast<float4*>(part)[i] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
   __syncthreads();
 
   for (int seg = wave; seg < pl.nseg; seg += kWaves) {
@@ -682,10 +691,22 @@ __global__ __launch_bounds__(kWaves * 64) void k_gemv_mfma(const uint8_t* __rest
                                                            __builtin_bit_cast(bf16x8_t, bw), acc[h], 0, 0, 0);
         }
       }
-      // partial tile of (group gi, segment): element (x row 4 g + i, weight row ln)
-      float* pt = part + (gi * pl.nseg + seg) * 256;
+      if constexpr (kAccum) {
+        // tile of (group gi, wave): element (x row 4 g + i, weight row ln) at
+        // ln * 16 + 4 g + i, so that a lane's four values are one 16-byte word
+        float4* pt = reinterpret_cast<float4*>(part + (gi * kWaves + wave) * 256 + ln * 16 + 4 * g);
+        float4 t = *pt;
+        t.x += acc[0][0] + acc[1][0];
+        t.y += acc[0][1] + acc[1][1];
+        t.z += acc[0][2] + acc[1][2];
+        t.w += acc[0][3] + acc[1][3];
+        *pt = t;
+      } else {
+        // tile of (group gi, segment): element (x row 4 g + i, weight row ln)
+        float* pt = part + (gi * pl.nseg + seg) * 256;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) pt[(4 * g + i) * 16 + ln] = acc[0][i] + acc[1][i];
+        for (int i = 0; i < 4; ++i) pt[(4 * g + i) * 16 + ln] = acc[0][i] + acc[1][i];
+      }
     };
     SegItem<kDQ> ia, ib;
     load_group(ia, 0);
@@ -698,21 +719,55 @@ __global__ __launch_bounds__(kWaves * 64) void k_gemv_mfma(const uint8_t* __rest
     }
   }
   __syncthreads();
-  for (int64_t t = threadIdx.x; t < kmine * 256; t += blockDim.x) {
-    const int64_t gi = t >> 8;
-    const int xm = static_cast<int>((t >> 4) & 15);
-    const int wn = static_cast<int>(t & 15);
-    const int64_t row = (blockIdx.x + gi * G) * 16 + wn;
-    if (xm >= m || row >= rows) continue;
-    float sum = 0.0f;
-    for (int sg = 0; sg < pl.nseg; ++sg) sum += part[(gi * pl.nseg + sg) * 256 + xm * 16 + wn];
-    if constexpr (kBf16Out) static_cast<uint16_t*>(y)[xm * rows + row] = static_cast<uint16_t>(f32_to_bf16(sum));
-    else static_cast<float*>(y)[xm * rows + row] = sum;
+  if constexpr (kAccum) {
+    // each thread adds one 16-byte word (x rows 4 q .. 4 q + 3 of weight
+    // row wn) over the 16 waves' tiles in order: consecutive threads read
+    // consecutive words
+    const float4* part4 = reinterpret_cast<const float4*>(part);
+    for (int64_t t = threadIdx.x; t < kmine * 64; t += blockDim.x) {
+      const int64_t gi = t >> 6;
+      const int wn = static_cast<int>((t >> 2) & 15);
+      const int q = static_cast<int>(t & 3);
+      const int64_t row = (blockIdx.x + gi * G) * 16 + wn;
+      if (4 * q >= m || row >= rows) continue;
+      float4 sum = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+      const float4* src = part4 + gi * kWaves * 64 + wn * 4 + q;
+#pragma unroll
+      for (int w = 0; w < kWaves; ++w) {
+        const float4 v = src[w * 64];
+        sum.x += v.x;
+        sum.y += v.y;
+        sum.z += v.z;
+        sum.w += v.w;
+      }
+      const float r[4] = {sum.x, sum.y, sum.z, sum.w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int xm = 4 * q + i;
+        if (xm >= m) continue;
+        if constexpr (kBf16Out) static_cast<uint16_t*>(y)[xm * rows + row] = static_cast<uint16_t>(f32_to_bf16(r[i]));
+        else static_cast<float*>(y)[xm * rows + row] = r[i];
+      }
+    }
+  } else {
+    for (int64_t t = threadIdx.x; t < kmine * 256; t += blockDim.x) {
+      const int64_t gi = t >> 8;
+      const int xm = static_cast<int>((t >> 4) & 15);
+      const int wn = static_cast<int>(t & 15);
+      const int64_t row = (blockIdx.x + gi * G) * 16 + wn;
+      if (xm >= m || row >= rows) continue;
+      float sum = 0.0f;
+      for (int sg = 0; sg < pl.nseg; ++sg) sum += part[(gi * pl.nseg + sg) * 256 + xm * 16 + wn];
+      if constexpr (kBf16Out) static_cast<uint16_t*>(y)[xm * rows + row] = static_cast<uint16_t>(f32_to_bf16(sum));
+      else static_cast<float*>(y)[xm * rows + row] = sum;
+    }
   }
 }
 
-// Plan: segments of at most kMfmaSeg blocks (balanced); grid of at least one
-// workgroup per CU, grown until each workgroup's (group, segment) tiles fit.
+// Plan: segments of at most kMfmaSeg blocks (balanced); grid of one
+// workgroup per CU (fewer for few groups).  If a workgroup's (group, segment)
+// tiles do not fit, the kernel keeps (group, wave) tiles instead and the grid
+// grows until a workgroup has at most kMfmaMaxGroups groups.
 MfmaPlan mfma_plan(int64_t rows, int64_t cols) {
   const int64_t cus = device_cus();
   const int64_t nblk = cols / 64;
@@ -721,17 +776,40 @@ MfmaPlan mfma_plan(int64_t rows, int64_t cols) {
   pl.seg_blocks = static_cast<int>((nblk + pl.nseg - 1) / pl.nseg);
   const int64_t ngroups = (rows + 15) / 16;
   int64_t g = cus < ngroups ? cus : ngroups;
-  while (((ngroups + g - 1) / g) * pl.nseg > kPartTiles) ++g;
+  pl.accum = ((ngroups + g - 1) / g) * pl.nseg > kPartTiles ? 1 : 0;
+  if (pl.accum)
+    while ((ngroups + g - 1) / g > kMfmaMaxGroups) ++g;
   pl.grid = static_cast<int>(g);
   pl.kmax = static_cast<int>((ngroups + g - 1) / g);
   return pl;
+}
+
+// One launch of the skinny kernel with the plan's tiles (kAccum: one per
+// (group, wave)) and the scale arrays' load form (kQ4).
+template <bool kDQ, bool kAccum>
+void launch_mfma_tiles(const uint8_t* packed, int64_t rows, int64_t cols, Scales sc, const uint16_t* x, int mi,
+                       void* y, int y_bf16, const Codebook& cb, const MfmaPlan& pl, bool q4, dim3 gd, dim3 bd,
+                       hipStream_t s) {
+#define NF4_MFMA(Q4, BF) \
+  do { \
+    if (sc.f8) hipLaunchKernelGGL((k_gemv_mfma<kMfmaWaves, kDQ, kDQ, Q4, BF, kAccum>), gd, bd, 0, s, packed, rows, cols, \
+                                  sc, x, mi, y, cb, pl); \
+    else hipLaunchKernelGGL((k_gemv_mfma<kMfmaWaves, kDQ, false, Q4, BF, kAccum>), gd, bd, 0, s, packed, rows, cols, sc, \
+                            x, mi, y, cb, pl); \
+  } while (0)
+  if (q4) {
+    if (y_bf16) NF4_MFMA(true, true); else NF4_MFMA(true, false);
+  } else {
+    if (y_bf16) NF4_MFMA(false, true); else NF4_MFMA(false, false);
+  }
+#undef NF4_MFMA
 }
 
 template <bool kDQ>
 hipError_t launch_mfma(const uint8_t* packed, int64_t rows, int64_t cols, Scales sc, const uint16_t* x, int64_t m,
                        void* y, int y_bf16, hipStream_t s) {
   const MfmaPlan pl = mfma_plan(rows, cols);
-  if (pl.nseg > kPartTiles) return hipErrorInvalidValue;
+  if (pl.accum ? pl.kmax > kMfmaMaxGroups : pl.kmax * pl.nseg > kPartTiles) return hipErrorInvalidValue;
   const Codebook& cb = codebook(sc.fp4);
   const dim3 gd(static_cast<unsigned>(pl.grid)), bd(64 * kMfmaWaves);
   const int mi = static_cast<int>(m);
@@ -739,21 +817,8 @@ hipError_t launch_mfma(const uint8_t* packed, int64_t rows, int64_t cols, Scales
   // arrays aligned for one 4-byte (int8 codes) or 16-byte (absmax) load
   const uintptr_t sa = kDQ ? reinterpret_cast<uintptr_t>(sc.q) : reinterpret_cast<uintptr_t>(sc.absmax);
   const bool q4 = pl.seg_blocks == kMfmaSeg && (cols / 64) % kMfmaSeg == 0 && (sa & (kDQ ? 3u : 15u)) == 0;
-  if (q4) {
-    if (y_bf16)
-      { if (sc.f8) hipLaunchKernelGGL((k_gemv_mfma<kMfmaWaves, kDQ, kDQ, true, true>), gd, bd, 0, s, packed, rows, cols, sc, x, mi, y, cb, pl);
-      else hipLaunchKernelGGL((k_gemv_mfma<kMfmaWaves, kDQ, false, true, true>), gd, bd, 0, s, packed, rows, cols, sc, x, mi, y, cb, pl); }
-    else
-      { if (sc.f8) hipLaunchKernelGGL((k_gemv_mfma<kMfmaWaves, kDQ, kDQ, true, false>), gd, bd, 0, s, packed, rows, cols, sc, x, mi, y, cb, pl);
-      else hipLaunchKernelGGL((k_gemv_mfma<kMfmaWaves, kDQ, false, true, false>), gd, bd, 0, s, packed, rows, cols, sc, x, mi, y, cb, pl); }
-  } else {
-    if (y_bf16)
-      { if (sc.f8) hipLaunchKernelGGL((k_gemv_mfma<kMfmaWaves, kDQ, kDQ, false, true>), gd, bd, 0, s, packed, rows, cols, sc, x, mi, y, cb, pl);
-      else hipLaunchKernelGGL((k_gemv_mfma<kMfmaWaves, kDQ, false, false, true>), gd, bd, 0, s, packed, rows, cols, sc, x, mi, y, cb, pl); }
-    else
-      { if (sc.f8) hipLaunchKernelGGL((k_gemv_mfma<kMfmaWaves, kDQ, kDQ, false, false>), gd, bd, 0, s, packed, rows, cols, sc, x, mi, y, cb, pl);
-      else hipLaunchKernelGGL((k_gemv_mfma<kMfmaWaves, kDQ, false, false, false>), gd, bd, 0, s, packed, rows, cols, sc, x, mi, y, cb, pl); }
-  }
+  if (pl.accum) launch_mfma_tiles<kDQ, true>(packed, rows, cols, sc, x, mi, y, y_bf16, cb, pl, q4, gd, bd, s);
+  else launch_mfma_tiles<kDQ, false>(packed, rows, cols, sc, x, mi, y, y_bf16, cb, pl, q4, gd, bd, s);
   return hipGetLastError();
 }
 
@@ -827,23 +892,21 @@ hipError_t launch_gemv(const uint8_t* packed, int64_t rows, int64_t cols, Scales
       else launch_m1<2, true>(packed, rows, cols, sc, x, y, y_bf16, 16, s);
     }
   } else {
-    // m = 2 (and m <= 4 on large matrices): the streaming kernel with the x
-    // rows sharing each lookup, which measured faster there than the matrix
-    // cores (e.g. 28672x8192: 35 against 78 us at m = 2, 55 against 80 us at
-    // m = 4; at m = 4 on 14336x4096 and at m >= 8 the matrix cores win).
-    // Otherwise skinny products on the matrix cores; wider rows in passes of
-    // up to 4 rows of x on the vector ALUs (8 waves, so nseg <= 8)
+    // m = 2 (and m <= 4 on matrices of at least 2^27 weights): the streaming
+    // kernel with the x rows sharing each lookup, which measured faster there
+    // than the matrix cores (e.g. 28672x8192: 31 against 59 us at m = 2, 46
+    // against 63 us at m = 4; 14336x4096 at m = 4: 17.8 against 15.0 us).
+    // Rows wider than 32768 columns there take the per-row-group kernel.
+    // Every other skinny product runs on the matrix cores.
     const bool rows_first = m <= 2 || (m <= 4 && rows * cols >= (int64_t{1} << 27));
-    if (rows_first && (cols / 64 + 63) / 64 <= 8) return launch_rows_multi(packed, rows, cols, sc, x, m, y, y_bf16, s);
-    if (mfma_plan(rows, cols).nseg <= kPartTiles) {
-      return sc.absmax ? launch_mfma<false>(packed, rows, cols, sc, x, m, y, y_bf16, s)
-                       : launch_mfma<true>(packed, rows, cols, sc, x, m, y, y_bf16, s);
+    if (rows_first) {
+      if ((cols / 64 + 63) / 64 <= 8) return launch_rows_multi(packed, rows, cols, sc, x, m, y, y_bf16, s);
+      if (y_bf16) hipLaunchKernelGGL((k_gemv<4, true>), grid, dim3(256), 0, s, packed, rows, cols, sc, x, mm, y, cb);
+      else hipLaunchKernelGGL((k_gemv<4, false>), grid, dim3(256), 0, s, packed, rows, cols, sc, x, mm, y, cb);
+      return hipGetLastError();
     }
-    if ((cols / 64 + 63) / 64 <= 8) {
-      return launch_rows_multi(packed, rows, cols, sc, x, m, y, y_bf16, s);
-    }
-    if (y_bf16) hipLaunchKernelGGL((k_gemv<4, true>), grid, dim3(256), 0, s, packed, rows, cols, sc, x, mm, y, cb);
-    else hipLaunchKernelGGL((k_gemv<4, false>), grid, dim3(256), 0, s, packed, rows, cols, sc, x, mm, y, cb);
+    return sc.absmax ? launch_mfma<false>(packed, rows, cols, sc, x, m, y, y_bf16, s)
+                     : launch_mfma<true>(packed, rows, cols, sc, x, m, y, y_bf16, s);
   }
   return hipGetLastError();
 }

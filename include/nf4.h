@@ -253,12 +253,11 @@ int nf4_dequantize(const nf4_weight* w, void* out, int out_dtype, void* stream);
  *    cols <= 65536 (m == 1) or cols <= 32768 (m > 1): the levels rounded to
  *    fp16 (11 significant bits, relative error <= 2^-11) and x exactly
  *    (scaled by a power of two per 64-block); the block scale is applied
- *    once per block in float32;
- *  - any other m <= 16 with cols <= 16384 (the matrix cores): the weight
- *    rounded once to bf16 after scaling, bf16(fl32(level * a_hat)), exactly
- *    as nf4_gemm takes it, and x exactly;
- *  - wider rows: the float32 levels (m > 1), or each level as a pair of bf16
- *    parts (16 significant bits, m == 1). */
+ *    once per block in float32; wider rows take the float32 levels (m > 1),
+ *    or each level as a pair of bf16 parts (16 significant bits, m == 1);
+ *  - any other m <= 16 (the matrix cores): the weight rounded once to bf16
+ *    after scaling, bf16(fl32(level * a_hat)), exactly as nf4_gemm takes it,
+ *    and x exactly. */
 int nf4_gemv(const nf4_weight* w, const void* x, int64_t m, void* y, int y_dtype,
              void* stream);
 

@@ -208,6 +208,11 @@ def _oracle_wdeq_kind(w_f32: np.ndarray, dq, kind: str) -> np.ndarray:
     (520, 4096, 8, None, "fp4"),      # plain absmax, one 16-byte load per segment
     (1040, 4096, 12, "int8", "fp4"),
     (2064, 2048, 16, "fp8", "nf4"),
+    # rows wider than 64 segments of 4 blocks: tiles per (row group, wave),
+    # summed over each wave's segments
+    (40, 16448, 7, None, "fp4"),
+    (33, 20480, 5, "fp8", "nf4"),
+    (520, 24576, 16, "int8", "nf4"),
 ])
 def test_gemv_skinny_matrix_cores_every_output(rows, cols, m, dq, kind):
     """For 5 <= m <= 16 the product runs on the matrix cores with the weight
@@ -231,6 +236,33 @@ def test_gemv_skinny_matrix_cores_every_output(rows, cols, m, dq, kind):
     check_full_product(_y_f64(yb), ref, sabs, terms=cols, tile=(16, 16), label="bf16 out")
     bound = cols * 2.0 ** -24 * sabs + 1e-30
     assert float((np.abs(_y_f64(y32) - ref) / bound).max()) <= 1.0
+
+
+@pytest.mark.parametrize("m", [8, 16])
+def test_gemv_skinny_wide_rows_several_groups(m):
+    """8192 x 16448 (65 segments of 4 blocks a row) on the matrix cores: the
+    kernel keeps a tile per (row group, wave) and a workgroup takes two row
+    groups.  Sampled rows (the first, the last and 128 random ones) against
+    the oracle's bf16 dequantized weight, with no weight term in the bound."""
+    say("gemv skinny wide rows", m)
+    torch = need_gpu()
+    rows, cols = 8192, 16448
+    w = syn.normal_f32((rows, cols), 0.02, 41 + m)
+    x = syn.to_bf16(syn.normal_f32((m, cols), 1.0, 42))
+    W = nf4.quantize_weight(to_dev(w), double_quant=True)
+    y = nf4.nf4_gemv(W, x.to("cuda"), y_dtype=torch.float32)
+    yb = nf4.nf4_gemv(W, x.to("cuda"))
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(43)
+    sel = np.unique(np.concatenate([[0, rows - 1], rng.choice(rows, 128, replace=False)]))
+    absmax_all = oracle.block_absmax(w.reshape(-1))
+    wdeq = oracle_rows_dequant_bf16(w[sel], sel, cols, absmax_all, True)
+    xf = syn.bf16_to_f32(x)
+    ref = oracle.matmul_ref(xf, wdeq)
+    sabs = np.abs(xf).astype(np.float64) @ np.abs(wdeq).astype(np.float64).T
+    check_full_product(_y_f64(yb)[:, sel], ref, sabs, terms=cols, tile=(16, 16), label="bf16 out")
+    bound = cols * 2.0 ** -24 * sabs + 1e-30
+    assert float((np.abs(_y_f64(y)[:, sel] - ref) / bound).max()) <= 1.0
 
 
 def test_gemv_x_dynamic_range():
@@ -258,8 +290,9 @@ def test_gemv_x_dynamic_range():
 
 @pytest.mark.parametrize("rows,cols,m", [(7, 65600, 1), (40, 131072, 1), (9, 32832, 3), (20, 40960, 16)])
 def test_gemv_wider_than_16_segments(rows, cols, m):
-    """Rows longer than 16 x 64 blocks (m = 1) or 8 x 64 blocks (m > 1) take
-    the per-row-group kernels."""
+    """Rows longer than 16 x 64 blocks at m = 1 take the per-row-group kernel;
+    at m > 1 these shapes run on the matrix cores with a tile per (row group,
+    wave)."""
     say("gemv wide", rows, cols, "m", m)
     torch = need_gpu()
     w = syn.normal_f32((rows, cols), 0.02, 61)
