@@ -180,6 +180,20 @@ def _alloc_on(stream, *shape_dtype_device):
     return t
 
 
+def _as_rows(t, n: int, stream=None):
+    """t as a [-, n] matrix.  A non-contiguous t is copied by reshape; that
+    copy is a tensor of the binding's own, read by work queued on `stream`,
+    so it is recorded there like the buffers _alloc_on makes (else the
+    caching allocator could reuse its memory while the kernel still reads
+    it)."""
+    torch = _torch()
+    t2 = t.reshape(-1, n)
+    if (stream is not None and t2.is_cuda and t2.untyped_storage().data_ptr() != t.untyped_storage().data_ptr()
+            and stream != torch.cuda.current_stream(t2.device)):
+        t2.record_stream(stream)
+    return t2
+
+
 def _ptr(t) -> Optional[int]:
     return None if t is None else int(t.data_ptr())
 
@@ -474,7 +488,7 @@ def nf4_dequantize(w: NF4Weight, out=None, out_dtype=None, stream=None):
 def nf4_gemv(w: NF4Weight, x, y=None, y_dtype=None, stream=None):
     """y = x . deq(W)^T for x bf16 [m, cols] with 1 <= m <= 16."""
     torch = _torch()
-    x2 = x.reshape(-1, w.cols)
+    x2 = _as_rows(x, w.cols, stream)
     _need_cuda(x2)
     if x2.dtype != torch.bfloat16:
         raise TypeError("x must be bf16")
@@ -519,7 +533,7 @@ def nf4_gemm(w: NF4Weight, x, y=None, lora_a=None, lora_b=None, lora_scale: floa
              workspace=None, stream=None):
     """y = x . deq(W)^T + lora_scale . (x . A^T) . B^T, bf16 in and out."""
     torch = _torch()
-    x2 = x.reshape(-1, w.cols)
+    x2 = _as_rows(x, w.cols, stream)
     _need_cuda(x2, lora_a, lora_b)
     m = x2.shape[0]
     r = 0 if lora_a is None else lora_a.shape[0]
@@ -549,7 +563,7 @@ def nf4_gemm_dx(w: NF4Weight, dy, dx=None, lora_a=None, lora_b=None, lora_scale:
                 workspace=None, stream=None):
     """dx = dy . deq(W) + lora_scale . (dy . B) . A, bf16 in and out."""
     torch = _torch()
-    dy2 = dy.reshape(-1, w.rows)
+    dy2 = _as_rows(dy, w.rows, stream)
     _need_cuda(dy2, lora_a, lora_b)
     m = dy2.shape[0]
     r = 0 if lora_a is None else lora_a.shape[0]
@@ -582,8 +596,8 @@ def nf4_lora_grads(x, dy, lora_a, lora_b, lora_scale: float, da=None, db=None, w
     torch = _torch()
     r, cols = lora_a.shape
     rows = lora_b.shape[0]
-    x2 = x.reshape(-1, cols)
-    dy2 = dy.reshape(-1, rows)
+    x2 = _as_rows(x, cols, stream)
+    dy2 = _as_rows(dy, rows, stream)
     _need_cuda(x2, dy2, lora_a, lora_b)
     m = x2.shape[0]
     if dy2.shape[0] != m or tuple(lora_b.shape) != (rows, r):

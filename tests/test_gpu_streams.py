@@ -62,3 +62,42 @@ def test_side_stream_calls_keep_their_buffers():
     del junk
     for i, (g, e) in enumerate(zip(got, ref)):
         assert torch.equal(g.view(torch.uint8), e.view(torch.uint8)), i
+
+
+def test_side_stream_calls_with_strided_inputs():
+    """Activations whose leading dimensions do not merge (a [seq, batch,
+    hidden] view of a [batch, seq, hidden] tensor): the binding's reshape to
+    rows copies them into contiguous tensors of its own, which must live
+    until the side stream has read them."""
+    torch = need_gpu()
+    rows, cols, r = 1024, 2048, 16
+    seq, batch = 12, 4  # m = 48 rows; the GEMV takes the first 4 x 4
+    say("side stream, non-mergeable activations", rows, cols, seq * batch, r)
+    w = to_dev(syn.normal_f32((rows, cols), 0.02, 311)).to(torch.bfloat16)
+    W = nf4.quantize_weight(w, double_quant=True)
+    xb = syn.to_bf16(syn.normal_f32((batch * seq, cols), 1.0, 312)).to("cuda").view(batch, seq, cols)
+    dyb = syn.to_bf16(syn.normal_f32((batch * seq, rows), 1.0, 313)).to("cuda").view(batch, seq, rows)
+    xs, dys = xb.transpose(0, 1), dyb.transpose(0, 1)  # [seq, batch, .]
+    assert xs.reshape(-1, cols).data_ptr() != xs.data_ptr()  # reshape must copy
+    a = syn.to_bf16(syn.normal_f32((r, cols), 0.01, 314)).to("cuda")
+    b = syn.to_bf16(syn.normal_f32((rows, r), 0.01, 315)).to("cuda")
+
+    def run(x, dy, stream):
+        y16 = nf4.nf4_gemv(W, x[:4], stream=stream)
+        ym = nf4.nf4_gemm(W, x, lora_a=a, lora_b=b, lora_scale=2.0, stream=stream)
+        dx = nf4.nf4_gemm_dx(W, dy, lora_a=a, lora_b=b, lora_scale=2.0, stream=stream)
+        da, db = nf4.nf4_lora_grads(x, dy, a, b, 2.0, stream=stream)
+        return [y16, ym, dx, da, db]
+
+    torch.cuda.synchronize()
+    ref = run(xs.contiguous(), dys.contiguous(), None)
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()  # default priority
+    side.wait_stream(torch.cuda.current_stream())
+    got = run(xs, dys, side)
+    junk = _scribble(torch, [xs.contiguous(), dys.contiguous()] + got)
+    side.synchronize()
+    torch.cuda.synchronize()
+    del junk
+    for i, (g, e) in enumerate(zip(got, ref)):
+        assert torch.equal(g.view(torch.uint8), e.view(torch.uint8)), i
